@@ -1,0 +1,40 @@
+"""CPU oracle for CacheBlend's per-layer KV fusion step (selective KV recompute).
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the tests, the smoke check in
+__graft_entry__ and the benchmark's CPU-baseline leg may import or run anything
+in this package.  The HIP library never calls it and shares no code with it.
+
+Everything here is plain NumPy in float64, written step by step from the pages:
+
+* CacheBlend explainer (0h-n0.github.io), sections "HKVD token selection"
+  (the KV deviation equation), "Gradual filtering", "Position encoding update"
+  (K_new = R(dp) K_cached) and "Pipelined design" (T_recompute / T_load);
+* the CacheBlend review (jaehun.me), section on the per-layer flow of the
+  selected tokens (fresh Q/K/V for selected rows, cached K/V for the rest,
+  selected queries attend causally to all available K/V, output to the next
+  layer).
+
+Where the pages are silent the oracle takes the plainest reading; each such
+reading is named in the function that takes it.
+
+Parity status per function (what pins each one, see tests/test_oracle_*.py):
+  rope_* ............ closed-form rotation algebra, complex-multiplication identity
+  rmsnorm, project,
+  attention, mlp .... Hugging Face Llama forward in float32 (library routine),
+                      torch scaled_dot_product_attention on CPU, brute-force softmax
+  topk_select ....... exhaustive brute force with forced ties
+  blend_layer,
+  blended_prefill ... special cases: ratio 1 = full prefill, single chunk at
+                      offset 0 = exact cache, ratio 0 + single chunk = cache,
+                      layer-1 identity, chunk-0 zero deviation, set invariants
+  which rows are HKVD on random weights ... parity unpinned (the pages print no
+                      worked example; only the invariants above constrain it)
+"""
+from .model import (  # noqa: F401
+    Precision, F64, round_bf16, rope_cos_sin, rope_rotate, rope_delta, rmsnorm, project,
+    causal_attention, mlp, full_prefill, chunk_caches, cache_nbytes,
+)
+from .blend import (  # noqa: F401
+    k_for_ratio, topk_select, kv_deviation, blend_layer, layer_rest, fuse_cache,
+    blended_prefill,
+)
