@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Benchmark of the blended (CacheBlend-fused) prefill on one MI355X.
+
+One step = one whole blended prefill of the Qwen2.5-1.5B-shaped workload: 28 decoder layers,
+d_model 1536, 12 query / 2 KV heads of 128, FFN 8960, bf16, random-init weights N(0, 0.02);
+10 independently cached chunks of 512 uniform-random tokens + a 64-token query; layer 1
+recomputes every row, layer 2 keeps 30% of the context rows, layers 3.. keep 15%.
+Per layer: RoPE position update of the cached K, RMSNorm + fresh K/V GEMM of the selected
+rows, deviation + scatter, top-k, Q GEMM + sparse-query attention of the kept rows, then
+o-projection and SwiGLU FFN on the kept rows.
+
+value = context tokens / s = N_ctx * steps / wall time of the timed steps, with every input
+(weights, chunk caches, token ids) resident in HBM when timing starts.  The pinned-host
+variant (cached KV fetched one layer ahead over PCIe on a second stream) is reported in
+extra fields, not as value.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def attention_flops(shape, records, n_query):
+    """4 * H_q * d_h * sum over kept rows of (position + 1), summed over layers."""
+    return [4.0 * shape.n_q_heads * shape.head_dim * float((r.new_sel.astype(np.int64) + 1).sum()) for r in records]
+
+
+def cpu_baseline(wl, budget_s: float = 25.0):
+    """The oracle (fp64 NumPy with bf16 rounding points) on a bounded sample of the same
+    workload: layer 1 (every row), layer 2 (all rows scored, 30% kept), layer 3 (15% kept)
+    and steady layers until the time budget; tokens/s extrapolated to all layers.  The chunk
+    caches are random bf16-valued arrays of the real shape (their values do not change the
+    oracle's cost); weights and tokens are the fixtures'."""
+    import fixtures as F
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    sh = wl.shape
+    prec = O.Precision("bf16")
+    rng = np.random.default_rng(0)
+    E = F.embedding(sh)
+    tokens = F.all_tokens(wl)
+    offs = F.chunk_offsets(wl)
+    n_ctx, n_tok, n_q = wl.n_ctx, wl.n_tokens, wl.n_query
+    hidden = np.asarray(E[tokens], np.float64)
+    del E
+    sel = np.arange(n_tok)
+    times = []
+    t_start = time.perf_counter()
+    for l in range(sh.n_layers):
+        w = F.layer_weights(sh, l + 1)
+        kc = prec.store(rng.standard_normal((n_ctx, sh.n_kv_heads, sh.head_dim)) * 0.3)
+        vc = prec.store(rng.standard_normal((n_ctx, sh.n_kv_heads, sh.head_dim)) * 0.3)
+        t0 = time.perf_counter()
+        fk, fv = O.fuse_cache(sh, prec, [(kc, vc)], [0, n_ctx], n_q)
+        r = O.blend_layer(sh, w, prec, hidden, fk, fv, n_ctx, sel, n_q, wl.schedule[l])
+        hidden = O.layer_rest(sh, w, prec, hidden, r["new_local"], r["out"])
+        sel = r["new_sel"]
+        times.append(time.perf_counter() - t0)
+        if l >= 4 and time.perf_counter() - t_start > budget_s:
+            break
+    steady = float(np.median(times[3:])) if len(times) > 3 else times[-1]
+    total = sum(times[:3]) + steady * (sh.n_layers - 3)
+    return {"value": n_ctx / total, "unit": "context tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"oracle (fp64 NumPy, bf16 rounding emulated) on layers 1-{len(times)} of the same workload "
+                       f"with random-valued chunk caches of the real shape; layer times "
+                       f"{[round(t, 3) for t in times]} s; blended prefill extrapolated as "
+                       f"T1+T2+T3+{sh.n_layers - 3}*median(steady) = {total:.2f} s")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="qwen")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=25.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the fusion step is built and timed on a single MI355X "
+              "(sharding across GPUs is a design note, not implemented)", file=sys.stderr)
+        return 2
+
+    import torch
+    import fixtures as F
+    from rag_kv_cache_amd import _lib as L
+    from rag_kv_cache_amd.pipeline import Engine, build_chunk_caches, make_buffers, run_layers
+
+    wl = F.get_config(args.config)
+    sh = wl.shape
+    chunks = F.chunk_tokens(wl)
+    tokens = F.all_tokens(wl)
+    offs = [int(o) for o in F.chunk_offsets(wl)]
+    n_ctx, n_tok = wl.n_ctx, wl.n_tokens
+    log(f"workload {wl.name}: {sh.n_layers} layers, d {sh.d_model}, heads {sh.n_q_heads}/{sh.n_kv_heads}, "
+        f"N_ctx {n_ctx} + query {wl.n_query}")
+
+    t0 = time.perf_counter()
+    eng = Engine(sh, max_tokens=n_tok + 64)
+    for l in range(sh.n_layers):
+        eng.load_layer(l, F.layer_weights(sh, l + 1))
+    eng.load_embedding(F.embedding(sh))
+    torch.cuda.synchronize()
+    log(f"weights uploaded in {time.perf_counter() - t0:.1f} s")
+    t0 = time.perf_counter()
+    cache, host = build_chunk_caches(eng, chunks, pinned_host=True)
+    log(f"chunk caches built in {time.perf_counter() - t0:.1f} s")
+
+    buf = make_buffers(eng, n_tok, len(chunks))
+    fused = [(eng.kv_empty(n_tok), eng.kv_empty(n_tok)) for _ in range(sh.n_layers)]
+    cs = eng.compute
+    rec = run_layers(eng, buf, tokens, offs, wl.n_query, wl.schedule, fused, cache=cache, record=True)
+    attn_fl = attention_flops(sh, rec.records, wl.n_query)
+    kept = [len(r.new_sel) for r in rec.records]
+
+    def step(**kw):
+        return run_layers(eng, buf, tokens, offs, wl.n_query, wl.schedule, fused, upload_inputs=False, **kw)
+
+    for _ in range(args.warmup):
+        step(cache=cache)
+    cs.synchronize()
+    torch.cuda.synchronize()
+    L.cb_profile_enable(eng.ctx, True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(cache=cache)
+    cs.synchronize()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    L.cb_profile_enable(eng.ctx, False)
+    wall = t1 - t0
+    ms_step = wall / args.steps * 1e3
+    value = n_ctx * args.steps / wall
+    log(f"blended prefill: {ms_step:.3f} ms/step, {value:,.0f} context tokens/s")
+
+    kernels = {}
+    for kid, name in enumerate(L.KERNEL_NAMES):
+        ms, n, work = L.cb_profile_read(eng.ctx, kid)
+        if n == 0:
+            continue
+        if kid == L.CB_K_ATTN:
+            work = sum(attn_fl) * args.steps
+        bound = "mfma" if kid in (L.CB_K_GEMM_KV, L.CB_K_GEMM_Q, L.CB_K_ATTN, L.CB_K_GEMM_O,
+                                  L.CB_K_GEMM_GATE_UP, L.CB_K_GEMM_DOWN) else "hbm"
+        rate = work / (ms * 1e-3) / (1e12 if bound == "mfma" else 1e9) if ms > 0 else 0.0
+        peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_HBM_GBS
+        kernels[name] = {"ms_total_per_step": round(ms / args.steps, 4), "launches_per_step": n // args.steps,
+                         "us_per_launch": round(ms * 1e3 / n, 2), "bound": bound,
+                         "achieved": round(rate, 2), "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+                         "frac": round(rate / peak, 4)}
+    dom = max(kernels, key=lambda k: kernels[k]["ms_total_per_step"])
+    dk = kernels[dom]
+    roofline = {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"],
+                "peak": PEAK_BF16_TFLOPS if dk["bound"] == "mfma" else PEAK_HBM_GBS, "unit": dk["unit"],
+                "frac": dk["frac"], "traffic": None}
+
+    # per-layer latency (one extra profiled step with events at layer boundaries)
+    evs = []
+    step(cache=cache, layer_events=evs)
+    cs.synchronize()
+    per_layer = [evs[i].elapsed_time(evs[i + 1]) for i in range(len(evs) - 1)]
+
+    # PCIe-inclusive variant: cached KV in pinned host memory, fetched one layer ahead
+    for _ in range(2):
+        step(host_cache=host)
+    cs.synchronize()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(host_cache=host)
+    cs.synchronize()
+    torch.cuda.synchronize()
+    wall_p = time.perf_counter() - t0
+    pcie_ms = wall_p / args.steps * 1e3
+
+    # full recompute on the same GPU and kernels (ratio 1 at every layer)
+    full_sched = [1.0] * sh.n_layers
+    run_layers(eng, buf, tokens, offs, wl.n_query, full_sched, fused, cache=cache, upload_inputs=False)
+    cs.synchronize()
+    t0 = time.perf_counter()
+    n_full = max(3, args.steps // 4)
+    for _ in range(n_full):
+        run_layers(eng, buf, tokens, offs, wl.n_query, full_sched, fused, cache=cache, upload_inputs=False)
+    cs.synchronize()
+    full_ms = (time.perf_counter() - t0) / n_full * 1e3
+    log(f"pinned-host prefetch: {pcie_ms:.3f} ms/step; full recompute: {full_ms:.3f} ms/step")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(wl, args.cpu_budget)
+        log(f"cpu oracle: {cpu['value']:.1f} context tokens/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": "blended-prefill context tokens/s @ r=15% + per-layer ms; % HBM/MFMA peak",
+        "value": round(value, 1), "unit": "context tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{wl.name}: Qwen2.5-1.5B-shaped blended prefill, 28 layers, 10x512-token cached "
+                               f"chunks + 64-token query, recompute 100% -> 30% -> 15%, cached KV resident in HBM",
+                   "n_ctx": n_ctx, "n_query": wl.n_query, "schedule": "1.0, 0.30, 0.15 x 26"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "per_layer_ms": {"layer1": round(per_layer[0], 4), "layer2": round(per_layer[1], 4),
+                         "layer3": round(per_layer[2], 4),
+                         "steady_median": round(float(np.median(per_layer[3:])), 4)},
+        "kept_rows_per_layer": kept[:4] + ["..."],
+        "kernels": kernels,
+        "pcie_prefetch": {"ms_per_step": round(pcie_ms, 4), "context_tokens_per_s": round(n_ctx / pcie_ms * 1e3, 1),
+                          "host_kv_bytes_per_step": int(2 * sh.n_layers * n_ctx * sh.n_kv_heads * sh.head_dim * 2)},
+        "full_recompute_ms": round(full_ms, 4),
+        "speedup_vs_full_recompute": round(full_ms / ms_step, 3),
+    }
+    print(json.dumps(out), flush=True)
+    eng.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,198 @@
+/*
+ * cacheblend.h - C ABI of the MI355X (gfx950) library for CacheBlend's per-layer
+ * KV fusion step (selective KV recompute).
+ *
+ * What the calls compute (from the pages):
+ *   - CacheBlend explainer (0h-n0.github.io), "HKVD token selection": the KV
+ *     deviation of token j at layer i is the L2 norm of cached minus recomputed KV.
+ *   - same page, "Gradual filtering": each layer recomputes the tokens kept by the
+ *     previous layer and narrows them to the r% of largest deviation.
+ *   - same page, "Position encoding update": a cached K is moved to its position
+ *     in the fused prompt by the rotation K_new = R(dp) K_cached.
+ *   - same page, "vLLM integration": the three calls fetch_kv(text, layer),
+ *     prefill_layer(input, KVCache) and synchronize().
+ *   - CacheBlend review (jaehun.me), section on which tokens are recomputed: per
+ *     layer, Q/K/V of the selected tokens are computed from their inputs, the other
+ *     tokens keep their cached K/V, the selected queries attend under the causal
+ *     mask to all available K/V, and the output goes to the next layer; section on
+ *     overlapping loading and recompute: T_layer ~ max(T_load, T_recompute).
+ *
+ * Conventions shared by every call:
+ *   - Layers are numbered 0 .. n_layers-1.
+ *   - Positions: the fused prompt is chunk 0, chunk 1, ..., then the query rows.
+ *     Row p of a fused K/V buffer holds the token at absolute position p.
+ *     chunk_offsets[c] is the first row of chunk c, chunk_offsets[n_chunks] is the
+ *     context length N_ctx; query rows are N_ctx .. N_ctx + n_query - 1.
+ *     Every chunk cache was computed alone at positions 0.. (offset 0).
+ *   - K/V layout: token-major [rows][n_kv_heads][head_dim], element type = dtype.
+ *     The K/V heads of a row are contiguous.
+ *   - Weights: row-major nn.Linear layout [out][in], element type = dtype,
+ *     RMSNorm gains fp32.  The residual stream (hidden rows) is always fp32.
+ *   - Every device pointer is caller-owned device memory (HBM) and must stay valid
+ *     until the work enqueued on the compute stream has finished.  The library
+ *     allocates only its context, its events and a RoPE table at cb_create.
+ *   - Every call is asynchronous: it validates its arguments on the host, returns
+ *     a non-OK status without enqueuing anything if they are wrong, and otherwise
+ *     enqueues kernels on the compute stream (copies on the copy stream).  Faults in
+ *     enqueued work surface at the caller's next synchronisation of that stream.
+ *   - Device-side index arrays (sel_idx ...) cannot be checked on the host; kernels
+ *     skip any out-of-range row instead of touching memory outside the buffers.
+ *   - One context per host thread.  cb_last_error() describes the last non-OK
+ *     status returned on the calling thread.
+ */
+#ifndef CACHEBLEND_H_
+#define CACHEBLEND_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CB_OK = 0,
+  CB_EINVAL = -1,        /* a NULL pointer, a negative size, a non-monotone offset list */
+  CB_ESHAPE = -2,        /* sizes inconsistent with each other or with the model */
+  CB_ESTATE = -3,        /* call order violated (e.g. blend before synchronize) */
+  CB_EHIP = -4,          /* a HIP runtime call or kernel launch failed */
+  CB_ENOMEM = -5,        /* workspace smaller than cb_workspace_size asks for */
+  CB_EUNSUPPORTED = -6   /* a shape the kernels do not implement */
+} cb_status;
+
+typedef enum {
+  CB_F32 = 0,   /* fp32 weights, K/V, Q and attention output */
+  CB_BF16 = 1   /* bfloat16 storage, fp32 accumulation and softmax */
+} cb_dtype;
+
+/* Model shape.  Requirements: n_q_heads % n_kv_heads == 0; head_dim 64 or 128
+ * (bf16: 128); d_model, n_q_heads*head_dim and ffn_dim multiples of 64;
+ * max_tokens >= the longest fused prompt the context will see. */
+typedef struct {
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab_size, max_tokens;
+  float rope_base;  /* RoPE angle of pair i at position p: p * rope_base^(-2i/head_dim) */
+  float rms_eps;    /* RMSNorm epsilon inside the square root */
+  int32_t dtype;    /* cb_dtype */
+} cb_model_desc;
+
+/* Device pointers of one decoder layer (retained, not copied). */
+typedef struct {
+  const void* w_qkv;      /* [(n_q_heads + 2 n_kv_heads) * head_dim][d_model]: Q rows, K rows, V rows */
+  const void* w_o;        /* [d_model][n_q_heads * head_dim] */
+  const void* w_gate_up;  /* [2 ffn_dim][d_model]: gate rows, then up rows */
+  const void* w_down;     /* [d_model][ffn_dim] */
+  const float* g_attn;    /* [d_model] gain of the pre-attention RMSNorm */
+  const float* g_ffn;     /* [d_model] gain of the pre-FFN RMSNorm */
+} cb_layer_weights;
+
+typedef struct cb_ctx cb_ctx;
+
+/* Create a context on HIP device `device`.  compute_stream / copy_stream are
+ * hipStream_t handles owned by the caller (NULL = the null stream; copy_stream NULL
+ * means copies go to the compute stream and nothing overlaps).  Builds the RoPE
+ * cos/sin table for positions 0 .. max_tokens-1 in double precision (stored fp32). */
+cb_status cb_create(const cb_model_desc* desc, int32_t device, void* compute_stream,
+                    void* copy_stream, cb_ctx** out);
+cb_status cb_destroy(cb_ctx* ctx);
+
+/* Register the weights of `layer`.  Must precede cb_blend_layer / cb_layer_rest on it. */
+cb_status cb_set_layer_weights(cb_ctx* ctx, int32_t layer, const cb_layer_weights* w);
+
+/* Bytes of workspace that cb_blend_layer and cb_layer_rest need for fused prompts of at
+ * most n_tokens rows and selected sets of at most n_sel_max rows. */
+cb_status cb_workspace_size(const cb_ctx* ctx, int32_t n_tokens, int32_t n_sel_max, size_t* bytes);
+
+/* hidden_out[i][:] = table[tokens[i]][:] as fp32.  tokens: device int32 [n];
+ * table: device [vocab_size][d_model] of dtype; hidden_out: device fp32 [n][d_model].
+ * Token ids outside [0, vocab_size) give zero rows. */
+cb_status cb_embed(cb_ctx* ctx, const int32_t* tokens, int32_t n, const void* table, float* hidden_out);
+
+/* Layer-pipelined load (explainer, "Pipelined design"; fetch_kv).  Enqueues, on the copy
+ * stream, host-to-device copies of layer `layer`'s cached K and V of every chunk:
+ * host_k[c], host_v[c] point to pinned host memory holding [len_c][n_kv_heads][head_dim]
+ * (len_c = chunk_offsets_host[c+1] - chunk_offsets_host[c]) and land in rows
+ * [chunk_offsets_host[c], chunk_offsets_host[c+1]) of fused_k / fused_v.  Records the
+ * layer's copy event.  The rows then hold the offset-0 cache; cb_blend_layer re-rotates
+ * them in place when it is passed kv_cached == kv_fused.
+ * CB_ESTATE if the layer already has a fetch that no cb_synchronize has consumed. */
+cb_status cb_fetch_layer(cb_ctx* ctx, int32_t layer, const void* const* host_k,
+                         const void* const* host_v, const int32_t* chunk_offsets_host,
+                         int32_t n_chunks, void* fused_k, void* fused_v);
+
+/* synchronize(): make the compute stream wait for layer `layer`'s copy event.  Does not
+ * block the host.  A no-op for a layer that was never fetched. */
+cb_status cb_synchronize(cb_ctx* ctx, int32_t layer);
+
+/* One layer of the fusion step (prefill_layer on the selected rows).  Enqueues:
+ *  1. position update: every context row j of chunk c gets K[j] <- R(o_c) K_cached[j],
+ *     V[j] <- V_cached[j] in kv_fused (skipped when kv_cached_k is NULL: the fused
+ *     buffer then already holds the re-rotated cache; in place when kv_cached_* ==
+ *     kv_fused_*);
+ *  2. x = RMSNorm(hidden_sel) and fresh K, V of the rows of S_l = sel_idx (RoPE at their
+ *     absolute positions);
+ *  3. deviation d_i = ||K_new - K_fused||^2 + ||V_new - V_fused||^2 (fp32) of the
+ *     context rows of S_l against the re-rotated cache, before it is overwritten;
+ *  4. k = floor(ratio * N_ctx + 0.5) (ratio as given, product in double) clamped to
+ *     [0, n_sel - n_query]; the kept set is the k context rows of largest d (ties to
+ *     the lower position) plus every query row, ascending;
+ *  5. fused rows sel_idx <- fresh K, V (every recomputed row);
+ *  6. Q of the kept rows (RoPE at their positions) and causal GQA attention of each
+ *     kept row over fused rows 0 .. its position.
+ * Arguments:
+ *   hidden_sel       device fp32 [n_sel][d_model]: residual-stream rows of S_l
+ *   kv_cached_k/_v   device [N_ctx][n_kv_heads][head_dim]: offset-0 chunk caches in
+ *                    prompt order, or NULL (see 1.)
+ *   kv_fused_k/_v    device [N_ctx + n_query][n_kv_heads][head_dim]: the layer's fused K/V
+ *   chunk_offsets_dev / _host  the same [n_chunks + 1] offsets on device and host;
+ *                    n_chunks may be 0 (no context: every row is a query row, which is
+ *                    how a chunk's own cache is built)
+ *   sel_idx          device int32 [n_sel] strictly ascending positions; its last n_query
+ *                    entries must be the query rows
+ *   new_sel_idx      device int32 [k + n_query] out: kept positions, ascending
+ *   new_sel_local    device int32 [k + n_query] out: index of each kept row within sel_idx
+ *   n_new            host out: k + n_query, set before the call returns
+ *   out_sel          device [k + n_query][n_q_heads * head_dim] out (dtype): attention
+ *                    output of the kept rows (before the o-projection)
+ *   deviation        device fp32 [n_sel] out or NULL: entries 0 .. n_sel-n_query-1 get d
+ *   workspace        device scratch of at least cb_workspace_size(N, n_sel) bytes
+ * CB_ESTATE if the layer was fetched and not yet synchronized. */
+cb_status cb_blend_layer(cb_ctx* ctx, int32_t layer, const float* hidden_sel,
+                         const void* kv_cached_k, const void* kv_cached_v,
+                         void* kv_fused_k, void* kv_fused_v,
+                         const int32_t* chunk_offsets_dev, const int32_t* chunk_offsets_host,
+                         int32_t n_chunks, const int32_t* sel_idx, int32_t n_sel, int32_t n_query,
+                         float ratio, int32_t* new_sel_idx, int32_t* new_sel_local, int32_t* n_new,
+                         void* out_sel, float* deviation, void* workspace, size_t workspace_bytes);
+
+/* Rest of the layer on the kept rows (the output passed to the next layer):
+ *   h1 = hidden_sel[new_sel_local] + out_sel W_o^T
+ *   hidden_next = h1 + W_down( silu(W_gate m) * (W_up m) ),  m = RMSNorm(h1)
+ * hidden_sel: device fp32 [n_sel][d]; new_sel_local / out_sel as returned by
+ * cb_blend_layer; hidden_next: device fp32 [n_new][d] (must not alias hidden_sel). */
+cb_status cb_layer_rest(cb_ctx* ctx, int32_t layer, const float* hidden_sel, int32_t n_sel,
+                        const int32_t* new_sel_local, int32_t n_new, const void* out_sel,
+                        float* hidden_next, void* workspace, size_t workspace_bytes);
+
+/* Thread-local description of the last non-OK status ("" if none). */
+const char* cb_last_error(void);
+
+/* Per-kernel timing with HIP events recorded on the compute stream around each launch.
+ * Ids of the timed operations: */
+typedef enum {
+  CB_K_EMBED = 0, CB_K_ROPE = 1, CB_K_RMSNORM = 2, CB_K_GEMM_KV = 3, CB_K_DEV_SCATTER = 4,
+  CB_K_TOPK = 5, CB_K_GEMM_Q = 6, CB_K_ATTN = 7, CB_K_GEMM_O = 8, CB_K_GEMM_GATE_UP = 9,
+  CB_K_GEMM_DOWN = 10, CB_K_COUNT = 11
+} cb_kernel_id;
+/* Start (on != 0) or stop recording; starting clears earlier records.  At most 16384 timed
+ * launches are kept; later ones are not timed. */
+cb_status cb_profile_enable(cb_ctx* ctx, int32_t on);
+/* Wait for the recorded events and report, for one id: total ms, number of launches, and
+ * the algorithmic work of those launches (flops for GEMM and attention, bytes moved for
+ * the others) as computed from their shapes. */
+cb_status cb_profile_read(cb_ctx* ctx, int32_t kernel_id, double* total_ms, int64_t* launches,
+                          double* work);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CACHEBLEND_H_ */

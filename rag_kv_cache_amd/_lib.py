@@ -1,0 +1,155 @@
+"""ctypes binding of include/cacheblend.h: the same names, argument marshalling only.
+
+Device pointers are passed as Python ints (0 = NULL); host arrays as sequences of ints.
+Every function raises CbError when the library returns a non-OK status.  There is no
+fallback: if the HIP library is not built, importing this module fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librag_kv_cache_amd.so")
+
+CB_OK, CB_EINVAL, CB_ESHAPE, CB_ESTATE, CB_EHIP, CB_ENOMEM, CB_EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
+STATUS_NAMES = {0: "CB_OK", -1: "CB_EINVAL", -2: "CB_ESHAPE", -3: "CB_ESTATE", -4: "CB_EHIP",
+                -5: "CB_ENOMEM", -6: "CB_EUNSUPPORTED"}
+CB_F32, CB_BF16 = 0, 1
+(CB_K_EMBED, CB_K_ROPE, CB_K_RMSNORM, CB_K_GEMM_KV, CB_K_DEV_SCATTER, CB_K_TOPK, CB_K_GEMM_Q, CB_K_ATTN,
+ CB_K_GEMM_O, CB_K_GEMM_GATE_UP, CB_K_GEMM_DOWN, CB_K_COUNT) = range(12)
+KERNEL_NAMES = ["embed", "rope_delta", "rmsnorm", "gemm_kv", "dev_scatter", "topk", "gemm_q", "attention",
+                "gemm_o", "gemm_gate_up", "gemm_down"]
+
+
+class CbError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class cb_model_desc(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("d_model", C.c_int32), ("n_q_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn_dim", C.c_int32),
+                ("vocab_size", C.c_int32), ("max_tokens", C.c_int32), ("rope_base", C.c_float),
+                ("rms_eps", C.c_float), ("dtype", C.c_int32)]
+
+
+class cb_layer_weights(C.Structure):
+    _fields_ = [("w_qkv", C.c_void_p), ("w_o", C.c_void_p), ("w_gate_up", C.c_void_p),
+                ("w_down", C.c_void_p), ("g_attn", C.c_void_p), ("g_ffn", C.c_void_p)]
+
+
+def _load() -> C.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"HIP library {LIB_PATH} is not built; run `python -m rag_kv_cache_amd.build`")
+    return C.CDLL(LIB_PATH)
+
+
+_L = _load()
+_P = C.c_void_p
+_I = C.c_int32
+_L.cb_last_error.restype = C.c_char_p
+_L.cb_last_error.argtypes = []
+_SIGS = {
+    "cb_create": [C.POINTER(cb_model_desc), _I, _P, _P, C.POINTER(_P)],
+    "cb_destroy": [_P],
+    "cb_set_layer_weights": [_P, _I, C.POINTER(cb_layer_weights)],
+    "cb_workspace_size": [_P, _I, _I, C.POINTER(C.c_size_t)],
+    "cb_embed": [_P, _P, _I, _P, _P],
+    "cb_fetch_layer": [_P, _I, C.POINTER(_P), C.POINTER(_P), C.POINTER(_I), _I, _P, _P],
+    "cb_synchronize": [_P, _I],
+    "cb_blend_layer": [_P, _I, _P, _P, _P, _P, _P, _P, C.POINTER(_I), _I, _P, _I, _I, C.c_float, _P, _P,
+                       C.POINTER(_I), _P, _P, _P, C.c_size_t],
+    "cb_layer_rest": [_P, _I, _P, _I, _P, _I, _P, _P, _P, C.c_size_t],
+    "cb_profile_enable": [_P, _I],
+    "cb_profile_read": [_P, _I, C.POINTER(C.c_double), C.POINTER(C.c_int64), C.POINTER(C.c_double)],
+}
+for _name, _args in _SIGS.items():
+    _f = getattr(_L, _name)
+    _f.argtypes = _args
+    _f.restype = C.c_int
+
+
+def _check(status: int) -> None:
+    if status != CB_OK:
+        raise CbError(status, _L.cb_last_error().decode())
+
+
+def _i32(seq: Sequence[int]):
+    return (_I * len(seq))(*[int(v) for v in seq])
+
+
+def cb_last_error() -> str:
+    return _L.cb_last_error().decode()
+
+
+def cb_create(desc: cb_model_desc, device: int = 0, compute_stream: int = 0, copy_stream: int = 0) -> int:
+    out = _P()
+    _check(_L.cb_create(C.byref(desc), device, compute_stream or None, copy_stream or None, C.byref(out)))
+    return out.value
+
+
+def cb_destroy(ctx: int) -> None:
+    _check(_L.cb_destroy(ctx))
+
+
+def cb_set_layer_weights(ctx: int, layer: int, w_qkv: int, w_o: int, w_gate_up: int, w_down: int,
+                         g_attn: int, g_ffn: int) -> None:
+    w = cb_layer_weights(w_qkv, w_o, w_gate_up, w_down, g_attn, g_ffn)
+    _check(_L.cb_set_layer_weights(ctx, layer, C.byref(w)))
+
+
+def cb_workspace_size(ctx: int, n_tokens: int, n_sel_max: int) -> int:
+    out = C.c_size_t()
+    _check(_L.cb_workspace_size(ctx, n_tokens, n_sel_max, C.byref(out)))
+    return out.value
+
+
+def cb_embed(ctx: int, tokens: int, n: int, table: int, hidden_out: int) -> None:
+    _check(_L.cb_embed(ctx, tokens, n, table, hidden_out))
+
+
+def cb_fetch_layer(ctx: int, layer: int, host_k: Sequence[int], host_v: Sequence[int],
+                   chunk_offsets_host: Sequence[int], n_chunks: int, fused_k: int, fused_v: int) -> None:
+    hk = (_P * max(len(host_k), 1))(*host_k)
+    hv = (_P * max(len(host_v), 1))(*host_v)
+    _check(_L.cb_fetch_layer(ctx, layer, hk, hv, _i32(chunk_offsets_host), n_chunks, fused_k, fused_v))
+
+
+def cb_synchronize(ctx: int, layer: int) -> None:
+    _check(_L.cb_synchronize(ctx, layer))
+
+
+def cb_blend_layer(ctx: int, layer: int, hidden_sel: int, kv_cached_k: int, kv_cached_v: int,
+                   kv_fused_k: int, kv_fused_v: int, chunk_offsets_dev: int,
+                   chunk_offsets_host: Sequence[int], n_chunks: int, sel_idx: int, n_sel: int,
+                   n_query: int, ratio: float, new_sel_idx: int, new_sel_local: int, out_sel: int,
+                   deviation: int, workspace: int, workspace_bytes: int) -> int:
+    """Returns n_new (= k + n_query)."""
+    n_new = _I()
+    _check(_L.cb_blend_layer(ctx, layer, hidden_sel, kv_cached_k or None, kv_cached_v or None, kv_fused_k,
+                             kv_fused_v, chunk_offsets_dev or None, _i32(chunk_offsets_host), n_chunks,
+                             sel_idx, n_sel, n_query, ratio, new_sel_idx, new_sel_local, C.byref(n_new),
+                             out_sel, deviation or None, workspace, workspace_bytes))
+    return n_new.value
+
+
+def cb_layer_rest(ctx: int, layer: int, hidden_sel: int, n_sel: int, new_sel_local: int, n_new: int,
+                  out_sel: int, hidden_next: int, workspace: int, workspace_bytes: int) -> None:
+    _check(_L.cb_layer_rest(ctx, layer, hidden_sel, n_sel, new_sel_local, n_new, out_sel, hidden_next,
+                            workspace, workspace_bytes))
+
+
+def cb_profile_enable(ctx: int, on: bool) -> None:
+    _check(_L.cb_profile_enable(ctx, 1 if on else 0))
+
+
+def cb_profile_read(ctx: int, kernel_id: int):
+    ms, n, work = C.c_double(), C.c_int64(), C.c_double()
+    _check(_L.cb_profile_read(ctx, kernel_id, C.byref(ms), C.byref(n), C.byref(work)))
+    return ms.value, n.value, work.value
+
+
+def exported_symbols() -> list:
+    return [n for n in list(_SIGS) + ["cb_last_error"] if hasattr(_L, n)]

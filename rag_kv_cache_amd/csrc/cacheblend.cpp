@@ -1,0 +1,546 @@
+// Host side of the C ABI declared in include/cacheblend.h: context, argument validation,
+// the fetch/synchronize state machine, workspace planning and launch sequencing.
+#include "../../include/cacheblend.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "cb_kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+cb_status fail(cb_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+cb_status hip_fail(hipError_t e, const char* what) {
+  return fail(CB_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+enum LayerState { LS_IDLE = 0, LS_FETCHED = 1 };
+
+struct ProfRec {
+  int kernel;
+  double work;
+  hipEvent_t start, stop;
+};
+
+constexpr int kMaxProf = 16384;
+constexpr int kGemmMaxSplits = 8;
+constexpr int kAttnMaxSplits = 16;
+constexpr int kPartialRows = 2048;  // split-K / split-KV partial buffers cover this many rows
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+}  // namespace
+
+struct cb_ctx {
+  cb_model_desc d{};
+  int device = 0;
+  hipStream_t cs = nullptr, xs = nullptr;
+  float2* rope = nullptr;  // [max_tokens][head_dim / 2]
+  std::vector<cb_layer_weights> w;
+  std::vector<char> have_w;
+  std::vector<hipEvent_t> fetch_ev;
+  std::vector<int> state;
+  bool prof = false;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> ev_pool;
+  size_t ev_used = 0;
+
+  int esize() const { return d.dtype == CB_BF16 ? 2 : 4; }
+  bool bf16() const { return d.dtype == CB_BF16; }
+};
+
+namespace {
+
+// Workspace layout (byte offsets), shared by blend_layer and layer_rest.
+struct WsPlan {
+  size_t x, fresh, dev, q, attn_o, attn_ml, h1, mnorm, act, gpart, total;
+  long attn_cap_rows;  // rows x splits the attention partials can hold
+  long gpart_elems;    // fp32 elements of the split-K partial buffer
+};
+
+WsPlan plan_ws(const cb_model_desc& d, int n_tokens, int n_sel) {
+  (void)n_tokens;
+  WsPlan p{};
+  const size_t es = d.dtype == CB_BF16 ? 2 : 4;
+  const size_t ns = (size_t)std::max(n_sel, 1);
+  const size_t qd = (size_t)d.n_q_heads * d.head_dim;
+  const size_t kvd = (size_t)d.n_kv_heads * d.head_dim;
+  const long prow = std::min<long>((long)ns, kPartialRows);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+  p.x = take(ns * d.d_model * es);
+  p.fresh = take(ns * 2 * kvd * es);
+  p.dev = take(ns * 4);
+  p.q = take(ns * qd * es);
+  p.attn_cap_rows = prow * kAttnMaxSplits;
+  p.attn_o = take((size_t)p.attn_cap_rows * qd * 4);
+  p.attn_ml = take((size_t)p.attn_cap_rows * d.n_q_heads * 2 * 4);
+  // layer_rest reuses the front of the workspace (blend_layer's buffers are dead by then)
+  size_t blend_end = off;
+  off = 0;
+  p.h1 = take(ns * d.d_model * 4);
+  p.mnorm = take(ns * d.d_model * es);
+  p.act = take(ns * d.ffn_dim * es);
+  off = std::max(off, blend_end);
+  const size_t maxn = std::max<size_t>({(size_t)d.d_model, qd, 2 * kvd});
+  p.gpart_elems = (long)(prow * maxn * kGemmMaxSplits);
+  p.gpart = take((size_t)p.gpart_elems * 4);
+  p.total = off;
+  return p;
+}
+
+// Split-K factor: enough workgroups to cover the chip twice, each split at least 4 K-steps,
+// K divisible by 64 * splits, partials within the buffer.
+int pick_splits(int M, int N, int K, long cap_elems) {
+  const int tiles = ((M + 63) / 64) * (N / 128);
+  if (tiles >= 256) return 1;
+  int s = std::min(kGemmMaxSplits, (512 + tiles - 1) / tiles);
+  while (s > 1 && ((K % (64 * s)) != 0 || K / s < 256 || (long)s * M * N > cap_elems)) --s;
+  return std::max(s, 1);
+}
+
+void attn_splits(int n_q, int hkv, int n_tok, long cap_rows, int& splits, int& split_len) {
+  const int wgs = ((n_q + 15) / 16) * hkv;
+  int s = 1;
+  if (wgs < 512) s = std::min(kAttnMaxSplits, (512 + wgs - 1) / wgs);
+  s = std::min(s, std::max(1, n_tok / 256));
+  while (s > 1 && (long)s * n_q > cap_rows) --s;
+  int len = (n_tok + s - 1) / s;
+  len = (len + 63) / 64 * 64;
+  if (len <= 0) len = 64;
+  splits = (n_tok + len - 1) / len;
+  if (splits < 1) splits = 1;
+  split_len = len;
+}
+
+struct Timed {
+  cb_ctx* c;
+  int kernel;
+  double work;
+  ProfRec* rec = nullptr;
+  Timed(cb_ctx* c_, int k, double w) : c(c_), kernel(k), work(w) {
+    if (!c->prof || c->ev_used + 2 > c->ev_pool.size()) return;
+    c->recs.push_back(ProfRec{kernel, work, c->ev_pool[c->ev_used], c->ev_pool[c->ev_used + 1]});
+    c->ev_used += 2;
+    rec = &c->recs.back();
+    hipEventRecord(rec->start, c->cs);
+  }
+  ~Timed() {
+    if (rec) hipEventRecord(rec->stop, c->cs);
+  }
+};
+
+cb_status check_ctx(const cb_ctx* c) {
+  if (!c) return fail(CB_EINVAL, "context is NULL");
+  return CB_OK;
+}
+
+cb_status check_layer(const cb_ctx* c, int layer, bool need_w) {
+  if (layer < 0 || layer >= c->d.n_layers)
+    return fail(CB_EINVAL, "layer %d outside [0, %d)", layer, c->d.n_layers);
+  if (need_w && !c->have_w[layer]) return fail(CB_ESTATE, "weights of layer %d not set", layer);
+  return CB_OK;
+}
+
+cb_status check_offsets(const cb_ctx* c, const int32_t* offs, int n_chunks) {
+  if (n_chunks < 0) return fail(CB_EINVAL, "n_chunks %d < 0", n_chunks);
+  if (!offs) return fail(CB_EINVAL, "chunk_offsets_host is NULL");
+  if (offs[0] != 0) return fail(CB_EINVAL, "chunk_offsets[0] = %d, must be 0", offs[0]);
+  for (int i = 0; i < n_chunks; ++i)
+    if (offs[i + 1] < offs[i]) return fail(CB_EINVAL, "chunk_offsets not monotone at %d", i);
+  if (offs[n_chunks] > c->d.max_tokens) return fail(CB_ESHAPE, "context %d > max_tokens", offs[n_chunks]);
+  return CB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* cb_last_error(void) { return g_err.c_str(); }
+
+cb_status cb_create(const cb_model_desc* desc, int32_t device, void* compute_stream, void* copy_stream,
+                    cb_ctx** out) {
+  if (!desc || !out) return fail(CB_EINVAL, "desc or out is NULL");
+  *out = nullptr;
+  const cb_model_desc& d = *desc;
+  if (d.n_layers <= 0 || d.d_model <= 0 || d.n_q_heads <= 0 || d.n_kv_heads <= 0 || d.head_dim <= 0 ||
+      d.ffn_dim <= 0 || d.vocab_size <= 0 || d.max_tokens <= 0)
+    return fail(CB_EINVAL, "model sizes must be positive");
+  if (d.dtype != CB_F32 && d.dtype != CB_BF16) return fail(CB_EINVAL, "unknown dtype %d", d.dtype);
+  if (d.n_q_heads % d.n_kv_heads) return fail(CB_ESHAPE, "n_q_heads not a multiple of n_kv_heads");
+  if (d.head_dim != 64 && d.head_dim != 128) return fail(CB_EUNSUPPORTED, "head_dim %d (64 or 128)", d.head_dim);
+  if (d.dtype == CB_BF16 && d.head_dim != 128) return fail(CB_EUNSUPPORTED, "bf16 path needs head_dim 128");
+  const int G = d.n_q_heads / d.n_kv_heads;
+  if (d.dtype == CB_BF16 && !(G == 1 || G == 2 || G == 4 || G == 6 || G == 7 || G == 8))
+    return fail(CB_EUNSUPPORTED, "GQA group %d not instantiated", G);
+  if (d.d_model % 128 || (d.n_q_heads * d.head_dim) % 128 || (2 * d.n_kv_heads * d.head_dim) % 128 ||
+      d.ffn_dim % 64)
+    return fail(CB_EUNSUPPORTED, "d_model, q width and 2*kv width must be multiples of 128, ffn of 64");
+  if (!(d.rope_base > 0.f) || !(d.rms_eps >= 0.f)) return fail(CB_EINVAL, "rope_base / rms_eps invalid");
+
+  hipError_t e = hipSetDevice(device);
+  if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+  cb_ctx* c = new cb_ctx();
+  c->d = d;
+  c->device = device;
+  c->cs = (hipStream_t)compute_stream;
+  c->xs = copy_stream ? (hipStream_t)copy_stream : c->cs;
+  c->w.resize(d.n_layers);
+  c->have_w.assign(d.n_layers, 0);
+  c->state.assign(d.n_layers, LS_IDLE);
+  c->fetch_ev.assign(d.n_layers, nullptr);
+  for (int l = 0; l < d.n_layers; ++l) {
+    e = hipEventCreateWithFlags(&c->fetch_ev[l], hipEventDisableTiming);
+    if (e != hipSuccess) { cb_destroy(c); return hip_fail(e, "hipEventCreate"); }
+  }
+  // RoPE table: angle p * base^(-2i/dh) and its cos/sin in double, stored as float.
+  const int half = d.head_dim / 2;
+  std::vector<float2> tab((size_t)d.max_tokens * half);
+  for (int i = 0; i < half; ++i) {
+    const double theta = std::pow((double)d.rope_base, -2.0 * i / d.head_dim);
+    for (int p = 0; p < d.max_tokens; ++p) {
+      const double ang = (double)p * theta;
+      tab[(size_t)p * half + i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+    }
+  }
+  e = hipMalloc((void**)&c->rope, tab.size() * sizeof(float2));
+  if (e != hipSuccess) { cb_destroy(c); return hip_fail(e, "hipMalloc(rope table)"); }
+  e = hipMemcpy(c->rope, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice);
+  if (e != hipSuccess) { cb_destroy(c); return hip_fail(e, "hipMemcpy(rope table)"); }
+  *out = c;
+  return CB_OK;
+}
+
+cb_status cb_destroy(cb_ctx* c) {
+  if (!c) return CB_OK;
+  hipSetDevice(c->device);
+  if (c->cs) hipStreamSynchronize(c->cs);
+  if (c->xs && c->xs != c->cs) hipStreamSynchronize(c->xs);
+  if (!c->cs) hipDeviceSynchronize();
+  for (hipEvent_t ev : c->fetch_ev)
+    if (ev) hipEventDestroy(ev);
+  for (hipEvent_t ev : c->ev_pool) hipEventDestroy(ev);
+  if (c->rope) hipFree(c->rope);
+  delete c;
+  return CB_OK;
+}
+
+cb_status cb_set_layer_weights(cb_ctx* c, int32_t layer, const cb_layer_weights* w) {
+  cb_status st = check_ctx(c);
+  if (st) return st;
+  if ((st = check_layer(c, layer, false))) return st;
+  if (!w || !w->w_qkv || !w->w_o || !w->w_gate_up || !w->w_down || !w->g_attn || !w->g_ffn)
+    return fail(CB_EINVAL, "a weight pointer of layer %d is NULL", layer);
+  c->w[layer] = *w;
+  c->have_w[layer] = 1;
+  return CB_OK;
+}
+
+cb_status cb_workspace_size(const cb_ctx* c, int32_t n_tokens, int32_t n_sel_max, size_t* bytes) {
+  cb_status st = check_ctx(c);
+  if (st) return st;
+  if (!bytes) return fail(CB_EINVAL, "bytes is NULL");
+  if (n_tokens < 0 || n_sel_max < 0) return fail(CB_EINVAL, "negative size");
+  if (n_sel_max > n_tokens) return fail(CB_ESHAPE, "n_sel_max %d > n_tokens %d", n_sel_max, n_tokens);
+  *bytes = plan_ws(c->d, n_tokens, n_sel_max).total;
+  return CB_OK;
+}
+
+cb_status cb_embed(cb_ctx* c, const int32_t* tokens, int32_t n, const void* table, float* hidden_out) {
+  cb_status st = check_ctx(c);
+  if (st) return st;
+  if (n < 0) return fail(CB_EINVAL, "n %d < 0", n);
+  if (n == 0) return CB_OK;
+  if (!tokens || !table || !hidden_out) return fail(CB_EINVAL, "NULL pointer");
+  Timed t(c, CB_K_EMBED, (double)n * c->d.d_model * (c->esize() + 4));
+  hipError_t e = cb::embed(tokens, n, table, c->d.vocab_size, c->d.d_model, c->bf16(), hidden_out, c->cs);
+  return e == hipSuccess ? CB_OK : hip_fail(e, "embed launch");
+}
+
+cb_status cb_fetch_layer(cb_ctx* c, int32_t layer, const void* const* host_k, const void* const* host_v,
+                         const int32_t* offs, int32_t n_chunks, void* fused_k, void* fused_v) {
+  cb_status st = check_ctx(c);
+  if (st) return st;
+  if ((st = check_layer(c, layer, false))) return st;
+  if ((st = check_offsets(c, offs, n_chunks))) return st;
+  if (c->state[layer] == LS_FETCHED) return fail(CB_ESTATE, "layer %d fetched twice without synchronize", layer);
+  if (n_chunks > 0 && (!host_k || !host_v || !fused_k || !fused_v)) return fail(CB_EINVAL, "NULL pointer");
+  const size_t row = (size_t)c->d.n_kv_heads * c->d.head_dim * c->esize();
+  for (int ch = 0; ch < n_chunks; ++ch)
+    if (offs[ch + 1] > offs[ch] && (!host_k[ch] || !host_v[ch])) return fail(CB_EINVAL, "chunk %d host pointer NULL", ch);
+  for (int ch = 0; ch < n_chunks; ++ch) {
+    const size_t bytes = (size_t)(offs[ch + 1] - offs[ch]) * row;
+    if (!bytes) continue;
+    hipError_t e = hipMemcpyAsync((char*)fused_k + (size_t)offs[ch] * row, host_k[ch], bytes, hipMemcpyHostToDevice, c->xs);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync((char*)fused_v + (size_t)offs[ch] * row, host_v[ch], bytes, hipMemcpyHostToDevice, c->xs);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(fetch)");
+  }
+  hipError_t e = hipEventRecord(c->fetch_ev[layer], c->xs);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord(fetch)");
+  c->state[layer] = LS_FETCHED;
+  return CB_OK;
+}
+
+cb_status cb_synchronize(cb_ctx* c, int32_t layer) {
+  cb_status st = check_ctx(c);
+  if (st) return st;
+  if ((st = check_layer(c, layer, false))) return st;
+  if (c->state[layer] != LS_FETCHED) return CB_OK;
+  if (c->xs != c->cs) {
+    hipError_t e = hipStreamWaitEvent(c->cs, c->fetch_ev[layer], 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  }
+  c->state[layer] = LS_IDLE;
+  return CB_OK;
+}
+
+cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, const void* kv_cached_k,
+                         const void* kv_cached_v, void* kv_fused_k, void* kv_fused_v, const int32_t* offs_dev,
+                         const int32_t* offs, int32_t n_chunks, const int32_t* sel_idx, int32_t n_sel,
+                         int32_t n_query, float ratio, int32_t* new_sel_idx, int32_t* new_sel_local,
+                         int32_t* n_new, void* out_sel, float* deviation, void* workspace, size_t ws_bytes) {
+  cb_status st = check_ctx(c);
+  if (st) return st;
+  if ((st = check_layer(c, layer, true))) return st;
+  if ((st = check_offsets(c, offs, n_chunks))) return st;
+  if (c->state[layer] == LS_FETCHED)
+    return fail(CB_ESTATE, "layer %d has a pending fetch: call cb_synchronize first", layer);
+  const cb_model_desc& d = c->d;
+  const int n_ctx = offs[n_chunks];
+  if (n_query < 0 || n_sel < 0) return fail(CB_EINVAL, "negative n_sel / n_query");
+  const long n_tok = (long)n_ctx + n_query;
+  if (n_tok > d.max_tokens) return fail(CB_ESHAPE, "prompt of %ld rows > max_tokens %d", n_tok, d.max_tokens);
+  if (n_sel < n_query) return fail(CB_ESHAPE, "n_sel %d < n_query %d: every query row must be selected", n_sel, n_query);
+  const int n_cand = n_sel - n_query;
+  if (n_cand > n_ctx) return fail(CB_ESHAPE, "%d context rows selected > N_ctx %d", n_cand, n_ctx);
+  if (!(ratio >= 0.f) || !std::isfinite(ratio)) return fail(CB_EINVAL, "ratio must be finite and >= 0");
+  if (!n_new) return fail(CB_EINVAL, "n_new is NULL");
+  if (n_sel > 0 && (!hidden_sel || !sel_idx || !new_sel_idx || !new_sel_local || !out_sel))
+    return fail(CB_EINVAL, "NULL pointer");
+  if (n_tok > 0 && (!kv_fused_k || !kv_fused_v)) return fail(CB_EINVAL, "kv_fused is NULL");
+  if ((kv_cached_k == nullptr) != (kv_cached_v == nullptr)) return fail(CB_EINVAL, "kv_cached_k / _v: both or neither");
+  if ((kv_cached_k == kv_fused_k) != (kv_cached_v == kv_fused_v))
+    return fail(CB_EINVAL, "kv_cached must alias kv_fused for both K and V or for neither");
+  if (n_chunks > 0 && !offs_dev) return fail(CB_EINVAL, "chunk_offsets_dev is NULL");
+  const WsPlan wp = plan_ws(d, (int)n_tok, n_sel);
+  if (!workspace || ws_bytes < wp.total)
+    return fail(CB_ENOMEM, "workspace %zu bytes < %zu needed", ws_bytes, wp.total);
+
+  long k = (long)std::floor((double)ratio * (double)n_ctx + 0.5);
+  k = std::max(0L, std::min(k, (long)n_cand));
+  const int nn = (int)k + n_query;
+  *n_new = nn;
+  if (n_sel == 0) return CB_OK;
+
+  char* ws = (char*)workspace;
+  const bool bf = c->bf16();
+  const int es = c->esize();
+  const int kvd = d.n_kv_heads * d.head_dim;
+  const int qd = d.n_q_heads * d.head_dim;
+  const int dm = d.d_model;
+  const cb_layer_weights& W = c->w[layer];
+  hipError_t e;
+
+  // 1. position update of the cached K (and copy of V) into the fused buffer
+  if (n_ctx > 0 && kv_cached_k) {
+    const bool inplace = kv_cached_k == kv_fused_k;
+    Timed t(c, CB_K_ROPE, (double)n_ctx * kvd * es * (inplace ? 2.0 : 4.0));
+    e = cb::rope_delta(kv_cached_k, kv_cached_v, kv_fused_k, kv_fused_v, n_ctx, d.n_kv_heads, d.head_dim, offs_dev,
+                       n_chunks, c->rope, bf, c->cs);
+    if (e != hipSuccess) return hip_fail(e, "rope_delta launch");
+  }
+  // 2. x = RMSNorm(hidden_sel)
+  void* x = ws + wp.x;
+  {
+    Timed t(c, CB_K_RMSNORM, (double)n_sel * dm * (4 + es));
+    e = cb::rmsnorm(hidden_sel, dm, n_sel, dm, W.g_attn, d.rms_eps, x, bf, c->cs);
+    if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
+  }
+  // 3. fresh K | V of the selected rows (RoPE on K at the rows' positions)
+  void* fresh = ws + wp.fresh;
+  {
+    cb::GemmArgs g{};
+    g.A = x; g.lda = dm; g.a_rows = nullptr;
+    g.B = (const char*)W.w_qkv + (size_t)qd * dm * es; g.ldb = dm;
+    g.M = n_sel; g.N = 2 * kvd; g.K = dm;
+    g.splits = bf ? pick_splits(g.M, g.N, g.K, wp.gpart_elems) : 1;
+    g.partial = (float*)(ws + wp.gpart);
+    g.epi = cb::EPI_ROPE; g.out = fresh; g.ldo = 2 * kvd;
+    g.pos = sel_idx; g.rope = c->rope; g.rope_cols = kvd; g.head_dim = d.head_dim; g.max_pos = d.max_tokens - 1;
+    Timed t(c, CB_K_GEMM_KV, 2.0 * g.M * g.N * g.K);
+    e = bf ? cb::gemm_bf16(g, c->cs) : cb::gemm_f32(g, c->cs);
+    if (e != hipSuccess) return hip_fail(e, "gemm(kv) launch");
+  }
+  // 4. deviation against the re-rotated cache, then scatter of the fresh rows
+  float* dev = deviation ? deviation : (float*)(ws + wp.dev);
+  {
+    Timed t(c, CB_K_DEV_SCATTER, (double)n_sel * 2 * kvd * es * 2 + (double)n_cand * 2 * kvd * es);
+    e = cb::dev_scatter(fresh, 2 * kvd, kv_fused_k, kv_fused_v, sel_idx, n_sel, n_cand, (int)n_tok, kvd,
+                        n_ctx > 0 ? dev : nullptr, bf, c->cs);
+    if (e != hipSuccess) return hip_fail(e, "dev_scatter launch");
+  }
+  // 5. gradual filtering: top-k of the context rows + every query row
+  {
+    Timed t(c, CB_K_TOPK, (double)n_cand * 4);
+    e = cb::topk_select(dev, sel_idx, n_cand, n_query, (int)k, new_sel_idx, new_sel_local, c->cs);
+    if (e != hipSuccess) return hip_fail(e, "topk launch");
+  }
+  if (nn == 0) return CB_OK;
+  // 6a. Q of the kept rows (RoPE at their positions)
+  void* q = ws + wp.q;
+  {
+    cb::GemmArgs g{};
+    g.A = x; g.lda = dm; g.a_rows = new_sel_local;
+    g.B = W.w_qkv; g.ldb = dm;
+    g.M = nn; g.N = qd; g.K = dm;
+    g.splits = bf ? pick_splits(g.M, g.N, g.K, wp.gpart_elems) : 1;
+    g.partial = (float*)(ws + wp.gpart);
+    g.epi = cb::EPI_ROPE; g.out = q; g.ldo = qd;
+    g.pos = new_sel_idx; g.rope = c->rope; g.rope_cols = qd; g.head_dim = d.head_dim; g.max_pos = d.max_tokens - 1;
+    Timed t(c, CB_K_GEMM_Q, 2.0 * g.M * g.N * g.K);
+    e = bf ? cb::gemm_bf16(g, c->cs) : cb::gemm_f32(g, c->cs);
+    if (e != hipSuccess) return hip_fail(e, "gemm(q) launch");
+  }
+  // 6b. causal attention of the kept rows over the fused K/V
+  {
+    cb::AttnArgs a{};
+    a.q = q; a.ldq = qd; a.qpos = new_sel_idx; a.n_q = nn;
+    a.k = kv_fused_k; a.v = kv_fused_v; a.n_tok = (int)n_tok; a.hq = d.n_q_heads; a.hkv = d.n_kv_heads;
+    a.dh = d.head_dim; a.out = out_sel; a.ldo = qd;
+    a.part_o = (float*)(ws + wp.attn_o); a.part_ml = (float*)(ws + wp.attn_ml);
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
+    if (bf) attn_splits(nn, d.n_kv_heads, (int)n_tok, wp.attn_cap_rows, a.splits, a.split_len);
+    else { a.splits = 1; a.split_len = (int)std::max<long>(n_tok, 1); }
+    // causal flops of the kept rows are not known on the host; the row count bounds them
+    Timed t(c, CB_K_ATTN, 0.0);
+    e = bf ? cb::attn_bf16(a, c->cs) : cb::attn_f32(a, c->cs);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+  }
+  return CB_OK;
+}
+
+cb_status cb_layer_rest(cb_ctx* c, int32_t layer, const float* hidden_sel, int32_t n_sel,
+                        const int32_t* new_sel_local, int32_t n_new, const void* out_sel, float* hidden_next,
+                        void* workspace, size_t ws_bytes) {
+  cb_status st = check_ctx(c);
+  if (st) return st;
+  if ((st = check_layer(c, layer, true))) return st;
+  const cb_model_desc& d = c->d;
+  if (n_sel < 0 || n_new < 0) return fail(CB_EINVAL, "negative size");
+  if (n_new > n_sel) return fail(CB_ESHAPE, "n_new %d > n_sel %d", n_new, n_sel);
+  if (n_new == 0) return CB_OK;
+  if (!hidden_sel || !new_sel_local || !out_sel || !hidden_next) return fail(CB_EINVAL, "NULL pointer");
+  if ((const void*)hidden_next == (const void*)hidden_sel) return fail(CB_EINVAL, "hidden_next aliases hidden_sel");
+  const WsPlan wp = plan_ws(d, n_sel, n_sel);
+  if (!workspace || ws_bytes < wp.total) return fail(CB_ENOMEM, "workspace %zu bytes < %zu needed", ws_bytes, wp.total);
+  char* ws = (char*)workspace;
+  const bool bf = c->bf16();
+  const int es = c->esize();
+  const int dm = d.d_model, qd = d.n_q_heads * d.head_dim, ff = d.ffn_dim;
+  const cb_layer_weights& W = c->w[layer];
+  float* h1 = (float*)(ws + wp.h1);
+  void* mn = ws + wp.mnorm;
+  void* act = ws + wp.act;
+  hipError_t e;
+  {  // h1 = hidden_sel[new_sel_local] + out_sel W_o^T
+    cb::GemmArgs g{};
+    g.A = out_sel; g.lda = qd; g.B = W.w_o; g.ldb = qd;
+    g.M = n_new; g.N = dm; g.K = qd;
+    g.splits = bf ? pick_splits(g.M, g.N, g.K, wp.gpart_elems) : 1;
+    g.partial = (float*)(ws + wp.gpart);
+    g.epi = cb::EPI_RESID; g.out = h1; g.ldo = dm; g.resid = hidden_sel; g.ldr = dm; g.resid_rows = new_sel_local;
+    Timed t(c, CB_K_GEMM_O, 2.0 * g.M * g.N * g.K);
+    e = bf ? cb::gemm_bf16(g, c->cs) : cb::gemm_f32(g, c->cs);
+    if (e != hipSuccess) return hip_fail(e, "gemm(o) launch");
+  }
+  {
+    Timed t(c, CB_K_RMSNORM, (double)n_new * dm * (4 + es));
+    e = cb::rmsnorm(h1, dm, n_new, dm, W.g_ffn, d.rms_eps, mn, bf, c->cs);
+    if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
+  }
+  {  // act = silu(m W_gate^T) * (m W_up^T)
+    cb::GemmArgs g{};
+    g.A = mn; g.lda = dm; g.B = W.w_gate_up; g.ldb = dm; g.swiglu_ffn = ff;
+    g.M = n_new; g.N = 2 * ff; g.K = dm; g.splits = 1;
+    g.epi = cb::EPI_SWIGLU; g.out = act; g.ldo = ff;
+    Timed t(c, CB_K_GEMM_GATE_UP, 2.0 * g.M * g.N * g.K);
+    e = bf ? cb::gemm_bf16(g, c->cs) : cb::gemm_f32(g, c->cs);
+    if (e != hipSuccess) return hip_fail(e, "gemm(gate_up) launch");
+  }
+  {  // hidden_next = h1 + act W_down^T
+    cb::GemmArgs g{};
+    g.A = act; g.lda = ff; g.B = W.w_down; g.ldb = ff;
+    g.M = n_new; g.N = dm; g.K = ff;
+    g.splits = bf ? pick_splits(g.M, g.N, g.K, wp.gpart_elems) : 1;
+    g.partial = (float*)(ws + wp.gpart);
+    g.epi = cb::EPI_RESID; g.out = hidden_next; g.ldo = dm; g.resid = h1; g.ldr = dm;
+    Timed t(c, CB_K_GEMM_DOWN, 2.0 * g.M * g.N * g.K);
+    e = bf ? cb::gemm_bf16(g, c->cs) : cb::gemm_f32(g, c->cs);
+    if (e != hipSuccess) return hip_fail(e, "gemm(down) launch");
+  }
+  return CB_OK;
+}
+
+cb_status cb_profile_enable(cb_ctx* c, int32_t on) {
+  cb_status st = check_ctx(c);
+  if (st) return st;
+  if (on) {
+    if (c->ev_pool.empty()) {
+      c->ev_pool.resize(2 * kMaxProf);
+      for (auto& ev : c->ev_pool) {
+        hipError_t e = hipEventCreate(&ev);
+        if (e != hipSuccess) return hip_fail(e, "hipEventCreate(profile)");
+      }
+    }
+    c->recs.clear();
+    c->recs.reserve(kMaxProf);
+    c->ev_used = 0;
+  }
+  c->prof = on != 0;
+  return CB_OK;
+}
+
+cb_status cb_profile_read(cb_ctx* c, int32_t kernel_id, double* total_ms, int64_t* launches, double* work) {
+  cb_status st = check_ctx(c);
+  if (st) return st;
+  if (kernel_id < 0 || kernel_id >= CB_K_COUNT) return fail(CB_EINVAL, "kernel id %d", kernel_id);
+  double ms = 0, wk = 0;
+  int64_t n = 0;
+  for (const ProfRec& r : c->recs) {
+    if (r.kernel != kernel_id) continue;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(profile)");
+    float t = 0;
+    e = hipEventElapsedTime(&t, r.start, r.stop);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    ms += t;
+    wk += r.work;
+    ++n;
+  }
+  if (total_ms) *total_ms = ms;
+  if (launches) *launches = n;
+  if (work) *work = wk;
+  return CB_OK;
+}
+
+}  // extern "C"

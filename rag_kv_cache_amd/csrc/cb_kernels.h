@@ -1,0 +1,48 @@
+// Internal launch interface between the C-ABI host code and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cb {
+
+enum Epi { EPI_STORE = 0, EPI_ROPE = 1, EPI_SWIGLU = 2, EPI_RESID = 3 };
+
+// C[M][N] = A[M][K] * B[N][K]^T with fp32 accumulation and a fused epilogue.
+struct GemmArgs {
+  const void* A; long lda; const int32_t* a_rows;  // A row of GEMM row m = a_rows ? a_rows[m] : m
+  const void* B; long ldb;
+  int swiglu_ffn;        // >0: tile t's columns 0..63 are B rows t*64.., columns 64..127 rows ffn + t*64..
+  int M, N, K, splits;   // N % 128 == 0, K % (64 * splits) == 0
+  float* partial;        // [splits][M][N] fp32 when splits > 1
+  int epi;               // Epi
+  void* out; long ldo;   // STORE/ROPE/SWIGLU: dtype; RESID: fp32
+  const int32_t* pos; const float2* rope; int rope_cols, head_dim, max_pos;  // ROPE
+  const float* resid; long ldr; const int32_t* resid_rows;                  // RESID
+};
+hipError_t gemm_bf16(const GemmArgs& g, hipStream_t s);
+hipError_t gemm_f32(const GemmArgs& g, hipStream_t s);
+
+// Causal GQA attention of n_q query rows (positions qpos, ascending) over K/V rows 0..N-1.
+struct AttnArgs {
+  const void* q; long ldq; const int32_t* qpos; int n_q;
+  const void* k; const void* v; int n_tok, hq, hkv, dh;
+  void* out; long ldo;
+  int splits, split_len;       // key range of split s: [s*split_len, (s+1)*split_len)
+  float* part_o; float* part_ml;
+  float scale_log2;            // log2(e) / sqrt(head_dim)
+};
+hipError_t attn_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t attn_f32(const AttnArgs& a, hipStream_t s);
+
+hipError_t embed(const int32_t* tok, int n, const void* table, int vocab, int d, int bf16, float* out,
+                 hipStream_t s);
+hipError_t rmsnorm(const float* h, long ldh, int n, int d, const float* g, float eps, void* out, int bf16,
+                   hipStream_t s);
+hipError_t rope_delta(const void* kc, const void* vc, void* kf, void* vf, int n_ctx, int hkv, int dh,
+                      const int32_t* offs, int n_chunks, const float2* table, int bf16, hipStream_t s);
+hipError_t dev_scatter(const void* fresh, long ld_fresh, void* fk, void* fv, const int32_t* sel, int n_sel,
+                       int n_cand, int n_tok, int row_elems, float* dev, int bf16, hipStream_t s);
+hipError_t topk_select(const float* dev, const int32_t* sel, int n_cand, int n_query, int k, int32_t* new_sel,
+                       int32_t* new_local, hipStream_t s);
+
+}  // namespace cb

@@ -1,0 +1,205 @@
+// Streaming kernels of the fusion step: embedding gather, RMSNorm, the RoPE position
+// update of cached K, and the fused deviation-score + scatter of fresh K/V rows.
+// All of them are HBM-bound; they use 16-byte vector accesses with consecutive lanes on
+// consecutive addresses, one wavefront (64 lanes) per row where a row reduction is needed.
+#include "cb_common.h"
+#include "cb_kernels.h"
+
+namespace cb {
+namespace {
+
+// ---------------------------------------------------------------- embedding gather
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* tok, int n, const T* table, int vocab, int d,
+                                                    float* out) {
+  const int row = blockIdx.x;
+  if (row >= n) return;
+  const int t = tok[row];
+  float* o = out + (long)row * d;
+  constexpr int VE = Vec16<T>::N;
+  for (int e = threadIdx.x * VE; e < d; e += blockDim.x * VE) {
+    float v[VE];
+    if (t >= 0 && t < vocab) {
+      Vec16<T>::load(table + (long)t * d + e, v);
+    } else {
+#pragma unroll
+      for (int i = 0; i < VE; ++i) v[i] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < VE; i += 4) *reinterpret_cast<float4*>(o + e + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+  }
+}
+
+// ---------------------------------------------------------------- RMSNorm
+// out[r] = h[r] / sqrt(mean(h[r]^2) + eps) * g, one wavefront per row, fp32 math.
+template <typename TO>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, long ldh, int n, int d, const float* g,
+                                                      float eps, TO* out) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n) return;
+  const float* x = h + (long)row * ldh;
+  float ss = 0.f;
+  for (int e = lane * 4; e < d; e += 256) {
+    float4 v = *reinterpret_cast<const float4*>(x + e);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)d + eps);
+  TO* o = out + (long)row * d;
+  for (int e = lane * 4; e < d; e += 256) {
+    float4 v = *reinterpret_cast<const float4*>(x + e);
+    float4 gg = *reinterpret_cast<const float4*>(g + e);
+    Elem<TO>::st(o + e + 0, v.x * r * gg.x);
+    Elem<TO>::st(o + e + 1, v.y * r * gg.y);
+    Elem<TO>::st(o + e + 2, v.z * r * gg.z);
+    Elem<TO>::st(o + e + 3, v.w * r * gg.w);
+  }
+}
+
+// ---------------------------------------------------------------- RoPE position update
+// For context row j of chunk c (offset o_c): K_f[j] = R(o_c) K_c[j] (half-split pairs
+// (i, i + dh/2), cos/sin of o_c * theta_i from the fp64-built table), V_f[j] = V_c[j] when
+// copy_v.  One work item = VE consecutive pairs of one head of one row: two 16-byte loads
+// (first and second half), two 16-byte stores.
+template <typename T>
+__global__ __launch_bounds__(256) void rope_delta_kernel(const T* kc, const T* vc, T* kf, T* vf, int n_ctx,
+                                                         int hkv, int dh, const int32_t* offs, int n_chunks,
+                                                         const float2* table, int copy_v) {
+  constexpr int VE = Vec16<T>::N;
+  const int half = dh >> 1;
+  const int vph = half / VE;
+  const int vpr = hkv * vph;
+  const long total = (long)n_ctx * vpr;
+  for (long it = (long)blockIdx.x * blockDim.x + threadIdx.x; it < total; it += (long)gridDim.x * blockDim.x) {
+    const int row = (int)(it / vpr);
+    const int rem = (int)(it - (long)row * vpr);
+    const int h = rem / vph;
+    const int i0 = (rem - h * vph) * VE;
+    int lo = 0, hi = n_chunks - 1;  // last chunk whose offset <= row
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (offs[mid] <= row) lo = mid; else hi = mid - 1;
+    }
+    const int o = offs[lo];
+    const long base = ((long)row * hkv + h) * dh + i0;
+    float a[VE], b[VE], ya[VE], yb[VE];
+    Vec16<T>::load(kc + base, a);
+    Vec16<T>::load(kc + base + half, b);
+    const float2* cs = table + (long)o * half + i0;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      const float2 t = cs[e];
+      ya[e] = a[e] * t.x - b[e] * t.y;
+      yb[e] = b[e] * t.x + a[e] * t.y;
+    }
+    Vec16<T>::store(kf + base, ya);
+    Vec16<T>::store(kf + base + half, yb);
+    if (copy_v) {
+      *reinterpret_cast<uint4*>(vf + base) = *reinterpret_cast<const uint4*>(vc + base);
+      *reinterpret_cast<uint4*>(vf + base + half) = *reinterpret_cast<const uint4*>(vc + base + half);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- deviation + scatter
+// One wavefront per recomputed row i (position j = sel[i]): for context rows (i < n_cand)
+// dev[i] = sum over the row's K and V elements of (fresh - fused)^2, read before the
+// fused row is overwritten; then fused[j] <- fresh[i].  fresh row layout: K heads then
+// V heads (row_elems each).  Per-lane sequential sums then a fixed butterfly: the result
+// does not depend on scheduling.
+template <typename T>
+__global__ __launch_bounds__(256) void dev_scatter_kernel(const T* fresh, long ld_fresh, T* fk, T* fv,
+                                                          const int32_t* sel, int n_sel, int n_cand, int n_tok,
+                                                          int row_elems, float* dev) {
+  constexpr int VE = Vec16<T>::N;
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (i >= n_sel) return;
+  const int j = sel[i];
+  const bool score = dev != nullptr && i < n_cand;
+  if (j < 0 || j >= n_tok) {
+    if (score && lane == 0) dev[i] = __builtin_nanf("");
+    return;
+  }
+  const T* fr = fresh + (long)i * ld_fresh;
+  T* dk = fk + (long)j * row_elems;
+  T* dv = fv + (long)j * row_elems;
+  float acc = 0.f;
+  for (int e = lane * VE; e < row_elems; e += 64 * VE) {
+    const uint4 nk = *reinterpret_cast<const uint4*>(fr + e);
+    const uint4 nv = *reinterpret_cast<const uint4*>(fr + row_elems + e);
+    if (score) {
+      float a[VE], b[VE];
+      Vec16<T>::load(fr + e, a);
+      Vec16<T>::load(dk + e, b);
+#pragma unroll
+      for (int q = 0; q < VE; ++q) { const float t = a[q] - b[q]; acc += t * t; }
+      Vec16<T>::load(fr + row_elems + e, a);
+      Vec16<T>::load(dv + e, b);
+#pragma unroll
+      for (int q = 0; q < VE; ++q) { const float t = a[q] - b[q]; acc += t * t; }
+    }
+    *reinterpret_cast<uint4*>(dk + e) = nk;
+    *reinterpret_cast<uint4*>(dv + e) = nv;
+  }
+  if (score) {
+    acc = wave_sum(acc);
+    if (lane == 0) dev[i] = acc;
+  }
+}
+
+}  // namespace
+
+hipError_t embed(const int32_t* tok, int n, const void* table, int vocab, int d, int bf16, float* out,
+                 hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(n), dim3(256), 0, s, tok, n, (const bf16_t*)table, vocab, d, out);
+  else
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(n), dim3(256), 0, s, tok, n, (const float*)table, vocab, d, out);
+  return hipGetLastError();
+}
+
+hipError_t rmsnorm(const float* h, long ldh, int n, int d, const float* g, float eps, void* out, int bf16,
+                   hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  dim3 grid((n + 3) / 4);
+  if (bf16)
+    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, grid, dim3(256), 0, s, h, ldh, n, d, g, eps, (bf16_t*)out);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, grid, dim3(256), 0, s, h, ldh, n, d, g, eps, (float*)out);
+  return hipGetLastError();
+}
+
+hipError_t rope_delta(const void* kc, const void* vc, void* kf, void* vf, int n_ctx, int hkv, int dh,
+                      const int32_t* offs, int n_chunks, const float2* table, int bf16, hipStream_t s) {
+  if (n_ctx <= 0) return hipSuccess;
+  const int ve = bf16 ? 8 : 4;
+  const long items = (long)n_ctx * hkv * (dh / 2 / ve);
+  long blocks = (items + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  const int copy_v = vc != vf;
+  if (bf16)
+    hipLaunchKernelGGL(rope_delta_kernel<bf16_t>, dim3((unsigned)blocks), dim3(256), 0, s, (const bf16_t*)kc,
+                       (const bf16_t*)vc, (bf16_t*)kf, (bf16_t*)vf, n_ctx, hkv, dh, offs, n_chunks, table, copy_v);
+  else
+    hipLaunchKernelGGL(rope_delta_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s, (const float*)kc,
+                       (const float*)vc, (float*)kf, (float*)vf, n_ctx, hkv, dh, offs, n_chunks, table, copy_v);
+  return hipGetLastError();
+}
+
+hipError_t dev_scatter(const void* fresh, long ld_fresh, void* fk, void* fv, const int32_t* sel, int n_sel,
+                       int n_cand, int n_tok, int row_elems, float* dev, int bf16, hipStream_t s) {
+  if (n_sel <= 0) return hipSuccess;
+  dim3 grid((n_sel + 3) / 4);
+  if (bf16)
+    hipLaunchKernelGGL(dev_scatter_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)fresh, ld_fresh,
+                       (bf16_t*)fk, (bf16_t*)fv, sel, n_sel, n_cand, n_tok, row_elems, dev);
+  else
+    hipLaunchKernelGGL(dev_scatter_kernel<float>, grid, dim3(256), 0, s, (const float*)fresh, ld_fresh,
+                       (float*)fk, (float*)fv, sel, n_sel, n_cand, n_tok, row_elems, dev);
+  return hipGetLastError();
+}
+
+}  // namespace cb

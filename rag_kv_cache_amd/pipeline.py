@@ -1,0 +1,270 @@
+"""Layer loop around the C ABI: weight upload, per-chunk cache build, blended prefill.
+
+PyTorch is used here only to allocate device memory, pinned host memory and streams; every
+step of the fusion runs in the HIP library through `rag_kv_cache_amd._lib`.
+
+The flow follows the pages:
+  * chunk caches: every chunk is prefilled alone at positions 0.. (CacheBlend explainer,
+    background: each retrieved document's KV can be precomputed independently);
+  * blended prefill: per layer, re-rotate the cache, recompute the selected rows, score and
+    narrow them, scatter, attend, then the rest of the layer on the kept rows (CacheBlend
+    review, per-layer flow; explainer, "Gradual filtering");
+  * the cached KV either sits in HBM, or in pinned host memory and is fetched one layer
+    ahead on a second stream (explainer, "Pipelined design": fetch_kv / synchronize).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Callable, Dict, List, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+def _ptr(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+class Engine:
+    """A library context plus the device weights of one model."""
+
+    def __init__(self, shape, max_tokens: int, device: int = 0, copy_stream: bool = True):
+        if not torch.cuda.is_available():
+            raise RuntimeError("a ROCm GPU is required: the fusion step runs only in the HIP library")
+        self.shape = shape
+        self.device = torch.device("cuda", device)
+        self.dtype = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+        self.compute = torch.cuda.Stream(self.device)
+        self.copy = torch.cuda.Stream(self.device) if copy_stream else None
+        desc = L.cb_model_desc(shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads,
+                               shape.head_dim, shape.ffn_dim, shape.vocab, max_tokens,
+                               float(shape.rope_base), float(shape.rms_eps),
+                               L.CB_BF16 if shape.dtype == "bf16" else L.CB_F32)
+        self.max_tokens = max_tokens
+        self.ctx = L.cb_create(desc, device, self.compute.cuda_stream,
+                               self.copy.cuda_stream if self.copy is not None else 0)
+        self.weights: List[Dict[str, torch.Tensor]] = [None] * shape.n_layers
+        self.emb: Optional[torch.Tensor] = None
+        self._ws: Optional[torch.Tensor] = None
+
+    def close(self):
+        if self.ctx:
+            L.cb_destroy(self.ctx)
+            self.ctx = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ------------------------------------------------------------ weights
+    def _dev(self, a: np.ndarray, dtype=None) -> torch.Tensor:
+        return torch.from_numpy(np.ascontiguousarray(a)).to(self.device).to(dtype or self.dtype)
+
+    def load_layer(self, layer: int, w: Dict[str, np.ndarray]) -> None:
+        """w: nn.Linear-layout float32 arrays w_q, w_k, w_v, w_o, w_gate, w_up, w_down, g_attn, g_ffn."""
+        t = {
+            "w_qkv": self._dev(np.concatenate([w["w_q"], w["w_k"], w["w_v"]])),
+            "w_o": self._dev(w["w_o"]),
+            "w_gate_up": self._dev(np.concatenate([w["w_gate"], w["w_up"]])),
+            "w_down": self._dev(w["w_down"]),
+            "g_attn": self._dev(w["g_attn"], torch.float32),
+            "g_ffn": self._dev(w["g_ffn"], torch.float32),
+        }
+        self.weights[layer] = t
+        L.cb_set_layer_weights(self.ctx, layer, _ptr(t["w_qkv"]), _ptr(t["w_o"]), _ptr(t["w_gate_up"]),
+                               _ptr(t["w_down"]), _ptr(t["g_attn"]), _ptr(t["g_ffn"]))
+
+    def load_embedding(self, emb: np.ndarray) -> None:
+        self.emb = self._dev(emb)
+
+    def load_all(self, layer_weights: Callable[[int], Dict[str, np.ndarray]], emb: np.ndarray) -> None:
+        """layer_weights(l) for l = 1..n_layers (1-based, as the fixtures number them)."""
+        for l in range(self.shape.n_layers):
+            self.load_layer(l, layer_weights(l + 1))
+        self.load_embedding(emb)
+        torch.cuda.synchronize(self.device)
+
+    # ------------------------------------------------------------ buffers
+    def workspace(self, n_tokens: int, n_sel_max: int) -> torch.Tensor:
+        need = L.cb_workspace_size(self.ctx, n_tokens, n_sel_max)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def kv_empty(self, rows: int) -> torch.Tensor:
+        s = self.shape
+        return torch.zeros(rows, s.n_kv_heads, s.head_dim, dtype=self.dtype, device=self.device)
+
+    # ------------------------------------------------------------ calls
+    def embed(self, tokens: torch.Tensor, out: torch.Tensor) -> None:
+        L.cb_embed(self.ctx, _ptr(tokens), int(tokens.numel()), _ptr(self.emb), _ptr(out))
+
+
+@dataclass
+class RunBuffers:
+    """Device buffers of one blended prefill of up to n_tokens rows."""
+    hidden: List[torch.Tensor]
+    sel: List[torch.Tensor]
+    iota: torch.Tensor
+    new_local: torch.Tensor
+    out_sel: torch.Tensor
+    dev: torch.Tensor
+    tokens: torch.Tensor
+    offsets: torch.Tensor
+    ws: torch.Tensor
+
+
+def make_buffers(eng: Engine, n_tokens: int, n_chunks: int) -> RunBuffers:
+    s, dv = eng.shape, eng.device
+    return RunBuffers(
+        hidden=[torch.empty(n_tokens, s.d_model, dtype=torch.float32, device=dv) for _ in range(2)],
+        sel=[torch.empty(n_tokens, dtype=torch.int32, device=dv) for _ in range(2)],
+        iota=torch.arange(n_tokens, dtype=torch.int32, device=dv),
+        new_local=torch.empty(n_tokens, dtype=torch.int32, device=dv),
+        out_sel=torch.empty(n_tokens, s.n_q_heads * s.head_dim, dtype=eng.dtype, device=dv),
+        dev=torch.empty(n_tokens, dtype=torch.float32, device=dv),
+        tokens=torch.empty(n_tokens, dtype=torch.int32, device=dv),
+        offsets=torch.empty(n_chunks + 1, dtype=torch.int32, device=dv),
+        ws=eng.workspace(n_tokens, n_tokens),
+    )
+
+
+@dataclass
+class LayerRecord:
+    sel: np.ndarray
+    new_sel: np.ndarray
+    deviation: np.ndarray
+    out_sel: np.ndarray
+    hidden_out: np.ndarray
+
+
+@dataclass
+class RunResult:
+    hidden: torch.Tensor          # [n_final, d] residual rows of the final kept set
+    sel: torch.Tensor             # [n_final] their positions
+    n_final: int
+    records: List[LayerRecord] = field(default_factory=list)
+
+
+def run_layers(eng: Engine, buf: RunBuffers, tokens: np.ndarray, offsets: Sequence[int], n_query: int,
+               schedule: Sequence[float], fused: List[Sequence[torch.Tensor]],
+               cache: Optional[List[Sequence[torch.Tensor]]] = None,
+               host_cache: Optional[List[List[Sequence[torch.Tensor]]]] = None,
+               record: bool = False, upload_inputs: bool = True,
+               layer_events: Optional[list] = None) -> RunResult:
+    """Blended prefill over every layer.
+
+    fused[l] = (K, V) device buffers [N, H_kv, d_h] of layer l (the fused cache, output).
+    cache[l] = (K, V) device [N_ctx, H_kv, d_h] offset-0 chunk caches in prompt order (HBM
+    mode: the position update copies them into fused[l]); or host_cache[l][c] = (K, V)
+    pinned host tensors of chunk c (prefetch mode: fetched one layer ahead into fused[l]
+    on the copy stream, then updated in place); or neither (the fused buffers are used as
+    they are, e.g. a full prefill with no context).
+    schedule[l] is the recompute ratio used at layer l.
+    upload_inputs=False reuses the token ids and offsets already on the device (a repeated
+    step then enqueues no host-to-device copy).  layer_events, if given, receives a CUDA event
+    recorded on the compute stream before the first layer and after every layer.
+    """
+    s = eng.shape
+    offs = [int(o) for o in offsets]
+    n_chunks = len(offs) - 1
+    n_ctx = offs[-1]
+    n_tok = n_ctx + n_query
+    assert len(tokens) == n_tok and len(schedule) == s.n_layers
+    cs = eng.compute
+    ctx = eng.ctx
+    with torch.cuda.stream(cs):
+        if upload_inputs:
+            buf.tokens[:n_tok].copy_(torch.from_numpy(np.asarray(tokens, np.int32)), non_blocking=False)
+            buf.offsets[: n_chunks + 1].copy_(torch.tensor(offs, dtype=torch.int32))
+    prefetch = host_cache is not None
+
+    def fetch(l):
+        if prefetch and l < s.n_layers:
+            hk = [_ptr(host_cache[l][c][0]) for c in range(n_chunks)]
+            hv = [_ptr(host_cache[l][c][1]) for c in range(n_chunks)]
+            L.cb_fetch_layer(ctx, l, hk, hv, offs, n_chunks, _ptr(fused[l][0]), _ptr(fused[l][1]))
+
+    if prefetch:
+        fetch(0)
+        fetch(1)
+    def mark():
+        if layer_events is not None:
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record(cs)
+            layer_events.append(ev)
+
+    L.cb_embed(ctx, _ptr(buf.tokens), n_tok, _ptr(eng.emb), _ptr(buf.hidden[0]))
+    mark()
+    n_sel, cur = n_tok, 0
+    records = []
+    ws = buf.ws
+    for l in range(s.n_layers):
+        if prefetch:
+            L.cb_synchronize(ctx, l)
+            fetch(l + 2)
+            ck, cv = fused[l]
+        elif cache is not None:
+            ck, cv = cache[l]
+        else:
+            ck, cv = None, None
+        fk, fv = fused[l]
+        h_in, h_out = buf.hidden[cur], buf.hidden[1 - cur]
+        sel_in = buf.iota if l == 0 else buf.sel[(l - 1) % 2]
+        sel_out = buf.sel[l % 2]
+        n_new = L.cb_blend_layer(ctx, l, _ptr(h_in), _ptr(ck), _ptr(cv), _ptr(fk), _ptr(fv),
+                                 _ptr(buf.offsets) if n_chunks else 0, offs, n_chunks, _ptr(sel_in), n_sel,
+                                 n_query, float(schedule[l]), _ptr(sel_out), _ptr(buf.new_local),
+                                 _ptr(buf.out_sel), _ptr(buf.dev), _ptr(ws), ws.numel())
+        L.cb_layer_rest(ctx, l, _ptr(h_in), n_sel, _ptr(buf.new_local), n_new, _ptr(buf.out_sel), _ptr(h_out),
+                        _ptr(ws), ws.numel())
+        if record:
+            cs.synchronize()
+            records.append(LayerRecord(
+                sel=sel_in[:n_sel].cpu().numpy().copy(), new_sel=sel_out[:n_new].cpu().numpy().copy(),
+                deviation=buf.dev[: n_sel - n_query].cpu().numpy().copy(),
+                out_sel=buf.out_sel[:n_new].float().cpu().numpy().copy(),
+                hidden_out=h_out[:n_new].cpu().numpy().copy()))
+        mark()
+        n_sel, cur = n_new, 1 - cur
+    final_sel = buf.sel[(s.n_layers - 1) % 2]
+    return RunResult(hidden=buf.hidden[cur], sel=final_sel, n_final=n_sel, records=records)
+
+
+def build_chunk_caches(eng: Engine, chunks: Sequence[np.ndarray], pinned_host: bool = False,
+                       keep_device: bool = True):
+    """Prefill every chunk alone at positions 0.. and keep its per-layer K/V.
+
+    Returns (device_cache, host_cache): device_cache[l] = (K, V) [N_ctx, H_kv, d_h] with chunk c
+    at rows [o_c, o_c + len_c) (or None); host_cache[l][c] = (K, V) pinned host tensors (or None).
+    """
+    s = eng.shape
+    lens = [len(c) for c in chunks]
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(int)
+    n_ctx = int(offs[-1])
+    dev_cache = [(eng.kv_empty(n_ctx), eng.kv_empty(n_ctx)) for _ in range(s.n_layers)] if keep_device else None
+    host_cache = [[None] * len(chunks) for _ in range(s.n_layers)] if pinned_host else None
+    lmax = max(lens)
+    buf = make_buffers(eng, lmax, 0)
+    tmp = [(eng.kv_empty(lmax), eng.kv_empty(lmax)) for _ in range(s.n_layers)]
+    for c, toks in enumerate(chunks):
+        n = len(toks)
+        fused = [(k[:n], v[:n]) for k, v in tmp]
+        run_layers(eng, buf, toks, [0], n, [1.0] * s.n_layers, fused)
+        with torch.cuda.stream(eng.compute):
+            for l in range(s.n_layers):
+                if keep_device:
+                    dev_cache[l][0][offs[c]:offs[c] + n].copy_(fused[l][0])
+                    dev_cache[l][1][offs[c]:offs[c] + n].copy_(fused[l][1])
+                if pinned_host:
+                    hk = torch.empty(fused[l][0].shape, dtype=eng.dtype, pin_memory=True)
+                    hv = torch.empty(fused[l][1].shape, dtype=eng.dtype, pin_memory=True)
+                    hk.copy_(fused[l][0])
+                    hv.copy_(fused[l][1])
+                    host_cache[l][c] = (hk, hv)
+        eng.compute.synchronize()
+    return dev_cache, host_cache

@@ -1,0 +1,59 @@
+"""CPU checks of the C-ABI library: it loads, exports every function include/cacheblend.h
+declares, and rejects invalid model descriptions before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cacheblend.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(cb_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ["cb_create", "cb_destroy", "cb_set_layer_weights", "cb_workspace_size", "cb_fetch_layer",
+              "cb_synchronize", "cb_blend_layer", "cb_layer_rest", "cb_last_error", "cb_embed"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    from rag_kv_cache_amd import _lib as L
+    lib = ctypes.CDLL(L.LIB_PATH)
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert sorted(L.exported_symbols()) == sorted(_declared())
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("n_layers", 0, -1), ("dtype", 7, -1), ("n_kv_heads", 3, -2), ("head_dim", 96, -6),
+    ("d_model", 200, -6), ("ffn_dim", 1000, -6), ("rope_base", -1.0, -1)])
+def test_create_rejects_bad_descriptions_without_gpu(field, value, status):
+    from rag_kv_cache_amd import _lib as L
+    d = L.cb_model_desc(2, 256, 4, 4, 64, 1024, 1000, 300, 10000.0, 1e-6, L.CB_F32)
+    setattr(d, field, value)
+    with pytest.raises(L.CbError) as e:
+        L.cb_create(d)
+    assert e.value.status == status
+    assert L.cb_last_error()
+
+
+def test_bf16_requires_head_dim_128():
+    from rag_kv_cache_amd import _lib as L
+    d = L.cb_model_desc(2, 256, 4, 4, 64, 1024, 1000, 300, 10000.0, 1e-6, L.CB_BF16)
+    with pytest.raises(L.CbError) as e:
+        L.cb_create(d)
+    assert e.value.status == L.CB_EUNSUPPORTED
+
+
+def test_null_context_is_rejected():
+    from rag_kv_cache_amd import _lib as L
+    with pytest.raises(L.CbError) as e:
+        L.cb_workspace_size(0, 10, 5)
+    assert e.value.status == L.CB_EINVAL

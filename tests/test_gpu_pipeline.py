@@ -1,0 +1,164 @@
+"""GPU parity of the whole fused prefill against the oracle (fixture workloads small enough
+for the oracle to finish in seconds; ragged chunk lengths; several GEMM/attention tiles)."""
+import numpy as np
+import pytest
+
+import fixtures as F
+import oracle as O
+from parity_util import assert_close, check_selected, local_index
+from gpu_setup import bits, engine, fused_buffers, to_np, weights
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_run(cfg, record=True):
+    from rag_kv_cache_amd.pipeline import build_chunk_caches, make_buffers, run_layers
+    wl = F.get_config(cfg)
+    eng = engine(cfg)
+    chunks, q = F.chunk_tokens(wl), F.query_tokens(wl)
+    cache, _ = build_chunk_caches(eng, chunks)
+    buf = make_buffers(eng, wl.n_tokens, len(chunks))
+    fused = fused_buffers(eng, wl.n_tokens)
+    res = run_layers(eng, buf, F.all_tokens(wl), F.chunk_offsets(wl), wl.n_query, wl.schedule, fused,
+                     cache=cache, record=record)
+    eng.compute.synchronize()
+    return wl, eng, cache, fused, res
+
+
+@pytest.mark.parametrize("cfg", ["tiny", "tiny3", "tiny_gqa"])
+def test_fp32_pipeline_matches_oracle(cfg):
+    wl, eng, cache, fused, res = _gpu_run(cfg)
+    sh = wl.shape
+    W, E = weights(cfg)
+    ref = O.blended_prefill(sh, W, E, F.chunk_tokens(wl), F.query_tokens(wl), wl.schedule)
+    offs = F.chunk_offsets(wl)
+    for l in range(sh.n_layers):  # chunk caches built on the GPU vs the oracle's
+        ck = np.concatenate([ref["caches"][c][l][0] for c in range(len(wl.chunk_lens))])
+        cv = np.concatenate([ref["caches"][c][l][1] for c in range(len(wl.chunk_lens))])
+        assert_close(to_np(cache[l][0]), ck, "f32", f"cache K layer {l}")
+        assert_close(to_np(cache[l][1]), cv, "f32", f"cache V layer {l}")
+    for l, (rec, L) in enumerate(zip(res.records, ref["layers"])):
+        n_cand = len(L["sel"]) - wl.n_query
+        assert np.array_equal(rec.sel, L["sel"]), f"layer {l}: S_l differs"
+        assert_close(rec.deviation, L["deviation"].astype(np.float32), "f32", f"deviation layer {l}")
+        flips = check_selected(rec.new_sel, L["new_sel"], L["deviation"], L["sel"][:n_cand], L["k"], wl.n_query)
+        assert flips == 0, f"layer {l}: near-tie flip breaks the pipeline comparison"
+        assert_close(to_np(fused[l][0]), L["fused_k"], "f32", f"fused K layer {l}")
+        assert_close(to_np(fused[l][1]), L["fused_v"], "f32", f"fused V layer {l}")
+        assert_close(rec.out_sel, L["out"], "f32", f"attention out layer {l}")
+        assert_close(rec.hidden_out, L["hidden_out"], "f32", f"hidden out layer {l}")
+    assert np.array_equal(res.sel[: res.n_final].cpu().numpy(), ref["sel"])
+
+
+def test_bf16_calls_teacher_forced():
+    """Each layer's blend_layer and layer_rest against the oracle on the GPU's own inputs
+    (bf16 rounding points emulated), so a near-tie resolved differently at one layer does not
+    propagate; plus the GPU chunk caches against the oracle's."""
+    cfg = "small_bf16"
+    wl, eng, cache, fused, res = _gpu_run(cfg)
+    sh = wl.shape
+    W, E = weights(cfg)
+    prec = O.Precision("bf16")
+    chunks = F.chunk_tokens(wl)
+    ref_caches = O.chunk_caches(sh, W, E, chunks, prec)
+    offs = F.chunk_offsets(wl)
+    for l in range(sh.n_layers):
+        assert_close(to_np(cache[l][0]), np.concatenate([c[l][0] for c in ref_caches]), "bf16", f"cache K {l}")
+        assert_close(to_np(cache[l][1]), np.concatenate([c[l][1] for c in ref_caches]), "bf16", f"cache V {l}")
+    hidden = np.asarray(E[F.all_tokens(wl)], np.float64)
+    flips_total = 0
+    for l, rec in enumerate(res.records):
+        gpu_cache = [(to_np(cache[l][0])[offs[c]:offs[c + 1]], to_np(cache[l][1])[offs[c]:offs[c + 1]])
+                     for c in range(len(chunks))]
+        fk, fv = O.fuse_cache(sh, prec, gpu_cache, offs, wl.n_query)
+        r = O.blend_layer(sh, W[l], prec, hidden, fk, fv, wl.n_ctx, rec.sel, wl.n_query, wl.schedule[l],
+                          new_sel_override=rec.new_sel)
+        # the oracle's own choice on the same inputs
+        r_own = O.blend_layer(sh, W[l], prec, hidden, fk, fv, wl.n_ctx, rec.sel, wl.n_query, wl.schedule[l])
+        n_cand = len(rec.sel) - wl.n_query
+        # rtol 1e-3 plus an absolute floor for layers where d is pure rounding noise (layer 1)
+        err = np.abs(rec.deviation - r["deviation"]) - 1e-3 * np.abs(r["deviation"])
+        assert err.max(initial=0.0) <= 1e-3, f"layer {l}: deviation err {err.max():.2e}"
+        flips_total += check_selected(rec.new_sel, r_own["new_sel"], r_own["deviation"], rec.sel[:n_cand],
+                                      r_own["k"], wl.n_query)
+        assert_close(to_np(fused[l][0]), r["fused_k"], "bf16", f"fused K layer {l}")
+        assert_close(to_np(fused[l][1]), r["fused_v"], "bf16", f"fused V layer {l}")
+        assert_close(rec.out_sel, r["out"], "bf16", f"attention out layer {l}")
+        h_ref = O.layer_rest(sh, W[l], prec, hidden, local_index(rec.sel, rec.new_sel), rec.out_sel)
+        assert_close(rec.hidden_out, h_ref, "bf16", f"hidden out layer {l}")
+        hidden = rec.hidden_out.astype(np.float64)
+    print(f"near-tie flips: {flips_total}")
+
+
+def test_repeat_runs_are_bit_identical():
+    from rag_kv_cache_amd.pipeline import make_buffers, run_layers
+    wl, eng, cache, fused, res = _gpu_run("small_bf16", record=False)
+    a = (res.hidden[: res.n_final].cpu().numpy().copy(), [bits(f[0]) for f in fused])
+    buf = make_buffers(eng, wl.n_tokens, len(wl.chunk_lens))
+    fused2 = fused_buffers(eng, wl.n_tokens)
+    res2 = run_layers(eng, buf, F.all_tokens(wl), F.chunk_offsets(wl), wl.n_query, wl.schedule, fused2,
+                      cache=cache)
+    eng.compute.synchronize()
+    assert res2.n_final == res.n_final
+    assert np.array_equal(res2.hidden[: res2.n_final].cpu().numpy(), a[0])
+    for x, y in zip(fused2, a[1]):
+        assert np.array_equal(bits(x[0]), y)
+
+
+def test_prefetch_path_equals_hbm_path():
+    """Pinned-host cache fetched a layer ahead on the copy stream and re-rotated in place gives
+    bit-identical results to the HBM-resident cache re-rotated by copy."""
+    from rag_kv_cache_amd.pipeline import build_chunk_caches, make_buffers, run_layers
+    cfg = "small_bf16"
+    wl = F.get_config(cfg)
+    eng = engine(cfg)
+    chunks = F.chunk_tokens(wl)
+    cache, host = build_chunk_caches(eng, chunks, pinned_host=True)
+    outs = []
+    for mode in ("hbm", "prefetch"):
+        buf = make_buffers(eng, wl.n_tokens, len(chunks))
+        fused = fused_buffers(eng, wl.n_tokens)
+        res = run_layers(eng, buf, F.all_tokens(wl), F.chunk_offsets(wl), wl.n_query, wl.schedule, fused,
+                         cache=cache if mode == "hbm" else None, host_cache=host if mode == "prefetch" else None)
+        eng.compute.synchronize()
+        outs.append((res.hidden[: res.n_final].cpu().numpy().copy(), res.sel[: res.n_final].cpu().numpy().copy(),
+                     [(bits(k), bits(v)) for k, v in fused]))
+    (h0, s0, f0), (h1, s1, f1) = outs
+    assert np.array_equal(s0, s1)
+    assert np.array_equal(h0, h1)
+    for (a, b), (c, d) in zip(f0, f1):
+        assert np.array_equal(a, c) and np.array_equal(b, d)
+
+
+@pytest.mark.parametrize("sched", [(1.0, 1.0, 1.0), (1.0, 0.0, 0.0)])
+def test_special_schedules(sched):
+    """Ratio 1 everywhere = full prefill of the whole prompt; ratio 0 keeps only query rows
+    and leaves the re-rotated cache in place."""
+    from rag_kv_cache_amd.pipeline import build_chunk_caches, make_buffers, run_layers
+    cfg = "tiny_gqa"
+    wl = F.get_config(cfg)
+    sh = wl.shape
+    W, E = weights(cfg)
+    eng = engine(cfg)
+    chunks = F.chunk_tokens(wl)
+    cache, _ = build_chunk_caches(eng, chunks)
+    buf = make_buffers(eng, wl.n_tokens, len(chunks))
+    fused = fused_buffers(eng, wl.n_tokens)
+    res = run_layers(eng, buf, F.all_tokens(wl), F.chunk_offsets(wl), wl.n_query, list(sched), fused,
+                     cache=cache, record=True)
+    eng.compute.synchronize()
+    if sched[1] == 1.0:
+        full = O.full_prefill(sh, W, E, F.all_tokens(wl))
+        for l in range(sh.n_layers):
+            assert_close(to_np(fused[l][0]), full["k"][l], "f32", f"K layer {l}")
+            assert_close(to_np(fused[l][1]), full["v"][l], "f32", f"V layer {l}")
+        assert_close(res.hidden[: res.n_final].cpu().numpy(), full["hidden"][-1], "f32", "hidden")
+    else:
+        assert res.records[1].new_sel.tolist() == list(range(wl.n_ctx, wl.n_tokens))
+        offs = F.chunk_offsets(wl)
+        for l in (2,):  # from layer 3 on no context row is recomputed: the re-rotated cache stays
+            rot = O.fuse_cache(sh, O.F64, [(to_np(cache[l][0])[offs[c]:offs[c + 1]],
+                                            to_np(cache[l][1])[offs[c]:offs[c + 1]]) for c in range(3)],
+                               offs, wl.n_query)
+            assert_close(to_np(fused[l][0])[: wl.n_ctx], rot[0][: wl.n_ctx], "f32", "rotated K")
+            assert np.array_equal(bits(fused[l][1][: wl.n_ctx]), bits(cache[l][1]))
