@@ -142,18 +142,23 @@ def main() -> int:
         step(cache=cache)
     cs.synchronize()
     torch.cuda.synchronize()
-    L.cb_profile_enable(eng.ctx, True)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step(cache=cache)
     cs.synchronize()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    L.cb_profile_enable(eng.ctx, False)
     wall = t1 - t0
     ms_step = wall / args.steps * 1e3
     value = n_ctx * args.steps / wall
     log(f"blended prefill: {ms_step:.3f} ms/step, {value:,.0f} context tokens/s")
+
+    # the same steps again with a HIP event pair around every launch (per-kernel durations)
+    L.cb_profile_enable(eng.ctx, True)
+    for _ in range(args.steps):
+        step(cache=cache)
+    cs.synchronize()
+    L.cb_profile_enable(eng.ctx, False)
 
     kernels = {}
     for kid, name in enumerate(L.KERNEL_NAMES):

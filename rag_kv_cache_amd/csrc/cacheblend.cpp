@@ -108,14 +108,20 @@ WsPlan plan_ws(const cb_model_desc& d, int n_tokens, int n_sel) {
   return p;
 }
 
-// Split-K factor: enough workgroups to cover the chip twice, each split at least 4 K-steps,
-// K divisible by 64 * splits, partials within the buffer.
+// Split-K factor: enough workgroups to cover the 256 CUs once (the large tile runs one
+// workgroup per CU), each split at least two 64-wide K-steps, K divisible by 64 * splits,
+// partials within the buffer.
 int pick_splits(int M, int N, int K, long cap_elems) {
-  const int tiles = ((M + 63) / 64) * (N / 128);
-  if (tiles >= 256) return 1;
-  int s = std::min(kGemmMaxSplits, (512 + tiles - 1) / tiles);
-  while (s > 1 && ((K % (64 * s)) != 0 || K / s < 256 || (long)s * M * N > cap_elems)) --s;
-  return std::max(s, 1);
+  const int tiles = cb::gemm_tiles(M, N);
+  if (tiles >= 200) return 1;
+  for (int s = 2; s <= kGemmMaxSplits; ++s) {
+    if (K % (64 * s) != 0 || K / s < 128 || (long)s * M * N > cap_elems) continue;
+    if (tiles * s >= 240) return s;
+  }
+  int best = 1;
+  for (int s = 2; s <= kGemmMaxSplits; ++s)
+    if (K % (64 * s) == 0 && K / s >= 128 && (long)s * M * N <= cap_elems) best = s;
+  return best;
 }
 
 void attn_splits(int n_q, int hkv, int n_tok, long cap_rows, int& splits, int& split_len) {

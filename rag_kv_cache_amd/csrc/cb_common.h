@@ -6,6 +6,8 @@
 typedef uint16_t bf16_t;  // bfloat16 storage
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));  // 16-byte staging register
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));  // 8-byte staging register
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
@@ -57,6 +59,25 @@ template <> struct Vec16<bf16_t> {
     *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 };
+
+// Two floats to packed bfloat16 (round to nearest even) with gfx950's v_cvt_pk_bf16_f32:
+// low half = lo, high half = hi.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  uint32_t r;
+  asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+  return r;
+}
+
+// gfx950 LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i
+// returns element i%4 of the 8 bytes addressed by lanes i/4, i/4+4, i/4+8, i/4+12 (in that
+// order): if lanes 4k..4k+3 address row k, dims 4q..4q+3 (q = lane%4) of a row-major tile,
+// lane i receives column i of the 4 rows.
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2_t lds_read_tr16(const bf16_t* p) {
+  typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
+  const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+  return __builtin_bit_cast(u32x2_t, r);
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -20,6 +20,10 @@ struct GemmArgs {
   const float* resid; long ldr; const int32_t* resid_rows;                  // RESID
 };
 hipError_t gemm_bf16(const GemmArgs& g, hipStream_t s);
+// Tile configuration the bf16 GEMM uses for an M x N problem, and its number of tiles
+// (the host sizes split-K from it).
+int gemm_config(int M, int N);
+int gemm_tiles(int M, int N);
 hipError_t gemm_f32(const GemmArgs& g, hipStream_t s);
 
 // Causal GQA attention of n_q query rows (positions qpos, ascending) over K/V rows 0..N-1.
@@ -32,6 +36,8 @@ struct AttnArgs {
   float scale_log2;            // log2(e) / sqrt(head_dim)
 };
 hipError_t attn_bf16(const AttnArgs& a, hipStream_t s);
+// Query rows per workgroup of the bf16 attention for n_q kept rows (16 or 32).
+int attn_rows_per_wg(int n_q);
 hipError_t attn_f32(const AttnArgs& a, hipStream_t s);
 
 hipError_t embed(const int32_t* tok, int n, const void* table, int vocab, int d, int bf16, float* out,

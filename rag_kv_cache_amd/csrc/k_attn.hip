@@ -23,163 +23,191 @@ namespace {
 
 constexpr float NEG_INF = -__builtin_huge_valf();
 
-template <int G>
+template <int G, int RB>
 __global__ __launch_bounds__(64 * G) void attn_bf16_kernel(AttnArgs a) {
-  constexpr int DH = 128, BKV = 64, NT = 64 * G;
-  constexpr int KSP = DH + 8;   // K tile pitch (bf16)
-  constexpr int VSP = BKV + 8;  // V^T tile pitch (bf16)
-  __shared__ __align__(16) bf16_t Ks[BKV * KSP];
-  __shared__ __align__(16) bf16_t Vt[DH * VSP];
+  constexpr int DH = 128, BKV = 64, NT = 64 * G, BQ = 16 * RB;
+  constexpr int KP = DH + 8;    // K tile pitch (272 B): 16-byte fragment reads of 16 rows hit disjoint banks
+  constexpr int VP = DH + 16;   // V tile pitch (288 B): transpose reads of 8 rows x 32 B hit disjoint banks
+  constexpr int NVEC = 2 * BKV * DH / 8;   // 16-byte vectors per K+V tile
+  constexpr int L_PT = (NVEC + NT - 1) / NT;
+  __shared__ __align__(16) bf16_t Ks[2][BKV * KP];
+  __shared__ __align__(16) bf16_t Vs[2][BKV * VP];
 
   const int qt = blockIdx.x / a.hkv;
   const int g = blockIdx.x - qt * a.hkv;
   const int split = blockIdx.y;
-  const int row0 = qt * 16;
-  const int last = min(row0 + 16, a.n_q) - 1;
+  const int row0 = qt * BQ;
+  const int last = min(row0 + BQ, a.n_q) - 1;
   const int maxpos = a.qpos[last];
   const int kbeg = split * a.split_len;
   if (kbeg > maxpos) return;
   const int kend = min(min(kbeg + a.split_len, maxpos + 1), a.n_tok);
   const int minpos = a.qpos[row0];
+  const int ntiles = (kend - kbeg + BKV - 1) / BKV;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = g * G + wave;
   const int l16 = lane & 15, lg = lane >> 4;
   const bf16_t* Q = reinterpret_cast<const bf16_t*>(a.q);
-  const bf16_t* Kg = reinterpret_cast<const bf16_t*>(a.k);
-  const bf16_t* Vg = reinterpret_cast<const bf16_t*>(a.v);
+  const bf16_t* Kg = reinterpret_cast<const bf16_t*>(a.k) + g * DH;
+  const bf16_t* Vg = reinterpret_cast<const bf16_t*>(a.v) + g * DH;
   const long kv_row = (long)a.hkv * DH;
+  const float c = a.scale_log2;
 
-  const int my_row = row0 + l16;
-  const bool row_ok = my_row < a.n_q;
-  const int mypos = row_ok ? a.qpos[my_row] : -1;
-  bf16x8_t qf[4];
+  int mypos[RB];
+  bf16x8_t qf[RB][4];
 #pragma unroll
-  for (int ds = 0; ds < 4; ++ds) {
-    if (row_ok)
-      qf[ds] = *reinterpret_cast<const bf16x8_t*>(Q + (long)my_row * a.ldq + h * DH + ds * 32 + lg * 8);
-    else
-      qf[ds] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = row0 + rb * 16 + l16;
+    const bool ok = r < a.n_q;
+    mypos[rb] = ok ? a.qpos[r] : -1;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds)
+      qf[rb][ds] = ok ? *reinterpret_cast<const bf16x8_t*>(Q + (long)r * a.ldq + h * DH + ds * 32 + lg * 8)
+                      : bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  float m_i[RB], l_i[RB];
+  f32x4_t o[RB][8];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_i[rb] = NEG_INF;
+    l_i[rb] = 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) o[rb][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  float m_i = NEG_INF, l_i = 0.f;
-  f32x4_t o[8];
-#pragma unroll
-  for (int d = 0; d < 8; ++d) o[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // K and V tiles staged through registers: vector v < 1024 is K (row v/16, 8 dims at
+  // 8*(v%16)), the rest V.  Keys past kend read key 0 (finite; masked out below).
+  u32x4_t rg[L_PT];
+#define CB_ALOAD(KT)                                                                                  \
+  _Pragma("unroll") for (int i = 0; i < L_PT; ++i) {                                                 \
+    const int v = tid + NT * i;                                                                      \
+    if (NVEC % NT == 0 || v < NVEC) {                                                                \
+      const int w = v & 1023;                                                                        \
+      int key = (KT) + (w >> 4);                                                                     \
+      key = key < kend ? key : 0;                                                                    \
+      const bf16_t* src = (v < 1024 ? Kg : Vg) + key * kv_row + (w & 15) * 8;                        \
+      rg[i] = *reinterpret_cast<const u32x4_t*>(src);                                                \
+    }                                                                                                \
+  }
+#define CB_AWRITE(ST)                                                                                 \
+  _Pragma("unroll") for (int i = 0; i < L_PT; ++i) {                                                 \
+    const int v = tid + NT * i;                                                                      \
+    if (NVEC % NT == 0 || v < NVEC) {                                                                \
+      const int w = v & 1023;                                                                        \
+      bf16_t* dst = v < 1024 ? &Ks[ST][(w >> 4) * KP + (w & 15) * 8] : &Vs[ST][(w >> 4) * VP + (w & 15) * 8]; \
+      *reinterpret_cast<u32x4_t*>(dst) = rg[i];                                                      \
+    }                                                                                                \
+  }
 
-  for (int kt = kbeg; kt < kend; kt += BKV) {
-    // K tile: 64 keys x 128 dims, 16-byte vectors, row-major in LDS
-    for (int v = tid; v < BKV * DH / 8; v += NT) {
-      const int kr = v >> 4, c = (v & 15) * 8;
-      const int key = kt + kr;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (key < kend) val = *reinterpret_cast<const uint4*>(Kg + key * kv_row + g * DH + c);
-      *reinterpret_cast<uint4*>(Ks + kr * KSP + c) = val;
-    }
-    // V tile transposed: micro-blocks of 4 keys x 4 dims (four 8-byte loads, four 8-byte stores)
-    for (int v = tid; v < (BKV / 4) * (DH / 4); v += NT) {
-      const int kb4 = v >> 5, d4 = v & 31;
-      uint2 r[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kt + kb4 * 4 + i;
-        r[i] = make_uint2(0, 0);
-        if (key < kend) r[i] = *reinterpret_cast<const uint2*>(Vg + key * kv_row + g * DH + d4 * 4);
-      }
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const int sh = (d & 1) * 16;
-        const uint32_t e0 = ((d < 2 ? r[0].x : r[0].y) >> sh) & 0xffffu;
-        const uint32_t e1 = ((d < 2 ? r[1].x : r[1].y) >> sh) & 0xffffu;
-        const uint32_t e2 = ((d < 2 ? r[2].x : r[2].y) >> sh) & 0xffffu;
-        const uint32_t e3 = ((d < 2 ? r[3].x : r[3].y) >> sh) & 0xffffu;
-        *reinterpret_cast<uint2*>(Vt + (d4 * 4 + d) * VSP + kb4 * 4) = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
-      }
-    }
-    __syncthreads();
+  CB_ALOAD(kbeg);
+  CB_AWRITE(0);
+  __syncthreads();
+  // V^T fragment addressing for the transpose reads: lane (group lg, j = l16) reads 8 bytes of key
+  // row 4*lg + j/4 (+16 for the second half), dims 16*d + 4*(j%4); it receives V[4 keys][dim 16*d + j].
+  const int vt_off = (4 * lg + (l16 >> 2)) * VP + 4 * (l16 & 3);
+  for (int t = 0; t < ntiles; ++t) {
+    const int st = t & 1;
+    const int kt = kbeg + t * BKV;
+    const bool more = t + 1 < ntiles;
+    if (more) { CB_ALOAD(kt + BKV); }
 
-    f32x4_t s[4];
+    f32x4_t s[RB][4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      s[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) s[rb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int ds = 0; ds < 4; ++ds) {
-        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(Ks + (kb * 16 + l16) * KSP + ds * 32 + lg * 8);
-        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[ds], s[kb], 0, 0, 0);
+        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(&Ks[st][(kb * 16 + l16) * KP + ds * 32 + lg * 8]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) s[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[rb][ds], s[rb][kb], 0, 0, 0);
+      }
+    // s[rb][kb][r] = raw score of row (rb*16 + l16) and key kt + 16*kb + 4*lg + r
+    const bool edge = (kt + BKV > kend) || (kt + BKV - 1 > minpos);
+    bf16x8_t pf[RB][2];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if (edge) {
+        const int thr = min(mypos[rb], kend - 1) - kt - 4 * lg;  // key offset 16*kb + r must be <= thr
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s[rb][kb][r] = (kb * 16 + r <= thr) ? s[rb][kb][r] : NEG_INF;
+      }
+      float mx = NEG_INF;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        mx = fmaxf(mx, fmaxf(fmaxf(s[rb][kb][0], s[rb][kb][1]), fmaxf(s[rb][kb][2], s[rb][kb][3])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_i[rb], mx);
+      const float alpha = (m_new == m_i[rb]) ? 1.f : __builtin_amdgcn_exp2f((m_i[rb] - m_new) * c);
+      const float mc = (m_new == NEG_INF) ? 0.f : m_new * c;
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[rb][kb][r], c, -mc));
+          s[rb][kb][r] = p;
+          rs += p;
+        }
+      rs += __shfl_xor(rs, 16, 64);
+      rs += __shfl_xor(rs, 32, 64);
+      l_i[rb] = l_i[rb] * alpha + rs;
+      m_i[rb] = m_new;
+      if (__ballot(alpha != 1.f)) {
+#pragma unroll
+        for (int d = 0; d < 8; ++d) o[rb][d] *= alpha;
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const u32x4_t w = {pack_bf16x2(s[rb][2 * ks][0], s[rb][2 * ks][1]), pack_bf16x2(s[rb][2 * ks][2], s[rb][2 * ks][3]),
+                           pack_bf16x2(s[rb][2 * ks + 1][0], s[rb][2 * ks + 1][1]),
+                           pack_bf16x2(s[rb][2 * ks + 1][2], s[rb][2 * ks + 1][3])};
+        pf[rb][ks] = __builtin_bit_cast(bf16x8_t, w);
       }
     }
-    const bool need_mask = (kt + BKV > kend) || (kt + BKV - 1 > minpos);
-    float mx = NEG_INF;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float x = s[kb][r] * a.scale_log2;
-        if (need_mask) {
-          const int key = kt + kb * 16 + lg * 4 + r;
-          if (key > mypos || key >= kend) x = NEG_INF;
-        }
-        s[kb][r] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_i, mx);
-    const bool dead = m_new == NEG_INF;
-    const float alpha = dead ? 1.f : exp2f(m_i - m_new);
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = dead ? 0.f : exp2f(s[kb][r] - m_new);
-        s[kb][r] = p;
-        rs += p;
-      }
-    rs += __shfl_xor(rs, 16, 64);
-    rs += __shfl_xor(rs, 32, 64);
-    l_i = l_i * alpha + rs;
-    m_i = m_new;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) o[d] *= alpha;
-
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t pf;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pf[r] = __builtin_bit_cast(__bf16, f32_to_bf16(s[2 * ks][r]));
-        pf[4 + r] = __builtin_bit_cast(__bf16, f32_to_bf16(s[2 * ks + 1][r]));
-      }
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
-        const bf16_t* vp = Vt + (d * 16 + l16) * VSP + ks * 32 + lg * 4;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vp);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16);
-        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf, o[d], 0, 0, 0);
+        const bf16_t* vp = &Vs[st][ks * 32 * VP + d * 16 + vt_off];
+        const u32x2_t lo = lds_read_tr16(vp);
+        const u32x2_t hi = lds_read_tr16(vp + 16 * VP);
+        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) o[rb][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[rb][ks], o[rb][d], 0, 0, 0);
       }
-    }
+    if (more) { CB_AWRITE(st ^ 1); }
     __syncthreads();
   }
+#undef CB_ALOAD
+#undef CB_AWRITE
 
-  if (!row_ok) return;
-  // o[d][r] = O[my_row][d*16 + 4*lg + r]
-  if (a.splits == 1) {
-    const float inv = l_i > 0.f ? 1.f / l_i : 0.f;
-    bf16_t* out = reinterpret_cast<bf16_t*>(a.out) + (long)my_row * a.ldo + h * DH + lg * 4;
+  // o[rb][d][r] = O[row rb*16 + l16][d*16 + 4*lg + r]
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      const uint32_t w0 = (uint32_t)f32_to_bf16(o[d][0] * inv) | ((uint32_t)f32_to_bf16(o[d][1] * inv) << 16);
-      const uint32_t w1 = (uint32_t)f32_to_bf16(o[d][2] * inv) | ((uint32_t)f32_to_bf16(o[d][3] * inv) << 16);
-      *reinterpret_cast<uint2*>(out + d * 16) = make_uint2(w0, w1);
+  for (int rb = 0; rb < RB; ++rb) {
+    const int my_row = row0 + rb * 16 + l16;
+    if (my_row >= a.n_q) continue;
+    if (a.splits == 1) {
+      const float inv = l_i[rb] > 0.f ? 1.f / l_i[rb] : 0.f;
+      bf16_t* out = reinterpret_cast<bf16_t*>(a.out) + (long)my_row * a.ldo + h * DH + lg * 4;
+#pragma unroll
+      for (int d = 0; d < 8; ++d)
+        *reinterpret_cast<u32x2_t*>(out + d * 16) =
+            u32x2_t{pack_bf16x2(o[rb][d][0] * inv, o[rb][d][1] * inv), pack_bf16x2(o[rb][d][2] * inv, o[rb][d][3] * inv)};
+    } else {
+      const long idx = ((long)split * a.n_q + my_row) * a.hq + h;
+      float* po = a.part_o + idx * DH + lg * 4;
+#pragma unroll
+      for (int d = 0; d < 8; ++d)
+        *reinterpret_cast<float4*>(po + d * 16) = make_float4(o[rb][d][0], o[rb][d][1], o[rb][d][2], o[rb][d][3]);
+      if (lg == 0) *reinterpret_cast<float2*>(a.part_ml + idx * 2) = make_float2(m_i[rb] * c, l_i[rb]);
     }
-  } else {
-    const long idx = ((long)split * a.n_q + my_row) * a.hq + h;
-    float* po = a.part_o + idx * DH + lg * 4;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) *reinterpret_cast<float4*>(po + d * 16) = make_float4(o[d][0], o[d][1], o[d][2], o[d][3]);
-    if (lg == 0) *reinterpret_cast<float2*>(a.part_ml + idx * 2) = make_float2(m_i, l_i);
   }
 }
 
@@ -252,22 +280,33 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
   for (int d = 0; d < DH; ++d) out[d] = acc[d] * inv;
 }
 
+template <int G>
+hipError_t launch_g(const AttnArgs& a, hipStream_t s) {
+  const int rows = attn_rows_per_wg(a.n_q);
+  dim3 grid(((a.n_q + rows - 1) / rows) * a.hkv, a.splits);
+  if (rows == 32)
+    hipLaunchKernelGGL((attn_bf16_kernel<G, 2>), grid, dim3(64 * G), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<G, 1>), grid, dim3(64 * G), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+int attn_rows_per_wg(int n_q) { return n_q >= 2048 ? 32 : 16; }
 
 hipError_t attn_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.n_q <= 0) return hipSuccess;
-  const int G = a.hq / a.hkv;
-  dim3 grid(((a.n_q + 15) / 16) * a.hkv, a.splits);
-  switch (G) {
-    case 1: hipLaunchKernelGGL(attn_bf16_kernel<1>, grid, dim3(64), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(attn_bf16_kernel<2>, grid, dim3(128), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(attn_bf16_kernel<4>, grid, dim3(256), 0, s, a); break;
-    case 6: hipLaunchKernelGGL(attn_bf16_kernel<6>, grid, dim3(384), 0, s, a); break;
-    case 7: hipLaunchKernelGGL(attn_bf16_kernel<7>, grid, dim3(448), 0, s, a); break;
-    case 8: hipLaunchKernelGGL(attn_bf16_kernel<8>, grid, dim3(512), 0, s, a); break;
+  hipError_t e;
+  switch (a.hq / a.hkv) {
+    case 1: e = launch_g<1>(a, s); break;
+    case 2: e = launch_g<2>(a, s); break;
+    case 4: e = launch_g<4>(a, s); break;
+    case 6: e = launch_g<6>(a, s); break;
+    case 7: e = launch_g<7>(a, s); break;
+    case 8: e = launch_g<8>(a, s); break;
     default: return hipErrorInvalidValue;
   }
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits <= 1) return e;
   const long total = (long)a.n_q * a.hq * (a.dh / 4);
   hipLaunchKernelGGL(attn_combine_kernel<bf16_t>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);

@@ -3,165 +3,150 @@
 // o-projection and the FFN down-projection (residual-add epilogue), and the FFN gate/up
 // projection (SwiGLU epilogue).
 //
-// bf16 path: v_mfma_f32_16x16x32_bf16 on gfx950.  Workgroup = 4 wavefronts (2 x 2), tile
-// BM x 128 x 64 (BM = 128 or 64), both operands staged through LDS with a 16-byte row pad,
-// double-buffered: the next K-slab is fetched into registers while the current one feeds
-// the MFMAs.  Rows of A may be gathered through an index list (the selected rows).
-// Tiles are assigned XCD-contiguously (see xcd_tile) so that the workgroups reading the
-// same weight columns run on one XCD and share its L2.
-// Split-K (grid.y > 1) writes fp32 partial tiles; a reduce kernel sums them and applies
-// the same epilogue.
+// Logical output columns are the weight rows in their natural order (for SwiGLU: the gate
+// rows, then the up rows).  The epilogues combine pairs of logical columns:
+//   RoPE   (n, n + head_dim/2) of the same head (rotation by the row's position),
+//   SwiGLU (f, ffn + f): silu(gate) * up of feature f,
+//   store / residual: independent columns.
 //
-// MFMA operand layout used (16x16x32, 8 bf16 per lane): lane l supplies row (l & 15) of A
-// and column (l & 15) of B, both with the same 8 reduction slots (l >> 4) * 8 .. + 7; lane l
-// receives C[4 * (l >> 4) + r][l & 15], r = 0..3.
+// bf16 path (v_mfma_f32_16x16x32_bf16, gfx950):
+//   * workgroup tile BM x BN x 64 with WM x WN wavefronts, each owning a (BM/WM) x (BN/WN)
+//     block of 16x16 MFMA tiles;
+//   * operands staged through two LDS buffers (rows padded by 16 bytes: the 16-byte fragment
+//     reads of 8 consecutive rows hit disjoint banks); global loads go to one of two register
+//     sets two K-steps ahead of the MFMAs that consume them, so each load has a whole K-step
+//     of MFMA work to hide behind and the LDS writes never wait on the newest loads;
+//   * inside each tile the weight rows are permuted in 16-row blocks so that the two
+//     columns of every epilogue pair land in adjacent MFMA tiles: the same lane then holds
+//     both values and the epilogue runs from registers;
+//   * rows of A may be gathered through an index list (the kept rows); rows past M read a
+//     clamped row (never stored), so the loads are branch-free;
+//   * tiles are assigned XCD-contiguously (xcd_tile) so that the workgroups reading the same
+//     weight rows share one XCD's L2;
+//   * split-K (grid.y > 1) writes fp32 partials in logical column order; a reduce kernel
+//     sums them and applies the same epilogue.
+//
+// MFMA 16x16x32 operand layout: lane l supplies row (l & 15) of A and column (l & 15) of B,
+// both with reduction slots (l >> 4) * 8 .. + 7; lane l receives C[4 * (l >> 4) + r][l & 15].
 #include "cb_common.h"
 #include "cb_kernels.h"
 
 namespace cb {
 namespace {
 
-constexpr int BN = 128;
 constexpr int BK = 64;
-constexpr int KP = BK + 8;    // LDS row pitch of A/B tiles (bf16 elements)
-constexpr int CP = BN + 4;    // LDS row pitch of the staged fp32 C tile
+constexpr int KP = BK + 8;  // LDS row pitch of A/B tiles (bf16 elements)
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
 
-// Column pair handled by epilogue item c (0..63) of a 128-wide tile.  RoPE rotates pairs
-// (i, i + head_dim/2) within each head; the other epilogues use (c, c + 64), which for the
-// SwiGLU tile is (gate, up) of the same FFN feature.
-__device__ __forceinline__ void epi_cols(int epi, int head_dim, int c, int& c0, int& c1) {
-  if (epi == EPI_ROPE) {
-    const int half = head_dim >> 1;
-    const int hb = c / half, i = c - hb * half;
-    c0 = hb * head_dim + i;
-    c1 = c0 + half;
+// Epilogue on one pair of logical columns (n_a, n_b) of row m.
+template <int EPI, typename TO>
+__device__ __forceinline__ void epi_pair(const GemmArgs& g, int m, int n_a, int n_b, float va, float vb) {
+  if (EPI == EPI_ROPE) {
+    if (n_a < g.rope_cols) {
+      int p = g.pos[m];
+      p = p < 0 ? 0 : (p > g.max_pos ? g.max_pos : p);
+      const float2 t = g.rope[(long)p * (g.head_dim >> 1) + (n_a % g.head_dim)];
+      const float ya = va * t.x - vb * t.y;
+      const float yb = vb * t.x + va * t.y;
+      va = ya;
+      vb = yb;
+    }
+    TO* o = (TO*)g.out + (long)m * g.ldo;
+    Elem<TO>::st(o + n_a, va);
+    Elem<TO>::st(o + n_b, vb);
+  } else if (EPI == EPI_SWIGLU) {
+    TO* o = (TO*)g.out + (long)m * g.ldo;
+    Elem<TO>::st(o + n_a, silu(va) * vb);
+  } else if (EPI == EPI_RESID) {
+    const long rr = g.resid_rows ? (long)g.resid_rows[m] : (long)m;
+    const float* r = g.resid + rr * g.ldr;
+    float* o = (float*)g.out + (long)m * g.ldo;
+    o[n_a] = r[n_a] + va;
+    o[n_b] = r[n_b] + vb;
   } else {
-    c0 = c;
-    c1 = c + 64;
+    TO* o = (TO*)g.out + (long)m * g.ldo;
+    Elem<TO>::st(o + n_a, va);
+    Elem<TO>::st(o + n_b, vb);
   }
 }
 
-template <typename TO>
-__device__ __forceinline__ void epi_apply(const GemmArgs& g, int m, int n0, int c0, int c1, float v0, float v1) {
-  switch (g.epi) {
-    case EPI_ROPE: {
-      const int n = n0 + c0;
-      if (n < g.rope_cols) {
-        int p = g.pos[m];
-        p = p < 0 ? 0 : (p > g.max_pos ? g.max_pos : p);
-        const int half = g.head_dim >> 1;
-        const float2 t = g.rope[(long)p * half + (n % g.head_dim)];
-        const float y0 = v0 * t.x - v1 * t.y;
-        const float y1 = v1 * t.x + v0 * t.y;
-        v0 = y0;
-        v1 = y1;
-      }
-      TO* o = (TO*)g.out + (long)m * g.ldo + n0;
-      Elem<TO>::st(o + c0, v0);
-      Elem<TO>::st(o + c1, v1);
-      break;
-    }
-    case EPI_SWIGLU: {
-      TO* o = (TO*)g.out + (long)m * g.ldo + (n0 >> 1);
-      Elem<TO>::st(o + c0, silu(v0) * v1);
-      break;
-    }
-    case EPI_RESID: {
-      const long rr = g.resid_rows ? (long)g.resid_rows[m] : (long)m;
-      const float* r = g.resid + rr * g.ldr + n0;
-      float* o = (float*)g.out + (long)m * g.ldo + n0;
-      o[c0] = r[c0] + v0;
-      o[c1] = r[c1] + v1;
-      break;
-    }
-    default: {
-      TO* o = (TO*)g.out + (long)m * g.ldo + n0;
-      Elem<TO>::st(o + c0, v0);
-      Elem<TO>::st(o + c1, v1);
-    }
+// Logical column of tile-local column tc (0..BN-1) of tile tn, for the bf16 kernel's
+// in-tile permutation.  Blocks of 16 columns come in pairs (2q, 2q+1) whose columns pair up.
+template <int EPI, int BN>
+__device__ __forceinline__ int logical_col(const GemmArgs& g, int tn, int tc) {
+  const int b = tc >> 4, j = tc & 15, q = b >> 1, odd = b & 1;
+  if (EPI == EPI_ROPE) {  // head_dim 128: block q of a head pairs dims 16q.. with 64 + 16q..
+    const int head = (tn * BN + tc) >> 7;
+    const int qh = q & 3;
+    return head * 128 + (odd ? 64 : 0) + qh * 16 + j;
   }
-}
-
-// Weight row feeding virtual column n of tile tn.
-__device__ __forceinline__ long b_row(const GemmArgs& g, int tn, int r) {
-  if (g.swiglu_ffn > 0) return r < 64 ? (long)tn * 64 + r : (long)g.swiglu_ffn + (long)tn * 64 + (r - 64);
-  return (long)tn * BN + r;
-}
-
-// Apply the epilogue to a BM x 128 fp32 tile staged in LDS (pitch CP).
-template <typename TO, int BMr, int NT>
-__device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const float* Cs, int m0, int n0) {
-  const int c = threadIdx.x & 63;
-  int c0, c1;
-  epi_cols(g.epi, g.head_dim, c, c0, c1);
-  for (int rr = threadIdx.x >> 6; rr < BMr; rr += NT / 64) {
-    const int m = m0 + rr;
-    if (m >= g.M) break;
-    epi_apply<TO>(g, m, n0, c0, c1, Cs[rr * CP + c0], Cs[rr * CP + c1]);
+  if (EPI == EPI_SWIGLU) {  // even blocks gate rows, odd blocks up rows of the same features
+    const int f = tn * (BN >> 1) + q * 16 + j;
+    return odd ? g.swiglu_ffn + f : f;
   }
+  return tn * BN + tc;
 }
 
-template <int BM>
-__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g) {
-  constexpr int WTM = BM / 2;        // wave tile rows (2 x 2 wavefronts)
-  constexpr int FM = WTM / 16;       // 16-row MFMA blocks per wave
-  constexpr int FN = 4;              // 16-col MFMA blocks per wave (64 cols)
-  constexpr int A_PT = BM * BK / 8 / 256;
-  constexpr int B_PT = BN * BK / 8 / 256;
+template <int BM, int BN, int WM, int WN, int EPI>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
+  constexpr int NT = 64 * WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 16, FN = WTN / 16;
+  constexpr int A_PT = BM * BK / 8 / NT;
+  constexpr int B_PT = BN * BK / 8 / NT;
+  constexpr int STAGE = (BM + BN) * KP;
+  static_assert(FN % 2 == 0 && A_PT >= 1 && B_PT >= 1, "tile shape");
   extern __shared__ __align__(16) unsigned char smem[];
-  bf16_t* As = reinterpret_cast<bf16_t*>(smem);  // [2][BM][KP]
-  bf16_t* Bs = As + 2 * BM * KP;                 // [2][BN][KP]
+  bf16_t* lds = reinterpret_cast<bf16_t*>(smem);
 
   const int tiles_m = (g.M + BM - 1) / BM;
   const int tiles_n = g.N / BN;
   const int tile = xcd_tile(blockIdx.x, tiles_m * tiles_n);
   if (tile < 0) return;
   const int tm = tile % tiles_m, tn = tile / tiles_m;
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * BM;
   const int k_len = g.K / g.splits;
-  const int kb = blockIdx.y * k_len, ke = kb + k_len;
+  const int kb = blockIdx.y * k_len;
+  const int nk = k_len / BK;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const bf16_t* A = reinterpret_cast<const bf16_t*>(g.A);
   const bf16_t* B = reinterpret_cast<const bf16_t*>(g.B);
 
   const bf16_t* a_src[A_PT];
-  bool a_ok[A_PT];
-  int a_off[A_PT];
+  int a_dst[A_PT];
 #pragma unroll
   for (int i = 0; i < A_PT; ++i) {
-    const int v = tid + 256 * i, r = v >> 3, c = (v & 7) * 8;
-    const int m = m0 + r;
-    a_ok[i] = m < g.M;
-    const long row = a_ok[i] ? (g.a_rows ? (long)g.a_rows[m] : (long)m) : 0;
-    a_src[i] = A + row * g.lda + c;
-    a_off[i] = r * KP + c;
+    const int v = tid + NT * i, r = v >> 3, c = (v & 7) * 8;
+    int m = m0 + r;
+    m = m < g.M ? m : g.M - 1;
+    const long row = g.a_rows ? (long)g.a_rows[m] : (long)m;
+    a_src[i] = A + row * g.lda + kb + c;
+    a_dst[i] = r * KP + c;
   }
   const bf16_t* b_src[B_PT];
-  int b_off[B_PT];
+  int b_dst[B_PT];
 #pragma unroll
   for (int i = 0; i < B_PT; ++i) {
-    const int v = tid + 256 * i, r = v >> 3, c = (v & 7) * 8;
-    b_src[i] = B + b_row(g, tn, r) * g.ldb + c;
-    b_off[i] = r * KP + c;
+    const int v = tid + NT * i, r = v >> 3, c = (v & 7) * 8;
+    b_src[i] = B + (long)logical_col<EPI, BN>(g, tn, r) * g.ldb + kb + c;
+    b_dst[i] = (BM + r) * KP + c;
   }
 
-  uint4 ra[A_PT], rb[B_PT];
-  auto gload = [&](int k) {
-#pragma unroll
-    for (int i = 0; i < A_PT; ++i) ra[i] = a_ok[i] ? *reinterpret_cast<const uint4*>(a_src[i] + k) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < B_PT; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + k);
-  };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < A_PT; ++i) *reinterpret_cast<uint4*>(As + buf * BM * KP + a_off[i]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < B_PT; ++i) *reinterpret_cast<uint4*>(Bs + buf * BN * KP + b_off[i]) = rb[i];
-  };
+  u32x4_t ra0[A_PT], rb0[B_PT], ra1[A_PT], rb1[B_PT];
+#define CB_GLOAD(RA, RB, KK)                                                                           \
+  {                                                                                                   \
+    _Pragma("unroll") for (int i = 0; i < A_PT; ++i) RA[i] = *reinterpret_cast<const u32x4_t*>(a_src[i] + (KK)); \
+    _Pragma("unroll") for (int i = 0; i < B_PT; ++i) RB[i] = *reinterpret_cast<const u32x4_t*>(b_src[i] + (KK)); \
+  }
+#define CB_SWRITE(RA, RB, S)                                                                           \
+  {                                                                                                   \
+    bf16_t* st_ = lds + (S) * STAGE;                                                                  \
+    _Pragma("unroll") for (int i = 0; i < A_PT; ++i) *reinterpret_cast<u32x4_t*>(st_ + a_dst[i]) = RA[i];        \
+    _Pragma("unroll") for (int i = 0; i < B_PT; ++i) *reinterpret_cast<u32x4_t*>(st_ + b_dst[i]) = RB[i];        \
+  }
 
   f32x4_t acc[FM][FN];
 #pragma unroll
@@ -169,110 +154,140 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  gload(kb);
-  swrite(0);
-  __syncthreads();
-  int buf = 0;
-  for (int k = kb; k < ke; k += BK) {
-    const bool more = k + BK < ke;
-    if (more) gload(k + BK);
-    const bf16_t* Ab = As + buf * BM * KP + (wm * WTM + (lane & 15)) * KP + (lane >> 4) * 8;
-    const bf16_t* Bb = Bs + buf * BN * KP + (wn * 64 + (lane & 15)) * KP + (lane >> 4) * 8;
-#pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      bf16x8_t af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(Ab + i * 16 * KP + ks * 32);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bb + j * 16 * KP + ks * 32);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (more) swrite(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
+  const int a_frag = (wm * WTM + (lane & 15)) * KP + (lane >> 4) * 8;
+  const int b_frag = (BM + wn * WTN + (lane & 15)) * KP + (lane >> 4) * 8;
+#define CB_COMPUTE(S)                                                                                  \
+  {                                                                                                   \
+    const bf16_t* Ab = lds + (S) * STAGE + a_frag;                                                    \
+    const bf16_t* Bb = lds + (S) * STAGE + b_frag;                                                    \
+    _Pragma("unroll") for (int ks = 0; ks < BK / 32; ++ks) {                                          \
+      bf16x8_t af[FM], bfr[FN];                                                                       \
+      _Pragma("unroll") for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(Ab + i * 16 * KP + ks * 32); \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bb + j * 16 * KP + ks * 32); \
+      _Pragma("unroll") for (int i = 0; i < FM; ++i)                                                  \
+        _Pragma("unroll") for (int j = 0; j < FN; ++j)                                                \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);    \
+    }                                                                                                 \
   }
 
-  if (g.splits > 1) {  // fp32 partial tile straight from registers
-    float* P = g.partial + (long)blockIdx.y * g.M * g.N;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = m0 + wm * WTM + i * 16 + (lane >> 4) * 4 + r;
-          const int n = n0 + wn * 64 + j * 16 + (lane & 15);
-          if (m < g.M) P[(long)m * g.N + n] = acc[i][j][r];
-        }
-    return;
+  // Prologue: K-step 0 into LDS stage 0, K-step 1 in flight in register set 1.
+  CB_GLOAD(ra0, rb0, 0);
+  if (nk > 1) CB_GLOAD(ra1, rb1, BK);
+  CB_SWRITE(ra0, rb0, 0);
+  __syncthreads();
+  for (int it = 0; it < nk; it += 2) {
+    // even K-step: LDS stage 0; register set 1 holds K-step it+1, set 0 is free
+    if (it + 2 < nk) CB_GLOAD(ra0, rb0, (it + 2) * BK);
+    CB_COMPUTE(0);
+    if (it + 1 < nk) CB_SWRITE(ra1, rb1, 1);
+    __syncthreads();
+    if (it + 1 >= nk) break;
+    // odd K-step: LDS stage 1; register set 0 holds K-step it+2, set 1 is free
+    if (it + 3 < nk) CB_GLOAD(ra1, rb1, (it + 3) * BK);
+    CB_COMPUTE(1);
+    if (it + 2 < nk) CB_SWRITE(ra0, rb0, 0);
+    __syncthreads();
   }
-  float* Cs = reinterpret_cast<float*>(smem);  // [BM][CP]; A/B tiles are no longer read
+#undef CB_GLOAD
+#undef CB_SWRITE
+#undef CB_COMPUTE
+
+  // Epilogue from registers: tiles (i, 2q) and (i, 2q+1) hold the two columns of each pair.
+  const int row_base = m0 + wm * WTM + (lane >> 4) * 4;
+  float* P = g.partial + (long)blockIdx.y * g.M * g.N;
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+    for (int q = 0; q < FN / 2; ++q) {
+      const int tc = wn * WTN + q * 32 + (lane & 15);
+      const int n_a = logical_col<EPI, BN>(g, tn, tc);
+      const int n_b = logical_col<EPI, BN>(g, tn, tc + 16);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        Cs[(wm * WTM + i * 16 + (lane >> 4) * 4 + r) * CP + wn * 64 + j * 16 + (lane & 15)] = acc[i][j][r];
-  __syncthreads();
-  tile_epilogue<bf16_t, BM, 256>(g, Cs, m0, n0);
+      for (int r = 0; r < 4; ++r) {
+        const int m = row_base + i * 16 + r;
+        if (m >= g.M) continue;
+        const float va = acc[i][2 * q][r], vb = acc[i][2 * q + 1][r];
+        if (g.splits > 1) {
+          P[(long)m * g.N + n_a] = va;
+          P[(long)m * g.N + n_b] = vb;
+        } else {
+          epi_pair<EPI, bf16_t>(g, m, n_a, n_b, va, vb);
+        }
+      }
+    }
 }
 
-// Sum split-K partials and apply the epilogue.  grid = (ceil(M/4), N/128), 256 threads:
-// 4 rows x 64 column pairs.
-template <typename TO>
+// Sum split-K partials (logical columns) and apply the epilogue.  One thread per column pair.
+template <int EPI>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
-  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int n0 = blockIdx.y * BN;
-  if (m >= g.M) return;
-  int c0, c1;
-  epi_cols(g.epi, g.head_dim, threadIdx.x & 63, c0, c1);
-  float v0 = 0.f, v1 = 0.f;
-  const long stride = (long)g.M * g.N;
-  const float* p = g.partial + (long)m * g.N + n0;
-  for (int s = 0; s < g.splits; ++s) {
-    v0 += p[s * stride + c0];
-    v1 += p[s * stride + c1];
+  const long half = g.N / 2;
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)g.M * half) return;
+  const int m = (int)(idx / half);
+  const int j = (int)(idx - (long)m * half);
+  int n_a, n_b;
+  if (EPI == EPI_ROPE) {
+    n_a = (j >> 6) * 128 + (j & 63);
+    n_b = n_a + 64;
+  } else if (EPI == EPI_SWIGLU) {
+    n_a = j;
+    n_b = j + g.swiglu_ffn;
+  } else {
+    n_a = j;
+    n_b = j + (int)half;
   }
-  epi_apply<TO>(g, m, n0, c0, c1, v0, v1);
+  const long stride = (long)g.M * g.N;
+  const float* p = g.partial + (long)m * g.N;
+  float va = 0.f, vb = 0.f;
+  for (int s = 0; s < g.splits; ++s) {
+    va += p[s * stride + n_a];
+    vb += p[s * stride + n_b];
+  }
+  epi_pair<EPI, bf16_t>(g, m, n_a, n_b, va, vb);
 }
 
-// fp32 path (correctness configurations): tile 64 x 128 x 16 on the vector ALUs, each
-// thread 4 rows x 8 columns, operands through LDS, same epilogues.
+// ------------------------------------------------------------------ fp32 path
+// Correctness configurations: tile 64 x 128 x 16 on the vector ALUs, each thread 4 rows x 8
+// columns, operands through LDS; the C tile is staged in LDS and the epilogue pairs columns
+// (c, c + 64) of the tile, with the weight rows mapped so that such a pair is a RoPE pair
+// (head_dim 64 or 128) or a (gate, up) pair.
+constexpr int FBN = 128;
+constexpr int FCP = FBN + 4;
+
+__device__ __forceinline__ long f32_b_row(const GemmArgs& g, int tn, int r) {
+  if (g.swiglu_ffn > 0) return r < 64 ? (long)tn * 64 + r : (long)g.swiglu_ffn + (long)tn * 64 + (r - 64);
+  return (long)tn * FBN + r;
+}
+
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   constexpr int FBM = 64, FBK = 16;
-  __shared__ __align__(16) float smem[FBM * CP];  // staged C tile; also holds the A/B tiles
+  __shared__ __align__(16) float smem[FBM * FCP];  // staged C tile; also holds the A/B tiles
   float* As = smem;                // [FBK][FBM]
-  float* Bs = smem + FBK * FBM;    // [FBK][BN]
+  float* Bs = smem + FBK * FBM;    // [FBK][FBN]
   const int tiles_m = (g.M + FBM - 1) / FBM;
   const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
-  const int m0 = tm * FBM, n0 = tn * BN;
+  const int m0 = tm * FBM, n0 = tn * FBN;
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   const float* A = reinterpret_cast<const float*>(g.A);
   const float* B = reinterpret_cast<const float*>(g.B);
   float acc[4][8] = {};
-  // A tile: 64 rows x 16 k = 256 float4, one per thread.  B tile: 128 x 16 = 512 float4.
   const int ar = tid >> 2, ak = (tid & 3) * 4;
   const int am = m0 + ar;
   const bool a_ok = am < g.M;
   const float* a_src = A + (a_ok ? (g.a_rows ? (long)g.a_rows[am] : (long)am) : 0) * g.lda + ak;
   const int br = tid >> 2, bk = (tid & 3) * 4;
-  const float* b_src0 = B + b_row(g, tn, br) * g.ldb + bk;
-  const float* b_src1 = B + b_row(g, tn, br + 64) * g.ldb + bk;
+  const float* b_src0 = B + f32_b_row(g, tn, br) * g.ldb + bk;
+  const float* b_src1 = B + f32_b_row(g, tn, br + 64) * g.ldb + bk;
   for (int k = 0; k < g.K; k += FBK) {
     const float4 av = a_ok ? *reinterpret_cast<const float4*>(a_src + k) : make_float4(0, 0, 0, 0);
     const float4 b0 = *reinterpret_cast<const float4*>(b_src0 + k);
     const float4 b1 = *reinterpret_cast<const float4*>(b_src1 + k);
     As[(ak + 0) * FBM + ar] = av.x; As[(ak + 1) * FBM + ar] = av.y;
     As[(ak + 2) * FBM + ar] = av.z; As[(ak + 3) * FBM + ar] = av.w;
-    Bs[(bk + 0) * BN + br] = b0.x; Bs[(bk + 1) * BN + br] = b0.y;
-    Bs[(bk + 2) * BN + br] = b0.z; Bs[(bk + 3) * BN + br] = b0.w;
-    Bs[(bk + 0) * BN + br + 64] = b1.x; Bs[(bk + 1) * BN + br + 64] = b1.y;
-    Bs[(bk + 2) * BN + br + 64] = b1.z; Bs[(bk + 3) * BN + br + 64] = b1.w;
+    Bs[(bk + 0) * FBN + br] = b0.x; Bs[(bk + 1) * FBN + br] = b0.y;
+    Bs[(bk + 2) * FBN + br] = b0.z; Bs[(bk + 3) * FBN + br] = b0.w;
+    Bs[(bk + 0) * FBN + br + 64] = b1.x; Bs[(bk + 1) * FBN + br + 64] = b1.y;
+    Bs[(bk + 2) * FBN + br + 64] = b1.z; Bs[(bk + 3) * FBN + br + 64] = b1.w;
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < FBK; ++kk) {
@@ -280,7 +295,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
       const float a[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float b = Bs[kk * BN + tx + 16 * j];
+        const float b = Bs[kk * FBN + tx + 16 * j];
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i][j] = fmaf(a[i], b, acc[i][j]);
       }
@@ -290,46 +305,87 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) smem[(ty * 4 + i) * CP + tx + 16 * j] = acc[i][j];
+    for (int j = 0; j < 8; ++j) smem[(ty * 4 + i) * FCP + tx + 16 * j] = acc[i][j];
   __syncthreads();
-  tile_epilogue<float, FBM, 256>(g, smem, m0, n0);
+  const int c = tid & 63;
+  int c0 = c, c1 = c + 64;
+  if (g.epi == EPI_ROPE) {
+    const int half = g.head_dim >> 1;
+    const int hb = c / half, i = c - hb * half;
+    c0 = hb * g.head_dim + i;
+    c1 = c0 + half;
+  }
+  for (int rr = tid >> 6; rr < FBM; rr += 4) {
+    const int m = m0 + rr;
+    if (m >= g.M) break;
+    const float v0 = smem[rr * FCP + c0], v1 = smem[rr * FCP + c1];
+    switch (g.epi) {
+      case EPI_ROPE: epi_pair<EPI_ROPE, float>(g, m, n0 + c0, n0 + c1, v0, v1); break;
+      case EPI_SWIGLU: epi_pair<EPI_SWIGLU, float>(g, m, tn * 64 + c, 0, v0, v1); break;
+      case EPI_RESID: epi_pair<EPI_RESID, float>(g, m, n0 + c0, n0 + c1, v0, v1); break;
+      default: epi_pair<EPI_STORE, float>(g, m, n0 + c0, n0 + c1, v0, v1);
+    }
+  }
 }
 
-template <int BM>
-constexpr int bf16_lds_bytes() {
-  return (2 * (BM + BN) * KP * 2) > (BM * CP * 4) ? (2 * (BM + BN) * KP * 2) : (BM * CP * 4);
-}
-
-template <int BM>
-hipError_t launch_bf16(const GemmArgs& g, hipStream_t s) {
+// ------------------------------------------------------------------ launch
+template <int BM, int BN, int WM, int WN, int EPI>
+hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
+  constexpr int lds = 2 * (BM + BN) * KP * 2;
   static bool attr_set = false;
-  constexpr int lds = bf16_lds_bytes<BM>();
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<BM>,
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<BM, BN, WM, WN, EPI>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int tiles = ((g.M + BM - 1) / BM) * (g.N / BN);
   const int grid_x = 8 * ((tiles + 7) / 8);
-  hipLaunchKernelGGL(gemm_bf16_kernel<BM>, dim3(grid_x, g.splits), dim3(256), lds, s, g);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI>), dim3(grid_x, g.splits), dim3(64 * WM * WN), lds, s, g);
+  return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
+  hipError_t e;
+  const int cfg = gemm_config(g.M, g.N);
+  if (cfg == 0) e = launch_cfg<128, 256, 2, 4, EPI>(g, s);
+  else if (cfg == 1) e = launch_cfg<64, 256, 1, 4, EPI>(g, s);
+  else e = launch_cfg<128, 128, 2, 2, EPI>(g, s);
+  if (e != hipSuccess || g.splits <= 1) return e;
+  const long items = (long)g.M * (g.N / 2);
+  hipLaunchKernelGGL(splitk_reduce_kernel<EPI>, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
 }  // namespace
 
+int gemm_config(int M, int N) {
+  if (N % 256 != 0) return 2;
+  return M > 64 ? 0 : 1;
+}
+
+int gemm_tiles(int M, int N) {
+  switch (gemm_config(M, N)) {
+    case 0: return ((M + 127) / 128) * (N / 256);
+    case 1: return ((M + 63) / 64) * (N / 256);
+    default: return ((M + 127) / 128) * (N / 128);
+  }
+}
+
 hipError_t gemm_bf16(const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0) return hipSuccess;
-  const int tiles128 = ((g.M + 127) / 128) * (g.N / BN);
-  hipError_t e = (tiles128 >= 240) ? launch_bf16<128>(g, s) : launch_bf16<64>(g, s);
-  if (e != hipSuccess || g.splits <= 1) return e;
-  hipLaunchKernelGGL(splitk_reduce_kernel<bf16_t>, dim3((g.M + 3) / 4, g.N / BN), dim3(256), 0, s, g);
-  return hipGetLastError();
+  switch (g.epi) {
+    case EPI_ROPE: return launch_epi<EPI_ROPE>(g, s);
+    case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(g, s);
+    case EPI_RESID: return launch_epi<EPI_RESID>(g, s);
+    default: return launch_epi<EPI_STORE>(g, s);
+  }
 }
 
 hipError_t gemm_f32(const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0) return hipSuccess;
-  const int tiles = ((g.M + 63) / 64) * (g.N / BN);
+  const int tiles = ((g.M + 63) / 64) * (g.N / FBN);
   hipLaunchKernelGGL(gemm_f32_kernel, dim3(tiles), dim3(256), 0, s, g);
   return hipGetLastError();
 }
