@@ -12,10 +12,8 @@
 // bf16 path (v_mfma_f32_16x16x32_bf16, gfx950):
 //   * workgroup tile BM x BN x 64 with WM x WN wavefronts, each owning a (BM/WM) x (BN/WN)
 //     block of 16x16 MFMA tiles;
-//   * operands staged through two LDS buffers (rows padded by 16 bytes: the 16-byte fragment
-//     reads of 8 consecutive rows hit disjoint banks); global loads go to one of two register
-//     sets two K-steps ahead of the MFMAs that consume them, so each load has a whole K-step
-//     of MFMA work to hide behind and the LDS writes never wait on the newest loads;
+//   * operands go global -> LDS directly (global_load_lds_dwordx4, no staging registers) into
+//     a 3-stage ring, two K-steps ahead of the MFMAs; one barrier per K-step;
 //   * inside each tile the weight rows are permuted in 16-row blocks so that the two
 //     columns of every epilogue pair land in adjacent MFMA tiles: the same lane then holds
 //     both values and the epilogue runs from registers;
@@ -35,7 +33,6 @@ namespace cb {
 namespace {
 
 constexpr int BK = 64;
-constexpr int KP = BK + 8;  // LDS row pitch of A/B tiles (bf16 elements)
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
 
@@ -88,17 +85,25 @@ __device__ __forceinline__ int logical_col(const GemmArgs& g, int tn, int tc) {
   return tn * BN + tc;
 }
 
+// Each global_load_lds_dwordx4 wave instruction writes its 64 lanes x 16 bytes contiguously
+// (lane l at byte 16 l), i.e. 8 tile rows of 128 bytes; the 16-byte chunks of row r are stored
+// XOR-swizzled (chunk c at slot c ^ (r & 7)) so that fragment reads of 8 consecutive rows hit
+// disjoint banks.
+typedef __attribute__((address_space(1))) void gvoid_t;
+typedef __attribute__((address_space(3))) void lvoid_t;
+
 template <int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
-  constexpr int NT = 64 * WM * WN;
+  constexpr int NT = 64 * WM * WN, NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 16, FN = WTN / 16;
-  constexpr int A_PT = BM * BK / 8 / NT;
-  constexpr int B_PT = BN * BK / 8 / NT;
-  constexpr int STAGE = (BM + BN) * KP;
-  static_assert(FN % 2 == 0 && A_PT >= 1 && B_PT >= 1, "tile shape");
+  constexpr int ROWB = BK * 2;                       // 128 bytes per tile row
+  constexpr int STAGE_B = (BM + BN) * ROWB;
+  constexpr int NSTAGE = 3;
+  constexpr int A_INS = BM / 8, B_INS = BN / 8;      // 1 KB wave instructions per tile
+  constexpr int A_PW = A_INS / NW, B_PW = B_INS / NW;
+  static_assert(FN % 2 == 0 && A_INS % NW == 0 && B_INS % NW == 0, "tile shape");
   extern __shared__ __align__(16) unsigned char smem[];
-  bf16_t* lds = reinterpret_cast<bf16_t*>(smem);
 
   const int tiles_m = (g.M + BM - 1) / BM;
   const int tiles_n = g.N / BN;
@@ -112,41 +117,35 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  const bf16_t* A = reinterpret_cast<const bf16_t*>(g.A);
-  const bf16_t* B = reinterpret_cast<const bf16_t*>(g.B);
-
-  const bf16_t* a_src[A_PT];
-  int a_dst[A_PT];
+  const char* A = reinterpret_cast<const char*>(g.A);
+  const char* B = reinterpret_cast<const char*>(g.B);
+  // this lane's source row / chunk inside each 8-row instruction block
+  const int r8 = lane >> 3, slot = lane & 7;
+  const int chunk = slot ^ r8;  // (tile row & 7) == r8 because blocks are 8-row aligned
+  const char* a_src[A_PW];
+  const char* b_src[B_PW];
 #pragma unroll
-  for (int i = 0; i < A_PT; ++i) {
-    const int v = tid + NT * i, r = v >> 3, c = (v & 7) * 8;
-    int m = m0 + r;
+  for (int i = 0; i < A_PW; ++i) {
+    const int row = (wave * A_PW + i) * 8 + r8;
+    int m = m0 + row;
     m = m < g.M ? m : g.M - 1;
-    const long row = g.a_rows ? (long)g.a_rows[m] : (long)m;
-    a_src[i] = A + row * g.lda + kb + c;
-    a_dst[i] = r * KP + c;
+    const long grow = g.a_rows ? (long)g.a_rows[m] : (long)m;
+    a_src[i] = A + (grow * g.lda + kb + chunk * 8) * 2;
   }
-  const bf16_t* b_src[B_PT];
-  int b_dst[B_PT];
 #pragma unroll
-  for (int i = 0; i < B_PT; ++i) {
-    const int v = tid + NT * i, r = v >> 3, c = (v & 7) * 8;
-    b_src[i] = B + (long)logical_col<EPI, BN>(g, tn, r) * g.ldb + kb + c;
-    b_dst[i] = (BM + r) * KP + c;
+  for (int i = 0; i < B_PW; ++i) {
+    const int row = (wave * B_PW + i) * 8 + r8;
+    b_src[i] = B + ((long)logical_col<EPI, BN>(g, tn, row) * g.ldb + kb + chunk * 8) * 2;
   }
-
-  u32x4_t ra0[A_PT], rb0[B_PT], ra1[A_PT], rb1[B_PT];
-#define CB_GLOAD(RA, RB, KK)                                                                           \
-  {                                                                                                   \
-    _Pragma("unroll") for (int i = 0; i < A_PT; ++i) RA[i] = *reinterpret_cast<const u32x4_t*>(a_src[i] + (KK)); \
-    _Pragma("unroll") for (int i = 0; i < B_PT; ++i) RB[i] = *reinterpret_cast<const u32x4_t*>(b_src[i] + (KK)); \
-  }
-#define CB_SWRITE(RA, RB, S)                                                                           \
-  {                                                                                                   \
-    bf16_t* st_ = lds + (S) * STAGE;                                                                  \
-    _Pragma("unroll") for (int i = 0; i < A_PT; ++i) *reinterpret_cast<u32x4_t*>(st_ + a_dst[i]) = RA[i];        \
-    _Pragma("unroll") for (int i = 0; i < B_PT; ++i) *reinterpret_cast<u32x4_t*>(st_ + b_dst[i]) = RB[i];        \
-  }
+  auto issue = [&](int kt, int st) __attribute__((always_inline)) {
+    unsigned char* base = smem + st * STAGE_B;
+#pragma unroll
+    for (int i = 0; i < A_PW; ++i)
+      __builtin_amdgcn_global_load_lds((gvoid_t*)(a_src[i] + kt * BK * 2), (lvoid_t*)(base + (wave * A_PW + i) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < B_PW; ++i)
+      __builtin_amdgcn_global_load_lds((gvoid_t*)(b_src[i] + kt * BK * 2), (lvoid_t*)(base + BM * ROWB + (wave * B_PW + i) * 1024), 16, 0, 0);
+  };
 
   f32x4_t acc[FM][FN];
 #pragma unroll
@@ -154,45 +153,45 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int a_frag = (wm * WTM + (lane & 15)) * KP + (lane >> 4) * 8;
-  const int b_frag = (BM + wn * WTN + (lane & 15)) * KP + (lane >> 4) * 8;
-#define CB_COMPUTE(S)                                                                                  \
-  {                                                                                                   \
-    const bf16_t* Ab = lds + (S) * STAGE + a_frag;                                                    \
-    const bf16_t* Bb = lds + (S) * STAGE + b_frag;                                                    \
-    _Pragma("unroll") for (int ks = 0; ks < BK / 32; ++ks) {                                          \
-      bf16x8_t af[FM], bfr[FN];                                                                       \
-      _Pragma("unroll") for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(Ab + i * 16 * KP + ks * 32); \
-      _Pragma("unroll") for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bb + j * 16 * KP + ks * 32); \
-      _Pragma("unroll") for (int i = 0; i < FM; ++i)                                                  \
-        _Pragma("unroll") for (int j = 0; j < FN; ++j)                                                \
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);    \
-    }                                                                                                 \
+  // fragment read offsets: row (l & 15) of each 16-row block, chunk 4*ks + (l >> 4), swizzled
+  const int fr = lane & 15, fc = lane >> 4;
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
+  for (int t = 0; t < nk; ++t) {
+    // K-step t's loads are this wave's oldest outstanding ones: allow only K-step t+1's
+    if (t + 1 < nk) __builtin_amdgcn_s_waitcnt(0x0F70 | (A_PW + B_PW));
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+    // Plain s_barrier: every wave has waited for its own loads of this stage above, and its
+    // reads of the stage being refilled were consumed before it reached here.  (The fence of
+    // __syncthreads would also drain the loads still in flight for the next K-step.)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (t + 2 < nk) issue(t + 2, (t + 2) % NSTAGE);
+    const unsigned char* sa = smem + (t % NSTAGE) * STAGE_B;
+    const unsigned char* sb = sa + BM * ROWB;
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      const int c = 4 * ks + fc;
+      bf16x8_t af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int row = wm * WTM + i * 16 + fr;
+        af[i] = *reinterpret_cast<const bf16x8_t*>(sa + row * ROWB + ((c ^ (row & 7)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int row = wn * WTN + j * 16 + fr;
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(sb + row * ROWB + ((c ^ (row & 7)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
   }
 
-  // Prologue: K-step 0 into LDS stage 0, K-step 1 in flight in register set 1.
-  CB_GLOAD(ra0, rb0, 0);
-  if (nk > 1) CB_GLOAD(ra1, rb1, BK);
-  CB_SWRITE(ra0, rb0, 0);
-  __syncthreads();
-  for (int it = 0; it < nk; it += 2) {
-    // even K-step: LDS stage 0; register set 1 holds K-step it+1, set 0 is free
-    if (it + 2 < nk) CB_GLOAD(ra0, rb0, (it + 2) * BK);
-    CB_COMPUTE(0);
-    if (it + 1 < nk) CB_SWRITE(ra1, rb1, 1);
-    __syncthreads();
-    if (it + 1 >= nk) break;
-    // odd K-step: LDS stage 1; register set 0 holds K-step it+2, set 1 is free
-    if (it + 3 < nk) CB_GLOAD(ra1, rb1, (it + 3) * BK);
-    CB_COMPUTE(1);
-    if (it + 2 < nk) CB_SWRITE(ra0, rb0, 0);
-    __syncthreads();
-  }
-#undef CB_GLOAD
-#undef CB_SWRITE
-#undef CB_COMPUTE
-
-  // Epilogue from registers: tiles (i, 2q) and (i, 2q+1) hold the two columns of each pair.
   const int row_base = m0 + wm * WTM + (lane >> 4) * 4;
   float* P = g.partial + (long)blockIdx.y * g.M * g.N;
 #pragma unroll
@@ -215,6 +214,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
         }
       }
     }
+}
+
+template <int BM, int BN, int WM, int WN, int EPI>
+hipError_t launch_dma(const GemmArgs& g, hipStream_t s) {
+  constexpr int lds = 3 * (BM + BN) * BK * 2;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<BM, BN, WM, WN, EPI>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int tiles = ((g.M + BM - 1) / BM) * (g.N / BN);
+  const int grid_x = 8 * ((tiles + 7) / 8);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI>), dim3(grid_x, g.splits), dim3(64 * WM * WN), lds, s, g);
+  return hipGetLastError();
 }
 
 // Sum split-K partials (logical columns) and apply the epilogue.  One thread per column pair.
@@ -329,29 +344,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 }
 
 // ------------------------------------------------------------------ launch
-template <int BM, int BN, int WM, int WN, int EPI>
-hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
-  constexpr int lds = 2 * (BM + BN) * KP * 2;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<BM, BN, WM, WN, EPI>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  const int tiles = ((g.M + BM - 1) / BM) * (g.N / BN);
-  const int grid_x = 8 * ((tiles + 7) / 8);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI>), dim3(grid_x, g.splits), dim3(64 * WM * WN), lds, s, g);
-  return hipGetLastError();
-}
-
 template <int EPI>
 hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
   hipError_t e;
   const int cfg = gemm_config(g.M, g.N);
-  if (cfg == 0) e = launch_cfg<128, 256, 2, 4, EPI>(g, s);
-  else if (cfg == 1) e = launch_cfg<64, 256, 1, 4, EPI>(g, s);
-  else e = launch_cfg<128, 128, 2, 2, EPI>(g, s);
+  if (cfg == 0) e = launch_dma<128, 256, 2, 4, EPI>(g, s);
+  else if (cfg == 1) e = launch_dma<64, 256, 1, 4, EPI>(g, s);
+  else e = launch_dma<128, 128, 2, 2, EPI>(g, s);
   if (e != hipSuccess || g.splits <= 1) return e;
   const long items = (long)g.M * (g.N / 2);
   hipLaunchKernelGGL(splitk_reduce_kernel<EPI>, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, g);
@@ -360,9 +359,12 @@ hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
 
 }  // namespace
 
+// 0: 128 x 256 tile, 8 wavefronts (the large GEMMs); 1: 64 x 256, 4 wavefronts (a handful of
+// rows); 2: 128 x 128, 4 wavefronts (narrow outputs, usually with split-K).
 int gemm_config(int M, int N) {
-  if (N % 256 != 0) return 2;
-  return M > 64 ? 0 : 1;
+  if (N % 256 == 0 && M <= 64) return 1;
+  if (N % 256 == 0 && ((M + 127) / 128) * (N / 256) >= 200) return 0;
+  return 2;
 }
 
 int gemm_tiles(int M, int N) {
