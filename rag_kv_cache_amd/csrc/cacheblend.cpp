@@ -88,7 +88,7 @@ WsPlan plan_ws(const cb_model_desc& d, int n_tokens, int n_sel) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
   p.x = take(ns * d.d_model * es);
-  p.fresh = take(ns * 2 * kvd * es);
+  p.fresh = take(ns * (qd + 2 * kvd) * es);  // fresh K|V, or Q|K|V when every candidate is kept
   p.dev = take(ns * 4);
   p.q = take(ns * qd * es);
   p.attn_cap_rows = prow * kAttnMaxSplits;
@@ -101,7 +101,7 @@ WsPlan plan_ws(const cb_model_desc& d, int n_tokens, int n_sel) {
   p.mnorm = take(ns * d.d_model * es);
   p.act = take(ns * d.ffn_dim * es);
   off = std::max(off, blend_end);
-  const size_t maxn = std::max<size_t>({(size_t)d.d_model, qd, 2 * kvd});
+  const size_t maxn = std::max<size_t>({(size_t)d.d_model, qd + 2 * kvd});
   p.gpart_elems = (long)(prow * maxn * kGemmMaxSplits);
   p.gpart = take((size_t)p.gpart_elems * 4);
   p.total = off;
@@ -382,17 +382,23 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
     e = cb::rmsnorm(hidden_sel, dm, n_sel, dm, W.g_attn, d.rms_eps, x, bf, c->cs);
     if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
   }
-  // 3. fresh K | V of the selected rows (RoPE on K at the rows' positions)
+  // 3. fresh K | V of the selected rows (RoPE on K at the rows' positions).  When the layer keeps
+  //    every candidate (k == n_cand: layer 1 and any layer whose ratio no longer narrows), the kept
+  //    rows are exactly the selected rows, so Q is produced by the same GEMM (Q | K | V).
+  const bool fuse_q = k == (long)n_cand;
   void* fresh = ws + wp.fresh;
+  const int fresh_ld = fuse_q ? qd + 2 * kvd : 2 * kvd;
+  void* fresh_kv = (char*)fresh + (fuse_q ? (size_t)qd * es : 0);
   {
     cb::GemmArgs g{};
     g.A = x; g.lda = dm; g.a_rows = nullptr;
-    g.B = (const char*)W.w_qkv + (size_t)qd * dm * es; g.ldb = dm;
-    g.M = n_sel; g.N = 2 * kvd; g.K = dm;
+    g.B = fuse_q ? W.w_qkv : (const char*)W.w_qkv + (size_t)qd * dm * es; g.ldb = dm;
+    g.M = n_sel; g.N = fresh_ld; g.K = dm;
     g.splits = bf ? pick_splits(g.M, g.N, g.K, wp.gpart_elems) : 1;
     g.partial = (float*)(ws + wp.gpart);
-    g.epi = cb::EPI_ROPE; g.out = fresh; g.ldo = 2 * kvd;
-    g.pos = sel_idx; g.rope = c->rope; g.rope_cols = kvd; g.head_dim = d.head_dim; g.max_pos = d.max_tokens - 1;
+    g.epi = cb::EPI_ROPE; g.out = fresh; g.ldo = fresh_ld;
+    g.pos = sel_idx; g.rope = c->rope; g.rope_cols = fuse_q ? qd + kvd : kvd; g.head_dim = d.head_dim;
+    g.max_pos = d.max_tokens - 1;
     Timed t(c, CB_K_GEMM_KV, 2.0 * g.M * g.N * g.K);
     e = bf ? cb::gemm_bf16(g, c->cs) : cb::gemm_f32(g, c->cs);
     if (e != hipSuccess) return hip_fail(e, "gemm(kv) launch");
@@ -401,7 +407,7 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
   float* dev = deviation ? deviation : (float*)(ws + wp.dev);
   {
     Timed t(c, CB_K_DEV_SCATTER, (double)n_sel * 2 * kvd * es * 2 + (double)n_cand * 2 * kvd * es);
-    e = cb::dev_scatter(fresh, 2 * kvd, kv_fused_k, kv_fused_v, sel_idx, n_sel, n_cand, (int)n_tok, kvd,
+    e = cb::dev_scatter(fresh_kv, fresh_ld, kv_fused_k, kv_fused_v, sel_idx, n_sel, n_cand, (int)n_tok, kvd,
                         n_ctx > 0 ? dev : nullptr, bf, c->cs);
     if (e != hipSuccess) return hip_fail(e, "dev_scatter launch");
   }
@@ -412,9 +418,10 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
     if (e != hipSuccess) return hip_fail(e, "topk launch");
   }
   if (nn == 0) return CB_OK;
-  // 6a. Q of the kept rows (RoPE at their positions)
-  void* q = ws + wp.q;
-  {
+  // 6a. Q of the kept rows (RoPE at their positions), unless the QKV GEMM already produced it
+  void* q = fuse_q ? fresh : (void*)(ws + wp.q);
+  const int q_ld = fuse_q ? fresh_ld : qd;
+  if (!fuse_q) {
     cb::GemmArgs g{};
     g.A = x; g.lda = dm; g.a_rows = new_sel_local;
     g.B = W.w_qkv; g.ldb = dm;
@@ -430,7 +437,7 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
   // 6b. causal attention of the kept rows over the fused K/V
   {
     cb::AttnArgs a{};
-    a.q = q; a.ldq = qd; a.qpos = new_sel_idx; a.n_q = nn;
+    a.q = q; a.ldq = q_ld; a.qpos = new_sel_idx; a.n_q = nn;
     a.k = kv_fused_k; a.v = kv_fused_v; a.n_tok = (int)n_tok; a.hq = d.n_q_heads; a.hkv = d.n_kv_heads;
     a.dh = d.head_dim; a.out = out_sel; a.ldo = qd;
     a.part_o = (float*)(ws + wp.attn_o); a.part_ml = (float*)(ws + wp.attn_ml);

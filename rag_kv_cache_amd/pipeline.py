@@ -268,3 +268,16 @@ def build_chunk_caches(eng: Engine, chunks: Sequence[np.ndarray], pinned_host: b
                     host_cache[l][c] = (hk, hv)
         eng.compute.synchronize()
     return dev_cache, host_cache
+
+
+def capture_step(eng: Engine, step: Callable[[], object]) -> "torch.cuda.CUDAGraph":
+    """Record one call of `step` (a whole blended prefill enqueued on the compute stream) as a
+    HIP graph; replaying it re-runs every kernel of the step with one launch.  The step must
+    only enqueue library kernels on buffers that stay alive (no allocation, no host copy), and
+    must have run once before so that one-time kernel attributes are set."""
+    graph = torch.cuda.CUDAGraph()
+    eng.compute.synchronize()
+    with torch.cuda.graph(graph, stream=eng.compute):
+        step()
+    eng.compute.synchronize()
+    return graph
