@@ -124,17 +124,17 @@ int pick_splits(int M, int N, int K, long cap_elems) {
   return best;
 }
 
-void attn_splits(int n_q, int hkv, int n_tok, long cap_rows, int& splits, int& split_len) {
-  const int wgs = ((n_q + 15) / 16) * hkv;
-  int s = 1;
-  if (wgs < 512) s = std::min(kAttnMaxSplits, (512 + wgs - 1) / wgs);
-  s = std::min(s, std::max(1, n_tok / 256));
+// Split-KV: key ranges of 1024 keys for small kept sets, 2048 for large ones (measured best for
+// the causal row-length mix of the fused prompt), bounded by the partial buffer.
+void attn_splits(int n_q, int n_tok, long cap_rows, int& splits, int& split_len) {
+  int len = n_q < 1200 ? 1024 : 2048;
+  int s = (n_tok + len - 1) / len;
+  s = std::min(s, kAttnMaxSplits);
   while (s > 1 && (long)s * n_q > cap_rows) --s;
-  int len = (n_tok + s - 1) / s;
+  len = (n_tok + s - 1) / s;
   len = (len + 63) / 64 * 64;
   if (len <= 0) len = 64;
-  splits = (n_tok + len - 1) / len;
-  if (splits < 1) splits = 1;
+  splits = std::max(1, (n_tok + len - 1) / len);
   split_len = len;
 }
 
@@ -442,7 +442,7 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
     a.dh = d.head_dim; a.out = out_sel; a.ldo = qd;
     a.part_o = (float*)(ws + wp.attn_o); a.part_ml = (float*)(ws + wp.attn_ml);
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
-    if (bf) attn_splits(nn, d.n_kv_heads, (int)n_tok, wp.attn_cap_rows, a.splits, a.split_len);
+    if (bf) attn_splits(nn, (int)n_tok, wp.attn_cap_rows, a.splits, a.split_len);
     else { a.splits = 1; a.split_len = (int)std::max<long>(n_tok, 1); }
     // causal flops of the kept rows are not known on the host; the row count bounds them
     Timed t(c, CB_K_ATTN, 0.0);

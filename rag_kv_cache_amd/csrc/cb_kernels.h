@@ -36,8 +36,8 @@ struct AttnArgs {
   float scale_log2;            // log2(e) / sqrt(head_dim)
 };
 hipError_t attn_bf16(const AttnArgs& a, hipStream_t s);
-// Query rows per workgroup of the bf16 attention for n_q kept rows (16 or 32).
-int attn_rows_per_wg(int n_q);
+// Query rows per workgroup of the bf16 attention for a GQA group of `group` query heads.
+int attn_rows_per_wg(int group);
 hipError_t attn_f32(const AttnArgs& a, hipStream_t s);
 
 hipError_t embed(const int32_t* tok, int n, const void* table, int vocab, int d, int bf16, float* out,

@@ -23,15 +23,25 @@ namespace {
 
 constexpr float NEG_INF = -__builtin_huge_valf();
 
-template <int G, int RB>
-__global__ __launch_bounds__(64 * G) void attn_bf16_kernel(AttnArgs a) {
-  constexpr int DH = 128, BKV = 64, NT = 64 * G, BQ = 16 * RB;
-  constexpr int KP = DH + 8;    // K tile pitch (272 B): 16-byte fragment reads of 16 rows hit disjoint banks
-  constexpr int VP = DH + 16;   // V tile pitch (288 B): transpose reads of 8 rows x 32 B hit disjoint banks
-  constexpr int NVEC = 2 * BKV * DH / 8;   // 16-byte vectors per K+V tile
-  constexpr int L_PT = (NVEC + NT - 1) / NT;
-  __shared__ __align__(16) bf16_t Ks[2][BKV * KP];
-  __shared__ __align__(16) bf16_t Vs[2][BKV * VP];
+typedef __attribute__((address_space(1))) void gvoid_t;
+typedef __attribute__((address_space(3))) void lvoid_t;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {  // s_waitcnt vmcnt(N), other counters not waited
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+constexpr int ATT_NS = 4;                     // LDS stages (K + V tile each)
+constexpr int ATT_STAGE_B = 2 * 64 * 256;     // 64 keys x 256 B (one head) for K, then V
+
+template <int G, int RB, int QT>
+__global__ __launch_bounds__(64 * G * QT) void attn_bf16_kernel(AttnArgs a) {
+  constexpr int DH = 128, BKV = 64, BQ = 16 * RB * QT, NW = G * QT;
+  constexpr int ROWB = DH * 2;                       // 256 bytes per K/V row
+  constexpr int TILE_B = BKV * ROWB;
+  constexpr int NINS = 2 * TILE_B / 1024;            // 1 KB wave instructions per K+V tile
+  constexpr int INS_HI = (NINS + NW - 1) / NW, INS_LO = NINS / NW, N_HI = NINS % NW;
+  extern __shared__ __align__(16) unsigned char smem[];
 
   const int qt = blockIdx.x / a.hkv;
   const int g = blockIdx.x - qt * a.hkv;
@@ -43,22 +53,61 @@ __global__ __launch_bounds__(64 * G) void attn_bf16_kernel(AttnArgs a) {
   if (kbeg > maxpos) return;
   const int kend = min(min(kbeg + a.split_len, maxpos + 1), a.n_tok);
   const int minpos = a.qpos[row0];
-  const int ntiles = (kend - kbeg + BKV - 1) / BKV;
+  const int nt = (kend - kbeg + BKV - 1) / BKV;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = g * G + wave;
+  const int h = g * G + wave % G;          // query head of this wave
+  const int wrow0 = row0 + (wave / G) * 16 * RB;  // first query row of this wave
   const int l16 = lane & 15, lg = lane >> 4;
   const bf16_t* Q = reinterpret_cast<const bf16_t*>(a.q);
-  const bf16_t* Kg = reinterpret_cast<const bf16_t*>(a.k) + g * DH;
-  const bf16_t* Vg = reinterpret_cast<const bf16_t*>(a.v) + g * DH;
-  const long kv_row = (long)a.hkv * DH;
+  const char* Kg = reinterpret_cast<const char*>(a.k) + g * ROWB;
+  const char* Vg = reinterpret_cast<const char*>(a.v) + g * ROWB;
+  const long kv_row_b = (long)a.hkv * ROWB;
   const float c = a.scale_log2;
+
+  // This wave's load instructions: ids wave, wave + NW, ...; id < 16 loads K rows 4*id.., else V.
+  // Lane l writes 16 bytes at slot l of the 1 KB block: row 4*(id%16) + l/16, slot l%16 holding
+  // the row's 16-byte chunk (l%16) ^ (row & 15).
+  const int my_ins = wave < N_HI ? INS_HI : INS_LO;
+  int ld_row[INS_HI], ld_lds[INS_HI];
+  const char* ld_src[INS_HI];
+#pragma unroll
+  for (int i = 0; i < INS_HI; ++i) {
+    const int id = wave + NW * i;
+    const int blk = id & 15;
+    const int row = 4 * blk + (lane >> 4);
+    const int chunk = (lane & 15) ^ (row & 15);
+    ld_row[i] = row;
+    ld_src[i] = (id < 16 ? Kg : Vg) + chunk * 16;
+    ld_lds[i] = (id < 16 ? 0 : TILE_B) + blk * 1024;
+  }
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const int kt = kbeg + t * BKV;
+    unsigned char* st = smem + (t % ATT_NS) * ATT_STAGE_B;
+#pragma unroll
+    for (int i = 0; i < INS_HI; ++i) {
+      if (i < my_ins) {
+        int key = kt + ld_row[i];
+        key = key < kend ? key : 0;
+        __builtin_amdgcn_global_load_lds((gvoid_t*)(ld_src[i] + key * kv_row_b), (lvoid_t*)(st + ld_lds[i]), 16, 0, 0);
+      }
+    }
+  };
+  // wait until tile t+1 has landed, with `more` = whether tile t+2 was issued after it (waves
+  // that issued INS_HI loads per tile wait for one load of tile t+2 too: over-waiting is safe)
+  auto wait_next = [&](bool more) __attribute__((always_inline)) {
+    if (more) wait_vmcnt<INS_LO>();
+    else wait_vmcnt<0>();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
 
   int mypos[RB];
   bf16x8_t qf[RB][4];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const int r = row0 + rb * 16 + l16;
+    const int r = wrow0 + rb * 16 + l16;
     const bool ok = r < a.n_q;
     mypos[rb] = ok ? a.qpos[r] : -1;
 #pragma unroll
@@ -76,62 +125,34 @@ __global__ __launch_bounds__(64 * G) void attn_bf16_kernel(AttnArgs a) {
     for (int d = 0; d < 8; ++d) o[rb][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // K and V tiles staged through registers: vector v < 1024 is K (row v/16, 8 dims at
-  // 8*(v%16)), the rest V.  Keys past kend read key 0 (finite; masked out below).
-  u32x4_t rg[L_PT];
-#define CB_ALOAD(KT)                                                                                  \
-  _Pragma("unroll") for (int i = 0; i < L_PT; ++i) {                                                 \
-    const int v = tid + NT * i;                                                                      \
-    if (NVEC % NT == 0 || v < NVEC) {                                                                \
-      const int w = v & 1023;                                                                        \
-      int key = (KT) + (w >> 4);                                                                     \
-      key = key < kend ? key : 0;                                                                    \
-      const bf16_t* src = (v < 1024 ? Kg : Vg) + key * kv_row + (w & 15) * 8;                        \
-      rg[i] = *reinterpret_cast<const u32x4_t*>(src);                                                \
-    }                                                                                                \
-  }
-#define CB_AWRITE(ST)                                                                                 \
-  _Pragma("unroll") for (int i = 0; i < L_PT; ++i) {                                                 \
-    const int v = tid + NT * i;                                                                      \
-    if (NVEC % NT == 0 || v < NVEC) {                                                                \
-      const int w = v & 1023;                                                                        \
-      bf16_t* dst = v < 1024 ? &Ks[ST][(w >> 4) * KP + (w & 15) * 8] : &Vs[ST][(w >> 4) * VP + (w & 15) * 8]; \
-      *reinterpret_cast<u32x4_t*>(dst) = rg[i];                                                      \
-    }                                                                                                \
-  }
-
-  CB_ALOAD(kbeg);
-  CB_AWRITE(0);
-  __syncthreads();
-  // V^T fragment addressing for the transpose reads: lane (group lg, j = l16) reads 8 bytes of key
-  // row 4*lg + j/4 (+16 for the second half), dims 16*d + 4*(j%4); it receives V[4 keys][dim 16*d + j].
-  const int vt_off = (4 * lg + (l16 >> 2)) * VP + 4 * (l16 & 3);
-  for (int t = 0; t < ntiles; ++t) {
-    const int st = t & 1;
-    const int kt = kbeg + t * BKV;
-    const bool more = t + 1 < ntiles;
-    if (more) { CB_ALOAD(kt + BKV); }
-
-    f32x4_t s[RB][4];
+  // S^T = K Q^T for the tile in stage st: s[rb][kb][r] = score of row rb*16+l16, key 16kb+4lg+r
+  auto qk = [&](int t, f32x4_t (&s)[RB][4]) __attribute__((always_inline)) {
+    const unsigned char* kb_ = smem + (t % ATT_NS) * ATT_STAGE_B;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) s[rb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 4; ++kb) {
+      const int row = kb * 16 + l16;
 #pragma unroll
       for (int ds = 0; ds < 4; ++ds) {
-        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(&Ks[st][(kb * 16 + l16) * KP + ds * 32 + lg * 8]);
+        const int chunk = ds * 4 + lg;
+        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kb_ + row * ROWB + ((chunk ^ (row & 15)) << 4));
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) s[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[rb][ds], s[rb][kb], 0, 0, 0);
       }
-    // s[rb][kb][r] = raw score of row (rb*16 + l16) and key kt + 16*kb + 4*lg + r
+    }
+  };
+  // online softmax of tile t's scores, then O += V P for that tile
+  auto softmax_pv = [&](int t, f32x4_t (&s)[RB][4]) __attribute__((always_inline)) {
+    const int kt = kbeg + t * BKV;
     const bool edge = (kt + BKV > kend) || (kt + BKV - 1 > minpos);
     bf16x8_t pf[RB][2];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       if (edge) {
-        const int thr = min(mypos[rb], kend - 1) - kt - 4 * lg;  // key offset 16*kb + r must be <= thr
+        const int thr = min(mypos[rb], kend - 1) - kt - 4 * lg;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -155,9 +176,7 @@ __global__ __launch_bounds__(64 * G) void attn_bf16_kernel(AttnArgs a) {
           s[rb][kb][r] = p;
           rs += p;
         }
-      rs += __shfl_xor(rs, 16, 64);
-      rs += __shfl_xor(rs, 32, 64);
-      l_i[rb] = l_i[rb] * alpha + rs;
+      l_i[rb] = l_i[rb] * alpha + rs;  // this lane's share of the row sum (reduced at the end)
       m_i[rb] = m_new;
       if (__ballot(alpha != 1.f)) {
 #pragma unroll
@@ -171,27 +190,64 @@ __global__ __launch_bounds__(64 * G) void attn_bf16_kernel(AttnArgs a) {
         pf[rb][ks] = __builtin_bit_cast(bf16x8_t, w);
       }
     }
+    // V^T fragments by transpose reads: lane (group lg, j = l16) reads 8 bytes of key row
+    // 32ks + 4lg + j/4 (+16), dims 16d + 4(j%4); it receives V[4 keys][dim 16d + j].
+    const unsigned char* vb_ = smem + (t % ATT_NS) * ATT_STAGE_B + TILE_B;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
-        const bf16_t* vp = &Vs[st][ks * 32 * VP + d * 16 + vt_off];
-        const u32x2_t lo = lds_read_tr16(vp);
-        const u32x2_t hi = lds_read_tr16(vp + 16 * VP);
+        const int row = ks * 32 + 4 * lg + (l16 >> 2);
+        const int chunk = 2 * d + ((l16 & 3) >> 1);
+        const int byte = (l16 & 1) * 8;
+        const u32x2_t lo = lds_read_tr16(reinterpret_cast<const bf16_t*>(vb_ + row * ROWB + ((chunk ^ (row & 15)) << 4) + byte));
+        const int row2 = row + 16;
+        const u32x2_t hi = lds_read_tr16(reinterpret_cast<const bf16_t*>(vb_ + row2 * ROWB + ((chunk ^ (row2 & 15)) << 4) + byte));
         const bf16x8_t va = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) o[rb][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[rb][ks], o[rb][d], 0, 0, 0);
       }
-    if (more) { CB_AWRITE(st ^ 1); }
-    __syncthreads();
-  }
-#undef CB_ALOAD
-#undef CB_AWRITE
+  };
 
-  // o[rb][d][r] = O[row rb*16 + l16][d*16 + 4*lg + r]
+  // Prologue: tiles 0..2 in flight, wait for tile 0, scores of tile 0.
+  issue(0);
+  if (nt > 1) issue(1);
+  if (nt > 2) issue(2);
+  if (nt > 2) wait_vmcnt<2 * INS_LO>();
+  else if (nt > 1) wait_vmcnt<INS_LO>();
+  else wait_vmcnt<0>();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  f32x4_t sa[RB][4], sb[RB][4];
+  qk(0, sa);
+  // Iteration t: tile t+1 landed -> barrier; refill the stage of tile t-1 with tile t+3; scores of
+  // tile t+1 (MFMA) next to the softmax of tile t (VALU); then O += V_t P_t.
+  for (int t = 0; t < nt; t += 2) {
+    if (t + 1 < nt) {
+      wait_next(t + 2 < nt);
+      if (t + 3 < nt) issue(t + 3);
+      qk(t + 1, sb);
+    }
+    softmax_pv(t, sa);
+    if (t + 1 >= nt) break;
+    if (t + 2 < nt) {
+      wait_next(t + 3 < nt);
+      if (t + 4 < nt) issue(t + 4);
+      qk(t + 2, sa);
+    }
+    softmax_pv(t + 1, sb);
+  }
+
+  // o[rb][d][r] = O[row rb*16 + l16][d*16 + 4*lg + r]; the row sum is spread over 4 lanes
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const int my_row = row0 + rb * 16 + l16;
+    l_i[rb] += __shfl_xor(l_i[rb], 16, 64);
+    l_i[rb] += __shfl_xor(l_i[rb], 32, 64);
+  }
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int my_row = wrow0 + rb * 16 + l16;
     if (my_row >= a.n_q) continue;
     if (a.splits == 1) {
       const float inv = l_i[rb] > 0.f ? 1.f / l_i[rb] : 0.f;
@@ -280,20 +336,30 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
   for (int d = 0; d < DH; ++d) out[d] = acc[d] * inv;
 }
 
+template <int G, int RB, int QT>
+hipError_t launch_gr(const AttnArgs& a, hipStream_t s) {
+  constexpr int lds = ATT_NS * ATT_STAGE_B;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<G, RB, QT>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  constexpr int BQ = 16 * RB * QT;
+  dim3 grid(((a.n_q + BQ - 1) / BQ) * a.hkv, a.splits);
+  hipLaunchKernelGGL((attn_bf16_kernel<G, RB, QT>), grid, dim3(64 * G * QT), lds, s, a);
+  return hipGetLastError();
+}
+
 template <int G>
 hipError_t launch_g(const AttnArgs& a, hipStream_t s) {
-  const int rows = attn_rows_per_wg(a.n_q);
-  dim3 grid(((a.n_q + rows - 1) / rows) * a.hkv, a.splits);
-  if (rows == 32)
-    hipLaunchKernelGGL((attn_bf16_kernel<G, 2>), grid, dim3(64 * G), 0, s, a);
-  else
-    hipLaunchKernelGGL((attn_bf16_kernel<G, 1>), grid, dim3(64 * G), 0, s, a);
-  return hipGetLastError();
+  constexpr int QT = G <= 6 ? 2 : 1;  // 12 wavefronts at most: more would cap registers below need
+  return launch_gr<G, 1, QT>(a, s);
 }
 
 }  // namespace
 
-int attn_rows_per_wg(int n_q) { return n_q >= 2048 ? 32 : 16; }
+int attn_rows_per_wg(int group) { return group <= 6 ? 32 : 16; }
 
 hipError_t attn_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.n_q <= 0) return hipSuccess;
