@@ -99,6 +99,10 @@ def main() -> int:
     ap.add_argument("--config", default="qwen")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=25.0)
+    ap.add_argument("--only-blend", action="store_true",
+                    help="skip the pinned-host and full-recompute passes (profiling runs)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one plain 256 MiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the fusion step is built and timed on a single MI355X "
@@ -205,30 +209,36 @@ def main() -> int:
     cs.synchronize()
     per_layer = [evs[i].elapsed_time(evs[i + 1]) for i in range(len(evs) - 1)]
 
-    # PCIe-inclusive variant: cached KV in pinned host memory, fetched one layer ahead
-    for _ in range(2):
-        step(host_cache=host)
-    cs.synchronize()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(host_cache=host)
-    cs.synchronize()
-    torch.cuda.synchronize()
-    wall_p = time.perf_counter() - t0
-    pcie_ms = wall_p / args.steps * 1e3
+    pcie_ms = full_ms = None
+    if not args.only_blend:
+        # PCIe-inclusive variant: cached KV in pinned host memory, fetched one layer ahead
+        for _ in range(2):
+            step(host_cache=host)
+        cs.synchronize()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(host_cache=host)
+        cs.synchronize()
+        torch.cuda.synchronize()
+        pcie_ms = (time.perf_counter() - t0) / args.steps * 1e3
 
-    # full recompute on the same GPU and kernels (ratio 1 at every layer)
-    full_sched = [1.0] * sh.n_layers
-    run_layers(eng, buf, tokens, offs, wl.n_query, full_sched, fused, cache=cache, upload_inputs=False)
-    cs.synchronize()
-    t0 = time.perf_counter()
-    n_full = max(3, args.steps // 4)
-    for _ in range(n_full):
+        # full recompute on the same GPU and kernels (ratio 1 at every layer)
+        full_sched = [1.0] * sh.n_layers
         run_layers(eng, buf, tokens, offs, wl.n_query, full_sched, fused, cache=cache, upload_inputs=False)
-    cs.synchronize()
-    full_ms = (time.perf_counter() - t0) / n_full * 1e3
-    log(f"pinned-host prefetch: {pcie_ms:.3f} ms/step; full recompute: {full_ms:.3f} ms/step")
+        cs.synchronize()
+        t0 = time.perf_counter()
+        n_full = max(3, args.steps // 4)
+        for _ in range(n_full):
+            run_layers(eng, buf, tokens, offs, wl.n_query, full_sched, fused, cache=cache, upload_inputs=False)
+        cs.synchronize()
+        full_ms = (time.perf_counter() - t0) / n_full * 1e3
+        log(f"pinned-host prefetch: {pcie_ms:.3f} ms/step; full recompute: {full_ms:.3f} ms/step")
+    if args.calib_copy:
+        src = torch.empty(128 << 20, dtype=torch.bfloat16, device=eng.device)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -251,11 +261,12 @@ def main() -> int:
                          "steady_median": round(float(np.median(per_layer[3:])), 4)},
         "kept_rows_per_layer": kept[:4] + ["..."],
         "kernels": kernels,
-        "pcie_prefetch": {"ms_per_step": round(pcie_ms, 4), "context_tokens_per_s": round(n_ctx / pcie_ms * 1e3, 1),
-                          "host_kv_bytes_per_step": int(2 * sh.n_layers * n_ctx * sh.n_kv_heads * sh.head_dim * 2)},
+        "pcie_prefetch": None if pcie_ms is None else {
+            "ms_per_step": round(pcie_ms, 4), "context_tokens_per_s": round(n_ctx / pcie_ms * 1e3, 1),
+            "host_kv_bytes_per_step": int(2 * sh.n_layers * n_ctx * sh.n_kv_heads * sh.head_dim * 2)},
         "eager_ms_per_step": round(eager_ms, 4),
-        "full_recompute_ms": round(full_ms, 4),
-        "speedup_vs_full_recompute": round(full_ms / ms_step, 3),
+        "full_recompute_ms": None if full_ms is None else round(full_ms, 4),
+        "speedup_vs_full_recompute": None if full_ms is None else round(full_ms / ms_step, 3),
     }
     print(json.dumps(out), flush=True)
     eng.close()
