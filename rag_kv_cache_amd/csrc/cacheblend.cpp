@@ -108,20 +108,12 @@ WsPlan plan_ws(const cb_model_desc& d, int n_tokens, int n_sel) {
   return p;
 }
 
-// Split-K factor: enough workgroups to cover the 256 CUs once (the large tile runs one
-// workgroup per CU), each split at least two 64-wide K-steps, K divisible by 64 * splits,
-// partials within the buffer.
-int pick_splits(int M, int N, int K, long cap_elems) {
-  const int tiles = cb::gemm_tiles(M, N);
-  if (tiles >= 200) return 1;
-  for (int s = 2; s <= kGemmMaxSplits; ++s) {
-    if (K % (64 * s) != 0 || K / s < 128 || (long)s * M * N > cap_elems) continue;
-    if (tiles * s >= 240) return s;
-  }
-  int best = 1;
-  for (int s = 2; s <= kGemmMaxSplits; ++s)
-    if (K % (64 * s) == 0 && K / s >= 128 && (long)s * M * N <= cap_elems) best = s;
-  return best;
+// Tile configuration and split-K factor of a bf16 GEMM (fp32 GEMMs never split).
+void plan_gemm(cb::GemmArgs& g, bool bf, long cap_elems) {
+  if (!bf) { g.splits = 1; return; }
+  const cb::GemmPlan p = cb::gemm_plan(g.M, g.N, g.K, g.epi, cap_elems);
+  g.cfg = p.cfg;
+  g.splits = p.splits;
 }
 
 // Split-KV: key ranges of 1024 keys for small kept sets, 2048 for large ones (measured best for
@@ -394,9 +386,9 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
     g.A = x; g.lda = dm; g.a_rows = nullptr;
     g.B = fuse_q ? W.w_qkv : (const char*)W.w_qkv + (size_t)qd * dm * es; g.ldb = dm;
     g.M = n_sel; g.N = fresh_ld; g.K = dm;
-    g.splits = bf ? pick_splits(g.M, g.N, g.K, wp.gpart_elems) : 1;
     g.partial = (float*)(ws + wp.gpart);
     g.epi = cb::EPI_ROPE; g.out = fresh; g.ldo = fresh_ld;
+    plan_gemm(g, bf, wp.gpart_elems);
     g.pos = sel_idx; g.rope = c->rope; g.rope_cols = fuse_q ? qd + kvd : kvd; g.head_dim = d.head_dim;
     g.max_pos = d.max_tokens - 1;
     Timed t(c, CB_K_GEMM_KV, 2.0 * g.M * g.N * g.K);
@@ -426,9 +418,9 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
     g.A = x; g.lda = dm; g.a_rows = new_sel_local;
     g.B = W.w_qkv; g.ldb = dm;
     g.M = nn; g.N = qd; g.K = dm;
-    g.splits = bf ? pick_splits(g.M, g.N, g.K, wp.gpart_elems) : 1;
     g.partial = (float*)(ws + wp.gpart);
     g.epi = cb::EPI_ROPE; g.out = q; g.ldo = qd;
+    plan_gemm(g, bf, wp.gpart_elems);
     g.pos = new_sel_idx; g.rope = c->rope; g.rope_cols = qd; g.head_dim = d.head_dim; g.max_pos = d.max_tokens - 1;
     Timed t(c, CB_K_GEMM_Q, 2.0 * g.M * g.N * g.K);
     e = bf ? cb::gemm_bf16(g, c->cs) : cb::gemm_f32(g, c->cs);
@@ -475,18 +467,19 @@ cb_status cb_layer_rest(cb_ctx* c, int32_t layer, const float* hidden_sel, int32
   void* mn = ws + wp.mnorm;
   void* act = ws + wp.act;
   hipError_t e;
-  {  // h1 = hidden_sel[new_sel_local] + out_sel W_o^T
+  {  // h1 = hidden_sel[new_sel_local] + out_sel W_o^T, and mn = RMSNorm(h1) (fused for bf16)
     cb::GemmArgs g{};
     g.A = out_sel; g.lda = qd; g.B = W.w_o; g.ldb = qd;
     g.M = n_new; g.N = dm; g.K = qd;
-    g.splits = bf ? pick_splits(g.M, g.N, g.K, wp.gpart_elems) : 1;
     g.partial = (float*)(ws + wp.gpart);
     g.epi = cb::EPI_RESID; g.out = h1; g.ldo = dm; g.resid = hidden_sel; g.ldr = dm; g.resid_rows = new_sel_local;
+    plan_gemm(g, bf, wp.gpart_elems);
+    if (bf) { g.norm_g = W.g_ffn; g.norm_eps = d.rms_eps; g.norm_out = mn; }
     Timed t(c, CB_K_GEMM_O, 2.0 * g.M * g.N * g.K);
     e = bf ? cb::gemm_bf16(g, c->cs) : cb::gemm_f32(g, c->cs);
     if (e != hipSuccess) return hip_fail(e, "gemm(o) launch");
   }
-  {
+  if (!bf) {
     Timed t(c, CB_K_RMSNORM, (double)n_new * dm * (4 + es));
     e = cb::rmsnorm(h1, dm, n_new, dm, W.g_ffn, d.rms_eps, mn, bf, c->cs);
     if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
@@ -494,8 +487,9 @@ cb_status cb_layer_rest(cb_ctx* c, int32_t layer, const float* hidden_sel, int32
   {  // act = silu(m W_gate^T) * (m W_up^T)
     cb::GemmArgs g{};
     g.A = mn; g.lda = dm; g.B = W.w_gate_up; g.ldb = dm; g.swiglu_ffn = ff;
-    g.M = n_new; g.N = 2 * ff; g.K = dm; g.splits = 1;
+    g.M = n_new; g.N = 2 * ff; g.K = dm;
     g.epi = cb::EPI_SWIGLU; g.out = act; g.ldo = ff;
+    plan_gemm(g, bf, 0);
     Timed t(c, CB_K_GEMM_GATE_UP, 2.0 * g.M * g.N * g.K);
     e = bf ? cb::gemm_bf16(g, c->cs) : cb::gemm_f32(g, c->cs);
     if (e != hipSuccess) return hip_fail(e, "gemm(gate_up) launch");
@@ -504,9 +498,9 @@ cb_status cb_layer_rest(cb_ctx* c, int32_t layer, const float* hidden_sel, int32
     cb::GemmArgs g{};
     g.A = act; g.lda = ff; g.B = W.w_down; g.ldb = ff;
     g.M = n_new; g.N = dm; g.K = ff;
-    g.splits = bf ? pick_splits(g.M, g.N, g.K, wp.gpart_elems) : 1;
     g.partial = (float*)(ws + wp.gpart);
     g.epi = cb::EPI_RESID; g.out = hidden_next; g.ldo = dm; g.resid = h1; g.ldr = dm;
+    plan_gemm(g, bf, wp.gpart_elems);
     Timed t(c, CB_K_GEMM_DOWN, 2.0 * g.M * g.N * g.K);
     e = bf ? cb::gemm_bf16(g, c->cs) : cb::gemm_f32(g, c->cs);
     if (e != hipSuccess) return hip_fail(e, "gemm(down) launch");

@@ -18,12 +18,15 @@ struct GemmArgs {
   void* out; long ldo;   // STORE/ROPE/SWIGLU: dtype; RESID: fp32
   const int32_t* pos; const float2* rope; int rope_cols, head_dim, max_pos;  // ROPE
   const float* resid; long ldr; const int32_t* resid_rows;                  // RESID
+  const float* norm_g; float norm_eps; void* norm_out;  // RESID: also RMSNorm(out) -> bf16 [M][N]
+  int cfg;               // bf16 tile configuration (GemmCfg), from gemm_plan
 };
 hipError_t gemm_bf16(const GemmArgs& g, hipStream_t s);
-// Tile configuration the bf16 GEMM uses for an M x N problem, and its number of tiles
-// (the host sizes split-K from it).
-int gemm_config(int M, int N);
-int gemm_tiles(int M, int N);
+enum GemmCfg { GEMM_128x512 = 0, GEMM_128x256 = 1, GEMM_64x256 = 2, GEMM_128x128 = 3 };
+struct GemmPlan { int cfg, splits; };
+// Tile configuration and split-K factor of the bf16 GEMM for an M x N x K product with
+// epilogue `epi`; split partials ([splits][M][N] fp32) must fit partial_cap_elems.
+GemmPlan gemm_plan(int M, int N, int K, int epi, long partial_cap_elems);
 hipError_t gemm_f32(const GemmArgs& g, hipStream_t s);
 
 // Causal GQA attention of n_q query rows (positions qpos, ascending) over K/V rows 0..N-1.

@@ -34,7 +34,7 @@ namespace {
 
 constexpr int BK = 64;
 
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+__device__ __forceinline__ float silu(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // Epilogue on one pair of logical columns (n_a, n_b) of row m.
 template <int EPI, typename TO>
@@ -85,6 +85,17 @@ __device__ __forceinline__ int logical_col(const GemmArgs& g, int tn, int tc) {
   return tn * BN + tc;
 }
 
+// Column of tile-local column tc in the staged output tile: the logical column relative to the
+// tile's first one (RoPE tiles hold whole heads); for SwiGLU the gate/up feature index, with up
+// columns after the BN/2 gate columns (fp32 staging; the bf16 staging uses the gate index).
+template <int EPI, int BN>
+__device__ __forceinline__ int stage_col(int tc) {
+  const int b = tc >> 4, j = tc & 15, q = b >> 1, odd = b & 1;
+  if (EPI == EPI_ROPE) return (tc & ~127) + (odd ? 64 : 0) + (q & 3) * 16 + j;
+  if (EPI == EPI_SWIGLU) return (odd ? BN / 2 : 0) + q * 16 + j;
+  return tc;
+}
+
 // Each global_load_lds_dwordx4 wave instruction writes its 64 lanes x 16 bytes contiguously
 // (lane l at byte 16 l), i.e. 8 tile rows of 128 bytes; the 16-byte chunks of row r are stored
 // XOR-swizzled (chunk c at slot c ^ (r & 7)) so that fragment reads of 8 consecutive rows hit
@@ -92,17 +103,35 @@ __device__ __forceinline__ int logical_col(const GemmArgs& g, int tn, int tc) {
 typedef __attribute__((address_space(1))) void gvoid_t;
 typedef __attribute__((address_space(3))) void lvoid_t;
 
-template <int BM, int BN, int WM, int WN, int EPI>
+// s_waitcnt with only vmcnt (N) or only lgkmcnt (0) constrained.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// Wait until at most `ahead` K-steps of LPW load instructions each are still in flight (the
+// count saturates at the counter's limit of 63, which only waits longer).
+template <int LPW>
+__device__ __forceinline__ void wait_vm_steps(int ahead) {
+  constexpr int c1 = LPW < 63 ? LPW : 63, c2 = 2 * LPW < 63 ? 2 * LPW : 63, c3 = 3 * LPW < 63 ? 3 * LPW : 63;
+  if (ahead <= 0) wait_vm<0>();
+  else if (ahead == 1) wait_vm<c1>();
+  else if (ahead == 2) wait_vm<c2>();
+  else wait_vm<c3>();
+}
+
+template <int BM, int BN, int WM, int WN, int NS, int EPI>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
-  constexpr int NT = 64 * WM * WN, NW = WM * WN;
+  constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 16, FN = WTN / 16;
   constexpr int ROWB = BK * 2;                       // 128 bytes per tile row
   constexpr int STAGE_B = (BM + BN) * ROWB;
-  constexpr int NSTAGE = 3;
   constexpr int A_INS = BM / 8, B_INS = BN / 8;      // 1 KB wave instructions per tile
   constexpr int A_PW = A_INS / NW, B_PW = B_INS / NW;
+  constexpr int LPW = A_PW + B_PW;                   // load instructions per wave per K-step
   static_assert(FN % 2 == 0 && A_INS % NW == 0 && B_INS % NW == 0, "tile shape");
+  static_assert(NS >= 2 && NS <= 4, "stages");
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int tiles_m = (g.M + BM - 1) / BM;
@@ -111,9 +140,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
   if (tile < 0) return;
   const int tm = tile % tiles_m, tn = tile / tiles_m;
   const int m0 = tm * BM;
-  const int k_len = g.K / g.splits;
-  const int kb = blockIdx.y * k_len;
-  const int nk = k_len / BK;
+  // K-steps of this split: an even share of the K / 64 steps (shares differ by at most one)
+  const int nk_all = g.K / BK;
+  const int kb0 = (int)((long)nk_all * blockIdx.y / g.splits);
+  const int nk = (int)((long)nk_all * (blockIdx.y + 1) / g.splits) - kb0;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -130,12 +160,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
     int m = m0 + row;
     m = m < g.M ? m : g.M - 1;
     const long grow = g.a_rows ? (long)g.a_rows[m] : (long)m;
-    a_src[i] = A + (grow * g.lda + kb + chunk * 8) * 2;
+    a_src[i] = A + (grow * g.lda + (long)kb0 * BK + chunk * 8) * 2;
   }
 #pragma unroll
   for (int i = 0; i < B_PW; ++i) {
     const int row = (wave * B_PW + i) * 8 + r8;
-    b_src[i] = B + ((long)logical_col<EPI, BN>(g, tn, row) * g.ldb + kb + chunk * 8) * 2;
+    b_src[i] = B + ((long)logical_col<EPI, BN>(g, tn, row) * g.ldb + (long)kb0 * BK + chunk * 8) * 2;
   }
   auto issue = [&](int kt, int st) __attribute__((always_inline)) {
     unsigned char* base = smem + st * STAGE_B;
@@ -153,90 +183,176 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // fragment read offsets: row (l & 15) of each 16-row block, chunk 4*ks + (l >> 4), swizzled
+  // Fragment reads: row (l & 15) of each 16-row block, 16-byte chunk 4*ks + (l >> 4) (swizzled).
+  // Block rows are multiples of 16, so the swizzle term depends on the lane only.
   const int fr = lane & 15, fc = lane >> 4;
-  issue(0, 0);
-  if (nk > 1) issue(1, 1);
-  for (int t = 0; t < nk; ++t) {
-    // K-step t's loads are this wave's oldest outstanding ones: allow only K-step t+1's
-    if (t + 1 < nk) __builtin_amdgcn_s_waitcnt(0x0F70 | (A_PW + B_PW));
-    else __builtin_amdgcn_s_waitcnt(0x0F70);
-    // Plain s_barrier: every wave has waited for its own loads of this stage above, and its
-    // reads of the stage being refilled were consumed before it reached here.  (The fence of
-    // __syncthreads would also drain the loads still in flight for the next K-step.)
+  const int a_off = (wm * WTM + fr) * ROWB, b_off = BM * ROWB + (wn * WTN + fr) * ROWB;
+  const int sw0 = ((fc) ^ (fr & 7)) << 4, sw1 = ((4 + fc) ^ (fr & 7)) << 4;
+  auto read = [&](int st, int ks, bf16x8_t (&af)[FM], bf16x8_t (&bfr)[FN]) __attribute__((always_inline)) {
+    const unsigned char* s = smem + st * STAGE_B + (ks ? sw1 : sw0);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(s + a_off + i * 16 * ROWB);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(s + b_off + j * 16 * ROWB);
+  };
+  auto mma = [&](const bf16x8_t (&af)[FM], const bf16x8_t (&bfr)[FN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  };
+  auto barrier = [&]() __attribute__((always_inline)) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (t + 2 < nk) issue(t + 2, (t + 2) % NSTAGE);
-    const unsigned char* sa = smem + (t % NSTAGE) * STAGE_B;
-    const unsigned char* sb = sa + BM * ROWB;
+  };
+
+  // Pipeline: K-steps t .. t+NS-1 occupy the NS stages; fragments of the two 32-wide halves of
+  // a K-step are double-buffered in registers, so the LDS reads of one half overlap the MFMAs
+  // of the other.  At the one barrier per K-step every wave has (a) waited for its own loads of
+  // K-step t+1 and (b) finished reading stage t, which is then refilled with K-step t+NS.
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      const int c = 4 * ks + fc;
-      bf16x8_t af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int row = wm * WTM + i * 16 + fr;
-        af[i] = *reinterpret_cast<const bf16x8_t*>(sa + row * ROWB + ((c ^ (row & 7)) << 4));
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int row = wn * WTN + j * 16 + fr;
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(sb + row * ROWB + ((c ^ (row & 7)) << 4));
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  for (int s = 0; s < NS; ++s)
+    if (s < nk) issue(s, s);
+  wait_vm_steps<LPW>(min(NS - 1, nk - 1));  // K-step 0 landed; later K-steps may be in flight
+  barrier();
+  bf16x8_t a0[FM], b0[FN], a1[FM], b1[FN];
+  read(0, 0, a0, b0);
+  int st = 0;
+  for (int t = 0; t < nk; ++t) {
+    read(st, 1, a1, b1);
+    mma(a0, b0);
+    if (t + 1 < nk) {
+      wait_lgkm0();  // this wave is done reading stage st
+      wait_vm_steps<LPW>(min(NS - 2, nk - 2 - t));  // K-step t+1 landed
+      barrier();
+      if (t + NS < nk) issue(t + NS, st);
+      st = st + 1 == NS ? 0 : st + 1;
+      read(st, 0, a0, b0);
     }
+    mma(a1, b1);
   }
 
-  const int row_base = m0 + wm * WTM + (lane >> 4) * 4;
-  float* P = g.partial + (long)blockIdx.y * g.M * g.N;
+  // Epilogue.  The pair math (RoPE rotation, SwiGLU) runs on the fp32 accumulators in
+  // registers; the results are staged in LDS (the operand stages are free by now) in output
+  // order and written out along rows with 16-byte stores.  Split-K partials and the residual
+  // epilogue stage fp32 values.
+  wait_lgkm0();
+  barrier();
+  const int rl_base = wm * WTM + (lane >> 4) * 4;  // tile row of acc[i][.][0] is rl_base + 16 i
+  if (g.splits > 1 || EPI == EPI_RESID) {
+    constexpr int PF = BN * 4 + 16;  // fp32 staging row pitch (bytes)
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int q = 0; q < FN / 2; ++q) {
-      const int tc = wn * WTN + q * 32 + (lane & 15);
-      const int n_a = logical_col<EPI, BN>(g, tn, tc);
-      const int n_b = logical_col<EPI, BN>(g, tn, tc + 16);
+      for (int q = 0; q < FN / 2; ++q) {
+        const int tc = wn * WTN + q * 32 + (lane & 15);
+        const int la = stage_col<EPI, BN>(tc), lb = stage_col<EPI, BN>(tc + 16);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = row_base + i * 16 + r;
-        if (m >= g.M) continue;
-        const float va = acc[i][2 * q][r], vb = acc[i][2 * q + 1][r];
-        if (g.splits > 1) {
-          P[(long)m * g.N + n_a] = va;
-          P[(long)m * g.N + n_b] = vb;
-        } else {
-          epi_pair<EPI, bf16_t>(g, m, n_a, n_b, va, vb);
+        for (int r = 0; r < 4; ++r) {
+          unsigned char* row = smem + (rl_base + i * 16 + r) * PF;
+          *reinterpret_cast<float*>(row + la * 4) = acc[i][2 * q][r];
+          *reinterpret_cast<float*>(row + lb * 4) = acc[i][2 * q + 1][r];
         }
       }
+    barrier();
+    constexpr int CPR = BN / 4;  // 16-byte chunks per row
+    for (int it = tid; it < BM * CPR; it += 64 * NW) {
+      const int rl = it / CPR, c = (it - rl * CPR) * 4;
+      const int m = m0 + rl;
+      if (m >= g.M) continue;
+      const float4 v = *reinterpret_cast<const float4*>(smem + rl * PF + c * 4);
+      if (g.splits > 1) {
+        int n;
+        if (EPI == EPI_SWIGLU) n = c < BN / 2 ? tn * (BN / 2) + c : g.swiglu_ffn + tn * (BN / 2) + (c - BN / 2);
+        else n = tn * BN + c;
+        *reinterpret_cast<float4*>(g.partial + ((long)blockIdx.y * g.M + m) * g.N + n) = v;
+      } else {
+        const long rr = g.resid_rows ? (long)g.resid_rows[m] : (long)m;
+        const float4 r4 = *reinterpret_cast<const float4*>(g.resid + rr * g.ldr + tn * BN + c);
+        *reinterpret_cast<float4*>((float*)g.out + (long)m * g.ldo + tn * BN + c) =
+            make_float4(r4.x + v.x, r4.y + v.y, r4.z + v.z, r4.w + v.w);
+      }
     }
+  } else {
+    constexpr int OW = EPI == EPI_SWIGLU ? BN / 2 : BN;  // output columns of the tile
+    constexpr int PB = OW * 2 + 16;                      // bf16 staging row pitch (bytes)
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int q = 0; q < FN / 2; ++q) {
+        const int tc = wn * WTN + q * 32 + (lane & 15);
+        const int la = stage_col<EPI, BN>(tc), lb = stage_col<EPI, BN>(tc + 16);
+        const int n_a = logical_col<EPI, BN>(g, tn, tc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rl = rl_base + i * 16 + r;
+          float va = acc[i][2 * q][r], vb = acc[i][2 * q + 1][r];
+          unsigned char* row = smem + rl * PB;
+          if (EPI == EPI_SWIGLU) {
+            *reinterpret_cast<bf16_t*>(row + la * 2) = f32_to_bf16(silu(va) * vb);
+          } else {
+            if (EPI == EPI_ROPE && n_a < g.rope_cols) {
+              int m = m0 + rl;
+              m = m < g.M ? m : g.M - 1;
+              int p = g.pos[m];
+              p = p < 0 ? 0 : (p > g.max_pos ? g.max_pos : p);
+              const float2 t = g.rope[(long)p * (g.head_dim >> 1) + (n_a % g.head_dim)];
+              const float ya = va * t.x - vb * t.y;
+              vb = vb * t.x + va * t.y;
+              va = ya;
+            }
+            *reinterpret_cast<bf16_t*>(row + la * 2) = f32_to_bf16(va);
+            *reinterpret_cast<bf16_t*>(row + lb * 2) = f32_to_bf16(vb);
+          }
+        }
+      }
+    barrier();
+    constexpr int CPR = OW / 8;
+    const int colbase = EPI == EPI_SWIGLU ? tn * (BN / 2) : tn * BN;
+    for (int it = tid; it < BM * CPR; it += 64 * NW) {
+      const int rl = it / CPR, c = (it - rl * CPR) * 8;
+      const int m = m0 + rl;
+      if (m >= g.M) continue;
+      *reinterpret_cast<uint4*>((bf16_t*)g.out + (long)m * g.ldo + colbase + c) =
+          *reinterpret_cast<const uint4*>(smem + rl * PB + c * 2);
+    }
+  }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+// LDS bytes one launch needs: the operand ring, or the staged output tile if larger.
+template <int BM, int BN, int NS, int EPI>
+constexpr int gemm_lds_bytes(bool f32_out) {
+  constexpr int ring = NS * (BM + BN) * BK * 2;
+  const int stage = f32_out ? BM * (BN * 4 + 16) : BM * ((EPI == EPI_SWIGLU ? BN / 2 : BN) * 2 + 16);
+  return ring > stage ? ring : stage;
+}
+
+template <int BM, int BN, int WM, int WN, int NS, int EPI>
 hipError_t launch_dma(const GemmArgs& g, hipStream_t s) {
-  constexpr int lds = 3 * (BM + BN) * BK * 2;
+  constexpr int kMaxLds = 160 * 1024;
+  static_assert(NS * (BM + BN) * BK * 2 <= kMaxLds, "LDS");
+  const int lds = gemm_lds_bytes<BM, BN, NS, EPI>(g.splits > 1 || EPI == EPI_RESID);
+  if (lds > kMaxLds || g.N % BN != 0 || g.splits < 1 || g.splits > g.K / BK) return hipErrorInvalidValue;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<BM, BN, WM, WN, EPI>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<BM, BN, WM, WN, NS, EPI>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int tiles = ((g.M + BM - 1) / BM) * (g.N / BN);
   const int grid_x = 8 * ((tiles + 7) / 8);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI>), dim3(grid_x, g.splits), dim3(64 * WM * WN), lds, s, g);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, NS, EPI>), dim3(grid_x, g.splits), dim3(64 * WM * WN), lds, s, g);
   return hipGetLastError();
 }
 
-// Sum split-K partials (logical columns) and apply the epilogue.  One thread per column pair.
+// Sum split-K partials (logical columns, in split order) and apply the epilogue: one thread
+// per 4 consecutive column pairs.
 template <int EPI>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
   const long half = g.N / 2;
-  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  const long idx = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
   if (idx >= (long)g.M * half) return;
   const int m = (int)(idx / half);
   const int j = (int)(idx - (long)m * half);
@@ -253,12 +369,56 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
   }
   const long stride = (long)g.M * g.N;
   const float* p = g.partial + (long)m * g.N;
-  float va = 0.f, vb = 0.f;
-  for (int s = 0; s < g.splits; ++s) {
-    va += p[s * stride + n_a];
-    vb += p[s * stride + n_b];
+  float4 va = *reinterpret_cast<const float4*>(p + n_a), vb = *reinterpret_cast<const float4*>(p + n_b);
+  for (int s = 1; s < g.splits; ++s) {
+    const float4 a = *reinterpret_cast<const float4*>(p + s * stride + n_a);
+    const float4 b = *reinterpret_cast<const float4*>(p + s * stride + n_b);
+    va.x += a.x; va.y += a.y; va.z += a.z; va.w += a.w;
+    vb.x += b.x; vb.y += b.y; vb.z += b.z; vb.w += b.w;
   }
-  epi_pair<EPI, bf16_t>(g, m, n_a, n_b, va, vb);
+  epi_pair<EPI, bf16_t>(g, m, n_a + 0, n_b + 0, va.x, vb.x);
+  epi_pair<EPI, bf16_t>(g, m, n_a + 1, n_b + 1, va.y, vb.y);
+  epi_pair<EPI, bf16_t>(g, m, n_a + 2, n_b + 2, va.z, vb.z);
+  epi_pair<EPI, bf16_t>(g, m, n_a + 3, n_b + 3, va.w, vb.w);
+}
+
+// Residual epilogue of a split-K GEMM, one wavefront per output row:
+//   out[m] = resid[resid_rows[m]] + sum_s partial[s][m]   (fp32, split order fixed)
+// and, when norm_out is set, the RMSNorm of that row (the next GEMM's bf16 A operand), with
+// the same arithmetic as the stand-alone RMSNorm kernel.
+__global__ __launch_bounds__(256) void splitk_resid_norm_kernel(GemmArgs g) {
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (m >= g.M) return;
+  const long stride = (long)g.M * g.N;
+  const float* p = g.partial + (long)m * g.N;
+  const long rr = g.resid_rows ? (long)g.resid_rows[m] : (long)m;
+  const float* r = g.resid + rr * g.ldr;
+  float* o = (float*)g.out + (long)m * g.ldo;
+  float ss = 0.f;
+  for (int e = lane * 4; e < g.N; e += 256) {
+    float4 v = *reinterpret_cast<const float4*>(p + e);
+    for (int s = 1; s < g.splits; ++s) {
+      const float4 a = *reinterpret_cast<const float4*>(p + s * stride + e);
+      v.x += a.x; v.y += a.y; v.z += a.z; v.w += a.w;
+    }
+    const float4 rv = *reinterpret_cast<const float4*>(r + e);
+    v = make_float4(rv.x + v.x, rv.y + v.y, rv.z + v.z, rv.w + v.w);
+    *reinterpret_cast<float4*>(o + e) = v;
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  if (!g.norm_out) return;
+  ss = wave_sum(ss);
+  const float rs = 1.0f / sqrtf(ss / (float)g.N + g.norm_eps);
+  bf16_t* x = (bf16_t*)g.norm_out + (long)m * g.N;
+  for (int e = lane * 4; e < g.N; e += 256) {
+    const float4 v = *reinterpret_cast<const float4*>(o + e);
+    const float4 gg = *reinterpret_cast<const float4*>(g.norm_g + e);
+    x[e + 0] = f32_to_bf16(v.x * rs * gg.x);
+    x[e + 1] = f32_to_bf16(v.y * rs * gg.y);
+    x[e + 2] = f32_to_bf16(v.z * rs * gg.z);
+    x[e + 3] = f32_to_bf16(v.w * rs * gg.w);
+  }
 }
 
 // ------------------------------------------------------------------ fp32 path
@@ -347,42 +507,69 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 template <int EPI>
 hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
   hipError_t e;
-  const int cfg = gemm_config(g.M, g.N);
-  if (cfg == 0) e = launch_dma<128, 256, 2, 4, EPI>(g, s);
-  else if (cfg == 1) e = launch_dma<64, 256, 1, 4, EPI>(g, s);
-  else e = launch_dma<128, 128, 2, 2, EPI>(g, s);
+  switch (g.cfg) {
+    case GEMM_128x512: e = launch_dma<128, 512, 2, 4, 2, EPI>(g, s); break;
+    case GEMM_128x256: e = launch_dma<128, 256, 2, 4, 3, EPI>(g, s); break;
+    case GEMM_64x256: e = launch_dma<64, 256, 1, 4, 3, EPI>(g, s); break;
+    case GEMM_128x128: e = launch_dma<128, 128, 2, 2, 3, EPI>(g, s); break;
+    default: return hipErrorInvalidValue;
+  }
   if (e != hipSuccess || g.splits <= 1) return e;
-  const long items = (long)g.M * (g.N / 2);
-  hipLaunchKernelGGL(splitk_reduce_kernel<EPI>, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, g);
+  if (EPI == EPI_RESID) {
+    hipLaunchKernelGGL(splitk_resid_norm_kernel, dim3((g.M + 3) / 4), dim3(256), 0, s, g);
+  } else {
+    const long items = (long)g.M * (g.N / 8);
+    hipLaunchKernelGGL(splitk_reduce_kernel<EPI>, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, g);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
-// 0: 128 x 256 tile, 8 wavefronts (the large GEMMs); 1: 64 x 256, 4 wavefronts (a handful of
-// rows); 2: 128 x 128, 4 wavefronts (narrow outputs, usually with split-K).
-int gemm_config(int M, int N) {
-  if (N % 256 == 0 && M <= 64) return 1;
-  if (N % 256 == 0 && ((M + 127) / 128) * (N / 256) >= 200) return 0;
-  return 2;
-}
-
-int gemm_tiles(int M, int N) {
-  switch (gemm_config(M, N)) {
-    case 0: return ((M + 127) / 128) * (N / 256);
-    case 1: return ((M + 63) / 64) * (N / 256);
-    default: return ((M + 127) / 128) * (N / 128);
+// Tile configuration and split-K factor for an M x N x K product (measured on MI355X at the
+// fusion step's shapes):
+//   * SwiGLU (gate/up, widest output): 128 x 512 tiles of 8 wavefronts, no split;
+//   * otherwise 128 x 256 tiles of 8 wavefronts (64 x 256 of 4 when M <= 64; 128 x 128 when N
+//     is not a multiple of 256); when the tiles cannot fill the chip, K is split so that about
+//     168 workgroups run, each keeping at least two 64-wide K-steps, within the partial buffer.
+GemmPlan gemm_plan(int M, int N, int K, int epi, long partial_cap_elems) {
+  GemmPlan p{GEMM_128x128, 1};
+  int bm = 128, bn = 128;
+  if (epi == EPI_SWIGLU) {
+    const int ffn = N / 2;
+    if (ffn % 256 == 0) { p.cfg = GEMM_128x512; bn = 512; }
+    else if (ffn % 128 == 0) { p.cfg = M <= 64 ? GEMM_64x256 : GEMM_128x256; bm = M <= 64 ? 64 : 128; bn = 256; }
+    return p;
   }
+  if (N % 256 == 0) {
+    p.cfg = M <= 64 ? GEMM_64x256 : GEMM_128x256;
+    bm = M <= 64 ? 64 : 128;
+    bn = 256;
+  }
+  const int tiles = ((M + bm - 1) / bm) * (N / bn);
+  if (tiles >= 200) return p;
+  const int nk = K / 64;
+  int sp = (168 + tiles / 2) / tiles;
+  sp = sp < 1 ? 1 : sp;
+  sp = sp > 8 ? 8 : sp;
+  while (sp > 1 && (nk / sp < 2 || (long)sp * M * N > partial_cap_elems)) --sp;
+  p.splits = sp;
+  return p;
 }
 
 hipError_t gemm_bf16(const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0) return hipSuccess;
+  hipError_t e;
   switch (g.epi) {
-    case EPI_ROPE: return launch_epi<EPI_ROPE>(g, s);
-    case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(g, s);
-    case EPI_RESID: return launch_epi<EPI_RESID>(g, s);
-    default: return launch_epi<EPI_STORE>(g, s);
+    case EPI_ROPE: e = launch_epi<EPI_ROPE>(g, s); break;
+    case EPI_SWIGLU: e = launch_epi<EPI_SWIGLU>(g, s); break;
+    case EPI_RESID: e = launch_epi<EPI_RESID>(g, s); break;
+    default: e = launch_epi<EPI_STORE>(g, s); break;
   }
+  // the RMSNorm of a residual output that was written directly (no split-K reduce)
+  if (e == hipSuccess && g.epi == EPI_RESID && g.norm_out && g.splits <= 1)
+    e = rmsnorm((const float*)g.out, g.ldo, g.M, g.N, g.norm_g, g.norm_eps, g.norm_out, 1, s);
+  return e;
 }
 
 hipError_t gemm_f32(const GemmArgs& g, hipStream_t s) {
