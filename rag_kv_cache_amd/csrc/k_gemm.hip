@@ -111,13 +111,20 @@ __device__ __forceinline__ void wait_vm() {
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 // Wait until at most `ahead` K-steps of LPW load instructions each are still in flight (the
 // count saturates at the counter's limit of 63, which only waits longer).
+template <int N>
+struct Sat63 { static constexpr int v = N < 63 ? N : 63; };
 template <int LPW>
 __device__ __forceinline__ void wait_vm_steps(int ahead) {
-  constexpr int c1 = LPW < 63 ? LPW : 63, c2 = 2 * LPW < 63 ? 2 * LPW : 63, c3 = 3 * LPW < 63 ? 3 * LPW : 63;
-  if (ahead <= 0) wait_vm<0>();
-  else if (ahead == 1) wait_vm<c1>();
-  else if (ahead == 2) wait_vm<c2>();
-  else wait_vm<c3>();
+  switch (ahead <= 0 ? 0 : (ahead > 7 ? 7 : ahead)) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<Sat63<LPW>::v>(); break;
+    case 2: wait_vm<Sat63<2 * LPW>::v>(); break;
+    case 3: wait_vm<Sat63<3 * LPW>::v>(); break;
+    case 4: wait_vm<Sat63<4 * LPW>::v>(); break;
+    case 5: wait_vm<Sat63<5 * LPW>::v>(); break;
+    case 6: wait_vm<Sat63<6 * LPW>::v>(); break;
+    default: wait_vm<Sat63<7 * LPW>::v>(); break;
+  }
 }
 
 template <int BM, int BN, int WM, int WN, int NS, int EPI>
@@ -131,7 +138,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int A_PW = A_INS / NW, B_PW = B_INS / NW;
   constexpr int LPW = A_PW + B_PW;                   // load instructions per wave per K-step
   static_assert(FN % 2 == 0 && A_INS % NW == 0 && B_INS % NW == 0, "tile shape");
-  static_assert(NS >= 2 && NS <= 4, "stages");
+  static_assert(NS >= 2 && NS <= 8, "stages");
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int tiles_m = (g.M + BM - 1) / BM;
@@ -277,13 +284,38 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
   } else {
     constexpr int OW = EPI == EPI_SWIGLU ? BN / 2 : BN;  // output columns of the tile
     constexpr int PB = OW * 2 + 16;                      // bf16 staging row pitch (bytes)
+    // RoPE: positions of this lane's rows, then the cos/sin of each of its column pairs (heads
+    // are 128 wide on the bf16 path; a pair's first column is dim < 64 of its head), loaded
+    // before any use so that the loads overlap.
+    constexpr int NR = EPI == EPI_ROPE ? FM * 4 : 1, NP = EPI == EPI_ROPE ? FM * (FN / 2) * 4 : 1;
+    int prow[NR];
+    float2 cs[NP];
+    if (EPI == EPI_ROPE) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          int m = m0 + rl_base + i * 16 + r;
+          m = m < g.M ? m : g.M - 1;
+          const int p = g.pos[m];
+          prow[i * 4 + r] = (p < 0 ? 0 : (p > g.max_pos ? g.max_pos : p)) * 64;
+        }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int q = 0; q < FN / 2; ++q) {
+          const int n_a = logical_col<EPI, BN>(g, tn, wn * WTN + q * 32 + (lane & 15));
+#pragma unroll
+          for (int r = 0; r < 4; ++r) cs[(i * (FN / 2) + q) * 4 + r] = g.rope[prow[i * 4 + r] + (n_a & 127)];
+        }
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int q = 0; q < FN / 2; ++q) {
         const int tc = wn * WTN + q * 32 + (lane & 15);
         const int la = stage_col<EPI, BN>(tc), lb = stage_col<EPI, BN>(tc + 16);
-        const int n_a = logical_col<EPI, BN>(g, tn, tc);
+        const bool rot = EPI == EPI_ROPE && logical_col<EPI, BN>(g, tn, tc) < g.rope_cols;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int rl = rl_base + i * 16 + r;
@@ -292,12 +324,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
           if (EPI == EPI_SWIGLU) {
             *reinterpret_cast<bf16_t*>(row + la * 2) = f32_to_bf16(silu(va) * vb);
           } else {
-            if (EPI == EPI_ROPE && n_a < g.rope_cols) {
-              int m = m0 + rl;
-              m = m < g.M ? m : g.M - 1;
-              int p = g.pos[m];
-              p = p < 0 ? 0 : (p > g.max_pos ? g.max_pos : p);
-              const float2 t = g.rope[(long)p * (g.head_dim >> 1) + (n_a % g.head_dim)];
+            if (rot) {
+              const float2 t = cs[(i * (FN / 2) + q) * 4 + r];
               const float ya = va * t.x - vb * t.y;
               vb = vb * t.x + va * t.y;
               va = ya;
@@ -508,10 +536,13 @@ template <int EPI>
 hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
   hipError_t e;
   switch (g.cfg) {
-    case GEMM_128x512: e = launch_dma<128, 512, 2, 4, 2, EPI>(g, s); break;
+    case GEMM_128x512:  // planned for the SwiGLU epilogue only
+      if constexpr (EPI == EPI_SWIGLU) { e = launch_dma<128, 512, 2, 4, 2, EPI>(g, s); break; }
+      return hipErrorInvalidValue;
     case GEMM_128x256: e = launch_dma<128, 256, 2, 4, 3, EPI>(g, s); break;
     case GEMM_64x256: e = launch_dma<64, 256, 1, 4, 3, EPI>(g, s); break;
     case GEMM_128x128: e = launch_dma<128, 128, 2, 2, 3, EPI>(g, s); break;
+    case GEMM_64x128: e = launch_dma<64, 128, 2, 2, 4, EPI>(g, s); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || g.splits <= 1) return e;
@@ -529,28 +560,38 @@ hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
 // Tile configuration and split-K factor for an M x N x K product (measured on MI355X at the
 // fusion step's shapes):
 //   * SwiGLU (gate/up, widest output): 128 x 512 tiles of 8 wavefronts, no split;
-//   * otherwise 128 x 256 tiles of 8 wavefronts (64 x 256 of 4 when M <= 64; 128 x 128 when N
-//     is not a multiple of 256); when the tiles cannot fill the chip, K is split so that about
-//     168 workgroups run, each keeping at least two 64-wide K-steps, within the partial buffer.
+//   * problems with >= 200 tiles of 128 x 256: those tiles (8 wavefronts), no split;
+//   * short reductions (K <= 2048: the Q/K/V and o-projections of the kept rows): 64 x 128
+//     tiles of 4 wavefronts with a 4-stage ring, split only while fewer than ~150 tiles;
+//   * long reductions (the FFN down-projection): 128 x 256 tiles, K split so that about 168
+//     workgroups run;
+//   each split keeps at least two 64-wide K-steps and its partials fit the buffer.
 GemmPlan gemm_plan(int M, int N, int K, int epi, long partial_cap_elems) {
   GemmPlan p{GEMM_128x128, 1};
-  int bm = 128, bn = 128;
   if (epi == EPI_SWIGLU) {
     const int ffn = N / 2;
-    if (ffn % 256 == 0) { p.cfg = GEMM_128x512; bn = 512; }
-    else if (ffn % 128 == 0) { p.cfg = M <= 64 ? GEMM_64x256 : GEMM_128x256; bm = M <= 64 ? 64 : 128; bn = 256; }
+    if (ffn % 256 == 0) p.cfg = GEMM_128x512;
+    else if (ffn % 128 == 0) p.cfg = M <= 64 ? GEMM_64x256 : GEMM_128x256;
     return p;
   }
-  if (N % 256 == 0) {
+  int bm = 128, bn = 128, target = 168;
+  if (N % 256 == 0 && ((M + 127) / 128) * (N / 256) >= 200) {
+    p.cfg = GEMM_128x256;
+    return p;
+  }
+  if (K <= 2048) {
+    p.cfg = GEMM_64x128;
+    bm = 64;
+    target = 150;
+  } else if (N % 256 == 0) {
     p.cfg = M <= 64 ? GEMM_64x256 : GEMM_128x256;
     bm = M <= 64 ? 64 : 128;
     bn = 256;
   }
   const int tiles = ((M + bm - 1) / bm) * (N / bn);
-  if (tiles >= 200) return p;
+  if (tiles >= target) return p;
   const int nk = K / 64;
-  int sp = (168 + tiles / 2) / tiles;
-  sp = sp < 1 ? 1 : sp;
+  int sp = (target + tiles - 1) / tiles;
   sp = sp > 8 ? 8 : sp;
   while (sp > 1 && (nk / sp < 2 || (long)sp * M * N > partial_cap_elems)) --sp;
   p.splits = sp;
