@@ -107,20 +107,38 @@ cb_status cb_workspace_size(const cb_ctx* ctx, int32_t n_tokens, int32_t n_sel_m
  * Token ids outside [0, vocab_size) give zero rows. */
 cb_status cb_embed(cb_ctx* ctx, const int32_t* tokens, int32_t n, const void* table, float* hidden_out);
 
-/* Layer-pipelined load (explainer, "Pipelined design"; fetch_kv).  Enqueues, on the copy
- * stream, host-to-device copies of layer `layer`'s cached K and V of every chunk:
- * host_k[c], host_v[c] point to pinned host memory holding [len_c][n_kv_heads][head_dim]
- * (len_c = chunk_offsets_host[c+1] - chunk_offsets_host[c]) and land in rows
- * [chunk_offsets_host[c], chunk_offsets_host[c+1]) of fused_k / fused_v.  Records the
- * layer's copy event.  The rows then hold the offset-0 cache; cb_blend_layer re-rotates
- * them in place when it is passed kv_cached == kv_fused.
- * CB_ESTATE if the layer already has a fetch that no cb_synchronize has consumed. */
+/* Layer-pipelined load (explainer, "Pipelined design"; fetch_kv) with the position update
+ * (explainer, "Position encoding update": K_new = R(delta p) K_cached).  Enqueues on the copy
+ * stream, once the compute stream is done with the last cb_blend_layer of this layer
+ * enqueued before the call (its fused rows are then free):
+ *   1. host-to-device copies of layer `layer`'s cached K and V of every chunk: host_k[c],
+ *      host_v[c] point to pinned host memory holding [len_c][n_kv_heads][head_dim]
+ *      (len_c = chunk_offsets_host[c+1] - chunk_offsets_host[c]) and land in rows
+ *      [chunk_offsets_host[c], chunk_offsets_host[c+1]) of fused_k / fused_v;
+ *   2. the position update of those rows in place: row j of chunk c gets K[j] <- R(o_c) K[j];
+ * and records the layer's event.  The rows then hold the re-rotated cache: pass
+ * kv_cached_k = kv_cached_v = NULL to cb_blend_layer.  chunk_offsets_dev: the same offsets
+ * on the device.  CB_ESTATE if the layer already has a fetch that no cb_synchronize has
+ * consumed. */
 cb_status cb_fetch_layer(cb_ctx* ctx, int32_t layer, const void* const* host_k,
                          const void* const* host_v, const int32_t* chunk_offsets_host,
-                         int32_t n_chunks, void* fused_k, void* fused_v);
+                         int32_t n_chunks, const int32_t* chunk_offsets_dev, void* fused_k,
+                         void* fused_v);
 
-/* synchronize(): make the compute stream wait for layer `layer`'s copy event.  Does not
- * block the host.  A no-op for a layer that was never fetched. */
+/* The same from a cache already in device memory: cache_k / cache_v are
+ * [N_ctx][n_kv_heads][head_dim] offset-0 chunk caches in prompt order; on the copy stream,
+ * fused K rows get R(o_c) K_cache and fused V rows a copy of V_cache (in place when the cache
+ * aliases the fused buffers), then the layer's event is recorded.  This moves the position
+ * update off the compute stream, where it would otherwise run inside cb_blend_layer. */
+cb_status cb_fetch_layer_device(cb_ctx* ctx, int32_t layer, const void* cache_k, const void* cache_v,
+                                const int32_t* chunk_offsets_host, int32_t n_chunks,
+                                const int32_t* chunk_offsets_dev, void* fused_k, void* fused_v);
+
+/* synchronize(): make the compute stream wait for layer `layer`'s fetch event.  Does not
+ * block the host.  A no-op for a layer that was never fetched.  (The fetch calls order the
+ * copy stream after earlier steps through events recorded outside any capture, so a HIP-graph
+ * capture should contain the compute-stream calls with kv_cached given to cb_blend_layer,
+ * not the fetch calls.) */
 cb_status cb_synchronize(cb_ctx* ctx, int32_t layer);
 
 /* One layer of the fusion step (prefill_layer on the selected rows).  Enqueues:
@@ -128,8 +146,8 @@ cb_status cb_synchronize(cb_ctx* ctx, int32_t layer);
  *     V[j] <- V_cached[j] in kv_fused (skipped when kv_cached_k is NULL: the fused
  *     buffer then already holds the re-rotated cache; in place when kv_cached_* ==
  *     kv_fused_*);
- *  2. x = RMSNorm(hidden_sel) and fresh K, V of the rows of S_l = sel_idx (RoPE at their
- *     absolute positions);
+ *  2. x = RMSNorm(hidden_sel) (or x_sel when given) and fresh K, V of the rows of
+ *     S_l = sel_idx (RoPE at their absolute positions);
  *  3. deviation d_i = ||K_new - K_fused||^2 + ||V_new - V_fused||^2 (fp32) of the
  *     context rows of S_l against the re-rotated cache, before it is overwritten;
  *  4. k = floor(ratio * N_ctx + 0.5) (ratio as given, product in double) clamped to
@@ -140,6 +158,9 @@ cb_status cb_synchronize(cb_ctx* ctx, int32_t layer);
  *     kept row over fused rows 0 .. its position.
  * Arguments:
  *   hidden_sel       device fp32 [n_sel][d_model]: residual-stream rows of S_l
+ *   x_sel            device [n_sel][d_model] (dtype) or NULL: RMSNorm(hidden_sel) with this
+ *                    layer's attention gain, already computed (cb_layer_rest's x_next of the
+ *                    previous layer); NULL computes it here
  *   kv_cached_k/_v   device [N_ctx][n_kv_heads][head_dim]: offset-0 chunk caches in
  *                    prompt order, or NULL (see 1.)
  *   kv_fused_k/_v    device [N_ctx + n_query][n_kv_heads][head_dim]: the layer's fused K/V
@@ -156,7 +177,7 @@ cb_status cb_synchronize(cb_ctx* ctx, int32_t layer);
  *   deviation        device fp32 [n_sel] out or NULL: entries 0 .. n_sel-n_query-1 get d
  *   workspace        device scratch of at least cb_workspace_size(N, n_sel) bytes
  * CB_ESTATE if the layer was fetched and not yet synchronized. */
-cb_status cb_blend_layer(cb_ctx* ctx, int32_t layer, const float* hidden_sel,
+cb_status cb_blend_layer(cb_ctx* ctx, int32_t layer, const float* hidden_sel, const void* x_sel,
                          const void* kv_cached_k, const void* kv_cached_v,
                          void* kv_fused_k, void* kv_fused_v,
                          const int32_t* chunk_offsets_dev, const int32_t* chunk_offsets_host,
@@ -168,10 +189,13 @@ cb_status cb_blend_layer(cb_ctx* ctx, int32_t layer, const float* hidden_sel,
  *   h1 = hidden_sel[new_sel_local] + out_sel W_o^T
  *   hidden_next = h1 + W_down( silu(W_gate m) * (W_up m) ),  m = RMSNorm(h1)
  * hidden_sel: device fp32 [n_sel][d]; new_sel_local / out_sel as returned by
- * cb_blend_layer; hidden_next: device fp32 [n_new][d] (must not alias hidden_sel). */
+ * cb_blend_layer; hidden_next: device fp32 [n_new][d] (must not alias hidden_sel).
+ * x_next: device [n_new][d] (dtype) or NULL: if given, also RMSNorm(hidden_next) with the
+ * attention gain of layer + 1 (which must exist and have its weights set), the x_sel of the
+ * next cb_blend_layer; it is fused with the down-projection's reduction. */
 cb_status cb_layer_rest(cb_ctx* ctx, int32_t layer, const float* hidden_sel, int32_t n_sel,
                         const int32_t* new_sel_local, int32_t n_new, const void* out_sel,
-                        float* hidden_next, void* workspace, size_t workspace_bytes);
+                        float* hidden_next, void* x_next, void* workspace, size_t workspace_bytes);
 
 /* Thread-local description of the last non-OK status ("" if none). */
 const char* cb_last_error(void);

@@ -57,11 +57,12 @@ _SIGS = {
     "cb_set_layer_weights": [_P, _I, C.POINTER(cb_layer_weights)],
     "cb_workspace_size": [_P, _I, _I, C.POINTER(C.c_size_t)],
     "cb_embed": [_P, _P, _I, _P, _P],
-    "cb_fetch_layer": [_P, _I, C.POINTER(_P), C.POINTER(_P), C.POINTER(_I), _I, _P, _P],
+    "cb_fetch_layer": [_P, _I, C.POINTER(_P), C.POINTER(_P), C.POINTER(_I), _I, _P, _P, _P],
+    "cb_fetch_layer_device": [_P, _I, _P, _P, C.POINTER(_I), _I, _P, _P, _P],
     "cb_synchronize": [_P, _I],
-    "cb_blend_layer": [_P, _I, _P, _P, _P, _P, _P, _P, C.POINTER(_I), _I, _P, _I, _I, C.c_float, _P, _P,
+    "cb_blend_layer": [_P, _I, _P, _P, _P, _P, _P, _P, _P, C.POINTER(_I), _I, _P, _I, _I, C.c_float, _P, _P,
                        C.POINTER(_I), _P, _P, _P, C.c_size_t],
-    "cb_layer_rest": [_P, _I, _P, _I, _P, _I, _P, _P, _P, C.c_size_t],
+    "cb_layer_rest": [_P, _I, _P, _I, _P, _I, _P, _P, _P, _P, C.c_size_t],
     "cb_profile_enable": [_P, _I],
     "cb_profile_read": [_P, _I, C.POINTER(C.c_double), C.POINTER(C.c_int64), C.POINTER(C.c_double)],
 }
@@ -111,10 +112,18 @@ def cb_embed(ctx: int, tokens: int, n: int, table: int, hidden_out: int) -> None
 
 
 def cb_fetch_layer(ctx: int, layer: int, host_k: Sequence[int], host_v: Sequence[int],
-                   chunk_offsets_host: Sequence[int], n_chunks: int, fused_k: int, fused_v: int) -> None:
+                   chunk_offsets_host: Sequence[int], n_chunks: int, chunk_offsets_dev: int, fused_k: int,
+                   fused_v: int) -> None:
     hk = (_P * max(len(host_k), 1))(*host_k)
     hv = (_P * max(len(host_v), 1))(*host_v)
-    _check(_L.cb_fetch_layer(ctx, layer, hk, hv, _i32(chunk_offsets_host), n_chunks, fused_k, fused_v))
+    _check(_L.cb_fetch_layer(ctx, layer, hk, hv, _i32(chunk_offsets_host), n_chunks, chunk_offsets_dev or None,
+                             fused_k, fused_v))
+
+
+def cb_fetch_layer_device(ctx: int, layer: int, cache_k: int, cache_v: int, chunk_offsets_host: Sequence[int],
+                          n_chunks: int, chunk_offsets_dev: int, fused_k: int, fused_v: int) -> None:
+    _check(_L.cb_fetch_layer_device(ctx, layer, cache_k or None, cache_v or None, _i32(chunk_offsets_host),
+                                    n_chunks, chunk_offsets_dev or None, fused_k, fused_v))
 
 
 def cb_synchronize(ctx: int, layer: int) -> None:
@@ -125,10 +134,10 @@ def cb_blend_layer(ctx: int, layer: int, hidden_sel: int, kv_cached_k: int, kv_c
                    kv_fused_k: int, kv_fused_v: int, chunk_offsets_dev: int,
                    chunk_offsets_host: Sequence[int], n_chunks: int, sel_idx: int, n_sel: int,
                    n_query: int, ratio: float, new_sel_idx: int, new_sel_local: int, out_sel: int,
-                   deviation: int, workspace: int, workspace_bytes: int) -> int:
+                   deviation: int, workspace: int, workspace_bytes: int, x_sel: int = 0) -> int:
     """Returns n_new (= k + n_query)."""
     n_new = _I()
-    _check(_L.cb_blend_layer(ctx, layer, hidden_sel, kv_cached_k or None, kv_cached_v or None, kv_fused_k,
+    _check(_L.cb_blend_layer(ctx, layer, hidden_sel, x_sel or None, kv_cached_k or None, kv_cached_v or None, kv_fused_k,
                              kv_fused_v, chunk_offsets_dev or None, _i32(chunk_offsets_host), n_chunks,
                              sel_idx, n_sel, n_query, ratio, new_sel_idx, new_sel_local, C.byref(n_new),
                              out_sel, deviation or None, workspace, workspace_bytes))
@@ -136,9 +145,9 @@ def cb_blend_layer(ctx: int, layer: int, hidden_sel: int, kv_cached_k: int, kv_c
 
 
 def cb_layer_rest(ctx: int, layer: int, hidden_sel: int, n_sel: int, new_sel_local: int, n_new: int,
-                  out_sel: int, hidden_next: int, workspace: int, workspace_bytes: int) -> None:
+                  out_sel: int, hidden_next: int, workspace: int, workspace_bytes: int, x_next: int = 0) -> None:
     _check(_L.cb_layer_rest(ctx, layer, hidden_sel, n_sel, new_sel_local, n_new, out_sel, hidden_next,
-                            workspace, workspace_bytes))
+                            x_next or None, workspace, workspace_bytes))
 
 
 def cb_profile_enable(ctx: int, on: bool) -> None:

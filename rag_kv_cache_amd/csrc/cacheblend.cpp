@@ -58,6 +58,7 @@ struct cb_ctx {
   std::vector<cb_layer_weights> w;
   std::vector<char> have_w;
   std::vector<hipEvent_t> fetch_ev;
+  std::vector<hipEvent_t> release_ev;  // per layer: the compute stream is done with its fused K/V
   std::vector<int> state;
   bool prof = false;
   std::vector<ProfRec> recs;
@@ -134,18 +135,26 @@ struct Timed {
   cb_ctx* c;
   int kernel;
   double work;
+  hipStream_t st;
   ProfRec* rec = nullptr;
-  Timed(cb_ctx* c_, int k, double w) : c(c_), kernel(k), work(w) {
+  Timed(cb_ctx* c_, int k, double w, hipStream_t s = nullptr) : c(c_), kernel(k), work(w), st(s ? s : c_->cs) {
     if (!c->prof || c->ev_used + 2 > c->ev_pool.size()) return;
     c->recs.push_back(ProfRec{kernel, work, c->ev_pool[c->ev_used], c->ev_pool[c->ev_used + 1]});
     c->ev_used += 2;
     rec = &c->recs.back();
-    hipEventRecord(rec->start, c->cs);
+    hipEventRecord(rec->start, st);
   }
   ~Timed() {
-    if (rec) hipEventRecord(rec->stop, c->cs);
+    if (rec) hipEventRecord(rec->stop, st);
   }
 };
+
+// The compute stream is done with layer `layer`'s fused K/V (end of cb_blend_layer).
+cb_status mark_release(cb_ctx* c, int layer) {
+  if (c->xs == c->cs) return CB_OK;
+  hipError_t e = hipEventRecord(c->release_ev[layer], c->cs);
+  return e == hipSuccess ? CB_OK : hip_fail(e, "hipEventRecord(release)");
+}
 
 cb_status check_ctx(const cb_ctx* c) {
   if (!c) return fail(CB_EINVAL, "context is NULL");
@@ -210,6 +219,11 @@ cb_status cb_create(const cb_model_desc* desc, int32_t device, void* compute_str
     e = hipEventCreateWithFlags(&c->fetch_ev[l], hipEventDisableTiming);
     if (e != hipSuccess) { cb_destroy(c); return hip_fail(e, "hipEventCreate"); }
   }
+  c->release_ev.assign(d.n_layers, nullptr);
+  for (int l = 0; l < d.n_layers; ++l) {
+    e = hipEventCreateWithFlags(&c->release_ev[l], hipEventDisableTiming);
+    if (e != hipSuccess) { cb_destroy(c); return hip_fail(e, "hipEventCreate"); }
+  }
   // RoPE table: angle p * base^(-2i/dh) and its cos/sin in double, stored as float.
   const int half = d.head_dim / 2;
   std::vector<float2> tab((size_t)d.max_tokens * half);
@@ -237,6 +251,8 @@ cb_status cb_destroy(cb_ctx* c) {
   for (hipEvent_t ev : c->fetch_ev)
     if (ev) hipEventDestroy(ev);
   for (hipEvent_t ev : c->ev_pool) hipEventDestroy(ev);
+  for (hipEvent_t ev : c->release_ev)
+    if (ev) hipEventDestroy(ev);
   if (c->rope) hipFree(c->rope);
   delete c;
   return CB_OK;
@@ -274,17 +290,60 @@ cb_status cb_embed(cb_ctx* c, const int32_t* tokens, int32_t n, const void* tabl
   return e == hipSuccess ? CB_OK : hip_fail(e, "embed launch");
 }
 
-cb_status cb_fetch_layer(cb_ctx* c, int32_t layer, const void* const* host_k, const void* const* host_v,
-                         const int32_t* offs, int32_t n_chunks, void* fused_k, void* fused_v) {
+}  // extern "C"
+
+namespace {
+
+// A fetch into layer l's fused buffers waits until the compute stream has finished the last
+// cb_blend_layer of that layer enqueued before it (a no-op for a layer never blended), so a
+// prefetch never overwrites rows that an earlier step still reads.
+cb_status wait_release(cb_ctx* c, int layer) {
+  if (c->xs == c->cs) return CB_OK;
+  hipError_t e = hipStreamWaitEvent(c->xs, c->release_ev[layer], 0);
+  return e == hipSuccess ? CB_OK : hip_fail(e, "hipStreamWaitEvent(release)");
+}
+
+cb_status check_fetch(cb_ctx* c, int layer, const int32_t* offs, int n_chunks, const int32_t* offs_dev,
+                      const void* fused_k, const void* fused_v) {
   cb_status st = check_ctx(c);
   if (st) return st;
   if ((st = check_layer(c, layer, false))) return st;
   if ((st = check_offsets(c, offs, n_chunks))) return st;
   if (c->state[layer] == LS_FETCHED) return fail(CB_ESTATE, "layer %d fetched twice without synchronize", layer);
-  if (n_chunks > 0 && (!host_k || !host_v || !fused_k || !fused_v)) return fail(CB_EINVAL, "NULL pointer");
+  if (n_chunks > 0 && offs[n_chunks] > 0 && (!fused_k || !fused_v || !offs_dev)) return fail(CB_EINVAL, "NULL pointer");
+  return CB_OK;
+}
+
+// Position update of the fetched rows on the copy stream, then the layer's event.
+cb_status finish_fetch(cb_ctx* c, int layer, const void* src_k, const void* src_v, void* fused_k, void* fused_v,
+                       const int32_t* offs_dev, int n_chunks, int n_ctx) {
+  if (n_ctx > 0) {
+    const bool inplace = src_k == fused_k;
+    Timed t(c, CB_K_ROPE, (double)n_ctx * c->d.n_kv_heads * c->d.head_dim * c->esize() * (inplace ? 2.0 : 4.0), c->xs);
+    hipError_t e = cb::rope_delta(src_k, src_v, fused_k, fused_v, n_ctx, c->d.n_kv_heads, c->d.head_dim, offs_dev,
+                                  n_chunks, c->rope, c->bf16(), c->xs);
+    if (e != hipSuccess) return hip_fail(e, "rope_delta launch");
+  }
+  hipError_t e = hipEventRecord(c->fetch_ev[layer], c->xs);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord(fetch)");
+  c->state[layer] = LS_FETCHED;
+  return CB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+cb_status cb_fetch_layer(cb_ctx* c, int32_t layer, const void* const* host_k, const void* const* host_v,
+                         const int32_t* offs, int32_t n_chunks, const int32_t* offs_dev, void* fused_k,
+                         void* fused_v) {
+  cb_status st = check_fetch(c, layer, offs, n_chunks, offs_dev, fused_k, fused_v);
+  if (st) return st;
+  if (n_chunks > 0 && (!host_k || !host_v)) return fail(CB_EINVAL, "NULL pointer");
   const size_t row = (size_t)c->d.n_kv_heads * c->d.head_dim * c->esize();
   for (int ch = 0; ch < n_chunks; ++ch)
     if (offs[ch + 1] > offs[ch] && (!host_k[ch] || !host_v[ch])) return fail(CB_EINVAL, "chunk %d host pointer NULL", ch);
+  if ((st = wait_release(c, layer))) return st;
   for (int ch = 0; ch < n_chunks; ++ch) {
     const size_t bytes = (size_t)(offs[ch + 1] - offs[ch]) * row;
     if (!bytes) continue;
@@ -293,10 +352,19 @@ cb_status cb_fetch_layer(cb_ctx* c, int32_t layer, const void* const* host_k, co
       e = hipMemcpyAsync((char*)fused_v + (size_t)offs[ch] * row, host_v[ch], bytes, hipMemcpyHostToDevice, c->xs);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(fetch)");
   }
-  hipError_t e = hipEventRecord(c->fetch_ev[layer], c->xs);
-  if (e != hipSuccess) return hip_fail(e, "hipEventRecord(fetch)");
-  c->state[layer] = LS_FETCHED;
-  return CB_OK;
+  return finish_fetch(c, layer, fused_k, fused_v, fused_k, fused_v, offs_dev, n_chunks, n_chunks > 0 ? offs[n_chunks] : 0);
+}
+
+cb_status cb_fetch_layer_device(cb_ctx* c, int32_t layer, const void* cache_k, const void* cache_v,
+                                const int32_t* offs, int32_t n_chunks, const int32_t* offs_dev, void* fused_k,
+                                void* fused_v) {
+  cb_status st = check_fetch(c, layer, offs, n_chunks, offs_dev, fused_k, fused_v);
+  if (st) return st;
+  const int n_ctx = n_chunks > 0 ? offs[n_chunks] : 0;
+  if (n_ctx > 0 && (!cache_k || !cache_v)) return fail(CB_EINVAL, "NULL pointer");
+  if ((cache_k == fused_k) != (cache_v == fused_v)) return fail(CB_EINVAL, "cache must alias fused for both K and V or for neither");
+  if ((st = wait_release(c, layer))) return st;
+  return finish_fetch(c, layer, cache_k, cache_v, fused_k, fused_v, offs_dev, n_chunks, n_ctx);
 }
 
 cb_status cb_synchronize(cb_ctx* c, int32_t layer) {
@@ -312,7 +380,7 @@ cb_status cb_synchronize(cb_ctx* c, int32_t layer) {
   return CB_OK;
 }
 
-cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, const void* kv_cached_k,
+cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, const void* x_sel, const void* kv_cached_k,
                          const void* kv_cached_v, void* kv_fused_k, void* kv_fused_v, const int32_t* offs_dev,
                          const int32_t* offs, int32_t n_chunks, const int32_t* sel_idx, int32_t n_sel,
                          int32_t n_query, float ratio, int32_t* new_sel_idx, int32_t* new_sel_local,
@@ -348,7 +416,7 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
   k = std::max(0L, std::min(k, (long)n_cand));
   const int nn = (int)k + n_query;
   *n_new = nn;
-  if (n_sel == 0) return CB_OK;
+  if (n_sel == 0) return mark_release(c, layer);
 
   char* ws = (char*)workspace;
   const bool bf = c->bf16();
@@ -367,12 +435,14 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
                        n_chunks, c->rope, bf, c->cs);
     if (e != hipSuccess) return hip_fail(e, "rope_delta launch");
   }
-  // 2. x = RMSNorm(hidden_sel)
-  void* x = ws + wp.x;
-  {
+  // 2. x = RMSNorm(hidden_sel), unless the caller passes it
+  const void* x = x_sel;
+  if (!x) {
+    void* xw = ws + wp.x;
     Timed t(c, CB_K_RMSNORM, (double)n_sel * dm * (4 + es));
-    e = cb::rmsnorm(hidden_sel, dm, n_sel, dm, W.g_attn, d.rms_eps, x, bf, c->cs);
+    e = cb::rmsnorm(hidden_sel, dm, n_sel, dm, W.g_attn, d.rms_eps, xw, bf, c->cs);
     if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
+    x = xw;
   }
   // 3. fresh K | V of the selected rows (RoPE on K at the rows' positions).  When the layer keeps
   //    every candidate (k == n_cand: layer 1 and any layer whose ratio no longer narrows), the kept
@@ -395,21 +465,23 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
     e = bf ? cb::gemm_bf16(g, c->cs) : cb::gemm_f32(g, c->cs);
     if (e != hipSuccess) return hip_fail(e, "gemm(kv) launch");
   }
-  // 4. deviation against the re-rotated cache, then scatter of the fresh rows
+  // 4. deviation against the re-rotated cache, then scatter of the fresh rows; when every
+  //    candidate is kept (fuse_q), the kept set is sel itself and the same kernel writes it
+  // 5. gradual filtering otherwise: top-k of the context rows + every query row
   float* dev = deviation ? deviation : (float*)(ws + wp.dev);
   {
     Timed t(c, CB_K_DEV_SCATTER, (double)n_sel * 2 * kvd * es * 2 + (double)n_cand * 2 * kvd * es);
     e = cb::dev_scatter(fresh_kv, fresh_ld, kv_fused_k, kv_fused_v, sel_idx, n_sel, n_cand, (int)n_tok, kvd,
-                        n_ctx > 0 ? dev : nullptr, bf, c->cs);
+                        n_ctx > 0 ? dev : nullptr, fuse_q ? new_sel_idx : nullptr, fuse_q ? new_sel_local : nullptr,
+                        bf, c->cs);
     if (e != hipSuccess) return hip_fail(e, "dev_scatter launch");
   }
-  // 5. gradual filtering: top-k of the context rows + every query row
-  {
+  if (!fuse_q) {
     Timed t(c, CB_K_TOPK, (double)n_cand * 4);
     e = cb::topk_select(dev, sel_idx, n_cand, n_query, (int)k, new_sel_idx, new_sel_local, c->cs);
     if (e != hipSuccess) return hip_fail(e, "topk launch");
   }
-  if (nn == 0) return CB_OK;
+  if (nn == 0) return mark_release(c, layer);
   // 6a. Q of the kept rows (RoPE at their positions), unless the QKV GEMM already produced it
   void* q = fuse_q ? fresh : (void*)(ws + wp.q);
   const int q_ld = fuse_q ? fresh_ld : qd;
@@ -441,12 +513,12 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
     e = bf ? cb::attn_bf16(a, c->cs) : cb::attn_f32(a, c->cs);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
   }
-  return CB_OK;
+  return mark_release(c, layer);
 }
 
 cb_status cb_layer_rest(cb_ctx* c, int32_t layer, const float* hidden_sel, int32_t n_sel,
                         const int32_t* new_sel_local, int32_t n_new, const void* out_sel, float* hidden_next,
-                        void* workspace, size_t ws_bytes) {
+                        void* x_next, void* workspace, size_t ws_bytes) {
   cb_status st = check_ctx(c);
   if (st) return st;
   if ((st = check_layer(c, layer, true))) return st;
@@ -456,6 +528,8 @@ cb_status cb_layer_rest(cb_ctx* c, int32_t layer, const float* hidden_sel, int32
   if (n_new == 0) return CB_OK;
   if (!hidden_sel || !new_sel_local || !out_sel || !hidden_next) return fail(CB_EINVAL, "NULL pointer");
   if ((const void*)hidden_next == (const void*)hidden_sel) return fail(CB_EINVAL, "hidden_next aliases hidden_sel");
+  if (x_next && (layer + 1 >= d.n_layers || !c->have_w[layer + 1]))
+    return fail(CB_ESTATE, "x_next needs the weights of layer %d", layer + 1);
   const WsPlan wp = plan_ws(d, n_sel, n_sel);
   if (!workspace || ws_bytes < wp.total) return fail(CB_ENOMEM, "workspace %zu bytes < %zu needed", ws_bytes, wp.total);
   char* ws = (char*)workspace;
@@ -501,9 +575,15 @@ cb_status cb_layer_rest(cb_ctx* c, int32_t layer, const float* hidden_sel, int32
     g.partial = (float*)(ws + wp.gpart);
     g.epi = cb::EPI_RESID; g.out = hidden_next; g.ldo = dm; g.resid = h1; g.ldr = dm;
     plan_gemm(g, bf, wp.gpart_elems);
+    if (bf && x_next) { g.norm_g = c->w[layer + 1].g_attn; g.norm_eps = d.rms_eps; g.norm_out = x_next; }
     Timed t(c, CB_K_GEMM_DOWN, 2.0 * g.M * g.N * g.K);
     e = bf ? cb::gemm_bf16(g, c->cs) : cb::gemm_f32(g, c->cs);
     if (e != hipSuccess) return hip_fail(e, "gemm(down) launch");
+  }
+  if (!bf && x_next) {
+    Timed t(c, CB_K_RMSNORM, (double)n_new * dm * (4 + es));
+    e = cb::rmsnorm(hidden_next, dm, n_new, dm, c->w[layer + 1].g_attn, d.rms_eps, x_next, bf, c->cs);
+    if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
   }
   return CB_OK;
 }

@@ -108,15 +108,22 @@ __global__ __launch_bounds__(256) void rope_delta_kernel(const T* kc, const T* v
 // fused row is overwritten; then fused[j] <- fresh[i].  fresh row layout: K heads then
 // V heads (row_elems each).  Per-lane sequential sums then a fixed butterfly: the result
 // does not depend on scheduling.
+// When the layer keeps every recomputed row (copy_sel set), the kept set is sel itself:
+// copy_sel[i] = sel[i], copy_local[i] = i.
 template <typename T>
 __global__ __launch_bounds__(256) void dev_scatter_kernel(const T* fresh, long ld_fresh, T* fk, T* fv,
                                                           const int32_t* sel, int n_sel, int n_cand, int n_tok,
-                                                          int row_elems, float* dev) {
+                                                          int row_elems, float* dev, int32_t* copy_sel,
+                                                          int32_t* copy_local) {
   constexpr int VE = Vec16<T>::N;
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (i >= n_sel) return;
   const int j = sel[i];
+  if (copy_sel && lane == 0) {
+    copy_sel[i] = j;
+    copy_local[i] = i;
+  }
   const bool score = dev != nullptr && i < n_cand;
   if (j < 0 || j >= n_tok) {
     if (score && lane == 0) dev[i] = __builtin_nanf("");
@@ -190,15 +197,16 @@ hipError_t rope_delta(const void* kc, const void* vc, void* kf, void* vf, int n_
 }
 
 hipError_t dev_scatter(const void* fresh, long ld_fresh, void* fk, void* fv, const int32_t* sel, int n_sel,
-                       int n_cand, int n_tok, int row_elems, float* dev, int bf16, hipStream_t s) {
+                       int n_cand, int n_tok, int row_elems, float* dev, int32_t* copy_sel, int32_t* copy_local,
+                       int bf16, hipStream_t s) {
   if (n_sel <= 0) return hipSuccess;
   dim3 grid((n_sel + 3) / 4);
   if (bf16)
     hipLaunchKernelGGL(dev_scatter_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)fresh, ld_fresh,
-                       (bf16_t*)fk, (bf16_t*)fv, sel, n_sel, n_cand, n_tok, row_elems, dev);
+                       (bf16_t*)fk, (bf16_t*)fv, sel, n_sel, n_cand, n_tok, row_elems, dev, copy_sel, copy_local);
   else
     hipLaunchKernelGGL(dev_scatter_kernel<float>, grid, dim3(256), 0, s, (const float*)fresh, ld_fresh,
-                       (float*)fk, (float*)fv, sel, n_sel, n_cand, n_tok, row_elems, dev);
+                       (float*)fk, (float*)fv, sel, n_sel, n_cand, n_tok, row_elems, dev, copy_sel, copy_local);
   return hipGetLastError();
 }
 

@@ -108,6 +108,7 @@ class Engine:
 class RunBuffers:
     """Device buffers of one blended prefill of up to n_tokens rows."""
     hidden: List[torch.Tensor]
+    xnorm: List[torch.Tensor]     # normalized rows handed from one layer to the next
     sel: List[torch.Tensor]
     iota: torch.Tensor
     new_local: torch.Tensor
@@ -122,6 +123,7 @@ def make_buffers(eng: Engine, n_tokens: int, n_chunks: int) -> RunBuffers:
     s, dv = eng.shape, eng.device
     return RunBuffers(
         hidden=[torch.empty(n_tokens, s.d_model, dtype=torch.float32, device=dv) for _ in range(2)],
+        xnorm=[torch.empty(n_tokens, s.d_model, dtype=eng.dtype, device=dv) for _ in range(2)],
         sel=[torch.empty(n_tokens, dtype=torch.int32, device=dv) for _ in range(2)],
         iota=torch.arange(n_tokens, dtype=torch.int32, device=dv),
         new_local=torch.empty(n_tokens, dtype=torch.int32, device=dv),
@@ -155,16 +157,18 @@ def run_layers(eng: Engine, buf: RunBuffers, tokens: np.ndarray, offsets: Sequen
                cache: Optional[List[Sequence[torch.Tensor]]] = None,
                host_cache: Optional[List[List[Sequence[torch.Tensor]]]] = None,
                record: bool = False, upload_inputs: bool = True,
-               layer_events: Optional[list] = None) -> RunResult:
+               layer_events: Optional[list] = None, rotate_on_copy_stream: bool = False) -> RunResult:
     """Blended prefill over every layer.
 
     fused[l] = (K, V) device buffers [N, H_kv, d_h] of layer l (the fused cache, output).
     cache[l] = (K, V) device [N_ctx, H_kv, d_h] offset-0 chunk caches in prompt order (HBM
-    mode: the position update copies them into fused[l]); or host_cache[l][c] = (K, V)
-    pinned host tensors of chunk c (prefetch mode: fetched one layer ahead into fused[l]
-    on the copy stream, then updated in place); or neither (the fused buffers are used as
-    they are, e.g. a full prefill with no context).
+    mode: the position update copies them into fused[l] on the copy stream, two layers
+    ahead); or host_cache[l][c] = (K, V) pinned host tensors of chunk c (prefetch mode:
+    copied two layers ahead into fused[l] on the copy stream and updated in place there); or
+    neither (the fused buffers are used as they are, e.g. a full prefill with no context).
     schedule[l] is the recompute ratio used at layer l.
+    rotate_on_copy_stream (HBM mode): run the position update on the copy stream, two layers
+    ahead (cb_fetch_layer_device), instead of inside cb_blend_layer on the compute stream.
     upload_inputs=False reuses the token ids and offsets already on the device (a repeated
     step then enqueues no host-to-device copy).  layer_events, if given, receives a CUDA event
     recorded on the compute stream before the first layer and after every layer.
@@ -182,14 +186,21 @@ def run_layers(eng: Engine, buf: RunBuffers, tokens: np.ndarray, offsets: Sequen
             buf.tokens[:n_tok].copy_(torch.from_numpy(np.asarray(tokens, np.int32)), non_blocking=False)
             buf.offsets[: n_chunks + 1].copy_(torch.tensor(offs, dtype=torch.int32))
     prefetch = host_cache is not None
+    fetched = prefetch or (cache is not None and n_ctx > 0 and rotate_on_copy_stream)
 
     def fetch(l):
-        if prefetch and l < s.n_layers:
+        # layer l's cache -> fused[l] with the position update, on the copy stream
+        if l >= s.n_layers:
+            return
+        if prefetch:
             hk = [_ptr(host_cache[l][c][0]) for c in range(n_chunks)]
             hv = [_ptr(host_cache[l][c][1]) for c in range(n_chunks)]
-            L.cb_fetch_layer(ctx, l, hk, hv, offs, n_chunks, _ptr(fused[l][0]), _ptr(fused[l][1]))
+            L.cb_fetch_layer(ctx, l, hk, hv, offs, n_chunks, _ptr(buf.offsets), _ptr(fused[l][0]), _ptr(fused[l][1]))
+        elif fetched:
+            L.cb_fetch_layer_device(ctx, l, _ptr(cache[l][0]), _ptr(cache[l][1]), offs, n_chunks, _ptr(buf.offsets),
+                                    _ptr(fused[l][0]), _ptr(fused[l][1]))
 
-    if prefetch:
+    if fetched:
         fetch(0)
         fetch(1)
     def mark():
@@ -204,11 +215,11 @@ def run_layers(eng: Engine, buf: RunBuffers, tokens: np.ndarray, offsets: Sequen
     records = []
     ws = buf.ws
     for l in range(s.n_layers):
-        if prefetch:
+        if fetched:  # the fused buffer already holds the re-rotated cache
             L.cb_synchronize(ctx, l)
             fetch(l + 2)
-            ck, cv = fused[l]
-        elif cache is not None:
+            ck, cv = None, None
+        elif cache is not None:  # position update inside cb_blend_layer (copy from the cache)
             ck, cv = cache[l]
         else:
             ck, cv = None, None
@@ -216,12 +227,15 @@ def run_layers(eng: Engine, buf: RunBuffers, tokens: np.ndarray, offsets: Sequen
         h_in, h_out = buf.hidden[cur], buf.hidden[1 - cur]
         sel_in = buf.iota if l == 0 else buf.sel[(l - 1) % 2]
         sel_out = buf.sel[l % 2]
+        # layer l-1's cb_layer_rest already normalized this layer's input rows (x_sel)
+        x_in = buf.xnorm[(l - 1) % 2] if l > 0 else None
+        x_out = buf.xnorm[l % 2] if l + 1 < s.n_layers else None
         n_new = L.cb_blend_layer(ctx, l, _ptr(h_in), _ptr(ck), _ptr(cv), _ptr(fk), _ptr(fv),
                                  _ptr(buf.offsets) if n_chunks else 0, offs, n_chunks, _ptr(sel_in), n_sel,
                                  n_query, float(schedule[l]), _ptr(sel_out), _ptr(buf.new_local),
-                                 _ptr(buf.out_sel), _ptr(buf.dev), _ptr(ws), ws.numel())
+                                 _ptr(buf.out_sel), _ptr(buf.dev), _ptr(ws), ws.numel(), x_sel=_ptr(x_in))
         L.cb_layer_rest(ctx, l, _ptr(h_in), n_sel, _ptr(buf.new_local), n_new, _ptr(buf.out_sel), _ptr(h_out),
-                        _ptr(ws), ws.numel())
+                        _ptr(ws), ws.numel(), x_next=_ptr(x_out))
         if record:
             cs.synchronize()
             records.append(LayerRecord(

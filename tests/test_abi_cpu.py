@@ -19,7 +19,8 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ["cb_create", "cb_destroy", "cb_set_layer_weights", "cb_workspace_size", "cb_fetch_layer",
-              "cb_synchronize", "cb_blend_layer", "cb_layer_rest", "cb_last_error", "cb_embed"]:
+              "cb_synchronize", "cb_blend_layer", "cb_layer_rest", "cb_last_error", "cb_embed",
+              "cb_fetch_layer_device"]:
         assert n in names
 
 

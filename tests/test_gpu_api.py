@@ -80,15 +80,21 @@ def test_fetch_synchronize_state_machine(tiny):
     hk = [torch.zeros(n, s.n_kv_heads, s.head_dim, pin_memory=True) for n in wl.chunk_lens]
     hv = [torch.zeros(n, s.n_kv_heads, s.head_dim, pin_memory=True) for n in wl.chunk_lens]
     fk, fv = eng.kv_empty(wl.n_tokens), eng.kv_empty(wl.n_tokens)
-    L.cb_fetch_layer(eng.ctx, 1, [_p(t) for t in hk], [_p(t) for t in hv], offs, len(offs) - 1, _p(fk), _p(fv))
+    offs_d = torch.tensor(offs, dtype=torch.int32, device=eng.device)
+    L.cb_fetch_layer(eng.ctx, 1, [_p(t) for t in hk], [_p(t) for t in hv], offs, len(offs) - 1, _p(offs_d),
+                     _p(fk), _p(fv))
     with pytest.raises(L.CbError) as e:  # fetched twice without synchronize
-        L.cb_fetch_layer(eng.ctx, 1, [_p(t) for t in hk], [_p(t) for t in hv], offs, len(offs) - 1, _p(fk), _p(fv))
+        L.cb_fetch_layer(eng.ctx, 1, [_p(t) for t in hk], [_p(t) for t in hv], offs, len(offs) - 1, _p(offs_d),
+                         _p(fk), _p(fv))
+    assert e.value.status == L.CB_ESTATE
+    with pytest.raises(L.CbError) as e:  # the device variant is subject to the same state machine
+        L.cb_fetch_layer_device(eng.ctx, 1, _p(fk), _p(fv), offs, len(offs) - 1, _p(offs_d), _p(fk), _p(fv))
     assert e.value.status == L.CB_ESTATE
     with pytest.raises(L.CbError) as e:  # blend before synchronize
-        _blend(eng, wl, l=1, fused=(fk, fv), cached=(fk, fv))
+        _blend(eng, wl, l=1, fused=(fk, fv), cached=(None, None))
     assert e.value.status == L.CB_ESTATE
     L.cb_synchronize(eng.ctx, 1)
-    assert _blend(eng, wl, l=1, fused=(fk, fv), cached=(fk, fv)) > 0
+    assert _blend(eng, wl, l=1, fused=(fk, fv), cached=(None, None)) > 0
     L.cb_synchronize(eng.ctx, 1)  # no pending fetch: no-op
     eng.compute.synchronize()
 

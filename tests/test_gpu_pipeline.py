@@ -106,8 +106,9 @@ def test_repeat_runs_are_bit_identical():
 
 
 def test_prefetch_path_equals_hbm_path():
-    """Pinned-host cache fetched a layer ahead on the copy stream and re-rotated in place gives
-    bit-identical results to the HBM-resident cache re-rotated by copy."""
+    """Pinned-host cache fetched two layers ahead on the copy stream and re-rotated in place
+    there, and the HBM-resident cache re-rotated by copy on the copy stream, both give
+    bit-identical results to the HBM-resident cache re-rotated inside cb_blend_layer."""
     from rag_kv_cache_amd.pipeline import build_chunk_caches, make_buffers, run_layers
     cfg = "small_bf16"
     wl = F.get_config(cfg)
@@ -115,19 +116,21 @@ def test_prefetch_path_equals_hbm_path():
     chunks = F.chunk_tokens(wl)
     cache, host = build_chunk_caches(eng, chunks, pinned_host=True)
     outs = []
-    for mode in ("hbm", "prefetch"):
+    for mode in ("hbm", "prefetch", "hbm_copy_stream"):
         buf = make_buffers(eng, wl.n_tokens, len(chunks))
         fused = fused_buffers(eng, wl.n_tokens)
         res = run_layers(eng, buf, F.all_tokens(wl), F.chunk_offsets(wl), wl.n_query, wl.schedule, fused,
-                         cache=cache if mode == "hbm" else None, host_cache=host if mode == "prefetch" else None)
+                         cache=None if mode == "prefetch" else cache, host_cache=host if mode == "prefetch" else None,
+                         rotate_on_copy_stream=mode == "hbm_copy_stream")
         eng.compute.synchronize()
         outs.append((res.hidden[: res.n_final].cpu().numpy().copy(), res.sel[: res.n_final].cpu().numpy().copy(),
                      [(bits(k), bits(v)) for k, v in fused]))
-    (h0, s0, f0), (h1, s1, f1) = outs
-    assert np.array_equal(s0, s1)
-    assert np.array_equal(h0, h1)
-    for (a, b), (c, d) in zip(f0, f1):
-        assert np.array_equal(a, c) and np.array_equal(b, d)
+    h0, s0, f0 = outs[0]
+    for h1, s1, f1 in outs[1:]:
+        assert np.array_equal(s0, s1)
+        assert np.array_equal(h0, h1)
+        for (a, b), (c, d) in zip(f0, f1):
+            assert np.array_equal(a, c) and np.array_equal(b, d)
 
 
 @pytest.mark.parametrize("sched", [(1.0, 1.0, 1.0), (1.0, 0.0, 0.0)])
