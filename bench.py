@@ -45,6 +45,35 @@ def attention_flops(shape, records, n_query):
     return [4.0 * shape.n_q_heads * shape.head_dim * float((r.new_sel.astype(np.int64) + 1).sum()) for r in records]
 
 
+def gate_up_traffic(shape, kept_rows):
+    """Mean HBM bytes per launch of the FFN gate/up GEMM over one step, from the committed
+    rocprofv3 counter summary (FETCH_SIZE / WRITE_SIZE, scaled by a plain copy's reading),
+    or None if that summary is missing or was taken on another version of the kernel source.
+    A launch on M rows runs ceil(M/128) x (2 ffn / 512) tiles of 512 threads, rounded up to a
+    multiple of 8 workgroups: that grid size identifies its counter line."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "gemm_gate_up_qwen_traffic.txt")
+    if not os.path.exists(path) or (2 * shape.ffn_dim) % 512:
+        return None
+    text = open(path).read()
+    m = re.search(r"source_sha256 (\S+): ([0-9a-f]{64})", text)
+    if not m:
+        return None
+    src = os.path.join(ROOT, m.group(1))
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != m.group(2):
+        return None
+    per_grid = {int(g): float(mb) for g, mb in re.findall(r"^\s*(\d+)\s+\d+\s+[\d.]+\s+[\d.]+\s+([\d.]+)\s+gemm", text, re.M)}
+    total = 0.0
+    for rows in kept_rows:
+        tiles = -(-rows // 128) * (2 * shape.ffn_dim // 512)
+        grid = 8 * (-(-tiles // 8)) * 512
+        if grid not in per_grid:
+            return None
+        total += per_grid[grid] * 1e6
+    return total / len(kept_rows)
+
+
 def cpu_baseline(wl, budget_s: float = 25.0):
     """The oracle (fp64 NumPy with bf16 rounding points) on a bounded sample of the same
     workload: layer 1 (every row), layer 2 (all rows scored, 30% kept), layer 3 (15% kept)
@@ -102,7 +131,7 @@ def main() -> int:
     ap.add_argument("--only-blend", action="store_true",
                     help="skip the pinned-host and full-recompute passes (profiling runs)")
     ap.add_argument("--calib-copy", action="store_true",
-                    help="also run one plain 256 MiB device-to-device copy (counter calibration)")
+                    help="also run a plain device-to-device copy of 256 MiB, 3 times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the fusion step is built and timed on a single MI355X "
@@ -199,9 +228,10 @@ def main() -> int:
                          "frac": round(rate / peak, 4)}
     dom = max(kernels, key=lambda k: kernels[k]["ms_total_per_step"])
     dk = kernels[dom]
+    traffic = gate_up_traffic(sh, kept) if dom == "gemm_gate_up" else None
     roofline = {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"],
                 "peak": PEAK_BF16_TFLOPS if dk["bound"] == "mfma" else PEAK_HBM_GBS, "unit": dk["unit"],
-                "frac": dk["frac"], "traffic": None}
+                "frac": dk["frac"], "traffic": None if traffic is None else round(traffic)}
 
     # per-layer latency (one extra profiled step with events at layer boundaries)
     evs = []
@@ -237,7 +267,8 @@ def main() -> int:
     if args.calib_copy:
         src = torch.empty(128 << 20, dtype=torch.bfloat16, device=eng.device)
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        for _ in range(3):
+            dst.copy_(src)
         torch.cuda.synchronize()
 
     cpu = None

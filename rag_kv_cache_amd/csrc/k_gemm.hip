@@ -413,7 +413,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
 // Residual epilogue of a split-K GEMM, one wavefront per output row:
 //   out[m] = resid[resid_rows[m]] + sum_s partial[s][m]   (fp32, split order fixed)
 // and, when norm_out is set, the RMSNorm of that row (the next GEMM's bf16 A operand), with
-// the same arithmetic as the stand-alone RMSNorm kernel.
+// the same arithmetic as the stand-alone RMSNorm kernel.  Lane l owns columns 4l + 256k;
+// two k at a time, so that 2 (splits + 1) loads per lane are in flight.
 __global__ __launch_bounds__(256) void splitk_resid_norm_kernel(GemmArgs g) {
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -424,16 +425,29 @@ __global__ __launch_bounds__(256) void splitk_resid_norm_kernel(GemmArgs g) {
   const float* r = g.resid + rr * g.ldr;
   float* o = (float*)g.out + (long)m * g.ldo;
   float ss = 0.f;
-  for (int e = lane * 4; e < g.N; e += 256) {
-    float4 v = *reinterpret_cast<const float4*>(p + e);
-    for (int s = 1; s < g.splits; ++s) {
-      const float4 a = *reinterpret_cast<const float4*>(p + s * stride + e);
-      v.x += a.x; v.y += a.y; v.z += a.z; v.w += a.w;
+  for (int e0 = lane * 4; e0 < g.N; e0 += 512) {
+    const bool two = e0 + 256 < g.N;
+    float4 v[2], rv[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = u ? (two ? e0 + 256 : e0) : e0;
+      v[u] = *reinterpret_cast<const float4*>(p + e);
+      rv[u] = *reinterpret_cast<const float4*>(r + e);
     }
-    const float4 rv = *reinterpret_cast<const float4*>(r + e);
-    v = make_float4(rv.x + v.x, rv.y + v.y, rv.z + v.z, rv.w + v.w);
-    *reinterpret_cast<float4*>(o + e) = v;
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    for (int s = 1; s < g.splits; ++s) {
+      float4 a[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) a[u] = *reinterpret_cast<const float4*>(p + s * stride + (u && two ? e0 + 256 : e0));
+#pragma unroll
+      for (int u = 0; u < 2; ++u) { v[u].x += a[u].x; v[u].y += a[u].y; v[u].z += a[u].z; v[u].w += a[u].w; }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (u && !two) break;
+      const float4 w = make_float4(rv[u].x + v[u].x, rv[u].y + v[u].y, rv[u].z + v[u].z, rv[u].w + v[u].w);
+      *reinterpret_cast<float4*>(o + e0 + 256 * u) = w;
+      ss += w.x * w.x + w.y * w.y + w.z * w.z + w.w * w.w;
+    }
   }
   if (!g.norm_out) return;
   ss = wave_sum(ss);
@@ -442,10 +456,9 @@ __global__ __launch_bounds__(256) void splitk_resid_norm_kernel(GemmArgs g) {
   for (int e = lane * 4; e < g.N; e += 256) {
     const float4 v = *reinterpret_cast<const float4*>(o + e);
     const float4 gg = *reinterpret_cast<const float4*>(g.norm_g + e);
-    x[e + 0] = f32_to_bf16(v.x * rs * gg.x);
-    x[e + 1] = f32_to_bf16(v.y * rs * gg.y);
-    x[e + 2] = f32_to_bf16(v.z * rs * gg.z);
-    x[e + 3] = f32_to_bf16(v.w * rs * gg.w);
+    *reinterpret_cast<uint2*>(x + e) =
+        make_uint2((uint32_t)f32_to_bf16(v.x * rs * gg.x) | ((uint32_t)f32_to_bf16(v.y * rs * gg.y) << 16),
+                   (uint32_t)f32_to_bf16(v.z * rs * gg.z) | ((uint32_t)f32_to_bf16(v.w * rs * gg.w) << 16));
   }
 }
 

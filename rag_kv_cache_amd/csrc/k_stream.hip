@@ -31,7 +31,47 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* tok, int n, c
 }
 
 // ---------------------------------------------------------------- RMSNorm
-// out[r] = h[r] / sqrt(mean(h[r]^2) + eps) * g, one wavefront per row, fp32 math.
+// out[r] = h[r] / sqrt(mean(h[r]^2) + eps) * g, one wavefront per row, fp32 math.  Lane l
+// owns elements 4l + 256k; the sum of squares adds them in increasing k (then a fixed
+// butterfly), with up to four 16-byte loads per lane in flight.
+template <typename TO>
+__device__ __forceinline__ void store4(TO* o, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<float>(float* o, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(o) = make_float4(a, b, c, d);
+}
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t* o, float a, float b, float c, float d) {
+  *reinterpret_cast<uint2*>(o) = make_uint2((uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16),
+                                            (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16));
+}
+
+__device__ __forceinline__ float sq4(float4 v) { return v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w; }
+
+// Sum of squares of one row (d % 256 == 0 not required: d % 4 == 0).
+__device__ __forceinline__ float row_sumsq(const float* x, int d, int lane) {
+  float ss = 0.f;
+  int e = lane * 4;
+  for (; e + 768 < d; e += 1024) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(x + e + 256 * u);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) ss += sq4(v[u]);
+  }
+  for (; e < d; e += 256) ss += sq4(*reinterpret_cast<const float4*>(x + e));
+  return wave_sum(ss);
+}
+
+template <typename TO>
+__device__ __forceinline__ void row_scale_store(const float* x, int d, const float* g, float r, TO* o, int lane) {
+  for (int e = lane * 4; e < d; e += 256) {
+    const float4 v = *reinterpret_cast<const float4*>(x + e);
+    const float4 gg = *reinterpret_cast<const float4*>(g + e);
+    store4<TO>(o + e, v.x * r * gg.x, v.y * r * gg.y, v.z * r * gg.z, v.w * r * gg.w);
+  }
+}
+
 template <typename TO>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, long ldh, int n, int d, const float* g,
                                                       float eps, TO* out) {
@@ -39,22 +79,9 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, long ldh, 
   const int lane = threadIdx.x & 63;
   if (row >= n) return;
   const float* x = h + (long)row * ldh;
-  float ss = 0.f;
-  for (int e = lane * 4; e < d; e += 256) {
-    float4 v = *reinterpret_cast<const float4*>(x + e);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-  }
-  ss = wave_sum(ss);
+  const float ss = row_sumsq(x, d, lane);
   const float r = 1.0f / sqrtf(ss / (float)d + eps);
-  TO* o = out + (long)row * d;
-  for (int e = lane * 4; e < d; e += 256) {
-    float4 v = *reinterpret_cast<const float4*>(x + e);
-    float4 gg = *reinterpret_cast<const float4*>(g + e);
-    Elem<TO>::st(o + e + 0, v.x * r * gg.x);
-    Elem<TO>::st(o + e + 1, v.y * r * gg.y);
-    Elem<TO>::st(o + e + 2, v.z * r * gg.z);
-    Elem<TO>::st(o + e + 3, v.w * r * gg.w);
-  }
+  row_scale_store<TO>(x, d, g, r, out + (long)row * d, lane);
 }
 
 // ---------------------------------------------------------------- RoPE position update
@@ -67,6 +94,12 @@ __global__ __launch_bounds__(256) void rope_delta_kernel(const T* kc, const T* v
                                                          int hkv, int dh, const int32_t* offs, int n_chunks,
                                                          const float2* table, int copy_v) {
   constexpr int VE = Vec16<T>::N;
+  constexpr int MAXC = 256;  // chunk offsets searched in LDS (more chunks: searched in global memory)
+  __shared__ int s_offs[MAXC + 1];
+  const bool in_lds = n_chunks <= MAXC;
+  if (in_lds)
+    for (int i = threadIdx.x; i <= n_chunks; i += blockDim.x) s_offs[i] = offs[i];
+  __syncthreads();
   const int half = dh >> 1;
   const int vph = half / VE;
   const int vpr = hkv * vph;
@@ -79,13 +112,18 @@ __global__ __launch_bounds__(256) void rope_delta_kernel(const T* kc, const T* v
     int lo = 0, hi = n_chunks - 1;  // last chunk whose offset <= row
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (offs[mid] <= row) lo = mid; else hi = mid - 1;
+      if ((in_lds ? s_offs[mid] : offs[mid]) <= row) lo = mid; else hi = mid - 1;
     }
-    const int o = offs[lo];
+    const int o = in_lds ? s_offs[lo] : offs[lo];
     const long base = ((long)row * hkv + h) * dh + i0;
     float a[VE], b[VE], ya[VE], yb[VE];
     Vec16<T>::load(kc + base, a);
     Vec16<T>::load(kc + base + half, b);
+    uint4 v0, v1;
+    if (copy_v) {
+      v0 = *reinterpret_cast<const uint4*>(vc + base);
+      v1 = *reinterpret_cast<const uint4*>(vc + base + half);
+    }
     const float2* cs = table + (long)o * half + i0;
 #pragma unroll
     for (int e = 0; e < VE; ++e) {
@@ -96,8 +134,8 @@ __global__ __launch_bounds__(256) void rope_delta_kernel(const T* kc, const T* v
     Vec16<T>::store(kf + base, ya);
     Vec16<T>::store(kf + base + half, yb);
     if (copy_v) {
-      *reinterpret_cast<uint4*>(vf + base) = *reinterpret_cast<const uint4*>(vc + base);
-      *reinterpret_cast<uint4*>(vf + base + half) = *reinterpret_cast<const uint4*>(vc + base + half);
+      *reinterpret_cast<uint4*>(vf + base) = v0;
+      *reinterpret_cast<uint4*>(vf + base + half) = v1;
     }
   }
 }
