@@ -10,7 +10,7 @@
 //   in registers as the B operand), so every lane owns one query row's scores: lane l has
 //   row (l & 15) and keys 4*(l >> 4) + r of each 16-key block;
 //   online softmax in fp32 (exp2 with log2(e)/sqrt(d) folded into the scale), row max and
-//   sum over the four lanes of a row by two xor-shuffles;
+//   sum over the four lanes of a row by two lane swaps (permlane16/32);
 //   O^T += V^T P^T: P (rounded to bf16) is already in B-operand layout, V^T is read as two
 //   8-byte pieces per lane with the matching key order;
 //   split-KV: grid.y splits the key range so short query sets still fill the chip; partial
@@ -25,6 +25,21 @@ constexpr float NEG_INF = -__builtin_huge_valf();
 
 typedef __attribute__((address_space(1))) void gvoid_t;
 typedef __attribute__((address_space(3))) void lvoid_t;
+
+// Reductions over the four lanes l, l^16, l^32, l^48 that hold one query row, with gfx950's
+// lane-swap instructions (VALU, no LDS crossbar); every lane gets the same value.
+__device__ __forceinline__ float max4_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum4_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {  // s_waitcnt vmcnt(N), other counters not waited
@@ -125,7 +140,8 @@ __global__ __launch_bounds__(64 * G * QT) void attn_bf16_kernel(AttnArgs a) {
     for (int d = 0; d < 8; ++d) o[rb][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // S^T = K Q^T for the tile in stage st: s[rb][kb][r] = score of row rb*16+l16, key 16kb+4lg+r
+  // S^T = K Q^T for the tile in stage st: s[rb][kb][r] = score of row rb*16+l16, key 16kb+4lg+r.
+  // Dimension steps outside, key blocks inside: four independent accumulation chains.
   auto qk = [&](int t, f32x4_t (&s)[RB][4]) __attribute__((always_inline)) {
     const unsigned char* kb_ = smem + (t % ATT_NS) * ATT_STAGE_B;
 #pragma unroll
@@ -133,15 +149,18 @@ __global__ __launch_bounds__(64 * G * QT) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) s[rb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int row = kb * 16 + l16;
+    for (int ds = 0; ds < 4; ++ds) {
+      const int chunk = ds * 4 + lg;
+      bf16x8_t ka[4];
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) {
-        const int chunk = ds * 4 + lg;
-        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kb_ + row * ROWB + ((chunk ^ (row & 15)) << 4));
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) s[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[rb][ds], s[rb][kb], 0, 0, 0);
+      for (int kb = 0; kb < 4; ++kb) {
+        const int row = kb * 16 + l16;
+        ka[kb] = *reinterpret_cast<const bf16x8_t*>(kb_ + row * ROWB + ((chunk ^ (row & 15)) << 4));
       }
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) s[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb], qf[rb][ds], s[rb][kb], 0, 0, 0);
     }
   };
   // online softmax of tile t's scores, then O += V P for that tile
@@ -162,8 +181,7 @@ __global__ __launch_bounds__(64 * G * QT) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
         mx = fmaxf(mx, fmaxf(fmaxf(s[rb][kb][0], s[rb][kb][1]), fmaxf(s[rb][kb][2], s[rb][kb][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = max4_rows(mx);
       const float m_new = fmaxf(m_i[rb], mx);
       const float alpha = (m_new == m_i[rb]) ? 1.f : __builtin_amdgcn_exp2f((m_i[rb] - m_new) * c);
       const float mc = (m_new == NEG_INF) ? 0.f : m_new * c;
@@ -241,10 +259,7 @@ __global__ __launch_bounds__(64 * G * QT) void attn_bf16_kernel(AttnArgs a) {
 
   // o[rb][d][r] = O[row rb*16 + l16][d*16 + 4*lg + r]; the row sum is spread over 4 lanes
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    l_i[rb] += __shfl_xor(l_i[rb], 16, 64);
-    l_i[rb] += __shfl_xor(l_i[rb], 32, 64);
-  }
+  for (int rb = 0; rb < RB; ++rb) l_i[rb] = sum4_rows(l_i[rb]);
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int my_row = wrow0 + rb * 16 + l16;
