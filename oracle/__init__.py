@@ -27,6 +27,9 @@ Parity status per function (what pins each one, see tests/test_oracle_*.py):
   blended_prefill ... special cases: ratio 1 = full prefill, single chunk at
                       offset 0 = exact cache, ratio 0 + single chunk = cache,
                       layer-1 identity, chunk-0 zero deviation, set invariants
+  cosine_deviation .. identical / opposite / orthogonal rows, scale invariance, the
+                      closed form 1 - cos(theta) for a rotation by theta
+  seam_positions .... hand-worked boundary windows (short chunks, window > chunk)
   which rows are HKVD on random weights ... parity unpinned (the pages print no
                       worked example; only the invariants above constrain it)
 """
@@ -35,6 +38,6 @@ from .model import (  # noqa: F401
     causal_attention, mlp, full_prefill, chunk_caches, cache_nbytes,
 )
 from .blend import (  # noqa: F401
-    k_for_ratio, topk_select, kv_deviation, blend_layer, layer_rest, fuse_cache,
-    blended_prefill,
+    k_for_ratio, topk_select, kv_deviation, cosine_deviation, seam_positions, blend_layer,
+    layer_rest, fuse_cache, blended_prefill,
 )

@@ -60,6 +60,45 @@ def kv_deviation(k_new, v_new, k_old, v_old) -> np.ndarray:
     return (dk * dk).sum(axis=(1, 2)) + (dv * dv).sum(axis=(1, 2))
 
 
+def cosine_deviation(k_new, v_new, k_old, v_old) -> np.ndarray:
+    """Per-row cosine deviation 1 - <a, b> / (|a| |b|), with a and b the row's fresh and cached
+    K and V concatenated over every KV head ([n, H_kv, d_h] each).  The KVBoost page
+    (section on seam repair, deviation-guided strategy) ranks tokens by the deviation of the
+    token-wise cosine similarity between cached and recomputed KV; the vector compared is the
+    same K|V row the L2 score uses (reading).  A zero vector has no direction: the deviation
+    is 0 when both rows are zero and 1 when only one is (reading)."""
+    a = np.concatenate([np.asarray(k_new, np.float64).reshape(len(k_new), -1),
+                        np.asarray(v_new, np.float64).reshape(len(v_new), -1)], axis=1)
+    b = np.concatenate([np.asarray(k_old, np.float64).reshape(len(k_old), -1),
+                        np.asarray(v_old, np.float64).reshape(len(v_old), -1)], axis=1)
+    dot = (a * b).sum(axis=1)
+    na = (a * a).sum(axis=1)
+    nb = (b * b).sum(axis=1)
+    out = np.empty(len(a))
+    for i in range(len(a)):
+        if na[i] == 0.0 or nb[i] == 0.0:
+            out[i] = 0.0 if na[i] == nb[i] else 1.0
+        else:
+            out[i] = 1.0 - dot[i] / math.sqrt(na[i] * nb[i])
+    return out
+
+
+def seam_positions(chunk_offsets: Sequence[int], n_query: int, window: int) -> np.ndarray:
+    """The spatial seam-repair set of the KVBoost page (section on seam repair, spatial
+    strategy): the `window` positions just before every chunk boundary (default 16 on the
+    page), re-encoded with the whole context, plus every query row; ascending.  The boundary
+    after the last chunk is the one with the query (reading: every chunk has a boundary
+    after it); a window longer than its chunk covers the whole chunk."""
+    offs = [int(o) for o in chunk_offsets]
+    pos = []
+    for c in range(len(offs) - 1):
+        lo, hi = offs[c], offs[c + 1]
+        pos.extend(range(max(lo, hi - int(window)), hi))
+    n_ctx = offs[-1]
+    pos.extend(range(n_ctx, n_ctx + int(n_query)))
+    return np.asarray(pos, dtype=np.int64)
+
+
 def fuse_cache(shape, prec: Precision, layer_cache: Sequence, chunk_offsets: Sequence[int],
                n_query: int):
     """Fused K/V buffers of one layer before any recompute: chunk c's cached K rotated by
@@ -79,10 +118,12 @@ def fuse_cache(shape, prec: Precision, layer_cache: Sequence, chunk_offsets: Seq
 
 def blend_layer(shape, w: Dict[str, np.ndarray], prec: Precision, hidden_sel: np.ndarray,
                 fused_k: np.ndarray, fused_v: np.ndarray, n_ctx: int, sel_idx: Sequence[int],
-                n_query: int, ratio: float, new_sel_override: Optional[Sequence[int]] = None):
+                n_query: int, ratio: float, new_sel_override: Optional[Sequence[int]] = None,
+                score: str = "l2"):
     """Steps 1-7 above for one layer.  fused_k / fused_v are not modified; updated copies are
     returned.  `new_sel_override` replaces the selected set (used to evaluate attention on a
-    set chosen elsewhere, e.g. when a near-tie was resolved the other way)."""
+    set chosen elsewhere, e.g. when a near-tie was resolved the other way).  score "l2" is
+    step 2's deviation, "cosine" the KVBoost variant (cosine_deviation)."""
     hq, hkv, dh = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
     sel = np.asarray(sel_idx, dtype=np.int64)
     n_sel = len(sel)
@@ -96,7 +137,8 @@ def blend_layer(shape, w: Dict[str, np.ndarray], prec: Precision, hidden_sel: np
     k_new = prec.store(rope_rotate(project(x, w["w_k"]).reshape(n_sel, hkv, dh), sel, shape.rope_base))
     v_new = prec.store(project(x, w["w_v"]).reshape(n_sel, hkv, dh))
 
-    dev = kv_deviation(k_new[:n_cand], v_new[:n_cand], fused_k[sel[:n_cand]], fused_v[sel[:n_cand]])
+    dev_fn = {"l2": kv_deviation, "cosine": cosine_deviation}[score]
+    dev = dev_fn(k_new[:n_cand], v_new[:n_cand], fused_k[sel[:n_cand]], fused_v[sel[:n_cand]])
     k = k_for_ratio(ratio, n_ctx, n_cand)
     keep = topk_select(dev, k)
     new_local = np.concatenate([keep, np.arange(n_cand, n_sel)]).astype(np.int64)
@@ -128,8 +170,11 @@ def layer_rest(shape, w: Dict[str, np.ndarray], prec: Precision, hidden_sel: np.
 
 def blended_prefill(shape, weights: List[Dict[str, np.ndarray]], emb: np.ndarray,
                     chunks: Sequence[np.ndarray], query: np.ndarray, schedule: Sequence[float],
-                    prec: Precision = F64, caches=None):
+                    prec: Precision = F64, caches=None, score: str = "l2",
+                    initial_sel: Optional[Sequence[int]] = None):
     """The whole fused prefill: per-chunk caches, then per layer fuse -> blend -> rest.
+    initial_sel: the rows recomputed at layer 1 (default every row; seam_positions gives the
+    spatial seam-repair set, kept at every layer with ratio 1).
     Returns dict(layers=[per-layer blend_layer results + 'sel'], hidden=final rows,
     sel=final selected set, caches=the chunk caches)."""
     if caches is None:
@@ -140,12 +185,12 @@ def blended_prefill(shape, weights: List[Dict[str, np.ndarray]], emb: np.ndarray
     tokens = np.concatenate(list(chunks) + [np.asarray(query)]).astype(np.int64)
     n_tok = len(tokens)
     assert len(schedule) == len(weights)
-    sel = np.arange(n_tok)
-    hidden = np.asarray(emb[tokens], np.float64)
+    sel = np.arange(n_tok) if initial_sel is None else np.asarray(initial_sel, np.int64)
+    hidden = np.asarray(emb[tokens[sel]], np.float64)
     layers = []
     for li, w in enumerate(weights):
         fk, fv = fuse_cache(shape, prec, [c[li] for c in caches], offs, n_query)
-        r = blend_layer(shape, w, prec, hidden, fk, fv, n_ctx, sel, n_query, schedule[li])
+        r = blend_layer(shape, w, prec, hidden, fk, fv, n_ctx, sel, n_query, schedule[li], score=score)
         r["sel"] = sel
         r["hidden_in"] = hidden
         hidden = layer_rest(shape, w, prec, hidden, r["new_local"], r["out"])
