@@ -197,6 +197,27 @@ cb_status cb_layer_rest(cb_ctx* ctx, int32_t layer, const float* hidden_sel, int
                         const int32_t* new_sel_local, int32_t n_new, const void* out_sel,
                         float* hidden_next, void* x_next, void* workspace, size_t workspace_bytes);
 
+/* Selection variants (KVBoost page, section on seam repair).
+ *
+ * Deviation score of cb_blend_layer on this context (default CB_SCORE_L2):
+ *   CB_SCORE_L2      d = ||K_new - K_fused||^2 + ||V_new - V_fused||^2 (CacheBlend explainer,
+ *                    "HKVD token selection");
+ *   CB_SCORE_COSINE  d = 1 - <a, b> / (|a| |b|) with a, b the row's fresh and fused K|V over
+ *                    all KV heads (the deviation-guided repair's token-wise cosine deviation;
+ *                    0 when both rows are zero, 1 when only one is).
+ * Ranking, ties and k are the same for both.  CB_EINVAL for another mode. */
+typedef enum { CB_SCORE_L2 = 0, CB_SCORE_COSINE = 1 } cb_score_mode;
+cb_status cb_set_score_mode(cb_ctx* ctx, int32_t mode);
+
+/* The spatial repair set: the `window` positions just before every chunk boundary (the page's
+ * default is 16; a window longer than its chunk covers the chunk), then the n_query query
+ * rows, ascending, written to out (host int32, capacity entries).  *n_out is the set size; if
+ * it exceeds capacity nothing is written and CB_ESHAPE is returned.  Recomputing exactly this
+ * set at every layer is cb_blend_layer with sel_idx = this set and a ratio >= 1.  Host-only,
+ * needs no context. */
+cb_status cb_seam_select(const int32_t* chunk_offsets_host, int32_t n_chunks, int32_t n_query,
+                         int32_t window, int32_t* out, int32_t capacity, int32_t* n_out);
+
 /* Thread-local description of the last non-OK status ("" if none). */
 const char* cb_last_error(void);
 

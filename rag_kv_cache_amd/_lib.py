@@ -63,6 +63,8 @@ _SIGS = {
     "cb_blend_layer": [_P, _I, _P, _P, _P, _P, _P, _P, _P, C.POINTER(_I), _I, _P, _I, _I, C.c_float, _P, _P,
                        C.POINTER(_I), _P, _P, _P, C.c_size_t],
     "cb_layer_rest": [_P, _I, _P, _I, _P, _I, _P, _P, _P, _P, C.c_size_t],
+    "cb_set_score_mode": [_P, _I],
+    "cb_seam_select": [C.POINTER(_I), _I, _I, _I, C.POINTER(_I), _I, C.POINTER(_I)],
     "cb_profile_enable": [_P, _I],
     "cb_profile_read": [_P, _I, C.POINTER(C.c_double), C.POINTER(C.c_int64), C.POINTER(C.c_double)],
 }
@@ -148,6 +150,22 @@ def cb_layer_rest(ctx: int, layer: int, hidden_sel: int, n_sel: int, new_sel_loc
                   out_sel: int, hidden_next: int, workspace: int, workspace_bytes: int, x_next: int = 0) -> None:
     _check(_L.cb_layer_rest(ctx, layer, hidden_sel, n_sel, new_sel_local, n_new, out_sel, hidden_next,
                             x_next or None, workspace, workspace_bytes))
+
+
+CB_SCORE_L2, CB_SCORE_COSINE = 0, 1
+
+
+def cb_set_score_mode(ctx: int, mode: int) -> None:
+    _check(_L.cb_set_score_mode(ctx, mode))
+
+
+def cb_seam_select(chunk_offsets_host: Sequence[int], n_chunks: int, n_query: int, window: int):
+    """The spatial seam-repair set (positions before every chunk boundary, then the query rows)."""
+    n = _I()
+    _L.cb_seam_select(_i32(chunk_offsets_host), n_chunks, n_query, window, None, 0, C.byref(n))
+    out = (_I * max(n.value, 1))()
+    _check(_L.cb_seam_select(_i32(chunk_offsets_host), n_chunks, n_query, window, out, n.value, C.byref(n)))
+    return [out[i] for i in range(n.value)]
 
 
 def cb_profile_enable(ctx: int, on: bool) -> None:

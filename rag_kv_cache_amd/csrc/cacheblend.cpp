@@ -60,6 +60,7 @@ struct cb_ctx {
   std::vector<hipEvent_t> fetch_ev;
   std::vector<hipEvent_t> release_ev;  // per layer: the compute stream is done with its fused K/V
   std::vector<int> state;
+  int score_mode = CB_SCORE_L2;
   bool prof = false;
   std::vector<ProfRec> recs;
   std::vector<hipEvent_t> ev_pool;
@@ -321,7 +322,7 @@ cb_status finish_fetch(cb_ctx* c, int layer, const void* src_k, const void* src_
     const bool inplace = src_k == fused_k;
     Timed t(c, CB_K_ROPE, (double)n_ctx * c->d.n_kv_heads * c->d.head_dim * c->esize() * (inplace ? 2.0 : 4.0), c->xs);
     hipError_t e = cb::rope_delta(src_k, src_v, fused_k, fused_v, n_ctx, c->d.n_kv_heads, c->d.head_dim, offs_dev,
-                                  n_chunks, c->rope, c->bf16(), c->xs);
+                                  n_chunks, c->rope, c->d.max_tokens, c->bf16(), c->xs);
     if (e != hipSuccess) return hip_fail(e, "rope_delta launch");
   }
   hipError_t e = hipEventRecord(c->fetch_ev[layer], c->xs);
@@ -432,7 +433,7 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
     const bool inplace = kv_cached_k == kv_fused_k;
     Timed t(c, CB_K_ROPE, (double)n_ctx * kvd * es * (inplace ? 2.0 : 4.0));
     e = cb::rope_delta(kv_cached_k, kv_cached_v, kv_fused_k, kv_fused_v, n_ctx, d.n_kv_heads, d.head_dim, offs_dev,
-                       n_chunks, c->rope, bf, c->cs);
+                       n_chunks, c->rope, d.max_tokens, bf, c->cs);
     if (e != hipSuccess) return hip_fail(e, "rope_delta launch");
   }
   // 2. x = RMSNorm(hidden_sel), unless the caller passes it
@@ -473,7 +474,7 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
     Timed t(c, CB_K_DEV_SCATTER, (double)n_sel * 2 * kvd * es * 2 + (double)n_cand * 2 * kvd * es);
     e = cb::dev_scatter(fresh_kv, fresh_ld, kv_fused_k, kv_fused_v, sel_idx, n_sel, n_cand, (int)n_tok, kvd,
                         n_ctx > 0 ? dev : nullptr, fuse_q ? new_sel_idx : nullptr, fuse_q ? new_sel_local : nullptr,
-                        bf, c->cs);
+                        c->score_mode == CB_SCORE_COSINE, bf, c->cs);
     if (e != hipSuccess) return hip_fail(e, "dev_scatter launch");
   }
   if (!fuse_q) {
@@ -585,6 +586,33 @@ cb_status cb_layer_rest(cb_ctx* c, int32_t layer, const float* hidden_sel, int32
     e = cb::rmsnorm(hidden_next, dm, n_new, dm, c->w[layer + 1].g_attn, d.rms_eps, x_next, bf, c->cs);
     if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
   }
+  return CB_OK;
+}
+
+cb_status cb_set_score_mode(cb_ctx* c, int32_t mode) {
+  cb_status st = check_ctx(c);
+  if (st) return st;
+  if (mode != CB_SCORE_L2 && mode != CB_SCORE_COSINE) return fail(CB_EINVAL, "unknown score mode %d", mode);
+  c->score_mode = mode;
+  return CB_OK;
+}
+
+cb_status cb_seam_select(const int32_t* offs, int32_t n_chunks, int32_t n_query, int32_t window, int32_t* out,
+                         int32_t capacity, int32_t* n_out) {
+  if (!offs || !n_out || (capacity > 0 && !out)) return fail(CB_EINVAL, "NULL pointer");
+  if (n_chunks < 0 || n_query < 0 || window < 0 || capacity < 0) return fail(CB_EINVAL, "negative size");
+  if (offs[0] != 0) return fail(CB_EINVAL, "chunk_offsets[0] = %d, must be 0", offs[0]);
+  for (int c = 0; c < n_chunks; ++c)
+    if (offs[c + 1] < offs[c]) return fail(CB_EINVAL, "chunk_offsets not monotone at %d", c);
+  long n = 0;
+  for (int c = 0; c < n_chunks; ++c) n += std::min<long>(window, offs[c + 1] - offs[c]);
+  n += n_query;
+  *n_out = (int32_t)n;
+  if (n > capacity) return fail(CB_ESHAPE, "%ld seam rows > capacity %d", n, capacity);
+  int32_t* o = out;
+  for (int c = 0; c < n_chunks; ++c)
+    for (int32_t p = std::max(offs[c], offs[c + 1] - window); p < offs[c + 1]; ++p) *o++ = p;
+  for (int32_t q = 0; q < n_query; ++q) *o++ = offs[n_chunks] + q;
   return CB_OK;
 }
 

@@ -47,11 +47,13 @@ hipError_t embed(const int32_t* tok, int n, const void* table, int vocab, int d,
                  hipStream_t s);
 hipError_t rmsnorm(const float* h, long ldh, int n, int d, const float* g, float eps, void* out, int bf16,
                    hipStream_t s);
+// table: [table_rows][dh / 2] cos/sin; a chunk offset outside [0, table_rows) is clamped.
 hipError_t rope_delta(const void* kc, const void* vc, void* kf, void* vf, int n_ctx, int hkv, int dh,
-                      const int32_t* offs, int n_chunks, const float2* table, int bf16, hipStream_t s);
+                      const int32_t* offs, int n_chunks, const float2* table, int table_rows, int bf16,
+                      hipStream_t s);
 hipError_t dev_scatter(const void* fresh, long ld_fresh, void* fk, void* fv, const int32_t* sel, int n_sel,
                        int n_cand, int n_tok, int row_elems, float* dev, int32_t* copy_sel, int32_t* copy_local,
-                       int bf16, hipStream_t s);
+                       int cosine, int bf16, hipStream_t s);
 hipError_t topk_select(const float* dev, const int32_t* sel, int n_cand, int n_query, int k, int32_t* new_sel,
                        int32_t* new_local, hipStream_t s);
 

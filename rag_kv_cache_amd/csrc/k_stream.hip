@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, long ldh, 
 template <typename T>
 __global__ __launch_bounds__(256) void rope_delta_kernel(const T* kc, const T* vc, T* kf, T* vf, int n_ctx,
                                                          int hkv, int dh, const int32_t* offs, int n_chunks,
-                                                         const float2* table, int copy_v) {
+                                                         const float2* table, int table_rows, int copy_v) {
   constexpr int VE = Vec16<T>::N;
   constexpr int MAXC = 256;  // chunk offsets searched in LDS (more chunks: searched in global memory)
   __shared__ int s_offs[MAXC + 1];
@@ -114,7 +114,8 @@ __global__ __launch_bounds__(256) void rope_delta_kernel(const T* kc, const T* v
       const int mid = (lo + hi + 1) >> 1;
       if ((in_lds ? s_offs[mid] : offs[mid]) <= row) lo = mid; else hi = mid - 1;
     }
-    const int o = in_lds ? s_offs[lo] : offs[lo];
+    int o = in_lds ? s_offs[lo] : offs[lo];
+    o = o < 0 ? 0 : (o >= table_rows ? table_rows - 1 : o);  // the device offsets are not host-checked
     const long base = ((long)row * hkv + h) * dh + i0;
     float a[VE], b[VE], ya[VE], yb[VE];
     Vec16<T>::load(kc + base, a);
@@ -147,12 +148,14 @@ __global__ __launch_bounds__(256) void rope_delta_kernel(const T* kc, const T* v
 // V heads (row_elems each).  Per-lane sequential sums then a fixed butterfly: the result
 // does not depend on scheduling.
 // When the layer keeps every recomputed row (copy_sel set), the kept set is sel itself:
-// copy_sel[i] = sel[i], copy_local[i] = i.
+// copy_sel[i] = sel[i], copy_local[i] = i.  cosine != 0 scores 1 - <fresh, fused> /
+// (|fresh| |fused|) over the row's K and V instead of the squared distance (0 when both rows
+// are zero, 1 when only one is).
 template <typename T>
 __global__ __launch_bounds__(256) void dev_scatter_kernel(const T* fresh, long ld_fresh, T* fk, T* fv,
                                                           const int32_t* sel, int n_sel, int n_cand, int n_tok,
                                                           int row_elems, float* dev, int32_t* copy_sel,
-                                                          int32_t* copy_local) {
+                                                          int32_t* copy_local, int cosine) {
   constexpr int VE = Vec16<T>::N;
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -170,26 +173,35 @@ __global__ __launch_bounds__(256) void dev_scatter_kernel(const T* fresh, long l
   const T* fr = fresh + (long)i * ld_fresh;
   T* dk = fk + (long)j * row_elems;
   T* dv = fv + (long)j * row_elems;
-  float acc = 0.f;
+  float acc = 0.f, na = 0.f, nb = 0.f;
   for (int e = lane * VE; e < row_elems; e += 64 * VE) {
     const uint4 nk = *reinterpret_cast<const uint4*>(fr + e);
     const uint4 nv = *reinterpret_cast<const uint4*>(fr + row_elems + e);
     if (score) {
       float a[VE], b[VE];
-      Vec16<T>::load(fr + e, a);
-      Vec16<T>::load(dk + e, b);
 #pragma unroll
-      for (int q = 0; q < VE; ++q) { const float t = a[q] - b[q]; acc += t * t; }
-      Vec16<T>::load(fr + row_elems + e, a);
-      Vec16<T>::load(dv + e, b);
+      for (int half = 0; half < 2; ++half) {
+        Vec16<T>::load(fr + half * row_elems + e, a);
+        Vec16<T>::load((half ? dv : dk) + e, b);
+        if (cosine) {
 #pragma unroll
-      for (int q = 0; q < VE; ++q) { const float t = a[q] - b[q]; acc += t * t; }
+          for (int q = 0; q < VE; ++q) { acc += a[q] * b[q]; na += a[q] * a[q]; nb += b[q] * b[q]; }
+        } else {
+#pragma unroll
+          for (int q = 0; q < VE; ++q) { const float t = a[q] - b[q]; acc += t * t; }
+        }
+      }
     }
     *reinterpret_cast<uint4*>(dk + e) = nk;
     *reinterpret_cast<uint4*>(dv + e) = nv;
   }
   if (score) {
     acc = wave_sum(acc);
+    if (cosine) {
+      na = wave_sum(na);
+      nb = wave_sum(nb);
+      acc = (na == 0.f || nb == 0.f) ? (na == nb ? 0.f : 1.f) : 1.0f - acc / (sqrtf(na) * sqrtf(nb));
+    }
     if (lane == 0) dev[i] = acc;
   }
 }
@@ -218,7 +230,8 @@ hipError_t rmsnorm(const float* h, long ldh, int n, int d, const float* g, float
 }
 
 hipError_t rope_delta(const void* kc, const void* vc, void* kf, void* vf, int n_ctx, int hkv, int dh,
-                      const int32_t* offs, int n_chunks, const float2* table, int bf16, hipStream_t s) {
+                      const int32_t* offs, int n_chunks, const float2* table, int table_rows, int bf16,
+                      hipStream_t s) {
   if (n_ctx <= 0) return hipSuccess;
   const int ve = bf16 ? 8 : 4;
   const long items = (long)n_ctx * hkv * (dh / 2 / ve);
@@ -227,24 +240,24 @@ hipError_t rope_delta(const void* kc, const void* vc, void* kf, void* vf, int n_
   const int copy_v = vc != vf;
   if (bf16)
     hipLaunchKernelGGL(rope_delta_kernel<bf16_t>, dim3((unsigned)blocks), dim3(256), 0, s, (const bf16_t*)kc,
-                       (const bf16_t*)vc, (bf16_t*)kf, (bf16_t*)vf, n_ctx, hkv, dh, offs, n_chunks, table, copy_v);
+                       (const bf16_t*)vc, (bf16_t*)kf, (bf16_t*)vf, n_ctx, hkv, dh, offs, n_chunks, table, table_rows, copy_v);
   else
     hipLaunchKernelGGL(rope_delta_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s, (const float*)kc,
-                       (const float*)vc, (float*)kf, (float*)vf, n_ctx, hkv, dh, offs, n_chunks, table, copy_v);
+                       (const float*)vc, (float*)kf, (float*)vf, n_ctx, hkv, dh, offs, n_chunks, table, table_rows, copy_v);
   return hipGetLastError();
 }
 
 hipError_t dev_scatter(const void* fresh, long ld_fresh, void* fk, void* fv, const int32_t* sel, int n_sel,
                        int n_cand, int n_tok, int row_elems, float* dev, int32_t* copy_sel, int32_t* copy_local,
-                       int bf16, hipStream_t s) {
+                       int cosine, int bf16, hipStream_t s) {
   if (n_sel <= 0) return hipSuccess;
   dim3 grid((n_sel + 3) / 4);
   if (bf16)
     hipLaunchKernelGGL(dev_scatter_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)fresh, ld_fresh,
-                       (bf16_t*)fk, (bf16_t*)fv, sel, n_sel, n_cand, n_tok, row_elems, dev, copy_sel, copy_local);
+                       (bf16_t*)fk, (bf16_t*)fv, sel, n_sel, n_cand, n_tok, row_elems, dev, copy_sel, copy_local, cosine);
   else
     hipLaunchKernelGGL(dev_scatter_kernel<float>, grid, dim3(256), 0, s, (const float*)fresh, ld_fresh,
-                       (float*)fk, (float*)fv, sel, n_sel, n_cand, n_tok, row_elems, dev, copy_sel, copy_local);
+                       (float*)fk, (float*)fv, sel, n_sel, n_cand, n_tok, row_elems, dev, copy_sel, copy_local, cosine);
   return hipGetLastError();
 }
 

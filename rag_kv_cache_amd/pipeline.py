@@ -111,6 +111,7 @@ class RunBuffers:
     xnorm: List[torch.Tensor]     # normalized rows handed from one layer to the next
     sel: List[torch.Tensor]
     iota: torch.Tensor
+    init_sel: torch.Tensor
     new_local: torch.Tensor
     out_sel: torch.Tensor
     dev: torch.Tensor
@@ -126,6 +127,7 @@ def make_buffers(eng: Engine, n_tokens: int, n_chunks: int) -> RunBuffers:
         xnorm=[torch.empty(n_tokens, s.d_model, dtype=eng.dtype, device=dv) for _ in range(2)],
         sel=[torch.empty(n_tokens, dtype=torch.int32, device=dv) for _ in range(2)],
         iota=torch.arange(n_tokens, dtype=torch.int32, device=dv),
+        init_sel=torch.empty(n_tokens, dtype=torch.int32, device=dv),
         new_local=torch.empty(n_tokens, dtype=torch.int32, device=dv),
         out_sel=torch.empty(n_tokens, s.n_q_heads * s.head_dim, dtype=eng.dtype, device=dv),
         dev=torch.empty(n_tokens, dtype=torch.float32, device=dv),
@@ -157,7 +159,8 @@ def run_layers(eng: Engine, buf: RunBuffers, tokens: np.ndarray, offsets: Sequen
                cache: Optional[List[Sequence[torch.Tensor]]] = None,
                host_cache: Optional[List[List[Sequence[torch.Tensor]]]] = None,
                record: bool = False, upload_inputs: bool = True,
-               layer_events: Optional[list] = None, rotate_on_copy_stream: bool = False) -> RunResult:
+               layer_events: Optional[list] = None, rotate_on_copy_stream: bool = False,
+               initial_sel: Optional[Sequence[int]] = None) -> RunResult:
     """Blended prefill over every layer.
 
     fused[l] = (K, V) device buffers [N, H_kv, d_h] of layer l (the fused cache, output).
@@ -167,6 +170,9 @@ def run_layers(eng: Engine, buf: RunBuffers, tokens: np.ndarray, offsets: Sequen
     copied two layers ahead into fused[l] on the copy stream and updated in place there); or
     neither (the fused buffers are used as they are, e.g. a full prefill with no context).
     schedule[l] is the recompute ratio used at layer l.
+    initial_sel: the rows recomputed at layer 1 (ascending, ending with every query row;
+    default every row), e.g. the spatial seam-repair set of cb_seam_select, kept at every layer
+    by a schedule of ratios >= 1.
     rotate_on_copy_stream (HBM mode): run the position update on the copy stream, two layers
     ahead (cb_fetch_layer_device), instead of inside cb_blend_layer on the compute stream.
     upload_inputs=False reuses the token ids and offsets already on the device (a repeated
@@ -182,8 +188,13 @@ def run_layers(eng: Engine, buf: RunBuffers, tokens: np.ndarray, offsets: Sequen
     cs = eng.compute
     ctx = eng.ctx
     with torch.cuda.stream(cs):
-        if upload_inputs:
+        if initial_sel is not None:  # layer 1 embeds the selected rows only
+            init = np.asarray(initial_sel, np.int32)
+            buf.init_sel[: len(init)].copy_(torch.from_numpy(init), non_blocking=False)
+            buf.tokens[: len(init)].copy_(torch.from_numpy(np.asarray(tokens, np.int32)[init]), non_blocking=False)
+        elif upload_inputs:
             buf.tokens[:n_tok].copy_(torch.from_numpy(np.asarray(tokens, np.int32)), non_blocking=False)
+        if upload_inputs or initial_sel is not None:
             buf.offsets[: n_chunks + 1].copy_(torch.tensor(offs, dtype=torch.int32))
     prefetch = host_cache is not None
     fetched = prefetch or (cache is not None and n_ctx > 0 and rotate_on_copy_stream)
@@ -209,9 +220,10 @@ def run_layers(eng: Engine, buf: RunBuffers, tokens: np.ndarray, offsets: Sequen
             ev.record(cs)
             layer_events.append(ev)
 
-    L.cb_embed(ctx, _ptr(buf.tokens), n_tok, _ptr(eng.emb), _ptr(buf.hidden[0]))
+    n_first = n_tok if initial_sel is None else len(initial_sel)
+    L.cb_embed(ctx, _ptr(buf.tokens), n_first, _ptr(eng.emb), _ptr(buf.hidden[0]))
     mark()
-    n_sel, cur = n_tok, 0
+    n_sel, cur = n_first, 0
     records = []
     ws = buf.ws
     for l in range(s.n_layers):
@@ -225,7 +237,7 @@ def run_layers(eng: Engine, buf: RunBuffers, tokens: np.ndarray, offsets: Sequen
             ck, cv = None, None
         fk, fv = fused[l]
         h_in, h_out = buf.hidden[cur], buf.hidden[1 - cur]
-        sel_in = buf.iota if l == 0 else buf.sel[(l - 1) % 2]
+        sel_in = (buf.iota if initial_sel is None else buf.init_sel) if l == 0 else buf.sel[(l - 1) % 2]
         sel_out = buf.sel[l % 2]
         # layer l-1's cb_layer_rest already normalized this layer's input rows (x_sel)
         x_in = buf.xnorm[(l - 1) % 2] if l > 0 else None

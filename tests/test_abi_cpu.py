@@ -58,3 +58,19 @@ def test_null_context_is_rejected():
     with pytest.raises(L.CbError) as e:
         L.cb_workspace_size(0, 10, 5)
     assert e.value.status == L.CB_EINVAL
+
+
+def test_seam_select_matches_oracle():
+    """cb_seam_select is host logic: compared with the oracle's seam windows on random chunk
+    layouts, and its size report / capacity error."""
+    import numpy as np
+    import oracle as O
+    from rag_kv_cache_amd import _lib as L
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        lens = rng.integers(0, 40, size=rng.integers(0, 7))
+        offs = [0] + np.cumsum(lens).astype(int).tolist()
+        nq, win = int(rng.integers(0, 9)), int(rng.integers(0, 20))
+        assert L.cb_seam_select(offs, len(offs) - 1, nq, win) == O.seam_positions(offs, nq, win).tolist()
+    with pytest.raises(L.CbError):
+        L.cb_seam_select([0, 3, 2], 2, 1, 4)
