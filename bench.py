@@ -74,6 +74,97 @@ def gate_up_traffic(shape, kept_rows):
     return total / len(kept_rows)
 
 
+def run_controller(eng, buf, tokens, offs, wl, fused, host, full_ms, steps):
+    """The loading controller on this GPU: the pinned-host load bandwidth measured by fetching a
+    whole step's cached KV alone, the prefill time per token from the full recompute, the ratio
+    cb_plan_ratio chooses (layer 1 stays at 1), and the pinned-host blended prefill run at it."""
+    import torch
+    from rag_kv_cache_amd import _lib as L
+    from rag_kv_cache_amd.pipeline import run_layers
+    sh = wl.shape
+    n_chunks = len(offs) - 1
+    kv_layer_tok = 2 * sh.n_kv_heads * sh.head_dim * 2
+
+    def fetch_all():
+        for l in range(sh.n_layers):
+            L.cb_fetch_layer(eng.ctx, l, [int(host[l][c][0].data_ptr()) for c in range(n_chunks)],
+                             [int(host[l][c][1].data_ptr()) for c in range(n_chunks)], offs, n_chunks,
+                             int(buf.offsets.data_ptr()), int(fused[l][0].data_ptr()), int(fused[l][1].data_ptr()))
+        for l in range(sh.n_layers):
+            L.cb_synchronize(eng.ctx, l)
+        eng.compute.synchronize()
+        eng.copy.synchronize()
+
+    fetch_all()
+    t0 = time.perf_counter()
+    for _ in range(3):
+        fetch_all()
+    load_s = (time.perf_counter() - t0) / 3
+    bw = sh.n_layers * wl.n_ctx * kv_layer_tok / load_s
+    pre = full_ms * 1e-3 / wl.n_tokens
+    plan = L.cb_plan_ratio(wl.n_ctx, sh.n_layers, kv_layer_tok, bw, pre, 0.0, 0.05, 1.0)
+    sched = [1.0] + [float(plan.ratio) if plan.load else 1.0] * (sh.n_layers - 1)
+    kw = dict(host_cache=host) if plan.load else dict(cache=None)
+    for _ in range(2):
+        run_layers(eng, buf, tokens, offs, wl.n_query, sched, fused, upload_inputs=False, **kw)
+    eng.compute.synchronize()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = max(3, steps // 2)
+    for _ in range(n):
+        run_layers(eng, buf, tokens, offs, wl.n_query, sched, fused, upload_inputs=False, **kw)
+    eng.compute.synchronize()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / n * 1e3
+    log(f"controller: load {bw / 1e9:.1f} GB/s, break-even {plan.break_even_bandwidth / 1e9:.1f} GB/s, "
+        f"ratio {plan.ratio:.3f} (load={plan.load}), predicted {plan.t_total * 1e3:.3f} ms, measured {ms:.3f} ms/step")
+    return {"load_bandwidth_GBps": round(bw / 1e9, 2), "prefill_us_per_token": round(pre * 1e6, 4),
+            "break_even_GBps": round(plan.break_even_bandwidth / 1e9, 2), "load": bool(plan.load),
+            "ratio": round(float(plan.ratio), 4), "predicted_ms_per_step": round(plan.t_total * 1e3, 4),
+            "measured_ms_per_step": round(ms, 4), "context_tokens_per_s": round(wl.n_ctx / ms * 1e3, 1),
+            "schedule": "1.0, then the planned ratio (pinned-host cache fetched two layers ahead)"}
+
+
+def run_variants(eng, buf, tokens, offs, wl, fused, cache, steps):
+    """The selection variants of the KVBoost page on the same workload (HBM-resident cache,
+    eager launches): the cosine deviation score with the same schedule, and the spatial seam
+    set (16 positions before every chunk boundary + the query) kept at every layer."""
+    import torch
+    from rag_kv_cache_amd import _lib as L
+    from rag_kv_cache_amd.pipeline import run_layers
+    sh = wl.shape
+    n = max(3, steps // 2)
+
+    def timed(**kw):
+        for _ in range(2):
+            run_layers(eng, buf, tokens, offs, wl.n_query, kw.get("sched", wl.schedule), fused, cache=cache,
+                       upload_inputs=False, initial_sel=kw.get("initial_sel"))
+        eng.compute.synchronize()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            run_layers(eng, buf, tokens, offs, wl.n_query, kw.get("sched", wl.schedule), fused, cache=cache,
+                       upload_inputs=False, initial_sel=kw.get("initial_sel"))
+        eng.compute.synchronize()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / n * 1e3
+
+    L.cb_set_score_mode(eng.ctx, L.CB_SCORE_COSINE)
+    cos_ms = timed()
+    L.cb_set_score_mode(eng.ctx, L.CB_SCORE_L2)
+    seam = L.cb_seam_select(offs, len(offs) - 1, wl.n_query, 16)
+    seam_ms = timed(sched=[1.0] * sh.n_layers, initial_sel=seam)
+    # leave the token ids on the device as the default runs expect them
+    buf.tokens[: wl.n_tokens].copy_(torch.from_numpy(np.asarray(tokens, np.int32)))
+    torch.cuda.synchronize()
+    log(f"variants: cosine score {cos_ms:.3f} ms/step; seam set ({len(seam)} rows) {seam_ms:.3f} ms/step")
+    return {"cosine_score": {"ms_per_step": round(cos_ms, 4), "context_tokens_per_s": round(wl.n_ctx / cos_ms * 1e3, 1),
+                             "schedule": "1.0, 0.30, 0.15 x 26 (eager)"},
+            "seam_set": {"rows": len(seam), "window": 16, "ms_per_step": round(seam_ms, 4),
+                         "context_tokens_per_s": round(wl.n_ctx / seam_ms * 1e3, 1),
+                         "schedule": "the seam set at every layer (eager)"}}
+
+
 def cpu_baseline(wl, budget_s: float = 25.0):
     """The oracle (fp64 NumPy with bf16 rounding points) on a bounded sample of the same
     workload: layer 1 (every row), layer 2 (all rows scored, 30% kept), layer 3 (15% kept)
@@ -239,7 +330,7 @@ def main() -> int:
     cs.synchronize()
     per_layer = [evs[i].elapsed_time(evs[i + 1]) for i in range(len(evs) - 1)]
 
-    pcie_ms = full_ms = None
+    pcie_ms = full_ms = controller = variants = None
     if not args.only_blend:
         # PCIe-inclusive variant: cached KV in pinned host memory, fetched one layer ahead
         for _ in range(2):
@@ -264,6 +355,8 @@ def main() -> int:
         cs.synchronize()
         full_ms = (time.perf_counter() - t0) / n_full * 1e3
         log(f"pinned-host prefetch: {pcie_ms:.3f} ms/step; full recompute: {full_ms:.3f} ms/step")
+        controller = run_controller(eng, buf, tokens, offs, wl, fused, host, full_ms, args.steps)
+        variants = run_variants(eng, buf, tokens, offs, wl, fused, cache, args.steps)
     if args.calib_copy:
         src = torch.empty(128 << 20, dtype=torch.bfloat16, device=eng.device)
         dst = torch.empty_like(src)
@@ -297,6 +390,8 @@ def main() -> int:
             "host_kv_bytes_per_step": int(2 * sh.n_layers * n_ctx * sh.n_kv_heads * sh.head_dim * 2)},
         "eager_ms_per_step": round(eager_ms, 4),
         "full_recompute_ms": None if full_ms is None else round(full_ms, 4),
+        "loading_controller": controller,
+        "selection_variants": variants,
         "speedup_vs_full_recompute": None if full_ms is None else round(full_ms / ms_step, 3),
     }
     print(json.dumps(out), flush=True)

@@ -218,6 +218,27 @@ cb_status cb_set_score_mode(cb_ctx* ctx, int32_t mode);
 cb_status cb_seam_select(const int32_t* chunk_offsets_host, int32_t n_chunks, int32_t n_query,
                          int32_t window, int32_t* out, int32_t capacity, int32_t* n_out);
 
+/* Loading controller (CacheBlend explainer, "Pipelined design" and the section on tuning the
+ * ratio to the storage; CacheBlend review, overlapping loading and recompute; LMCache blog,
+ * section 5, break-even).  Host-only, needs no context.  Per layer:
+ *   T_load      = n_ctx * kv_bytes_per_token_layer / bandwidth + latency_layer_s
+ *   T_prefill_l = n_ctx * prefill_s_per_token / n_layers   (full prefill of one layer)
+ *   break-even  = kv_bytes_per_token_layer * n_layers / prefill_s_per_token  (bytes/s)
+ * At or below break-even the plan is load = 0, ratio = 1 (recompute every row: loading
+ * cannot win).  Above it, ratio = T_load / T_prefill_l clamped to [r_min, r_max]: the largest
+ * recompute that still hides under the load, T_recompute = ratio * T_prefill_l, and
+ * T_layer = max(T_load, T_recompute), t_total = n_layers * T_layer (pipeline fill and drain
+ * left aside).  CB_EINVAL for non-positive sizes, bandwidth or prefill time, or ratios outside
+ * 0 <= r_min <= r_max <= 1. */
+typedef struct {
+  int32_t load;
+  float ratio;
+  double t_load_layer, t_recompute_layer, t_layer, t_total, break_even_bandwidth;
+} cb_ratio_plan;
+cb_status cb_plan_ratio(int32_t n_ctx, int32_t n_layers, double kv_bytes_per_token_layer, double bandwidth,
+                        double prefill_s_per_token, double latency_layer_s, float r_min, float r_max,
+                        cb_ratio_plan* out);
+
 /* Thread-local description of the last non-OK status ("" if none). */
 const char* cb_last_error(void);
 

@@ -65,6 +65,7 @@ _SIGS = {
     "cb_layer_rest": [_P, _I, _P, _I, _P, _I, _P, _P, _P, _P, C.c_size_t],
     "cb_set_score_mode": [_P, _I],
     "cb_seam_select": [C.POINTER(_I), _I, _I, _I, C.POINTER(_I), _I, C.POINTER(_I)],
+    "cb_plan_ratio": [_I, _I, C.c_double, C.c_double, C.c_double, C.c_double, C.c_float, C.c_float, _P],
     "cb_profile_enable": [_P, _I],
     "cb_profile_read": [_P, _I, C.POINTER(C.c_double), C.POINTER(C.c_int64), C.POINTER(C.c_double)],
 }
@@ -166,6 +167,19 @@ def cb_seam_select(chunk_offsets_host: Sequence[int], n_chunks: int, n_query: in
     out = (_I * max(n.value, 1))()
     _check(_L.cb_seam_select(_i32(chunk_offsets_host), n_chunks, n_query, window, out, n.value, C.byref(n)))
     return [out[i] for i in range(n.value)]
+
+
+class cb_ratio_plan(C.Structure):
+    _fields_ = [("load", _I), ("ratio", C.c_float), ("t_load_layer", C.c_double), ("t_recompute_layer", C.c_double),
+                ("t_layer", C.c_double), ("t_total", C.c_double), ("break_even_bandwidth", C.c_double)]
+
+
+def cb_plan_ratio(n_ctx: int, n_layers: int, kv_bytes_per_token_layer: float, bandwidth: float,
+                  prefill_s_per_token: float, latency_layer_s: float, r_min: float, r_max: float) -> cb_ratio_plan:
+    out = cb_ratio_plan()
+    _check(_L.cb_plan_ratio(n_ctx, n_layers, kv_bytes_per_token_layer, bandwidth, prefill_s_per_token,
+                            latency_layer_s, r_min, r_max, C.byref(out)))
+    return out
 
 
 def cb_profile_enable(ctx: int, on: bool) -> None:

@@ -616,6 +616,34 @@ cb_status cb_seam_select(const int32_t* offs, int32_t n_chunks, int32_t n_query,
   return CB_OK;
 }
 
+cb_status cb_plan_ratio(int32_t n_ctx, int32_t n_layers, double kvb, double bw, double pre, double lat, float r_min,
+                        float r_max, cb_ratio_plan* out) {
+  if (!out) return fail(CB_EINVAL, "out is NULL");
+  if (n_ctx <= 0 || n_layers <= 0 || !(kvb > 0) || !(bw > 0) || !(pre > 0) || !(lat >= 0))
+    return fail(CB_EINVAL, "sizes, bandwidth and prefill time must be positive, latency >= 0");
+  if (!(r_min >= 0.f) || !(r_max >= r_min) || !(r_max <= 1.f)) return fail(CB_EINVAL, "need 0 <= r_min <= r_max <= 1");
+  const double t_pre_layer = (double)n_ctx * pre / n_layers;
+  const double be = kvb * n_layers / pre;
+  cb_ratio_plan p{};
+  p.break_even_bandwidth = be;
+  if (bw <= be) {
+    p.load = 0;
+    p.ratio = 1.f;
+    p.t_load_layer = 0.0;
+    p.t_recompute_layer = p.t_layer = t_pre_layer;
+  } else {
+    p.load = 1;
+    p.t_load_layer = (double)n_ctx * kvb / bw + lat;
+    const double r = std::min<double>(std::max<double>(p.t_load_layer / t_pre_layer, r_min), r_max);
+    p.ratio = (float)r;
+    p.t_recompute_layer = r * t_pre_layer;
+    p.t_layer = std::max(p.t_load_layer, p.t_recompute_layer);
+  }
+  p.t_total = n_layers * p.t_layer;
+  *out = p;
+  return CB_OK;
+}
+
 cb_status cb_profile_enable(cb_ctx* c, int32_t on) {
   cb_status st = check_ctx(c);
   if (st) return st;

@@ -74,3 +74,31 @@ def test_seam_select_matches_oracle():
         assert L.cb_seam_select(offs, len(offs) - 1, nq, win) == O.seam_positions(offs, nq, win).tolist()
     with pytest.raises(L.CbError):
         L.cb_seam_select([0, 3, 2], 2, 1, 4)
+
+
+def test_plan_ratio_matches_oracle():
+    """cb_plan_ratio is host logic: compared with the oracle's controller on random inputs
+    spanning both sides of break-even, plus its argument checks."""
+    import numpy as np
+    from oracle import controller as C
+    from rag_kv_cache_amd import _lib as L
+    rng = np.random.default_rng(9)
+    for _ in range(500):
+        n_ctx, nl = int(rng.integers(1, 20000)), int(rng.integers(1, 100))
+        kvb = float(rng.uniform(256, 40000))
+        pre = float(10 ** rng.uniform(-6.5, -3.5))
+        bw = float(10 ** rng.uniform(7, 12))
+        lat = float(rng.choice([0.0, 1e-5]))
+        r_min = float(np.float32(rng.uniform(0, 0.3)))
+        r_max = float(np.float32(rng.uniform(r_min, 1.0)))
+        got = L.cb_plan_ratio(n_ctx, nl, kvb, bw, pre, lat, r_min, r_max)
+        ref = C.plan_ratio(n_ctx, nl, kvb, bw, pre, r_min, r_max, latency_layer=lat)
+        assert bool(got.load) == ref.load
+        assert abs(got.ratio - ref.ratio) <= 1e-6 * max(1.0, ref.ratio)
+        for f in ("t_load_layer", "t_recompute_layer", "t_layer", "t_total"):
+            assert abs(getattr(got, f) - getattr(ref, f)) <= 1e-9 * max(1.0, abs(getattr(ref, f))) + 1e-15, f
+        assert abs(got.break_even_bandwidth - ref.break_even) <= 1e-9 * ref.break_even
+    for bad in [(0, 28, 1024.0, 1e9, 1e-6, 0.0, 0.1, 0.5), (10, 28, 1024.0, 0.0, 1e-6, 0.0, 0.1, 0.5),
+                (10, 28, 1024.0, 1e9, 1e-6, 0.0, 0.6, 0.5), (10, 28, 1024.0, 1e9, 1e-6, 0.0, 0.1, 1.5)]:
+        with pytest.raises(L.CbError):
+            L.cb_plan_ratio(*bad)
