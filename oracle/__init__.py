@@ -30,6 +30,8 @@ Parity status per function (what pins each one, see tests/test_oracle_*.py):
   cosine_deviation .. identical / opposite / orthogonal rows, scale invariance, the
                       closed form 1 - cos(theta) for a rotation by theta
   seam_positions .... hand-worked boundary windows (short chunks, window > chunk)
+  decode_step ....... after a full-recompute prefill, decoding equals full prefill of the
+                      longer prompt; one step of two tokens equals two steps of one
   controller ........ the break-even and load/recompute numbers the LMCache page and the
                       CacheBlend review print
   which rows are HKVD on random weights ... parity unpinned (the pages print no
@@ -41,6 +43,6 @@ from .model import (  # noqa: F401
 )
 from .blend import (  # noqa: F401
     k_for_ratio, topk_select, kv_deviation, cosine_deviation, seam_positions, blend_layer,
-    layer_rest, fuse_cache, blended_prefill,
+    layer_rest, fuse_cache, blended_prefill, decode_step,
 )
 from . import controller  # noqa: F401

@@ -198,3 +198,28 @@ def blended_prefill(shape, weights: List[Dict[str, np.ndarray]], emb: np.ndarray
         layers.append(r)
         sel = r["new_sel"]
     return {"layers": layers, "hidden": hidden, "sel": sel, "caches": caches, "offsets": offs}
+
+
+def decode_step(shape, weights: List[Dict[str, np.ndarray]], emb: np.ndarray, prec: Precision,
+                fused: Sequence, n_past: int, tokens: Sequence[int]):
+    """Generation with the fused KV (CacheBlend review: generate with the fused KV cache after
+    the blended prefill): the n_new = len(tokens) new tokens at positions n_past .. get fresh
+    Q/K/V at every layer, their K/V are appended to the layer's fused KV (rows n_past ..), and
+    they attend causally to every fused row up to their position.  This is step 1-8 above with
+    every past row as (already fused) context, the new rows as query rows and nothing to rank.
+    fused[l] = (K, V) [n_past, H_kv, d_h]; returns the extended fused KV per layer, the new
+    rows' hidden state after the last layer and each layer's attention output."""
+    toks = np.asarray(tokens, np.int64)
+    n_new = len(toks)
+    sel = np.arange(n_past, n_past + n_new)
+    hidden = np.asarray(emb[toks], np.float64)
+    out_fused, outs = [], []
+    for li, w in enumerate(weights):
+        k0, v0 = fused[li]
+        fk = np.concatenate([np.asarray(k0, np.float64)[:n_past], np.zeros((n_new,) + k0.shape[1:])])
+        fv = np.concatenate([np.asarray(v0, np.float64)[:n_past], np.zeros((n_new,) + v0.shape[1:])])
+        r = blend_layer(shape, w, prec, hidden, fk, fv, n_past, sel, n_new, 0.0)
+        hidden = layer_rest(shape, w, prec, hidden, r["new_local"], r["out"])
+        out_fused.append((r["fused_k"], r["fused_v"]))
+        outs.append(r["out"])
+    return {"fused": out_fused, "hidden": hidden, "out": outs}
