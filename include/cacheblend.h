@@ -164,7 +164,9 @@ cb_status cb_synchronize(cb_ctx* ctx, int32_t layer);
  *   kv_cached_k/_v   device [N_ctx][n_kv_heads][head_dim]: offset-0 chunk caches in
  *                    prompt order, or NULL (see 1.)
  *   kv_fused_k/_v    device [N_ctx + n_query][n_kv_heads][head_dim]: the layer's fused K/V
- *   chunk_offsets_dev / _host  the same [n_chunks + 1] offsets on device and host;
+ *   chunk_offsets_dev / _host  the same [n_chunks + 1] offsets on device and host (the device
+ *                    copy is read only by the position update, so it may be NULL when
+ *                    kv_cached_k is NULL);
  *                    n_chunks may be 0 (no context: every row is a query row, which is
  *                    how a chunk's own cache is built)
  *   sel_idx          device int32 [n_sel] strictly ascending positions; its last n_query
@@ -184,6 +186,21 @@ cb_status cb_blend_layer(cb_ctx* ctx, int32_t layer, const float* hidden_sel, co
                          int32_t n_chunks, const int32_t* sel_idx, int32_t n_sel, int32_t n_query,
                          float ratio, int32_t* new_sel_idx, int32_t* new_sel_local, int32_t* n_new,
                          void* out_sel, float* deviation, void* workspace, size_t workspace_bytes);
+
+/* Generation with the fused KV (CacheBlend review: the answer is generated with the fused KV
+ * cache).  One layer of a decode step for n_new new tokens at positions n_past .. n_past +
+ * n_new - 1: fresh Q/K/V of the new rows (RoPE at their positions) from hidden_new (device fp32
+ * [n_new][d_model]; or x_new, its RMSNorm, as in cb_blend_layer), their K/V written to rows
+ * n_past .. of kv_fused (which must hold the fused rows 0 .. n_past - 1 and have room), and
+ * their causal attention over fused rows 0 .. position into out_sel [n_new][n_q_heads *
+ * head_dim].  pos_dev: device int32 [n_new] holding n_past, n_past + 1, ... (kernels bound
+ * positions by n_past + n_new).  Then cb_layer_rest on the same rows with new_sel_local =
+ * 0 .. n_new - 1.  The workspace is cb_workspace_size(n_past + n_new, n_new).  It is
+ * cb_blend_layer with the past rows as one already-fused context span and the new rows as
+ * query rows; few rows split the key range finely (256-key ranges) to fill the chip. */
+cb_status cb_decode_layer(cb_ctx* ctx, int32_t layer, const float* hidden_new, const void* x_new,
+                          void* kv_fused_k, void* kv_fused_v, int32_t n_past, int32_t n_new,
+                          const int32_t* pos_dev, void* out_sel, void* workspace, size_t workspace_bytes);
 
 /* Rest of the layer on the kept rows (the output passed to the next layer):
  *   h1 = hidden_sel[new_sel_local] + out_sel W_o^T

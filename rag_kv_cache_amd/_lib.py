@@ -63,6 +63,7 @@ _SIGS = {
     "cb_blend_layer": [_P, _I, _P, _P, _P, _P, _P, _P, _P, C.POINTER(_I), _I, _P, _I, _I, C.c_float, _P, _P,
                        C.POINTER(_I), _P, _P, _P, C.c_size_t],
     "cb_layer_rest": [_P, _I, _P, _I, _P, _I, _P, _P, _P, _P, C.c_size_t],
+    "cb_decode_layer": [_P, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P, C.c_size_t],
     "cb_set_score_mode": [_P, _I],
     "cb_seam_select": [C.POINTER(_I), _I, _I, _I, C.POINTER(_I), _I, C.POINTER(_I)],
     "cb_plan_ratio": [_I, _I, C.c_double, C.c_double, C.c_double, C.c_double, C.c_float, C.c_float, _P],
@@ -145,6 +146,13 @@ def cb_blend_layer(ctx: int, layer: int, hidden_sel: int, kv_cached_k: int, kv_c
                              sel_idx, n_sel, n_query, ratio, new_sel_idx, new_sel_local, C.byref(n_new),
                              out_sel, deviation or None, workspace, workspace_bytes))
     return n_new.value
+
+
+def cb_decode_layer(ctx: int, layer: int, hidden_new: int, kv_fused_k: int, kv_fused_v: int, n_past: int,
+                    n_new: int, pos_dev: int, out_sel: int, workspace: int, workspace_bytes: int,
+                    x_new: int = 0) -> None:
+    _check(_L.cb_decode_layer(ctx, layer, hidden_new, x_new or None, kv_fused_k, kv_fused_v, n_past, n_new,
+                              pos_dev, out_sel, workspace, workspace_bytes))
 
 
 def cb_layer_rest(ctx: int, layer: int, hidden_sel: int, n_sel: int, new_sel_local: int, n_new: int,

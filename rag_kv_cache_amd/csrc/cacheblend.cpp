@@ -43,6 +43,8 @@ struct ProfRec {
 constexpr int kMaxProf = 16384;
 constexpr int kGemmMaxSplits = 8;
 constexpr int kAttnMaxSplits = 16;
+constexpr int kAttnSmallRows = 64;     // kept sets this small (decode) get finer key splits:
+constexpr int kAttnSmallSplits = 64;   // up to this many
 constexpr int kPartialRows = 2048;  // split-K / split-KV partial buffers cover this many rows
 constexpr size_t kAlign = 256;
 
@@ -74,7 +76,7 @@ namespace {
 
 // Workspace layout (byte offsets), shared by blend_layer and layer_rest.
 struct WsPlan {
-  size_t x, fresh, dev, q, attn_o, attn_ml, h1, mnorm, act, gpart, total;
+  size_t x, fresh, dev, q, attn_o, attn_ml, didx, h1, mnorm, act, gpart, total;
   long attn_cap_rows;  // rows x splits the attention partials can hold
   long gpart_elems;    // fp32 elements of the split-K partial buffer
 };
@@ -93,9 +95,12 @@ WsPlan plan_ws(const cb_model_desc& d, int n_tokens, int n_sel) {
   p.fresh = take(ns * (qd + 2 * kvd) * es);  // fresh K|V, or Q|K|V when every candidate is kept
   p.dev = take(ns * 4);
   p.q = take(ns * qd * es);
-  p.attn_cap_rows = prow * kAttnMaxSplits;
+  // split-KV partials: up to kAttnMaxSplits key ranges per row, or kAttnSmallSplits for the
+  // few rows of a decode step
+  p.attn_cap_rows = std::max<long>(prow * kAttnMaxSplits, std::min<long>((long)ns, kAttnSmallRows) * kAttnSmallSplits);
   p.attn_o = take((size_t)p.attn_cap_rows * qd * 4);
   p.attn_ml = take((size_t)p.attn_cap_rows * d.n_q_heads * 2 * 4);
+  p.didx = take(ns * 2 * 4);  // decode: kept positions and their local indices
   // layer_rest reuses the front of the workspace (blend_layer's buffers are dead by then)
   size_t blend_end = off;
   off = 0;
@@ -118,12 +123,14 @@ void plan_gemm(cb::GemmArgs& g, bool bf, long cap_elems) {
   g.splits = p.splits;
 }
 
-// Split-KV: key ranges of 1024 keys for small kept sets, 2048 for large ones (measured best for
+// Split-KV: key ranges of 256 keys for the few rows of a decode step, 1024 keys for small kept
+// sets, 2048 for large ones (measured best for
 // the causal row-length mix of the fused prompt), bounded by the partial buffer.
 void attn_splits(int n_q, int n_tok, long cap_rows, int& splits, int& split_len) {
-  int len = n_q < 1200 ? 1024 : 2048;
+  const bool small = n_q <= kAttnSmallRows;
+  int len = small ? 256 : (n_q < 1200 ? 1024 : 2048);
   int s = (n_tok + len - 1) / len;
-  s = std::min(s, kAttnMaxSplits);
+  s = std::min(s, small ? kAttnSmallSplits : kAttnMaxSplits);
   while (s > 1 && (long)s * n_q > cap_rows) --s;
   len = (n_tok + s - 1) / s;
   len = (len + 63) / 64 * 64;
@@ -408,7 +415,7 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
   if ((kv_cached_k == nullptr) != (kv_cached_v == nullptr)) return fail(CB_EINVAL, "kv_cached_k / _v: both or neither");
   if ((kv_cached_k == kv_fused_k) != (kv_cached_v == kv_fused_v))
     return fail(CB_EINVAL, "kv_cached must alias kv_fused for both K and V or for neither");
-  if (n_chunks > 0 && !offs_dev) return fail(CB_EINVAL, "chunk_offsets_dev is NULL");
+  if (n_chunks > 0 && kv_cached_k && !offs_dev) return fail(CB_EINVAL, "chunk_offsets_dev is NULL");
   const WsPlan wp = plan_ws(d, (int)n_tok, n_sel);
   if (!workspace || ws_bytes < wp.total)
     return fail(CB_ENOMEM, "workspace %zu bytes < %zu needed", ws_bytes, wp.total);
@@ -515,6 +522,26 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
     if (e != hipSuccess) return hip_fail(e, "attention launch");
   }
   return mark_release(c, layer);
+}
+
+cb_status cb_decode_layer(cb_ctx* c, int32_t layer, const float* hidden_new, const void* x_new, void* kv_fused_k,
+                          void* kv_fused_v, int32_t n_past, int32_t n_new, const int32_t* pos_dev, void* out_sel,
+                          void* workspace, size_t ws_bytes) {
+  cb_status st = check_ctx(c);
+  if (st) return st;
+  if (n_past < 0 || n_new < 0) return fail(CB_EINVAL, "negative size");
+  if ((long)n_past + n_new > c->d.max_tokens) return fail(CB_ESHAPE, "%d + %d rows > max_tokens", n_past, n_new);
+  if (n_new > 0 && !pos_dev) return fail(CB_EINVAL, "pos_dev is NULL");
+  const WsPlan wp = plan_ws(c->d, n_past + n_new, n_new);
+  if (!workspace || ws_bytes < wp.total) return fail(CB_ENOMEM, "workspace %zu bytes < %zu needed", ws_bytes, wp.total);
+  int32_t* idx = (int32_t*)((char*)workspace + wp.didx);
+  const int32_t offs[2] = {0, n_past};
+  int32_t nn = 0;
+  // every past row is already-fused context (nothing to re-rotate, nothing to rank); the new
+  // rows are the query rows and are all kept
+  return cb_blend_layer(c, layer, hidden_new, x_new, nullptr, nullptr, kv_fused_k, kv_fused_v, nullptr, offs,
+                        n_past > 0 ? 1 : 0, pos_dev, n_new, n_new, 0.f, idx, idx + std::max(n_new, 1), &nn, out_sel,
+                        nullptr, workspace, ws_bytes);
 }
 
 cb_status cb_layer_rest(cb_ctx* c, int32_t layer, const float* hidden_sel, int32_t n_sel,

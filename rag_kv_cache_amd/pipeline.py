@@ -307,3 +307,33 @@ def capture_step(eng: Engine, step: Callable[[], object]) -> "torch.cuda.CUDAGra
         step()
     eng.compute.synchronize()
     return graph
+
+
+def decode(eng: Engine, buf: RunBuffers, new_tokens: Sequence[int], n_past: int,
+           fused: List[Sequence[torch.Tensor]]) -> torch.Tensor:
+    """One decode step of len(new_tokens) tokens at positions n_past .. with the fused KV of
+    every layer (rows 0 .. n_past - 1 filled by a blended prefill or earlier decode steps;
+    the new rows are appended).  Returns the new rows' hidden state after the last layer
+    ([n_new, d] fp32, a view into buf), enqueued on the engine's compute stream: synchronize
+    it before reading.  Token ids are given: choosing them needs the LM head, which is not part
+    of this library."""
+    s = eng.shape
+    n_new = len(new_tokens)
+    cs = eng.compute
+    ctx = eng.ctx
+    with torch.cuda.stream(cs):
+        buf.tokens[:n_new].copy_(torch.from_numpy(np.asarray(new_tokens, np.int32)), non_blocking=False)
+        buf.init_sel[:n_new].copy_(torch.arange(n_past, n_past + n_new, dtype=torch.int32), non_blocking=False)
+    L.cb_embed(ctx, _ptr(buf.tokens), n_new, _ptr(eng.emb), _ptr(buf.hidden[0]))
+    ws = buf.ws
+    cur = 0
+    for l in range(s.n_layers):
+        h_in, h_out = buf.hidden[cur], buf.hidden[1 - cur]
+        x_in = buf.xnorm[(l - 1) % 2] if l > 0 else None
+        x_out = buf.xnorm[l % 2] if l + 1 < s.n_layers else None
+        L.cb_decode_layer(ctx, l, _ptr(h_in), _ptr(fused[l][0]), _ptr(fused[l][1]), n_past, n_new,
+                          _ptr(buf.init_sel), _ptr(buf.out_sel), _ptr(ws), ws.numel(), x_new=_ptr(x_in))
+        L.cb_layer_rest(ctx, l, _ptr(h_in), n_new, _ptr(buf.iota), n_new, _ptr(buf.out_sel), _ptr(h_out),
+                        _ptr(ws), ws.numel(), x_next=_ptr(x_out))
+        cur = 1 - cur
+    return buf.hidden[cur][:n_new]
