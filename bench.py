@@ -34,6 +34,7 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+DECODE_ROWS = 32           # fused-KV rows kept free after the prompt for the decode steps
 
 
 def log(msg: str) -> None:
@@ -165,6 +166,33 @@ def run_variants(eng, buf, tokens, offs, wl, fused, cache, steps):
                          "schedule": "the seam set at every layer (eager)"}}
 
 
+def run_decode(eng, buf, tokens, offs, wl, fused, cache):
+    """Generation with the fused KV after one blended prefill: single-token decode steps through
+    all layers (given token ids; no LM head), ms per token, eager launches."""
+    import torch
+    from rag_kv_cache_amd.pipeline import decode, run_layers
+    run_layers(eng, buf, tokens, offs, wl.n_query, wl.schedule, fused, cache=cache, upload_inputs=False)
+    eng.compute.synchronize()
+    n = wl.n_tokens
+    steps = 16
+    assert steps + 2 <= DECODE_ROWS
+    for i in range(2):  # warmup (appends rows n, n+1; overwritten below)
+        decode(eng, buf, [i + 1], n + i, fused)
+    eng.compute.synchronize()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        decode(eng, buf, [(7 * i) % wl.shape.vocab], n + i, fused)
+    eng.compute.synchronize()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    buf.tokens[: wl.n_tokens].copy_(torch.from_numpy(np.asarray(tokens, np.int32)))
+    torch.cuda.synchronize()
+    log(f"decode: {ms:.3f} ms/token ({steps} single-token steps after the blended prefill)")
+    return {"ms_per_token": round(ms, 4), "tokens_per_s": round(1e3 / ms, 1), "steps": steps,
+            "context_rows": n, "note": "single-token steps on the fused KV, eager launches, given token ids"}
+
+
 def cpu_baseline(wl, budget_s: float = 25.0):
     """The oracle (fp64 NumPy with bf16 rounding points) on a bounded sample of the same
     workload: layer 1 (every row), layer 2 (all rows scored, 30% kept), layer 3 (15% kept)
@@ -244,7 +272,7 @@ def main() -> int:
         f"N_ctx {n_ctx} + query {wl.n_query}")
 
     t0 = time.perf_counter()
-    eng = Engine(sh, max_tokens=n_tok + 64)
+    eng = Engine(sh, max_tokens=n_tok + 64)  # room for decode steps after the prefill
     for l in range(sh.n_layers):
         eng.load_layer(l, F.layer_weights(sh, l + 1))
     eng.load_embedding(F.embedding(sh))
@@ -254,8 +282,9 @@ def main() -> int:
     cache, host = build_chunk_caches(eng, chunks, pinned_host=True)
     log(f"chunk caches built in {time.perf_counter() - t0:.1f} s")
 
-    buf = make_buffers(eng, n_tok, len(chunks))
-    fused = [(eng.kv_empty(n_tok), eng.kv_empty(n_tok)) for _ in range(sh.n_layers)]
+    extra = DECODE_ROWS  # rows after the prompt for the decode steps
+    buf = make_buffers(eng, n_tok + extra, len(chunks))
+    fused = [(eng.kv_empty(n_tok + extra), eng.kv_empty(n_tok + extra)) for _ in range(sh.n_layers)]
     cs = eng.compute
     rec = run_layers(eng, buf, tokens, offs, wl.n_query, wl.schedule, fused, cache=cache, record=True)
     attn_fl = attention_flops(sh, rec.records, wl.n_query)
@@ -330,7 +359,7 @@ def main() -> int:
     cs.synchronize()
     per_layer = [evs[i].elapsed_time(evs[i + 1]) for i in range(len(evs) - 1)]
 
-    pcie_ms = full_ms = controller = variants = None
+    pcie_ms = full_ms = controller = variants = decode_ms = None
     if not args.only_blend:
         # PCIe-inclusive variant: cached KV in pinned host memory, fetched one layer ahead
         for _ in range(2):
@@ -357,6 +386,7 @@ def main() -> int:
         log(f"pinned-host prefetch: {pcie_ms:.3f} ms/step; full recompute: {full_ms:.3f} ms/step")
         controller = run_controller(eng, buf, tokens, offs, wl, fused, host, full_ms, args.steps)
         variants = run_variants(eng, buf, tokens, offs, wl, fused, cache, args.steps)
+        decode_ms = run_decode(eng, buf, tokens, offs, wl, fused, cache)
     if args.calib_copy:
         src = torch.empty(128 << 20, dtype=torch.bfloat16, device=eng.device)
         dst = torch.empty_like(src)
@@ -392,6 +422,7 @@ def main() -> int:
         "full_recompute_ms": None if full_ms is None else round(full_ms, 4),
         "loading_controller": controller,
         "selection_variants": variants,
+        "decode": decode_ms,
         "speedup_vs_full_recompute": None if full_ms is None else round(full_ms / ms_step, 3),
     }
     print(json.dumps(out), flush=True)
