@@ -34,6 +34,9 @@ Parity status per function (what pins each one, see tests/test_oracle_*.py):
                       longer prompt; one step of two tokens equals two steps of one
   controller ........ the break-even and load/recompute numbers the LMCache page and the
                       CacheBlend review print
+  store ............. FIPS 180-2 SHA-256 examples rebuilt from token and key bytes, the
+                      LRU cyclic-scan trap the LMCache page measures, LRU's stack property,
+                      a hand-worked eviction sequence
   which rows are HKVD on random weights ... parity unpinned (the pages print no
                       worked example; only the invariants above constrain it)
 """
@@ -45,4 +48,4 @@ from .blend import (  # noqa: F401
     k_for_ratio, topk_select, kv_deviation, cosine_deviation, seam_positions, blend_layer,
     layer_rest, fuse_cache, blended_prefill, decode_step,
 )
-from . import controller  # noqa: F401
+from . import controller, store  # noqa: F401
