@@ -256,6 +256,81 @@ cb_status cb_plan_ratio(int32_t n_ctx, int32_t n_layers, double kv_bytes_per_tok
                         double prefill_s_per_token, double latency_layer_s, float r_min, float r_max,
                         cb_ratio_plan* out);
 
+/* ---------------------------------------------------------------- chunk KV store
+ * The offline side of the path: every chunk is prefilled alone at positions 0.. (CacheBlend
+ * explainer, background: documents' KV precomputed independently) and its per-layer K and V
+ * kept in host memory, found again through a hash table in CPU memory (explainer, integration
+ * with vLLM: about 16 MB per million chunks).  Host-only except cb_store_put_layer.  Every
+ * store call is thread-safe (one lock per store). */
+
+/* FIPS 180-4 SHA-256 of n bytes into digest[32]. */
+cb_status cb_sha256(const void* data, size_t n, uint8_t* digest);
+
+/* 64-bit chunk key (KVBoost article, dual hash keys; the explainer's RAG example keeps the first
+ * 64 bits of a SHA-256 digest): the first 8 digest bytes, read big-endian, of SHA-256 over
+ * n_prior earlier keys (8 bytes big-endian each) followed by the n token ids (int32,
+ * little-endian).  n_prior = 0 gives the content key (position-free); the content keys of
+ * every earlier chunk of the prompt as prior give the prefix key.  CB_EINVAL for negative
+ * lengths or NULL arrays of non-zero length. */
+cb_status cb_chunk_key(const int32_t* tokens, int32_t n, const uint64_t* prior, int32_t n_prior, uint64_t* key);
+
+typedef struct cb_store cb_store;
+
+/* A store of n_slots chunks of at most max_chunk_tokens tokens for the model desc (its
+ * n_layers, n_kv_heads, head_dim, dtype).  One slot holds, per layer, K then V, each
+ * [max_chunk_tokens][n_kv_heads][head_dim] of dtype; the arena of n_slots slots is allocated
+ * once, pinned (hipHostMalloc, pinned != 0; the form cb_fetch_layer copies from without a
+ * staging copy) or pageable (malloc).  The index is open addressing with linear probing over
+ * n_slots * 5/4 + 1 buckets of 16 bytes (key, slot), kept at most 80% full; deletion moves
+ * later buckets back (no tombstones).  CB_EINVAL for non-positive sizes, CB_ENOMEM when the
+ * arena cannot be allocated. */
+cb_status cb_store_create(const cb_model_desc* desc, int32_t max_chunk_tokens, int32_t n_slots, int32_t pinned,
+                          cb_store** out);
+/* Frees the arena.  Copies into or out of it must have completed. */
+cb_status cb_store_destroy(cb_store* store);
+
+/* Slot of the committed entry whose tokens and prior keys equal these (key match verified
+ * against the stored tokens), else -1 (counted as a miss).  A hit makes the entry the most
+ * recently used; pin != 0 also holds it (not evictable) until cb_store_release. */
+cb_status cb_store_lookup(cb_store* store, const int32_t* tokens, int32_t n, const uint64_t* prior,
+                          int32_t n_prior, int32_t pin, int32_t* slot);
+
+/* Find or make the entry of this chunk (1 <= n <= max_chunk_tokens, else CB_ESHAPE).  Already
+ * present (committed or not): made most recent, *is_new = 0.  Otherwise the lowest free slot,
+ * or else the least recently used entry that nobody holds is evicted (*evicted = its slot,
+ * else -1), and the new entry is uncommitted, *is_new = 1: the caller fills its layers
+ * (cb_store_put_layer, or writes through cb_store_layer) and then calls cb_store_commit;
+ * lookups miss it until then.  pin != 0 holds the entry.  CB_ESTATE when every entry is
+ * held (nothing is changed). */
+cb_status cb_store_insert(cb_store* store, const int32_t* tokens, int32_t n, const uint64_t* prior,
+                          int32_t n_prior, int32_t pin, int32_t* slot, int32_t* is_new, int32_t* evicted);
+
+/* Mark the entry's data complete (after the stream that filled it has been synchronized). */
+cb_status cb_store_commit(cb_store* store, int32_t slot);
+
+/* Drop one hold of the entry (CB_ESTATE if it has none). */
+cb_status cb_store_release(cb_store* store, int32_t slot);
+
+/* Host addresses of layer `layer`'s K and V rows of the entry in `slot`, and its token count.
+ * The rows are [n_tokens][n_kv_heads][head_dim], K at positions 0.. (offset-0 cache): the
+ * host_k[c] / host_v[c] that cb_fetch_layer takes.  Valid while the entry is not evicted. */
+cb_status cb_store_layer(cb_store* store, int32_t slot, int32_t layer, void** host_k, void** host_v,
+                         int32_t* n_tokens);
+
+/* Producer: enqueue on the context's compute stream the device-to-host copies of the entry's
+ * n_tokens rows of layer `layer` from dev_k / dev_v (device [n_tokens][n_kv_heads][head_dim],
+ * the K/V a prefill of the chunk alone at positions 0.. wrote for that layer).  CB_ESHAPE
+ * when the store was made for another model. */
+cb_status cb_store_put_layer(cb_ctx* ctx, cb_store* store, int32_t slot, int32_t layer, const void* dev_k,
+                             const void* dev_v);
+
+typedef struct {
+  int64_t hits, misses, evictions;
+  int32_t entries, capacity;
+  size_t index_bytes, arena_bytes, slot_bytes;
+} cb_store_stats;
+cb_status cb_store_get_stats(cb_store* store, cb_store_stats* out);
+
 /* Thread-local description of the last non-OK status ("" if none). */
 const char* cb_last_error(void);
 

@@ -10,6 +10,8 @@ import ctypes as C
 import os
 from typing import Optional, Sequence
 
+import numpy as np
+
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librag_kv_cache_amd.so")
 
 CB_OK, CB_EINVAL, CB_ESHAPE, CB_ESTATE, CB_EHIP, CB_ENOMEM, CB_EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
@@ -67,6 +69,17 @@ _SIGS = {
     "cb_set_score_mode": [_P, _I],
     "cb_seam_select": [C.POINTER(_I), _I, _I, _I, C.POINTER(_I), _I, C.POINTER(_I)],
     "cb_plan_ratio": [_I, _I, C.c_double, C.c_double, C.c_double, C.c_double, C.c_float, C.c_float, _P],
+    "cb_sha256": [_P, C.c_size_t, _P],
+    "cb_chunk_key": [_P, _I, _P, _I, C.POINTER(C.c_uint64)],
+    "cb_store_create": [C.POINTER(cb_model_desc), _I, _I, _I, C.POINTER(_P)],
+    "cb_store_destroy": [_P],
+    "cb_store_lookup": [_P, _P, _I, _P, _I, _I, C.POINTER(_I)],
+    "cb_store_insert": [_P, _P, _I, _P, _I, _I, C.POINTER(_I), C.POINTER(_I), C.POINTER(_I)],
+    "cb_store_commit": [_P, _I],
+    "cb_store_release": [_P, _I],
+    "cb_store_layer": [_P, _I, _I, C.POINTER(_P), C.POINTER(_P), C.POINTER(_I)],
+    "cb_store_put_layer": [_P, _P, _I, _I, _P, _P],
+    "cb_store_get_stats": [_P, _P],
     "cb_profile_enable": [_P, _I],
     "cb_profile_read": [_P, _I, C.POINTER(C.c_double), C.POINTER(C.c_int64), C.POINTER(C.c_double)],
 }
@@ -187,6 +200,86 @@ def cb_plan_ratio(n_ctx: int, n_layers: int, kv_bytes_per_token_layer: float, ba
     out = cb_ratio_plan()
     _check(_L.cb_plan_ratio(n_ctx, n_layers, kv_bytes_per_token_layer, bandwidth, prefill_s_per_token,
                             latency_layer_s, r_min, r_max, C.byref(out)))
+    return out
+
+
+def _arr(a, dtype):
+    """(keep-alive array, address) of a contiguous host copy, or (None, 0) when empty."""
+    a = np.ascontiguousarray(np.asarray(a if a is not None else [], dtype=dtype))
+    return a, (a.ctypes.data if a.size else 0)
+
+
+def cb_sha256(data: bytes) -> bytes:
+    out = (C.c_uint8 * 32)()
+    buf = C.create_string_buffer(bytes(data), len(data)) if data else None
+    _check(_L.cb_sha256(C.addressof(buf) if buf is not None else None, len(data), C.addressof(out)))
+    return bytes(out)
+
+
+def cb_chunk_key(tokens, prior=None) -> int:
+    t, tp = _arr(tokens, np.int32)
+    p, pp = _arr(prior, np.uint64)
+    k = C.c_uint64()
+    _check(_L.cb_chunk_key(tp or None, t.size, pp or None, p.size, C.byref(k)))
+    return k.value
+
+
+class cb_store_stats(C.Structure):
+    _fields_ = [("hits", C.c_int64), ("misses", C.c_int64), ("evictions", C.c_int64), ("entries", _I),
+                ("capacity", _I), ("index_bytes", C.c_size_t), ("arena_bytes", C.c_size_t),
+                ("slot_bytes", C.c_size_t)]
+
+
+def cb_store_create(desc: cb_model_desc, max_chunk_tokens: int, n_slots: int, pinned: bool) -> int:
+    out = _P()
+    _check(_L.cb_store_create(C.byref(desc), max_chunk_tokens, n_slots, 1 if pinned else 0, C.byref(out)))
+    return out.value
+
+
+def cb_store_destroy(store: int) -> None:
+    _check(_L.cb_store_destroy(store))
+
+
+def cb_store_lookup(store: int, tokens, prior=None, pin: bool = False) -> int:
+    t, tp = _arr(tokens, np.int32)
+    p, pp = _arr(prior, np.uint64)
+    slot = _I()
+    _check(_L.cb_store_lookup(store, tp or None, t.size, pp or None, p.size, 1 if pin else 0, C.byref(slot)))
+    return slot.value
+
+
+def cb_store_insert(store: int, tokens, prior=None, pin: bool = False):
+    """Returns (slot, is_new, evicted_slot or -1)."""
+    t, tp = _arr(tokens, np.int32)
+    p, pp = _arr(prior, np.uint64)
+    slot, new, ev = _I(), _I(), _I()
+    _check(_L.cb_store_insert(store, tp or None, t.size, pp or None, p.size, 1 if pin else 0, C.byref(slot),
+                              C.byref(new), C.byref(ev)))
+    return slot.value, bool(new.value), ev.value
+
+
+def cb_store_commit(store: int, slot: int) -> None:
+    _check(_L.cb_store_commit(store, slot))
+
+
+def cb_store_release(store: int, slot: int) -> None:
+    _check(_L.cb_store_release(store, slot))
+
+
+def cb_store_layer(store: int, slot: int, layer: int):
+    """Returns (host K address, host V address, n_tokens)."""
+    k, v, n = _P(), _P(), _I()
+    _check(_L.cb_store_layer(store, slot, layer, C.byref(k), C.byref(v), C.byref(n)))
+    return k.value, v.value, n.value
+
+
+def cb_store_put_layer(ctx: int, store: int, slot: int, layer: int, dev_k: int, dev_v: int) -> None:
+    _check(_L.cb_store_put_layer(ctx, store, slot, layer, dev_k, dev_v))
+
+
+def cb_store_get_stats(store: int) -> cb_store_stats:
+    out = cb_store_stats()
+    _check(_L.cb_store_get_stats(store, C.byref(out)))
     return out
 
 

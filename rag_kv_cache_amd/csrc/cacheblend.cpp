@@ -12,19 +12,25 @@
 #include <string>
 #include <vector>
 
+#include "cb_host.h"
 #include "cb_kernels.h"
 
 namespace {
 
 thread_local std::string g_err;
 
-cb_status fail(cb_status st, const char* fmt, ...) {
+cb_status vfail(cb_status st, const char* fmt, va_list ap) {
   char buf[512];
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  g_err = buf;
+  return st;
+}
+
+cb_status fail(cb_status st, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
+  vfail(st, fmt, ap);
   va_end(ap);
-  g_err = buf;
   return st;
 }
 
@@ -187,6 +193,17 @@ cb_status check_offsets(const cb_ctx* c, const int32_t* offs, int n_chunks) {
 }
 
 }  // namespace
+
+cb_status cbi_fail(cb_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vfail(st, fmt, ap);
+  va_end(ap);
+  return st;
+}
+hipStream_t cbi_compute_stream(const cb_ctx* c) { return c->cs; }
+int cbi_device(const cb_ctx* c) { return c->device; }
+const cb_model_desc* cbi_desc(const cb_ctx* c) { return &c->d; }
 
 extern "C" {
 

@@ -13,7 +13,7 @@ HEADER = os.path.join(ROOT, "include", "cacheblend.h")
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(cb_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(cb_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_the_boundary():
