@@ -193,6 +193,57 @@ def run_decode(eng, buf, tokens, offs, wl, fused, cache):
             "context_rows": n, "note": "single-token steps on the fused KV, eager launches, given token ids"}
 
 
+def run_store(eng, buf, tokens, offs, wl, fused, steps):
+    """Chunk-cache producer into a pinned host store, prompt lookup, and the blended prefill
+    fetched from the store's arena (same fetch path as the separately pinned caches)."""
+    import torch
+    from rag_kv_cache_amd.pipeline import ChunkStore, produce_chunks, run_layers
+    import fixtures as F
+    sh = wl.shape
+    chunks = F.chunk_tokens(wl)
+    store = ChunkStore(eng, max(wl.chunk_lens), len(chunks) + 2, pinned=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    produce_chunks(eng, store, chunks)
+    t_prod = time.perf_counter() - t0
+    reps = 200
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        slots = store.lookup_prompt(chunks, hold=True)
+        for sl in slots:
+            store.release(sl)
+    t_look = (time.perf_counter() - t0) / (reps * len(chunks))
+    slots = store.lookup_prompt(chunks, hold=True)
+    hc = store.host_cache(slots)
+    cs = eng.compute
+
+    def step():
+        run_layers(eng, buf, tokens, offs, wl.n_query, wl.schedule, fused, host_cache=hc, upload_inputs=False)
+
+    for _ in range(2):
+        step()
+    cs.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    cs.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    st = store.stats()
+    for sl in slots:
+        store.release(sl)
+    store.close()
+    out = {"producer_context_tokens_per_s": round(wl.n_ctx / t_prod, 1),
+           "producer_s": round(t_prod, 4),
+           "lookup_us_per_chunk": round(t_look * 1e6, 2),
+           "chunk_tokens": max(wl.chunk_lens),
+           "prefill_from_store_ms": round(ms, 4),
+           "store_bytes_per_chunk": int(st.slot_bytes), "index_bytes": int(st.index_bytes),
+           "entries": int(st.entries)}
+    log(f"chunk store: producer {out['producer_context_tokens_per_s']:.0f} tok/s, lookup "
+        f"{out['lookup_us_per_chunk']:.1f} us/chunk, prefill from store {ms:.3f} ms/step")
+    return out
+
+
 def cpu_baseline(wl, budget_s: float = 25.0):
     """The oracle (fp64 NumPy with bf16 rounding points) on a bounded sample of the same
     workload: layer 1 (every row), layer 2 (all rows scored, 30% kept), layer 3 (15% kept)
@@ -359,7 +410,7 @@ def main() -> int:
     cs.synchronize()
     per_layer = [evs[i].elapsed_time(evs[i + 1]) for i in range(len(evs) - 1)]
 
-    pcie_ms = full_ms = controller = variants = decode_ms = None
+    pcie_ms = full_ms = controller = variants = decode_ms = store_res = None
     if not args.only_blend:
         # PCIe-inclusive variant: cached KV in pinned host memory, fetched one layer ahead
         for _ in range(2):
@@ -387,6 +438,7 @@ def main() -> int:
         controller = run_controller(eng, buf, tokens, offs, wl, fused, host, full_ms, args.steps)
         variants = run_variants(eng, buf, tokens, offs, wl, fused, cache, args.steps)
         decode_ms = run_decode(eng, buf, tokens, offs, wl, fused, cache)
+        store_res = run_store(eng, buf, tokens, offs, wl, fused, args.steps)
     if args.calib_copy:
         src = torch.empty(128 << 20, dtype=torch.bfloat16, device=eng.device)
         dst = torch.empty_like(src)
@@ -423,6 +475,7 @@ def main() -> int:
         "loading_controller": controller,
         "selection_variants": variants,
         "decode": decode_ms,
+        "chunk_store": store_res,
         "speedup_vs_full_recompute": None if full_ms is None else round(full_ms / ms_step, 3),
     }
     print(json.dumps(out), flush=True)

@@ -23,8 +23,11 @@ import torch
 from . import _lib as L
 
 
-def _ptr(t: Optional[torch.Tensor]) -> int:
-    return 0 if t is None else int(t.data_ptr())
+def _ptr(t) -> int:
+    """Address of a tensor, or an address given as an int (0 = NULL)."""
+    if t is None:
+        return 0
+    return int(t) if isinstance(t, int) else int(t.data_ptr())
 
 
 class Engine:
@@ -43,6 +46,7 @@ class Engine:
                                float(shape.rope_base), float(shape.rms_eps),
                                L.CB_BF16 if shape.dtype == "bf16" else L.CB_F32)
         self.max_tokens = max_tokens
+        self.desc = desc
         self.ctx = L.cb_create(desc, device, self.compute.cuda_stream,
                                self.copy.cuda_stream if self.copy is not None else 0)
         self.weights: List[Dict[str, torch.Tensor]] = [None] * shape.n_layers
@@ -294,6 +298,91 @@ def build_chunk_caches(eng: Engine, chunks: Sequence[np.ndarray], pinned_host: b
                     host_cache[l][c] = (hk, hv)
         eng.compute.synchronize()
     return dev_cache, host_cache
+
+
+class ChunkStore:
+    """The library's host chunk store (cb_store_*) for one engine's model: per chunk, every
+    layer's K and V of the chunk prefilled alone at positions 0.., found by its token ids."""
+
+    def __init__(self, eng: Engine, max_chunk_tokens: int, n_slots: int, pinned: bool = True):
+        self.n_layers = eng.shape.n_layers
+        self.handle = L.cb_store_create(eng.desc, max_chunk_tokens, n_slots, pinned)
+
+    def close(self):
+        if self.handle:
+            L.cb_store_destroy(self.handle)
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def lookup(self, tokens, hold: bool = False) -> int:
+        return L.cb_store_lookup(self.handle, tokens, None, hold)
+
+    def release(self, slot: int) -> None:
+        L.cb_store_release(self.handle, slot)
+
+    def stats(self):
+        return L.cb_store_get_stats(self.handle)
+
+    def host_cache(self, slots: Sequence[int]) -> List[List[tuple]]:
+        """host_cache[l][c] = (K address, V address) of layer l of the entry in slots[c], the
+        form run_layers fetches from."""
+        out = []
+        for l in range(self.n_layers):
+            out.append([L.cb_store_layer(self.handle, sl, l)[:2] for sl in slots])
+        return out
+
+    def lookup_prompt(self, chunks: Sequence[np.ndarray], hold: bool = True) -> Optional[List[int]]:
+        """Slots of every chunk (each held when hold), or None, holding nothing, if any chunk
+        is missing."""
+        slots = []
+        for c in chunks:
+            sl = self.lookup(c, hold)
+            if sl < 0:
+                if hold:
+                    for h in slots:
+                        self.release(h)
+                return None
+            slots.append(sl)
+        return slots
+
+
+def produce_chunks(eng: Engine, store: ChunkStore, chunks: Sequence[np.ndarray], hold: bool = False) -> List[int]:
+    """Chunk-cache producer: every chunk not yet in the store is prefilled alone at positions
+    0.. (full recompute of every row at every layer) and each layer's K and V is copied from the
+    device into its entry; entries become visible to lookups once the copies are done.
+    Returns the slot of every chunk (held when hold; otherwise released before returning)."""
+    s = eng.shape
+    lmax = max(len(c) for c in chunks)
+    buf = make_buffers(eng, lmax, 0)
+    tmp = [(eng.kv_empty(lmax), eng.kv_empty(lmax)) for _ in range(s.n_layers)]
+    slots, fresh, done = [], [], False
+    try:
+        for toks in chunks:
+            slot, new, _ = L.cb_store_insert(store.handle, toks, None, True)
+            slots.append(slot)
+            if not new:
+                continue
+            n = len(toks)
+            fused = [(k[:n], v[:n]) for k, v in tmp]
+            run_layers(eng, buf, toks, [0], n, [1.0] * s.n_layers, fused)
+            # same stream as the prefill: the next chunk's prefill reuses tmp only after these
+            for l in range(s.n_layers):
+                L.cb_store_put_layer(eng.ctx, store.handle, slot, l, _ptr(fused[l][0]), _ptr(fused[l][1]))
+            fresh.append(slot)
+        eng.compute.synchronize()
+        for slot in fresh:
+            L.cb_store_commit(store.handle, slot)
+        done = True
+    finally:
+        if not hold or not done:
+            for slot in slots:
+                L.cb_store_release(store.handle, slot)
+    return slots
 
 
 def capture_step(eng: Engine, step: Callable[[], object]) -> "torch.cuda.CUDAGraph":
