@@ -512,7 +512,7 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
   const int q_ld = fuse_q ? fresh_ld : qd;
   if (!fuse_q) {
     cb::GemmArgs g{};
-    g.A = x; g.lda = dm; g.a_rows = new_sel_local;
+    g.A = x; g.lda = dm; g.a_rows = new_sel_local; g.a_rows_total = n_sel;
     g.B = W.w_qkv; g.ldb = dm;
     g.M = nn; g.N = qd; g.K = dm;
     g.partial = (float*)(ws + wp.gpart);

@@ -93,3 +93,11 @@ __device__ __forceinline__ int xcd_tile(int bid, int T) {
   const int t = (bid & 7) * per + (bid >> 3);
   return t < T ? t : -1;
 }
+
+// 16-byte buffer load of this lane's bytes [voff + soff, +16) of the buffer at `base` (nbytes
+// long) straight into LDS: the wave's 64 lanes fill 1 KB at `lds` (wave-uniform), lane l at
+// byte 16 l.  The descriptor, soff and lds are scalar, so a load costs no vector ALU work.
+__device__ __forceinline__ void buffer_load_lds16(const void* base, int nbytes, void* lds, uint32_t voff, int soff) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff, soff, 0, 0);
+}

@@ -10,6 +10,7 @@ enum Epi { EPI_STORE = 0, EPI_ROPE = 1, EPI_SWIGLU = 2, EPI_RESID = 3 };
 // C[M][N] = A[M][K] * B[N][K]^T with fp32 accumulation and a fused epilogue.
 struct GemmArgs {
   const void* A; long lda; const int32_t* a_rows;  // A row of GEMM row m = a_rows ? a_rows[m] : m
+  int a_rows_total;      // rows of A the a_rows entries may address (0: M)
   const void* B; long ldb;
   int swiglu_ffn;        // >0: tile t's columns 0..63 are B rows t*64.., columns 64..127 rows ffn + t*64..
   int M, N, K, splits;   // N % 128 == 0, K % (64 * splits) == 0
@@ -22,7 +23,7 @@ struct GemmArgs {
   int cfg;               // bf16 tile configuration (GemmCfg), from gemm_plan
 };
 hipError_t gemm_bf16(const GemmArgs& g, hipStream_t s);
-enum GemmCfg { GEMM_128x512 = 0, GEMM_128x256 = 1, GEMM_64x256 = 2, GEMM_128x128 = 3, GEMM_64x128 = 4 };
+enum GemmCfg { GEMM_128x512 = 0, GEMM_128x256 = 1, GEMM_64x256 = 2, GEMM_128x128 = 3, GEMM_64x128 = 4, GEMM_256x256 = 5 };
 struct GemmPlan { int cfg, splits; };
 // Tile configuration and split-K factor of the bf16 GEMM for an M x N x K product with
 // epilogue `epi`; split partials ([splits][M][N] fp32) must fit partial_cap_elems.

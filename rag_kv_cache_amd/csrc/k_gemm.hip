@@ -12,7 +12,7 @@
 // bf16 path (v_mfma_f32_16x16x32_bf16, gfx950):
 //   * workgroup tile BM x BN x 64 with WM x WN wavefronts, each owning a (BM/WM) x (BN/WN)
 //     block of 16x16 MFMA tiles;
-//   * operands go global -> LDS directly (global_load_lds_dwordx4, no staging registers) into
+//   * operands go global -> LDS directly (buffer_load_dwordx4 ... lds, no staging registers) into
 //     a 3-stage ring, two K-steps ahead of the MFMAs; one barrier per K-step;
 //   * inside each tile the weight rows are permuted in 16-row blocks so that the two
 //     columns of every epilogue pair land in adjacent MFMA tiles: the same lane then holds
@@ -96,12 +96,10 @@ __device__ __forceinline__ int stage_col(int tc) {
   return tc;
 }
 
-// Each global_load_lds_dwordx4 wave instruction writes its 64 lanes x 16 bytes contiguously
+// Each buffer_load_dwordx4 ... lds wave instruction writes its 64 lanes x 16 bytes contiguously
 // (lane l at byte 16 l), i.e. 8 tile rows of 128 bytes; the 16-byte chunks of row r are stored
 // XOR-swizzled (chunk c at slot c ^ (r & 7)) so that fragment reads of 8 consecutive rows hit
 // disjoint banks.
-typedef __attribute__((address_space(1))) void gvoid_t;
-typedef __attribute__((address_space(3))) void lvoid_t;
 
 // s_waitcnt with only vmcnt (N) or only lgkmcnt (0) constrained.
 template <int N>
@@ -127,8 +125,10 @@ __device__ __forceinline__ void wait_vm_steps(int ahead) {
   }
 }
 
+// amdgpu_waves_per_eu(2): a register budget of 256 arch VGPRs; with more, the 4-wave tiles
+// get their accumulators in AGPRs and copy them around in the main loop.
 template <int BM, int BN, int WM, int WN, int NS, int EPI>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2))) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 16, FN = WTN / 16;
@@ -154,34 +154,35 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  const char* A = reinterpret_cast<const char*>(g.A);
-  const char* B = reinterpret_cast<const char*>(g.B);
-  // this lane's source row / chunk inside each 8-row instruction block
+  const int wv = __builtin_amdgcn_readfirstlane(wave);  // the same value, in a scalar register
+  // this lane's source row / chunk inside each 8-row instruction block; byte offsets from the
+  // operand bases (below 2 GiB: checked at launch), advanced per K-step by a scalar offset
   const int r8 = lane >> 3, slot = lane & 7;
   const int chunk = slot ^ r8;  // (tile row & 7) == r8 because blocks are 8-row aligned
-  const char* a_src[A_PW];
-  const char* b_src[B_PW];
+  const int a_bytes = (int)((long)(g.a_rows_total ? g.a_rows_total : g.M) * g.lda * 2);
+  const int b_bytes = (int)((long)g.N * g.ldb * 2);
+  uint32_t a_vo[A_PW], b_vo[B_PW];
 #pragma unroll
   for (int i = 0; i < A_PW; ++i) {
     const int row = (wave * A_PW + i) * 8 + r8;
     int m = m0 + row;
     m = m < g.M ? m : g.M - 1;
     const long grow = g.a_rows ? (long)g.a_rows[m] : (long)m;
-    a_src[i] = A + (grow * g.lda + (long)kb0 * BK + chunk * 8) * 2;
+    a_vo[i] = (uint32_t)((grow * g.lda + (long)kb0 * BK + chunk * 8) * 2);
   }
 #pragma unroll
   for (int i = 0; i < B_PW; ++i) {
     const int row = (wave * B_PW + i) * 8 + r8;
-    b_src[i] = B + ((long)logical_col<EPI, BN>(g, tn, row) * g.ldb + (long)kb0 * BK + chunk * 8) * 2;
+    b_vo[i] = (uint32_t)(((long)logical_col<EPI, BN>(g, tn, row) * g.ldb + (long)kb0 * BK + chunk * 8) * 2);
   }
   auto issue = [&](int kt, int st) __attribute__((always_inline)) {
     unsigned char* base = smem + st * STAGE_B;
+    const int koff = kt * BK * 2;
 #pragma unroll
-    for (int i = 0; i < A_PW; ++i)
-      __builtin_amdgcn_global_load_lds((gvoid_t*)(a_src[i] + kt * BK * 2), (lvoid_t*)(base + (wave * A_PW + i) * 1024), 16, 0, 0);
+    for (int i = 0; i < A_PW; ++i) buffer_load_lds16(g.A, a_bytes, base + (wv * A_PW + i) * 1024, a_vo[i], koff);
 #pragma unroll
     for (int i = 0; i < B_PW; ++i)
-      __builtin_amdgcn_global_load_lds((gvoid_t*)(b_src[i] + kt * BK * 2), (lvoid_t*)(base + BM * ROWB + (wave * B_PW + i) * 1024), 16, 0, 0);
+      buffer_load_lds16(g.B, b_bytes, base + BM * ROWB + (wv * B_PW + i) * 1024, b_vo[i], koff);
   };
 
   f32x4_t acc[FM][FN];
@@ -217,7 +218,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
   // Pipeline: K-steps t .. t+NS-1 occupy the NS stages; fragments of the two 32-wide halves of
   // a K-step are double-buffered in registers, so the LDS reads of one half overlap the MFMAs
   // of the other.  At the one barrier per K-step every wave has (a) waited for its own loads of
-  // K-step t+1 and (b) finished reading stage t, which is then refilled with K-step t+NS.
+  // K-step t+1 and (b) finished reading stage t, which is then refilled with K-step t+NS.  The
+  // steady loop has a constant wait and no branch; the last NS-1 K-steps drain separately.
 #pragma unroll
   for (int s = 0; s < NS; ++s)
     if (s < nk) issue(s, s);
@@ -225,20 +227,31 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
   barrier();
   bf16x8_t a0[FM], b0[FN], a1[FM], b1[FN];
   read(0, 0, a0, b0);
-  int st = 0;
-  for (int t = 0; t < nk; ++t) {
+  int st = 0, t = 0;
+  for (; t + NS < nk; ++t) {
     read(st, 1, a1, b1);
     mma(a0, b0);
-    if (t + 1 < nk) {
-      wait_lgkm0();  // this wave is done reading stage st
-      wait_vm_steps<LPW>(min(NS - 2, nk - 2 - t));  // K-step t+1 landed
-      barrier();
-      if (t + NS < nk) issue(t + NS, st);
-      st = st + 1 == NS ? 0 : st + 1;
-      read(st, 0, a0, b0);
-    }
+    wait_lgkm0();                        // this wave is done reading stage st
+    wait_vm<Sat63<(NS - 2) * LPW>::v>();  // K-step t+1 landed (t+2 .. t+NS-1 may be in flight)
+    barrier();
+    issue(t + NS, st);
+    st = st + 1 == NS ? 0 : st + 1;
+    read(st, 0, a0, b0);
     mma(a1, b1);
   }
+  for (; t + 1 < nk; ++t) {
+    read(st, 1, a1, b1);
+    mma(a0, b0);
+    wait_lgkm0();
+    wait_vm_steps<LPW>(nk - 2 - t);  // K-step t+1 landed
+    barrier();
+    st = st + 1 == NS ? 0 : st + 1;
+    read(st, 0, a0, b0);
+    mma(a1, b1);
+  }
+  read(st, 1, a1, b1);
+  mma(a0, b0);
+  mma(a1, b1);
 
   // Epilogue.  The pair math (RoPE rotation, SwiGLU) runs on the fp32 accumulators in
   // registers; the results are staged in LDS (the operand stages are free by now) in output
@@ -362,6 +375,9 @@ hipError_t launch_dma(const GemmArgs& g, hipStream_t s) {
   static_assert(NS * (BM + BN) * BK * 2 <= kMaxLds, "LDS");
   const int lds = gemm_lds_bytes<BM, BN, NS, EPI>(g.splits > 1 || EPI == EPI_RESID);
   if (lds > kMaxLds || g.N % BN != 0 || g.splits < 1 || g.splits > g.K / BK) return hipErrorInvalidValue;
+  // operand byte offsets are 32-bit buffer offsets
+  const long a_rows = g.a_rows_total ? g.a_rows_total : g.M;
+  if (a_rows * g.lda * 2 >= (1L << 31) || (long)g.N * g.ldb * 2 >= (1L << 31)) return hipErrorInvalidValue;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<BM, BN, WM, WN, NS, EPI>,
@@ -552,6 +568,11 @@ hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
     case GEMM_128x512:  // planned for the SwiGLU epilogue only
       if constexpr (EPI == EPI_SWIGLU) { e = launch_dma<128, 512, 2, 4, 2, EPI>(g, s); break; }
       return hipErrorInvalidValue;
+    case GEMM_256x256:  // bf16 output, no split (the fp32 staged tile would not fit in LDS)
+      if constexpr (EPI != EPI_RESID) {
+        if (g.splits == 1) { e = launch_dma<256, 256, 2, 4, 2, EPI>(g, s); break; }
+      }
+      return hipErrorInvalidValue;
     case GEMM_128x256: e = launch_dma<128, 256, 2, 4, 3, EPI>(g, s); break;
     case GEMM_64x256: e = launch_dma<64, 256, 1, 4, 3, EPI>(g, s); break;
     case GEMM_128x128: e = launch_dma<128, 128, 2, 2, 3, EPI>(g, s); break;
@@ -572,22 +593,29 @@ hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
 
 // Tile configuration and split-K factor for an M x N x K product (measured on MI355X at the
 // fusion step's shapes):
+//   * large M (>= 2048 rows, e.g. the first layer's full prompt) with a bf16 output and
+//     N % 256 == 0: 256 x 256 tiles of 8 wavefronts, no split (the fewest operand bytes per
+//     flop: 7-18% faster than the next best there);
 //   * SwiGLU (gate/up, widest output): 128 x 512 tiles of 8 wavefronts, no split;
 //   * problems with >= 200 tiles of 128 x 256: those tiles (8 wavefronts), no split;
 //   * short reductions (K <= 2048: the Q/K/V and o-projections of the kept rows): 64 x 128
 //     tiles of 4 wavefronts with a 4-stage ring, split only while fewer than ~150 tiles;
-//   * long reductions (the FFN down-projection): 128 x 256 tiles, K split so that about 168
+//   * long reductions (the FFN down-projection): 128 x 256 tiles, K split so that about 210
 //     workgroups run;
 //   each split keeps at least two 64-wide K-steps and its partials fit the buffer.
 GemmPlan gemm_plan(int M, int N, int K, int epi, long partial_cap_elems) {
   GemmPlan p{GEMM_128x128, 1};
+  if (M >= 2048 && epi != EPI_RESID && N % 256 == 0) {
+    p.cfg = GEMM_256x256;
+    return p;
+  }
   if (epi == EPI_SWIGLU) {
     const int ffn = N / 2;
     if (ffn % 256 == 0) p.cfg = GEMM_128x512;
     else if (ffn % 128 == 0) p.cfg = M <= 64 ? GEMM_64x256 : GEMM_128x256;
     return p;
   }
-  int bm = 128, bn = 128, target = 168;
+  int bm = 128, bn = 128, target = 210;
   if (N % 256 == 0 && ((M + 127) / 128) * (N / 256) >= 200) {
     p.cfg = GEMM_128x256;
     return p;
