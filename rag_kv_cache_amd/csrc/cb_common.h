@@ -60,12 +60,14 @@ template <> struct Vec16<bf16_t> {
   }
 };
 
-// Two floats to packed bfloat16 (round to nearest even) with gfx950's v_cvt_pk_bf16_f32:
-// low half = lo, high half = hi.
+// Two floats to packed bfloat16 (round to nearest even): low half = lo, high half = hi.  The
+// casts lower to gfx950's v_cvt_pk_bf16_f32; written as casts (not inline asm) so that the
+// compiler sees the instruction and inserts the wait states it needs after a transcendental
+// (v_exp_f32) producing its inputs.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  uint32_t r;
-  asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
-  return r;
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // gfx950 LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i
