@@ -284,9 +284,11 @@ __global__ __launch_bounds__(64 * G * QT) void attn_bf16_kernel(AttnArgs a) {
 
 // Merge split-KV partials: out = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).  Only splits
 // whose first key is <= the row's position hold keys of that row.  One thread per
-// (row, head, 4 dims).
+// (row, head, 4 dims); the (m, l) and O partials of up to 8 splits are loaded at once, and
+// summed in split order.
 template <typename TO>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  constexpr int NSB = 8;  // splits per batch of loads
   const int d4n = a.dh / 4;
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   const long total = (long)a.n_q * a.hq * d4n;
@@ -296,16 +298,33 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int h = rem / d4n, d0 = (rem - h * d4n) * 4;
   const int ns = min(a.qpos[row] / a.split_len + 1, a.splits);
   float M = NEG_INF;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_ml[(((long)s * a.n_q + row) * a.hq + h) * 2]);
+  for (int s0 = 0; s0 < ns; s0 += NSB) {
+    float mv[NSB];
+#pragma unroll
+    for (int j = 0; j < NSB; ++j)
+      mv[j] = s0 + j < ns ? a.part_ml[(((long)(s0 + j) * a.n_q + row) * a.hq + h) * 2] : NEG_INF;
+#pragma unroll
+    for (int j = 0; j < NSB; ++j) M = fmaxf(M, mv[j]);
+  }
   float L = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < ns; ++s) {
-    const long pi = ((long)s * a.n_q + row) * a.hq + h;
-    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + pi * 2);
-    if (ml.x == NEG_INF) continue;
-    const float w = exp2f(ml.x - M);
-    L += ml.y * w;
-    const float4 v = *reinterpret_cast<const float4*>(a.part_o + pi * a.dh + d0);
-    acc[0] += v.x * w; acc[1] += v.y * w; acc[2] += v.z * w; acc[3] += v.w * w;
+  for (int s0 = 0; s0 < ns; s0 += NSB) {
+    float2 ml[NSB];
+    float4 v[NSB];
+#pragma unroll
+    for (int j = 0; j < NSB; ++j) {
+      if (s0 + j < ns) {
+        const long pi = ((long)(s0 + j) * a.n_q + row) * a.hq + h;
+        ml[j] = *reinterpret_cast<const float2*>(a.part_ml + pi * 2);
+        v[j] = *reinterpret_cast<const float4*>(a.part_o + pi * a.dh + d0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NSB; ++j) {
+      if (s0 + j >= ns || ml[j].x == NEG_INF) continue;
+      const float w = exp2f(ml[j].x - M);
+      L += ml[j].y * w;
+      acc[0] += v[j].x * w; acc[1] += v[j].y * w; acc[2] += v[j].z * w; acc[3] += v[j].w * w;
+    }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   TO* out = reinterpret_cast<TO*>(a.out) + (long)row * a.ldo + h * a.dh + d0;

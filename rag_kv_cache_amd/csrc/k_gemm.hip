@@ -426,56 +426,76 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
   epi_pair<EPI, bf16_t>(g, m, n_a + 3, n_b + 3, va.w, vb.w);
 }
 
-// Residual epilogue of a split-K GEMM, one wavefront per output row:
+// Residual epilogue of a split-K GEMM, one workgroup per output row and one wavefront per
+// 256-column block (blocks k = wave, wave + waves, ...):
 //   out[m] = resid[resid_rows[m]] + sum_s partial[s][m]   (fp32, split order fixed)
-// and, when norm_out is set, the RMSNorm of that row (the next GEMM's bf16 A operand), with
-// the same arithmetic as the stand-alone RMSNorm kernel.  Lane l owns columns 4l + 256k;
-// two k at a time, so that 2 (splits + 1) loads per lane are in flight.
-__global__ __launch_bounds__(256) void splitk_resid_norm_kernel(GemmArgs g) {
-  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (m >= g.M) return;
+// with every split's partial of a block loaded at once, and, when norm_out is set, the RMSNorm
+// of that row (the next GEMM's bf16 A operand) with the same arithmetic as the stand-alone
+// RMSNorm kernel: lane l's sum of squares adds blocks k = 0, 1, ... in increasing k (gathered
+// through LDS), then the same butterfly.
+constexpr int kResidMaxBlocks = 64;   // N <= 16384
+constexpr int kResidWavesMax = 8;
+__global__ __launch_bounds__(64 * kResidWavesMax) void splitk_resid_norm_kernel(GemmArgs g) {
+  __shared__ float sq[kResidMaxBlocks][64];
+  constexpr int KW = kResidMaxBlocks / kResidWavesMax;  // blocks per wave kept in registers
+  const int m = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int nb = (g.N + 255) / 256;
   const long stride = (long)g.M * g.N;
   const float* p = g.partial + (long)m * g.N;
   const long rr = g.resid_rows ? (long)g.resid_rows[m] : (long)m;
   const float* r = g.resid + rr * g.ldr;
   float* o = (float*)g.out + (long)m * g.ldo;
-  float ss = 0.f;
-  for (int e0 = lane * 4; e0 < g.N; e0 += 512) {
-    const bool two = e0 + 256 < g.N;
-    float4 v[2], rv[2];
+  float4 w[KW];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int e = u ? (two ? e0 + 256 : e0) : e0;
-      v[u] = *reinterpret_cast<const float4*>(p + e);
-      rv[u] = *reinterpret_cast<const float4*>(r + e);
+  for (int j = 0; j < KW; ++j) {
+    const int k = wave + j * nw;
+    if (k >= nb) break;
+    const int e = k * 256 + lane * 4;
+    float q = 0.f;
+    if (e < g.N) {
+      float4 a[8];
+#pragma unroll
+      for (int sp = 0; sp < 8; ++sp)
+        if (sp < g.splits) a[sp] = *reinterpret_cast<const float4*>(p + sp * stride + e);
+      const float4 rv = *reinterpret_cast<const float4*>(r + e);
+      float4 v = a[0];
+#pragma unroll
+      for (int sp = 1; sp < 8; ++sp)
+        if (sp < g.splits) { v.x += a[sp].x; v.y += a[sp].y; v.z += a[sp].z; v.w += a[sp].w; }
+      w[j] = make_float4(rv.x + v.x, rv.y + v.y, rv.z + v.z, rv.w + v.w);
+      *reinterpret_cast<float4*>(o + e) = w[j];
+      q = w[j].x * w[j].x + w[j].y * w[j].y + w[j].z * w[j].z + w[j].w * w[j].w;
     }
-    for (int s = 1; s < g.splits; ++s) {
-      float4 a[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) a[u] = *reinterpret_cast<const float4*>(p + s * stride + (u && two ? e0 + 256 : e0));
-#pragma unroll
-      for (int u = 0; u < 2; ++u) { v[u].x += a[u].x; v[u].y += a[u].y; v[u].z += a[u].z; v[u].w += a[u].w; }
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (u && !two) break;
-      const float4 w = make_float4(rv[u].x + v[u].x, rv[u].y + v[u].y, rv[u].z + v[u].z, rv[u].w + v[u].w);
-      *reinterpret_cast<float4*>(o + e0 + 256 * u) = w;
-      ss += w.x * w.x + w.y * w.y + w.z * w.z + w.w * w.w;
-    }
+    sq[k][lane] = q;
   }
   if (!g.norm_out) return;
+  __syncthreads();
+  float ss = 0.f;
+  for (int k = 0; k < nb; ++k) {
+    if (k * 256 + lane * 4 < g.N) ss += sq[k][lane];
+  }
   ss = wave_sum(ss);
   const float rs = 1.0f / sqrtf(ss / (float)g.N + g.norm_eps);
   bf16_t* x = (bf16_t*)g.norm_out + (long)m * g.N;
-  for (int e = lane * 4; e < g.N; e += 256) {
-    const float4 v = *reinterpret_cast<const float4*>(o + e);
-    const float4 gg = *reinterpret_cast<const float4*>(g.norm_g + e);
-    *reinterpret_cast<uint2*>(x + e) =
-        make_uint2((uint32_t)f32_to_bf16(v.x * rs * gg.x) | ((uint32_t)f32_to_bf16(v.y * rs * gg.y) << 16),
-                   (uint32_t)f32_to_bf16(v.z * rs * gg.z) | ((uint32_t)f32_to_bf16(v.w * rs * gg.w) << 16));
+#pragma unroll
+  for (int j = 0; j < KW; ++j) {
+    const int k = wave + j * nw;
+    if (k >= nb) break;
+    const int e = k * 256 + lane * 4;
+    if (e < g.N) {
+      const float4 gg = *reinterpret_cast<const float4*>(g.norm_g + e);
+      *reinterpret_cast<uint2*>(x + e) =
+          make_uint2((uint32_t)f32_to_bf16(w[j].x * rs * gg.x) | ((uint32_t)f32_to_bf16(w[j].y * rs * gg.y) << 16),
+                     (uint32_t)f32_to_bf16(w[j].z * rs * gg.z) | ((uint32_t)f32_to_bf16(w[j].w * rs * gg.w) << 16));
+    }
   }
+}
+
+// Workgroup size of splitk_resid_norm_kernel for N columns.
+inline int resid_norm_threads(int N) {
+  const int nb = (N + 255) / 256;
+  return 64 * (nb < kResidWavesMax ? nb : kResidWavesMax);
 }
 
 // ------------------------------------------------------------------ fp32 path
@@ -581,7 +601,8 @@ hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
   }
   if (e != hipSuccess || g.splits <= 1) return e;
   if (EPI == EPI_RESID) {
-    hipLaunchKernelGGL(splitk_resid_norm_kernel, dim3((g.M + 3) / 4), dim3(256), 0, s, g);
+    if (g.N > 256 * kResidMaxBlocks || g.splits > 8) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(splitk_resid_norm_kernel, dim3(g.M), dim3(resid_norm_threads(g.N)), 0, s, g);
   } else {
     const long items = (long)g.M * (g.N / 8);
     hipLaunchKernelGGL(splitk_reduce_kernel<EPI>, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, g);

@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* tok, int n, c
 // ---------------------------------------------------------------- RMSNorm
 // out[r] = h[r] / sqrt(mean(h[r]^2) + eps) * g, one wavefront per row, fp32 math.  Lane l
 // owns elements 4l + 256k; the sum of squares adds them in increasing k (then a fixed
-// butterfly), with up to four 16-byte loads per lane in flight.
+// butterfly).
 template <typename TO>
 __device__ __forceinline__ void store4(TO* o, float a, float b, float c, float d);
 template <>
@@ -48,18 +48,19 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t* o, float a, float b, floa
 
 __device__ __forceinline__ float sq4(float4 v) { return v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w; }
 
-// Sum of squares of one row (d % 256 == 0 not required: d % 4 == 0).
+// Sum of squares of one row (d % 4 == 0): lane l adds its 16-byte blocks k = 0, 1, ... (elements
+// 4l + 256k) in increasing k, then the wave's butterfly; up to eight loads per lane in flight.
 __device__ __forceinline__ float row_sumsq(const float* x, int d, int lane) {
   float ss = 0.f;
-  int e = lane * 4;
-  for (; e + 768 < d; e += 1024) {
-    float4 v[4];
+  for (int e0 = lane * 4; e0 < d; e0 += 2048) {
+    float4 v[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(x + e + 256 * u);
+    for (int u = 0; u < 8; ++u)
+      if (e0 + 256 * u < d) v[u] = *reinterpret_cast<const float4*>(x + e0 + 256 * u);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) ss += sq4(v[u]);
+    for (int u = 0; u < 8; ++u)
+      if (e0 + 256 * u < d) ss += sq4(v[u]);
   }
-  for (; e < d; e += 256) ss += sq4(*reinterpret_cast<const float4*>(x + e));
   return wave_sum(ss);
 }
 
@@ -79,9 +80,32 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, long ldh, 
   const int lane = threadIdx.x & 63;
   if (row >= n) return;
   const float* x = h + (long)row * ldh;
+  TO* o = out + (long)row * d;
+  if (d <= 2048) {  // the row stays in registers: one read, every load in flight at once
+    float4 v[8];
+    const int e0 = lane * 4;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (e0 + 256 * u < d) v[u] = *reinterpret_cast<const float4*>(x + e0 + 256 * u);
+    float ss = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (e0 + 256 * u < d) ss += sq4(v[u]);
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + 256 * u;
+      if (e < d) {
+        const float4 gg = *reinterpret_cast<const float4*>(g + e);
+        store4<TO>(o + e, v[u].x * r * gg.x, v[u].y * r * gg.y, v[u].z * r * gg.z, v[u].w * r * gg.w);
+      }
+    }
+    return;
+  }
   const float ss = row_sumsq(x, d, lane);
   const float r = 1.0f / sqrtf(ss / (float)d + eps);
-  row_scale_store<TO>(x, d, g, r, out + (long)row * d, lane);
+  row_scale_store<TO>(x, d, g, r, o, lane);
 }
 
 // ---------------------------------------------------------------- RoPE position update
