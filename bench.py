@@ -51,7 +51,8 @@ def gate_up_traffic(shape, kept_rows):
     rocprofv3 counter summary (FETCH_SIZE / WRITE_SIZE, scaled by a plain copy's reading),
     or None if that summary is missing or was taken on another version of the kernel source.
     A launch on M rows runs ceil(M/128) x (2 ffn / 512) tiles of 512 threads, rounded up to a
-    multiple of 8 workgroups: that grid size identifies its counter line."""
+    multiple of 8 workgroups: that grid size identifies its counter line.  (At M >= 2048 rows
+    the launch uses 256 x 256 tiles of 512 threads instead: ceil(M/256) x (2 ffn / 256).)"""
     import hashlib
     import re
     path = os.path.join(ROOT, "profiles", "gemm_gate_up_qwen_traffic.txt")
@@ -67,7 +68,10 @@ def gate_up_traffic(shape, kept_rows):
     per_grid = {int(g): float(mb) for g, mb in re.findall(r"^\s*(\d+)\s+\d+\s+[\d.]+\s+[\d.]+\s+([\d.]+)\s+gemm", text, re.M)}
     total = 0.0
     for rows in kept_rows:
-        tiles = -(-rows // 128) * (2 * shape.ffn_dim // 512)
+        if rows >= 2048:
+            tiles = -(-rows // 256) * (2 * shape.ffn_dim // 256)
+        else:
+            tiles = -(-rows // 128) * (2 * shape.ffn_dim // 512)
         grid = 8 * (-(-tiles // 8)) * 512
         if grid not in per_grid:
             return None

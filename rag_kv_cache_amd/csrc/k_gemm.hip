@@ -19,8 +19,8 @@
 //     both values and the epilogue runs from registers;
 //   * rows of A may be gathered through an index list (the kept rows); rows past M read a
 //     clamped row (never stored), so the loads are branch-free;
-//   * tiles are assigned XCD-contiguously (xcd_tile) so that the workgroups reading the same
-//     weight rows share one XCD's L2;
+//   * tiles are assigned XCD-contiguously (xcd_tile) and in bands of 8 M-tiles, so that the
+//     workgroups running together on one XCD share their A rows and weight rows in its L2;
 //   * split-K (grid.y > 1) writes fp32 partials in logical column order; a reduce kernel
 //     sums them and applies the same epilogue.
 //
@@ -145,7 +145,14 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
   const int tiles_n = g.N / BN;
   const int tile = xcd_tile(blockIdx.x, tiles_m * tiles_n);
   if (tile < 0) return;
-  const int tm = tile % tiles_m, tn = tile / tiles_m;
+  // grouped order: bands of up to 8 M-tiles, M fastest inside a band, so that the workgroups
+  // running together on one XCD share both their A row blocks and their weight blocks in L2
+  constexpr int GM = 8;
+  const int band = tile / (GM * tiles_n);
+  const int bm0 = band * GM;
+  const int bh = min(GM, tiles_m - bm0);
+  const int in_band = tile - band * GM * tiles_n;
+  const int tm = bm0 + in_band % bh, tn = in_band / bh;
   const int m0 = tm * BM;
   // K-steps of this split: an even share of the K / 64 steps (shares differ by at most one)
   const int nk_all = g.K / BK;
