@@ -134,6 +134,21 @@ cb_status cb_fetch_layer_device(cb_ctx* ctx, int32_t layer, const void* cache_k,
                                 const int32_t* chunk_offsets_host, int32_t n_chunks,
                                 const int32_t* chunk_offsets_dev, void* fused_k, void* fused_v);
 
+/* The position update of several layers at once, for caches already in device memory
+ * (explainer, "Position encoding update"): on the compute stream, one launch (per 64 layers)
+ * writes, for every layer l in [first_layer, first_layer + n_layers) and every context row j
+ * of chunk c, fused_k[i][j] <- R(o_c) cache_k[i][j] and fused_v[i][j] <- cache_v[i][j]
+ * (i = l - first_layer; in place when a layer's cache aliases its fused buffers, which must
+ * then hold for K and V and for every layer).  Arrays of n_layers device pointers, in host
+ * memory; layouts as for cb_fetch_layer_device.  The fused rows then hold the re-rotated cache:
+ * pass kv_cached_k = kv_cached_v = NULL to cb_blend_layer.  With the whole cache resident in
+ * HBM there is no load to hide behind the layers, and one launch replaces one per layer.
+ * CB_EINVAL for a layer range outside the model or NULL pointers, CB_ESTATE if a layer has a
+ * pending fetch. */
+cb_status cb_rotate_layers(cb_ctx* ctx, int32_t first_layer, int32_t n_layers, const void* const* cache_k,
+                           const void* const* cache_v, const int32_t* chunk_offsets_host, int32_t n_chunks,
+                           const int32_t* chunk_offsets_dev, void* const* fused_k, void* const* fused_v);
+
 /* synchronize(): make the compute stream wait for layer `layer`'s fetch event.  Does not
  * block the host.  A no-op for a layer that was never fetched.  (The fetch calls order the
  * copy stream after earlier steps through events recorded outside any capture, so a HIP-graph

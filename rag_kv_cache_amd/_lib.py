@@ -61,6 +61,7 @@ _SIGS = {
     "cb_embed": [_P, _P, _I, _P, _P],
     "cb_fetch_layer": [_P, _I, C.POINTER(_P), C.POINTER(_P), C.POINTER(_I), _I, _P, _P, _P],
     "cb_fetch_layer_device": [_P, _I, _P, _P, C.POINTER(_I), _I, _P, _P, _P],
+    "cb_rotate_layers": [_P, _I, _I, C.POINTER(_P), C.POINTER(_P), C.POINTER(_I), _I, _P, C.POINTER(_P), C.POINTER(_P)],
     "cb_synchronize": [_P, _I],
     "cb_blend_layer": [_P, _I, _P, _P, _P, _P, _P, _P, _P, C.POINTER(_I), _I, _P, _I, _I, C.c_float, _P, _P,
                        C.POINTER(_I), _P, _P, _P, C.c_size_t],
@@ -141,6 +142,16 @@ def cb_fetch_layer_device(ctx: int, layer: int, cache_k: int, cache_v: int, chun
                           n_chunks: int, chunk_offsets_dev: int, fused_k: int, fused_v: int) -> None:
     _check(_L.cb_fetch_layer_device(ctx, layer, cache_k or None, cache_v or None, _i32(chunk_offsets_host),
                                     n_chunks, chunk_offsets_dev or None, fused_k, fused_v))
+
+
+def cb_rotate_layers(ctx: int, first_layer: int, cache_k: Sequence[int], cache_v: Sequence[int],
+                     chunk_offsets: Sequence[int], n_chunks: int, chunk_offsets_dev: int, fused_k: Sequence[int],
+                     fused_v: Sequence[int]) -> None:
+    n = len(cache_k)
+    assert len(cache_v) == len(fused_k) == len(fused_v) == n
+    arr = lambda v: (_P * max(n, 1))(*[int(x) or None for x in v])
+    _check(_L.cb_rotate_layers(ctx, first_layer, n, arr(cache_k), arr(cache_v), _i32(chunk_offsets), n_chunks,
+                               chunk_offsets_dev or None, arr(fused_k), arr(fused_v)))
 
 
 def cb_synchronize(ctx: int, layer: int) -> None:

@@ -392,6 +392,42 @@ cb_status cb_fetch_layer_device(cb_ctx* c, int32_t layer, const void* cache_k, c
   return finish_fetch(c, layer, cache_k, cache_v, fused_k, fused_v, offs_dev, n_chunks, n_ctx);
 }
 
+cb_status cb_rotate_layers(cb_ctx* c, int32_t first_layer, int32_t n_layers, const void* const* cache_k,
+                           const void* const* cache_v, const int32_t* offs, int32_t n_chunks, const int32_t* offs_dev,
+                           void* const* fused_k, void* const* fused_v) {
+  cb_status st = check_ctx(c);
+  if (st) return st;
+  if (n_layers < 0 || first_layer < 0 || first_layer + n_layers > c->d.n_layers)
+    return fail(CB_EINVAL, "layers [%d, %d) outside [0, %d)", first_layer, first_layer + n_layers, c->d.n_layers);
+  if ((st = check_offsets(c, offs, n_chunks))) return st;
+  const int n_ctx = n_chunks > 0 ? offs[n_chunks] : 0;
+  if (n_layers == 0 || n_ctx == 0) return CB_OK;
+  if (!cache_k || !cache_v || !fused_k || !fused_v || !offs_dev) return fail(CB_EINVAL, "NULL pointer");
+  const bool v_alias = cache_v[0] == fused_v[0];
+  for (int i = 0; i < n_layers; ++i) {
+    const int l = first_layer + i;
+    if (c->state[l] == LS_FETCHED) return fail(CB_ESTATE, "layer %d has a pending fetch", l);
+    if (!cache_k[i] || !cache_v[i] || !fused_k[i] || !fused_v[i]) return fail(CB_EINVAL, "NULL pointer (layer %d)", l);
+    if ((cache_k[i] == fused_k[i]) != (cache_v[i] == fused_v[i]) || (cache_v[i] == fused_v[i]) != v_alias)
+      return fail(CB_EINVAL, "cache must alias fused for both K and V or for neither, the same in every layer");
+  }
+  for (int b = 0; b < n_layers; b += cb::kRopeMaxLayers) {
+    const int nb = std::min(cb::kRopeMaxLayers, n_layers - b);
+    cb::RopeLayers L{};
+    for (int i = 0; i < nb; ++i) {
+      L.kc[i] = cache_k[b + i];
+      L.vc[i] = cache_v[b + i];
+      L.kf[i] = fused_k[b + i];
+      L.vf[i] = fused_v[b + i];
+    }
+    Timed t(c, CB_K_ROPE, (double)nb * n_ctx * c->d.n_kv_heads * c->d.head_dim * c->esize() * (v_alias ? 2.0 : 4.0));
+    hipError_t e = cb::rope_delta_layers(L, nb, n_ctx, c->d.n_kv_heads, c->d.head_dim, offs_dev, n_chunks, c->rope,
+                                         c->d.max_tokens, v_alias ? 0 : 1, c->bf16(), c->cs);
+    if (e != hipSuccess) return hip_fail(e, "rope_delta_layers launch");
+  }
+  return CB_OK;
+}
+
 cb_status cb_synchronize(cb_ctx* c, int32_t layer) {
   cb_status st = check_ctx(c);
   if (st) return st;

@@ -48,6 +48,17 @@ hipError_t embed(const int32_t* tok, int n, const void* table, int vocab, int d,
                  hipStream_t s);
 hipError_t rmsnorm(const float* h, long ldh, int n, int d, const float* g, float eps, void* out, int bf16,
                    hipStream_t s);
+// Per-layer buffers of a batched position update (at most kRopeMaxLayers per launch).
+constexpr int kRopeMaxLayers = 64;
+struct RopeLayers {
+  const void* kc[kRopeMaxLayers];
+  const void* vc[kRopeMaxLayers];
+  void* kf[kRopeMaxLayers];
+  void* vf[kRopeMaxLayers];
+};
+// rope_delta for n_layers layers in one launch; copy_v = 0 when every V cache aliases its fused V.
+hipError_t rope_delta_layers(const RopeLayers& L, int n_layers, int n_ctx, int hkv, int dh, const int32_t* offs,
+                             int n_chunks, const float2* table, int table_rows, int copy_v, int bf16, hipStream_t s);
 // table: [table_rows][dh / 2] cos/sin; a chunk offset outside [0, table_rows) is clamped.
 hipError_t rope_delta(const void* kc, const void* vc, void* kf, void* vf, int n_ctx, int hkv, int dh,
                       const int32_t* offs, int n_chunks, const float2* table, int table_rows, int bf16,

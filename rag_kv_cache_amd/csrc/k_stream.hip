@@ -165,6 +165,65 @@ __global__ __launch_bounds__(256) void rope_delta_kernel(const T* kc, const T* v
   }
 }
 
+// The same position update for several layers in one launch: blockIdx.y = layer; every layer
+// has its own cache and fused buffers (same shape, same chunk offsets).
+template <typename T>
+__global__ __launch_bounds__(256) void rope_delta_layers_kernel(RopeLayers L, int n_ctx, int hkv, int dh,
+                                                                const int32_t* offs, int n_chunks,
+                                                                const float2* table, int table_rows, int copy_v) {
+  constexpr int VE = Vec16<T>::N;
+  constexpr int MAXC = 256;
+  __shared__ int s_offs[MAXC + 1];
+  const bool in_lds = n_chunks <= MAXC;
+  if (in_lds)
+    for (int i = threadIdx.x; i <= n_chunks; i += blockDim.x) s_offs[i] = offs[i];
+  __syncthreads();
+  const int l = blockIdx.y;
+  const T* kc = reinterpret_cast<const T*>(L.kc[l]);
+  const T* vc = reinterpret_cast<const T*>(L.vc[l]);
+  T* kf = reinterpret_cast<T*>(L.kf[l]);
+  T* vf = reinterpret_cast<T*>(L.vf[l]);
+  const int half = dh >> 1;
+  const int vph = half / VE;
+  const int vpr = hkv * vph;
+  const long total = (long)n_ctx * vpr;
+  for (long it = (long)blockIdx.x * blockDim.x + threadIdx.x; it < total; it += (long)gridDim.x * blockDim.x) {
+    const int row = (int)(it / vpr);
+    const int rem = (int)(it - (long)row * vpr);
+    const int h = rem / vph;
+    const int i0 = (rem - h * vph) * VE;
+    int lo = 0, hi = n_chunks - 1;  // last chunk whose offset <= row
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((in_lds ? s_offs[mid] : offs[mid]) <= row) lo = mid; else hi = mid - 1;
+    }
+    int o = in_lds ? s_offs[lo] : offs[lo];
+    o = o < 0 ? 0 : (o >= table_rows ? table_rows - 1 : o);  // the device offsets are not host-checked
+    const long base = ((long)row * hkv + h) * dh + i0;
+    float a[VE], b[VE], ya[VE], yb[VE];
+    Vec16<T>::load(kc + base, a);
+    Vec16<T>::load(kc + base + half, b);
+    uint4 v0, v1;
+    if (copy_v) {
+      v0 = *reinterpret_cast<const uint4*>(vc + base);
+      v1 = *reinterpret_cast<const uint4*>(vc + base + half);
+    }
+    const float2* cs = table + (long)o * half + i0;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      const float2 t = cs[e];
+      ya[e] = a[e] * t.x - b[e] * t.y;
+      yb[e] = b[e] * t.x + a[e] * t.y;
+    }
+    Vec16<T>::store(kf + base, ya);
+    Vec16<T>::store(kf + base + half, yb);
+    if (copy_v) {
+      *reinterpret_cast<uint4*>(vf + base) = v0;
+      *reinterpret_cast<uint4*>(vf + base + half) = v1;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- deviation + scatter
 // One wavefront per recomputed row i (position j = sel[i]): for context rows (i < n_cand)
 // dev[i] = sum over the row's K and V elements of (fresh - fused)^2, read before the
@@ -268,6 +327,24 @@ hipError_t rope_delta(const void* kc, const void* vc, void* kf, void* vf, int n_
   else
     hipLaunchKernelGGL(rope_delta_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s, (const float*)kc,
                        (const float*)vc, (float*)kf, (float*)vf, n_ctx, hkv, dh, offs, n_chunks, table, table_rows, copy_v);
+  return hipGetLastError();
+}
+
+hipError_t rope_delta_layers(const RopeLayers& L, int n_layers, int n_ctx, int hkv, int dh, const int32_t* offs,
+                             int n_chunks, const float2* table, int table_rows, int copy_v, int bf16, hipStream_t s) {
+  if (n_ctx <= 0 || n_layers <= 0) return hipSuccess;
+  if (n_layers > kRopeMaxLayers) return hipErrorInvalidValue;
+  const int ve = bf16 ? 8 : 4;
+  const long items = (long)n_ctx * hkv * (dh / 2 / ve);
+  long blocks = (items + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  const dim3 grid((unsigned)blocks, (unsigned)n_layers);
+  if (bf16)
+    hipLaunchKernelGGL(rope_delta_layers_kernel<bf16_t>, grid, dim3(256), 0, s, L, n_ctx, hkv, dh, offs, n_chunks,
+                       table, table_rows, copy_v);
+  else
+    hipLaunchKernelGGL(rope_delta_layers_kernel<float>, grid, dim3(256), 0, s, L, n_ctx, hkv, dh, offs, n_chunks,
+                       table, table_rows, copy_v);
   return hipGetLastError();
 }
 

@@ -164,7 +164,7 @@ def run_layers(eng: Engine, buf: RunBuffers, tokens: np.ndarray, offsets: Sequen
                host_cache: Optional[List[List[Sequence[torch.Tensor]]]] = None,
                record: bool = False, upload_inputs: bool = True,
                layer_events: Optional[list] = None, rotate_on_copy_stream: bool = False,
-               initial_sel: Optional[Sequence[int]] = None) -> RunResult:
+               initial_sel: Optional[Sequence[int]] = None, batch_rotation: bool = True) -> RunResult:
     """Blended prefill over every layer.
 
     fused[l] = (K, V) device buffers [N, H_kv, d_h] of layer l (the fused cache, output).
@@ -179,6 +179,8 @@ def run_layers(eng: Engine, buf: RunBuffers, tokens: np.ndarray, offsets: Sequen
     by a schedule of ratios >= 1.
     rotate_on_copy_stream (HBM mode): run the position update on the copy stream, two layers
     ahead (cb_fetch_layer_device), instead of inside cb_blend_layer on the compute stream.
+    batch_rotation (HBM mode, otherwise): the position update of every layer in one launch
+    before the first layer (cb_rotate_layers); False runs it inside each cb_blend_layer.
     upload_inputs=False reuses the token ids and offsets already on the device (a repeated
     step then enqueues no host-to-device copy).  layer_events, if given, receives a CUDA event
     recorded on the compute stream before the first layer and after every layer.
@@ -202,6 +204,7 @@ def run_layers(eng: Engine, buf: RunBuffers, tokens: np.ndarray, offsets: Sequen
             buf.offsets[: n_chunks + 1].copy_(torch.tensor(offs, dtype=torch.int32))
     prefetch = host_cache is not None
     fetched = prefetch or (cache is not None and n_ctx > 0 and rotate_on_copy_stream)
+    batched = cache is not None and not fetched and n_ctx > 0 and batch_rotation
 
     def fetch(l):
         # layer l's cache -> fused[l] with the position update, on the copy stream
@@ -224,6 +227,9 @@ def run_layers(eng: Engine, buf: RunBuffers, tokens: np.ndarray, offsets: Sequen
             ev.record(cs)
             layer_events.append(ev)
 
+    if batched:  # every layer's position update in one launch on the compute stream
+        L.cb_rotate_layers(ctx, 0, [_ptr(c[0]) for c in cache], [_ptr(c[1]) for c in cache], offs, n_chunks,
+                           _ptr(buf.offsets), [_ptr(f[0]) for f in fused], [_ptr(f[1]) for f in fused])
     n_first = n_tok if initial_sel is None else len(initial_sel)
     L.cb_embed(ctx, _ptr(buf.tokens), n_first, _ptr(eng.emb), _ptr(buf.hidden[0]))
     mark()
@@ -235,7 +241,7 @@ def run_layers(eng: Engine, buf: RunBuffers, tokens: np.ndarray, offsets: Sequen
             L.cb_synchronize(ctx, l)
             fetch(l + 2)
             ck, cv = None, None
-        elif cache is not None:  # position update inside cb_blend_layer (copy from the cache)
+        elif cache is not None and not batched:  # position update inside cb_blend_layer (copy from the cache)
             ck, cv = cache[l]
         else:
             ck, cv = None, None

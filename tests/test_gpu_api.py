@@ -93,6 +93,16 @@ def test_fetch_synchronize_state_machine(tiny):
     with pytest.raises(L.CbError) as e:  # blend before synchronize
         _blend(eng, wl, l=1, fused=(fk, fv), cached=(None, None))
     assert e.value.status == L.CB_ESTATE
+    with pytest.raises(L.CbError) as e:  # the batched position update may not overwrite a pending fetch
+        L.cb_rotate_layers(eng.ctx, 1, [_p(fk)], [_p(fv)], offs, len(offs) - 1, _p(offs_d), [_p(fk)], [_p(fv)])
+    assert e.value.status == L.CB_ESTATE
+    with pytest.raises(L.CbError) as e:  # layers outside the model
+        L.cb_rotate_layers(eng.ctx, 1, [_p(fk)] * 2, [_p(fv)] * 2, offs, len(offs) - 1, _p(offs_d), [_p(fk)] * 2,
+                           [_p(fv)] * 2)
+    assert e.value.status == L.CB_EINVAL
+    with pytest.raises(L.CbError) as e:  # K aliased, V not
+        L.cb_rotate_layers(eng.ctx, 0, [_p(fk)], [_p(hk[0])], offs, len(offs) - 1, _p(offs_d), [_p(fk)], [_p(fv)])
+    assert e.value.status == L.CB_EINVAL
     L.cb_synchronize(eng.ctx, 1)
     assert _blend(eng, wl, l=1, fused=(fk, fv), cached=(None, None)) > 0
     L.cb_synchronize(eng.ctx, 1)  # no pending fetch: no-op

@@ -107,8 +107,9 @@ def test_repeat_runs_are_bit_identical():
 
 def test_prefetch_path_equals_hbm_path():
     """Pinned-host cache fetched two layers ahead on the copy stream and re-rotated in place
-    there, and the HBM-resident cache re-rotated by copy on the copy stream, both give
-    bit-identical results to the HBM-resident cache re-rotated inside cb_blend_layer."""
+    there, the HBM-resident cache re-rotated by copy on the copy stream, and re-rotated inside
+    each cb_blend_layer, all give bit-identical results to the HBM-resident cache re-rotated for
+    every layer in one launch (cb_rotate_layers)."""
     from rag_kv_cache_amd.pipeline import build_chunk_caches, make_buffers, run_layers
     cfg = "small_bf16"
     wl = F.get_config(cfg)
@@ -116,12 +117,12 @@ def test_prefetch_path_equals_hbm_path():
     chunks = F.chunk_tokens(wl)
     cache, host = build_chunk_caches(eng, chunks, pinned_host=True)
     outs = []
-    for mode in ("hbm", "prefetch", "hbm_copy_stream"):
+    for mode in ("hbm", "prefetch", "hbm_copy_stream", "hbm_per_layer"):
         buf = make_buffers(eng, wl.n_tokens, len(chunks))
         fused = fused_buffers(eng, wl.n_tokens)
         res = run_layers(eng, buf, F.all_tokens(wl), F.chunk_offsets(wl), wl.n_query, wl.schedule, fused,
                          cache=None if mode == "prefetch" else cache, host_cache=host if mode == "prefetch" else None,
-                         rotate_on_copy_stream=mode == "hbm_copy_stream")
+                         rotate_on_copy_stream=mode == "hbm_copy_stream", batch_rotation=mode != "hbm_per_layer")
         eng.compute.synchronize()
         outs.append((res.hidden[: res.n_final].cpu().numpy().copy(), res.sel[: res.n_final].cpu().numpy().copy(),
                      [(bits(k), bits(v)) for k, v in fused]))
