@@ -23,7 +23,7 @@ struct GemmArgs {
   int cfg;               // bf16 tile configuration (GemmCfg), from gemm_plan
 };
 hipError_t gemm_bf16(const GemmArgs& g, hipStream_t s);
-enum GemmCfg { GEMM_128x512 = 0, GEMM_128x256 = 1, GEMM_64x256 = 2, GEMM_128x128 = 3, GEMM_64x128 = 4, GEMM_256x256 = 5 };
+enum GemmCfg { GEMM_128x512 = 0, GEMM_128x256 = 1, GEMM_64x256 = 2, GEMM_128x128 = 3, GEMM_64x128 = 4, GEMM_256x256 = 5, GEMM_GEMV = 6 };
 struct GemmPlan { int cfg, splits; };
 // Tile configuration and split-K factor of the bf16 GEMM for an M x N x K product with
 // epilogue `epi`; split partials ([splits][M][N] fp32) must fit partial_cap_elems.

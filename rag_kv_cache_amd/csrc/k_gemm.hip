@@ -505,6 +505,118 @@ inline int resid_norm_threads(int N) {
   return 64 * (nb < kResidWavesMax ? nb : kResidWavesMax);
 }
 
+// ------------------------------------------------------------------ skinny products
+// M <= 4 rows (a decode step): weight streaming, not MFMA, bounds the product.  A workgroup of
+// four wavefronts owns GV_P epilogue column pairs (2 GV_P weight rows) and splits K in four;
+// lane l of a wavefront takes the 16-byte chunks l, l + 64, ... of its K range and keeps fp32
+// dot products of every A row with every weight row; the wavefront sums its lanes, the four
+// partial sums are added in wavefront order through LDS, and one thread per (row, pair) applies
+// the same pair epilogue as the split-K reduce.
+constexpr int GV_P = 4;
+
+__device__ __forceinline__ void gv_pair_cols(const GemmArgs& g, int epi, int j, int& n_a, int& n_b) {
+  if (epi == EPI_ROPE) {
+    n_a = (j >> 6) * 128 + (j & 63);
+    n_b = n_a + 64;
+  } else if (epi == EPI_SWIGLU) {
+    n_a = j;
+    n_b = j + g.swiglu_ffn;
+  } else {
+    n_a = j;
+    n_b = j + g.N / 2;
+  }
+}
+
+__device__ __forceinline__ float dot8_bf16(const uint4 a, const uint4 w) {
+  const uint32_t av[4] = {a.x, a.y, a.z, a.w}, wv[4] = {w.x, w.y, w.z, w.w};
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s = fmaf(__uint_as_float(av[i] << 16), __uint_as_float(wv[i] << 16), s);
+    s = fmaf(__uint_as_float(av[i] & 0xffff0000u), __uint_as_float(wv[i] & 0xffff0000u), s);
+  }
+  return s;
+}
+
+template <int EPI, int MR>
+__global__ __launch_bounds__(256) void gemv_bf16_kernel(GemmArgs g) {
+  constexpr int NR = 2 * GV_P;  // weight rows of the workgroup
+  __shared__ float part[4][MR][NR];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j0 = blockIdx.x * GV_P;
+  const int n_pairs = g.N / 2;
+  const bf16_t* A = reinterpret_cast<const bf16_t*>(g.A);
+  const bf16_t* B = reinterpret_cast<const bf16_t*>(g.B);
+  const bf16_t* wrow[NR];
+#pragma unroll
+  for (int q = 0; q < GV_P; ++q) {
+    int n_a, n_b;
+    gv_pair_cols(g, EPI, min(j0 + q, n_pairs - 1), n_a, n_b);
+    wrow[2 * q] = B + (long)n_a * g.ldb;
+    wrow[2 * q + 1] = B + (long)n_b * g.ldb;
+  }
+  const bf16_t* arow[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    const int mm = m < g.M ? m : g.M - 1;
+    arow[m] = A + (g.a_rows ? (long)g.a_rows[mm] : (long)mm) * g.lda;
+  }
+  const int kq = g.K / 4;  // this wavefront's K range: [wave * kq, (wave + 1) * kq)
+  float acc[MR][NR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int r = 0; r < NR; ++r) acc[m][r] = 0.f;
+  for (int k = wave * kq + lane * 8; k < (wave + 1) * kq; k += 512) {
+    uint4 w[NR], a[MR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) w[r] = *reinterpret_cast<const uint4*>(wrow[r] + k);
+#pragma unroll
+    for (int m = 0; m < MR; ++m) a[m] = *reinterpret_cast<const uint4*>(arow[m] + k);
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int r = 0; r < NR; ++r) acc[m][r] += dot8_bf16(a[m], w[r]);
+  }
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const float v = wave_sum(acc[m][r]);
+      if (lane == 0) part[wave][m][r] = v;
+    }
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < MR * GV_P) {
+    const int m = t / GV_P, q = t - m * GV_P;
+    const int j = j0 + q;
+    if (m < g.M && j < n_pairs) {
+      float va = 0.f, vb = 0.f;
+#pragma unroll
+      for (int wv = 0; wv < 4; ++wv) {
+        va += part[wv][m][2 * q];
+        vb += part[wv][m][2 * q + 1];
+      }
+      int n_a, n_b;
+      gv_pair_cols(g, EPI, j, n_a, n_b);
+      epi_pair<EPI, bf16_t>(g, m, n_a, n_b, va, vb);
+    }
+  }
+}
+
+template <int EPI>
+hipError_t launch_gemv(const GemmArgs& g, hipStream_t s) {
+  if (g.M > 4 || g.K % 32 != 0 || g.N % 2 != 0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((g.N / 2 + GV_P - 1) / GV_P));
+  if (g.M == 1)
+    hipLaunchKernelGGL((gemv_bf16_kernel<EPI, 1>), grid, dim3(256), 0, s, g);
+  else if (g.M == 2)
+    hipLaunchKernelGGL((gemv_bf16_kernel<EPI, 2>), grid, dim3(256), 0, s, g);
+  else
+    hipLaunchKernelGGL((gemv_bf16_kernel<EPI, 4>), grid, dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ fp32 path
 // Correctness configurations: tile 64 x 128 x 16 on the vector ALUs, each thread 4 rows x 8
 // columns, operands through LDS; the C tile is staged in LDS and the epilogue pairs columns
@@ -592,6 +704,8 @@ template <int EPI>
 hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
   hipError_t e;
   switch (g.cfg) {
+    case GEMM_GEMV:
+      return launch_gemv<EPI>(g, s);
     case GEMM_128x512:  // planned for the SwiGLU epilogue only
       if constexpr (EPI == EPI_SWIGLU) { e = launch_dma<128, 512, 2, 4, 2, EPI>(g, s); break; }
       return hipErrorInvalidValue;
@@ -621,6 +735,7 @@ hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
 
 // Tile configuration and split-K factor for an M x N x K product (measured on MI355X at the
 // fusion step's shapes):
+//   * M <= 4 rows (a decode step): the skinny product, no split;
 //   * large M (>= 2048 rows, e.g. the first layer's full prompt) with a bf16 output and
 //     N % 256 == 0: 256 x 256 tiles of 8 wavefronts, no split (the fewest operand bytes per
 //     flop: 7-18% faster than the next best there);
@@ -633,6 +748,10 @@ hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
 //   each split keeps at least two 64-wide K-steps and its partials fit the buffer.
 GemmPlan gemm_plan(int M, int N, int K, int epi, long partial_cap_elems) {
   GemmPlan p{GEMM_128x128, 1};
+  if (M <= 4 && K % 32 == 0) {  // a few rows (decode): weight streaming on the vector ALUs
+    p.cfg = GEMM_GEMV;
+    return p;
+  }
   if (M >= 2048 && epi != EPI_RESID && N % 256 == 0) {
     p.cfg = GEMM_256x256;
     return p;
