@@ -120,6 +120,15 @@ cb_status cb_embed(cb_ctx* ctx, const int32_t* tokens, int32_t n, const void* ta
  * kv_cached_k = kv_cached_v = NULL to cb_blend_layer.  chunk_offsets_dev: the same offsets
  * on the device.  CB_ESTATE if the layer already has a fetch that no cb_synchronize has
  * consumed. */
+/* How cb_fetch_layer moves the rows.  CB_FETCH_KERNEL (default): when every chunk pointer is
+ * page-locked host memory that kernels can read at the same address (hipHostMalloc, torch's
+ * pinned tensors), one kernel on the copy stream reads the rows over PCIe, rotates K and writes
+ * K and V into the fused buffers (one pass, no per-chunk copy commands); other pointers fall
+ * back to the copy engine.  CB_FETCH_COPY: always the copy engine (hipMemcpyAsync per chunk),
+ * then the rotation in place.  Results are identical.  CB_EINVAL for another mode. */
+typedef enum { CB_FETCH_COPY = 0, CB_FETCH_KERNEL = 1 } cb_fetch_mode;
+cb_status cb_set_fetch_mode(cb_ctx* ctx, int32_t mode);
+
 cb_status cb_fetch_layer(cb_ctx* ctx, int32_t layer, const void* const* host_k,
                          const void* const* host_v, const int32_t* chunk_offsets_host,
                          int32_t n_chunks, const int32_t* chunk_offsets_dev, void* fused_k,

@@ -61,6 +61,7 @@ _SIGS = {
     "cb_embed": [_P, _P, _I, _P, _P],
     "cb_fetch_layer": [_P, _I, C.POINTER(_P), C.POINTER(_P), C.POINTER(_I), _I, _P, _P, _P],
     "cb_fetch_layer_device": [_P, _I, _P, _P, C.POINTER(_I), _I, _P, _P, _P],
+    "cb_set_fetch_mode": [_P, _I],
     "cb_rotate_layers": [_P, _I, _I, C.POINTER(_P), C.POINTER(_P), C.POINTER(_I), _I, _P, C.POINTER(_P), C.POINTER(_P)],
     "cb_synchronize": [_P, _I],
     "cb_blend_layer": [_P, _I, _P, _P, _P, _P, _P, _P, _P, C.POINTER(_I), _I, _P, _I, _I, C.c_float, _P, _P,
@@ -142,6 +143,13 @@ def cb_fetch_layer_device(ctx: int, layer: int, cache_k: int, cache_v: int, chun
                           n_chunks: int, chunk_offsets_dev: int, fused_k: int, fused_v: int) -> None:
     _check(_L.cb_fetch_layer_device(ctx, layer, cache_k or None, cache_v or None, _i32(chunk_offsets_host),
                                     n_chunks, chunk_offsets_dev or None, fused_k, fused_v))
+
+
+CB_FETCH_COPY, CB_FETCH_KERNEL = 0, 1
+
+
+def cb_set_fetch_mode(ctx: int, mode: int) -> None:
+    _check(_L.cb_set_fetch_mode(ctx, mode))
 
 
 def cb_rotate_layers(ctx: int, first_layer: int, cache_k: Sequence[int], cache_v: Sequence[int],

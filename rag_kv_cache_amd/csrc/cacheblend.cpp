@@ -51,6 +51,7 @@ constexpr int kGemmMaxSplits = 8;
 constexpr int kAttnMaxSplits = 16;
 constexpr int kAttnSmallRows = 64;     // kept sets this small (decode) get finer key splits:
 constexpr int kAttnSmallSplits = 64;   // up to this many
+constexpr int kFetchBlocks = 8;  // fetch workgroups: PCIe-bound; each holds a CU that a full-chip GEMM wave would use
 constexpr int kPartialRows = 2048;  // split-K / split-KV partial buffers cover this many rows
 constexpr size_t kAlign = 256;
 
@@ -69,6 +70,7 @@ struct cb_ctx {
   std::vector<hipEvent_t> release_ev;  // per layer: the compute stream is done with its fused K/V
   std::vector<int> state;
   int score_mode = CB_SCORE_L2;
+  int fetch_mode = CB_FETCH_KERNEL;
   bool prof = false;
   std::vector<ProfRec> recs;
   std::vector<hipEvent_t> ev_pool;
@@ -359,6 +361,31 @@ cb_status finish_fetch(cb_ctx* c, int layer, const void* src_k, const void* src_
 
 extern "C" {
 
+namespace {
+
+// Whether p lies in page-locked host memory that kernels may read at the same address (so a
+// fetch kernel can read it over PCIe); anything else goes through the copy engine.
+bool kernel_readable_host(const void* p) {
+  hipPointerAttribute_t a{};
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();  // pageable memory is not an error here: clear it
+    return false;
+  }
+  if (a.type != hipMemoryTypeHost || !a.devicePointer) return false;
+  const char* host = a.hostPointer ? (const char*)a.hostPointer : (const char*)p;
+  return (const char*)a.devicePointer + ((const char*)p - host) == (const char*)p;
+}
+
+}  // namespace
+
+cb_status cb_set_fetch_mode(cb_ctx* c, int32_t mode) {
+  cb_status st = check_ctx(c);
+  if (st) return st;
+  if (mode != CB_FETCH_COPY && mode != CB_FETCH_KERNEL) return fail(CB_EINVAL, "unknown fetch mode %d", mode);
+  c->fetch_mode = mode;
+  return CB_OK;
+}
+
 cb_status cb_fetch_layer(cb_ctx* c, int32_t layer, const void* const* host_k, const void* const* host_v,
                          const int32_t* offs, int32_t n_chunks, const int32_t* offs_dev, void* fused_k,
                          void* fused_v) {
@@ -368,7 +395,32 @@ cb_status cb_fetch_layer(cb_ctx* c, int32_t layer, const void* const* host_k, co
   const size_t row = (size_t)c->d.n_kv_heads * c->d.head_dim * c->esize();
   for (int ch = 0; ch < n_chunks; ++ch)
     if (offs[ch + 1] > offs[ch] && (!host_k[ch] || !host_v[ch])) return fail(CB_EINVAL, "chunk %d host pointer NULL", ch);
+  bool direct = c->fetch_mode == CB_FETCH_KERNEL;
+  for (int ch = 0; direct && ch < n_chunks; ++ch)
+    if (offs[ch + 1] > offs[ch] && !(kernel_readable_host(host_k[ch]) && kernel_readable_host(host_v[ch])))
+      direct = false;
   if ((st = wait_release(c, layer))) return st;
+  const int n_ctx = n_chunks > 0 ? offs[n_chunks] : 0;
+  if (direct && n_ctx > 0) {  // one kernel per 64 chunks reads, rotates and writes the rows
+    Timed t(c, CB_K_ROPE, (double)n_ctx * c->d.n_kv_heads * c->d.head_dim * c->esize() * 4.0, c->xs);
+    for (int c0 = 0; c0 < n_chunks; c0 += cb::kFetchMaxChunks) {
+      cb::FetchChunks F{};
+      F.n = std::min(cb::kFetchMaxChunks, n_chunks - c0);
+      for (int i = 0; i < F.n; ++i) {
+        F.hk[i] = host_k[c0 + i];
+        F.hv[i] = host_v[c0 + i];
+        F.offs[i] = offs[c0 + i];
+      }
+      F.offs[F.n] = offs[c0 + F.n];
+      hipError_t e = cb::fetch_rope(F, fused_k, fused_v, c->d.n_kv_heads, c->d.head_dim, c->rope, c->d.max_tokens,
+                                    c->bf16(), kFetchBlocks, c->xs);
+      if (e != hipSuccess) return hip_fail(e, "fetch kernel launch");
+    }
+    hipError_t e = hipEventRecord(c->fetch_ev[layer], c->xs);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(fetch)");
+    c->state[layer] = LS_FETCHED;
+    return CB_OK;
+  }
   for (int ch = 0; ch < n_chunks; ++ch) {
     const size_t bytes = (size_t)(offs[ch + 1] - offs[ch]) * row;
     if (!bytes) continue;

@@ -59,6 +59,18 @@ struct RopeLayers {
 // rope_delta for n_layers layers in one launch; copy_v = 0 when every V cache aliases its fused V.
 hipError_t rope_delta_layers(const RopeLayers& L, int n_layers, int n_ctx, int hkv, int dh, const int32_t* offs,
                              int n_chunks, const float2* table, int table_rows, int copy_v, int bf16, hipStream_t s);
+// One layer's cached rows of up to kFetchMaxChunks chunks in pinned host memory (device-
+// accessible addresses): chunk c holds rows [offs[c], offs[c+1]) of the fused buffers.
+constexpr int kFetchMaxChunks = 64;
+struct FetchChunks {
+  const void* hk[kFetchMaxChunks];
+  const void* hv[kFetchMaxChunks];
+  int offs[kFetchMaxChunks + 1];
+  int n;
+};
+// Read them, rotate K by R(o_c), copy V, into kf / vf (device); n_blocks workgroups.
+hipError_t fetch_rope(const FetchChunks& F, void* kf, void* vf, int hkv, int dh, const float2* table, int table_rows,
+                      int bf16, int n_blocks, hipStream_t s);
 // table: [table_rows][dh / 2] cos/sin; a chunk offset outside [0, table_rows) is clamped.
 hipError_t rope_delta(const void* kc, const void* vc, void* kf, void* vf, int n_ctx, int hkv, int dh,
                       const int32_t* offs, int n_chunks, const float2* table, int table_rows, int bf16,

@@ -224,6 +224,90 @@ __global__ __launch_bounds__(256) void rope_delta_layers_kernel(RopeLayers L, in
   }
 }
 
+// ---------------------------------------------------------------- fetch from pinned host memory
+// fetch_kv in one pass: the kernel reads one layer's cached rows of every chunk straight from
+// pinned host memory (over PCIe), rotates K by R(o_c) and copies V into the fused buffers in
+// device memory.  A few workgroups of 1024 threads, each thread with the host loads of FU items
+// in flight: the link, not the number of workgroups, bounds it, and the compute kernels keep
+// the other CUs.
+template <typename T>
+__device__ __forceinline__ void unpack16(const uint4 v, float* o);
+template <>
+__device__ __forceinline__ void unpack16<float>(const uint4 v, float* o) {
+  o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y); o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+}
+template <>
+__device__ __forceinline__ void unpack16<bf16_t>(const uint4 v, float* o) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = __uint_as_float(w[i] << 16);
+    o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(1024) void fetch_rope_kernel(FetchChunks F, T* kf, T* vf, int hkv, int dh,
+                                                         const float2* table, int table_rows) {
+  constexpr int VE = Vec16<T>::N;
+  constexpr int FU = 4;
+  const int half = dh >> 1;
+  const int vph = half / VE;
+  const int vpr = hkv * vph;
+  const int r0 = F.offs[0];
+  const long total = (long)(F.offs[F.n] - r0) * vpr;
+  const long stride = (long)gridDim.x * blockDim.x;
+  for (long it0 = (long)blockIdx.x * blockDim.x + threadIdx.x; it0 < total; it0 += stride * FU) {
+    uint4 k0[FU], k1[FU], v0[FU], v1[FU];
+    long dst[FU];
+    int off[FU], i0s[FU];
+#pragma unroll
+    for (int u = 0; u < FU; ++u) {
+      const long it = it0 + u * stride;
+      dst[u] = -1;
+      if (it >= total) continue;
+      const int row = r0 + (int)(it / vpr);
+      const int rem = (int)(it - (long)(row - r0) * vpr);
+      const int h = rem / vph;
+      const int i0 = (rem - h * vph) * VE;
+      int lo = 0, hi = F.n - 1;  // last chunk whose first row <= row
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (F.offs[mid] <= row) lo = mid; else hi = mid - 1;
+      }
+      const long src = ((long)(row - F.offs[lo]) * hkv + h) * dh + i0;
+      const T* hk = reinterpret_cast<const T*>(F.hk[lo]) + src;
+      const T* hv = reinterpret_cast<const T*>(F.hv[lo]) + src;
+      k0[u] = *reinterpret_cast<const uint4*>(hk);
+      k1[u] = *reinterpret_cast<const uint4*>(hk + half);
+      v0[u] = *reinterpret_cast<const uint4*>(hv);
+      v1[u] = *reinterpret_cast<const uint4*>(hv + half);
+      int o = F.offs[lo];
+      off[u] = o < 0 ? 0 : (o >= table_rows ? table_rows - 1 : o);
+      i0s[u] = i0;
+      dst[u] = ((long)row * hkv + h) * dh + i0;
+    }
+#pragma unroll
+    for (int u = 0; u < FU; ++u) {
+      if (dst[u] < 0) continue;
+      float a[VE], b[VE], ya[VE], yb[VE];
+      unpack16<T>(k0[u], a);
+      unpack16<T>(k1[u], b);
+      const float2* cs = table + (long)off[u] * half + i0s[u];
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        const float2 t = cs[e];
+        ya[e] = a[e] * t.x - b[e] * t.y;
+        yb[e] = b[e] * t.x + a[e] * t.y;
+      }
+      Vec16<T>::store(kf + dst[u], ya);
+      Vec16<T>::store(kf + dst[u] + half, yb);
+      *reinterpret_cast<uint4*>(vf + dst[u]) = v0[u];
+      *reinterpret_cast<uint4*>(vf + dst[u] + half) = v1[u];
+    }
+  }
+}
+
 // ---------------------------------------------------------------- deviation + scatter
 // One wavefront per recomputed row i (position j = sel[i]): for context rows (i < n_cand)
 // dev[i] = sum over the row's K and V elements of (fresh - fused)^2, read before the
@@ -345,6 +429,19 @@ hipError_t rope_delta_layers(const RopeLayers& L, int n_layers, int n_ctx, int h
   else
     hipLaunchKernelGGL(rope_delta_layers_kernel<float>, grid, dim3(256), 0, s, L, n_ctx, hkv, dh, offs, n_chunks,
                        table, table_rows, copy_v);
+  return hipGetLastError();
+}
+
+hipError_t fetch_rope(const FetchChunks& F, void* kf, void* vf, int hkv, int dh, const float2* table, int table_rows,
+                      int bf16, int n_blocks, hipStream_t s) {
+  if (F.n <= 0 || F.offs[F.n] <= F.offs[0]) return hipSuccess;
+  if (F.n > kFetchMaxChunks) return hipErrorInvalidValue;
+  if (bf16)
+    hipLaunchKernelGGL(fetch_rope_kernel<bf16_t>, dim3(n_blocks), dim3(1024), 0, s, F, (bf16_t*)kf, (bf16_t*)vf, hkv,
+                       dh, table, table_rows);
+  else
+    hipLaunchKernelGGL(fetch_rope_kernel<float>, dim3(n_blocks), dim3(1024), 0, s, F, (float*)kf, (float*)vf, hkv, dh,
+                       table, table_rows);
   return hipGetLastError();
 }
 

@@ -106,24 +106,32 @@ def test_repeat_runs_are_bit_identical():
 
 
 def test_prefetch_path_equals_hbm_path():
-    """Pinned-host cache fetched two layers ahead on the copy stream and re-rotated in place
-    there, the HBM-resident cache re-rotated by copy on the copy stream, and re-rotated inside
-    each cb_blend_layer, all give bit-identical results to the HBM-resident cache re-rotated for
-    every layer in one launch (cb_rotate_layers)."""
+    """Pinned-host cache fetched two layers ahead on the copy stream (read over PCIe and
+    rotated by one kernel, or copied by the copy engine and rotated in place, or from pageable
+    memory, which falls back to the copy engine), the HBM-resident cache re-rotated by copy on
+    the copy stream, and re-rotated inside each cb_blend_layer, all give bit-identical results
+    to the HBM-resident cache re-rotated for every layer in one launch (cb_rotate_layers)."""
     from rag_kv_cache_amd.pipeline import build_chunk_caches, make_buffers, run_layers
     cfg = "small_bf16"
     wl = F.get_config(cfg)
     eng = engine(cfg)
     chunks = F.chunk_tokens(wl)
+    from rag_kv_cache_amd import _lib as L
     cache, host = build_chunk_caches(eng, chunks, pinned_host=True)
+    pageable = [[(k.clone(), v.clone()) for k, v in layer] for layer in host]  # not page-locked
+    assert not pageable[0][0][0].is_pinned()
     outs = []
-    for mode in ("hbm", "prefetch", "hbm_copy_stream", "hbm_per_layer"):
+    for mode in ("hbm", "prefetch", "prefetch_copy", "prefetch_pageable", "hbm_copy_stream", "hbm_per_layer"):
         buf = make_buffers(eng, wl.n_tokens, len(chunks))
         fused = fused_buffers(eng, wl.n_tokens)
+        pre = mode.startswith("prefetch")
+        L.cb_set_fetch_mode(eng.ctx, L.CB_FETCH_COPY if mode == "prefetch_copy" else L.CB_FETCH_KERNEL)
         res = run_layers(eng, buf, F.all_tokens(wl), F.chunk_offsets(wl), wl.n_query, wl.schedule, fused,
-                         cache=None if mode == "prefetch" else cache, host_cache=host if mode == "prefetch" else None,
+                         cache=None if pre else cache,
+                         host_cache=(pageable if mode == "prefetch_pageable" else host) if pre else None,
                          rotate_on_copy_stream=mode == "hbm_copy_stream", batch_rotation=mode != "hbm_per_layer")
         eng.compute.synchronize()
+        L.cb_set_fetch_mode(eng.ctx, L.CB_FETCH_KERNEL)
         outs.append((res.hidden[: res.n_final].cpu().numpy().copy(), res.sel[: res.n_final].cpu().numpy().copy(),
                      [(bits(k), bits(v)) for k, v in fused]))
     h0, s0, f0 = outs[0]
