@@ -3,7 +3,8 @@
 //
 // One workgroup of 1024 threads (16 wavefronts).  The k-th largest key is found exactly by
 // an MSB-first radix select over order-preserving uint32 images of the fp32 scores (four
-// 8-bit digits, LDS histograms with integer atomics, so the counts are exact).  Rows are
+// 8-bit digits, LDS histograms with integer atomics, so the counts are exact; the digit is
+// located by a suffix scan of the histogram across one wavefront).  Rows are
 // then compacted in index order with wavefront ballots + popcounts and a 16-entry LDS
 // prefix: rows above the threshold are all kept, rows equal to it are kept lowest index
 // first until k is reached.
@@ -64,15 +65,22 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const float* dev, cons
         if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
       }
       __syncthreads();
-      if (tid == 0) {  // digit of the remaining-th largest among the matching keys
-        uint32_t above = 0;
-        int b = 255;
-        for (; b > 0; --b) {
-          if (above + hist[b] >= remaining) break;
-          above += hist[b];
+      if (tid < 64) {  // digit of the remaining-th largest among the matching keys: the one bin b
+        // with above(b) < remaining <= above(b) + hist[b], above(b) = count in bins > b; lane l
+        // holds bins 4l .. 4l+3, a suffix scan over the lanes gives above() of its top bin
+        const uint32_t h0 = hist[4 * tid], h1 = hist[4 * tid + 1], h2 = hist[4 * tid + 2], h3 = hist[4 * tid + 3];
+        const uint32_t own = h0 + h1 + h2 + h3;
+        uint32_t incl = own;  // sum over lanes >= tid
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const uint32_t t = __shfl_down(incl, d);
+          if (tid + d < 64) incl += t;
         }
-        s_digit = (uint32_t)b;
-        s_rem = remaining - above;
+        const uint32_t a3 = incl - own, a2 = a3 + h3, a1 = a2 + h2, a0 = a1 + h1;
+        if (a3 < remaining && remaining <= a3 + h3) { s_digit = 4 * tid + 3; s_rem = remaining - a3; }
+        if (a2 < remaining && remaining <= a2 + h2) { s_digit = 4 * tid + 2; s_rem = remaining - a2; }
+        if (a1 < remaining && remaining <= a1 + h1) { s_digit = 4 * tid + 1; s_rem = remaining - a1; }
+        if (a0 < remaining && remaining <= a0 + h0) { s_digit = 4 * tid; s_rem = remaining - a0; }
       }
       __syncthreads();
       prefix |= s_digit << shift;

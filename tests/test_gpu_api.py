@@ -181,3 +181,50 @@ def test_empty_and_degenerate_sizes(tiny):
     # context rows only, no query rows, ratio keeps 0 of them -> nothing kept, nothing attended
     assert _blend(eng, wl, n_query=0, n_sel=wl.n_ctx, ratio=0.0) == 0
     eng.compute.synchronize()
+
+
+def test_topk_ties_take_lowest_positions(tiny):
+    """Gradual filtering with exact ties: a cache equal to the fresh K/V gives deviation 0 at
+    every row except a chosen set D, whose rows get distinct positive deviations; with k = |D| +
+    20 the kept set is D, the 20 lowest positions outside D, and every query row (ascending)."""
+    from rag_kv_cache_amd import _lib as L
+    eng, wl = tiny
+    s = wl.shape
+    n_tok, n_q = wl.n_tokens, wl.n_query
+    n_ctx = n_tok - n_q
+    offs = [0, n_ctx]  # one chunk at offset 0: the position update is the identity
+    d = eng.device
+    torch.manual_seed(0)
+    h = torch.randn(n_tok, s.d_model, device=d) * 0.5
+    sel = torch.arange(n_tok, dtype=torch.int32, device=d)
+    offs_d = torch.tensor(offs, dtype=torch.int32, device=d)
+    new_sel = torch.empty(n_tok, dtype=torch.int32, device=d)
+    new_loc = torch.empty(n_tok, dtype=torch.int32, device=d)
+    out = torch.empty(n_tok, s.n_q_heads * s.head_dim, device=d)
+    dev = torch.empty(n_tok, device=d)
+    ws = eng.workspace(n_tok, n_tok)
+
+    def blend(cache, fk, fv, ratio):
+        n = L.cb_blend_layer(eng.ctx, 1, _p(h), _p(cache[0]), _p(cache[1]), _p(fk), _p(fv), _p(offs_d), offs, 1,
+                             _p(sel), n_tok, n_q, ratio, _p(new_sel), _p(new_loc), _p(out), _p(dev), _p(ws),
+                             ws.numel())
+        eng.compute.synchronize()
+        return n
+
+    fk, fv = eng.kv_empty(n_tok), eng.kv_empty(n_tok)
+    blend((None, None), fk, fv, 1.0)  # every row recomputed: fk, fv hold the fresh K/V
+    rng = np.random.default_rng(5)
+    D = np.sort(rng.choice(n_ctx, size=60, replace=False))
+    ck, cv = fk.clone(), fv.clone()
+    bump = torch.tensor(np.linspace(0.05, 3.0, len(D)), dtype=torch.float32, device=d)
+    ck[torch.from_numpy(D).to(d)] += bump[:, None, None]
+    k = len(D) + 20
+    fk2, fv2 = eng.kv_empty(n_tok), eng.kv_empty(n_tok)
+    n_new = blend((ck, cv), fk2, fv2, k / n_ctx)
+    assert n_new == k + n_q
+    devs = dev[:n_ctx].cpu().numpy()
+    outside = np.setdiff1d(np.arange(n_ctx), D)
+    assert np.all(devs[outside] == 0.0) and np.all(devs[D] > 0.0)
+    expect = np.concatenate([np.sort(np.concatenate([D, outside[:20]])), np.arange(n_ctx, n_tok)])
+    assert np.array_equal(new_sel[:n_new].cpu().numpy(), expect)
+    assert np.array_equal(new_loc[:n_new].cpu().numpy(), expect)  # sel is the identity here

@@ -174,3 +174,38 @@ def test_special_schedules(sched):
                                offs, wl.n_query)
             assert_close(to_np(fused[l][0])[: wl.n_ctx], rot[0][: wl.n_ctx], "f32", "rotated K")
             assert np.array_equal(bits(fused[l][1][: wl.n_ctx]), bits(cache[l][1]))
+
+
+def test_many_chunks_and_layers_batched_paths():
+    """More than 64 chunks (the fetch kernel then runs in batches of 64) and more than 64 layers
+    (cb_rotate_layers then launches per 64 layers): both batched paths give bit-identical results
+    to the per-layer paths (copy engine + rotation inside cb_blend_layer)."""
+    from dataclasses import replace
+    from rag_kv_cache_amd import _lib as L
+    from rag_kv_cache_amd.pipeline import Engine, build_chunk_caches, make_buffers, run_layers
+    base = F.get_config("tiny")
+    sh = replace(base.shape, name="tiny-deep", n_layers=66, d_model=128, ffn_dim=256, vocab=500)
+    wl = F.Workload("many_chunks", sh, (4,) * 70 + (9,), 7, (1.0,) + (0.3,) * 65)
+    W = [F.layer_weights(sh, l) for l in range(1, sh.n_layers + 1)]
+    eng = Engine(sh, max_tokens=wl.n_tokens + 8)
+    eng.load_all(lambda l: W[l - 1], F.embedding(sh))
+    chunks = F.chunk_tokens(wl)
+    cache, host = build_chunk_caches(eng, chunks, pinned_host=True)
+    outs = []
+    for mode in ("hbm_batched", "hbm_per_layer", "prefetch_kernel", "prefetch_copy"):
+        L.cb_set_fetch_mode(eng.ctx, L.CB_FETCH_COPY if mode == "prefetch_copy" else L.CB_FETCH_KERNEL)
+        buf = make_buffers(eng, wl.n_tokens, len(chunks))
+        fused = fused_buffers(eng, wl.n_tokens)
+        pre = mode.startswith("prefetch")
+        res = run_layers(eng, buf, F.all_tokens(wl), F.chunk_offsets(wl), wl.n_query, wl.schedule, fused,
+                         cache=None if pre else cache, host_cache=host if pre else None,
+                         batch_rotation=mode == "hbm_batched")
+        eng.compute.synchronize()
+        outs.append((res.hidden[: res.n_final].cpu().numpy().copy(), [(bits(k), bits(v)) for k, v in fused]))
+    L.cb_set_fetch_mode(eng.ctx, L.CB_FETCH_KERNEL)
+    h0, f0 = outs[0]
+    for h1, f1 in outs[1:]:
+        assert np.array_equal(h0, h1)
+        for (a, b), (c, d) in zip(f0, f1):
+            assert np.array_equal(a, c) and np.array_equal(b, d)
+    eng.close()
