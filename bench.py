@@ -41,6 +41,29 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def schedule_text(sched):
+    """'1.0, 0.30, 0.15 x 26' for a schedule whose last ratio repeats."""
+    s = [float(x) for x in sched]
+    head = s
+    n_tail = 1
+    while n_tail < len(s) and s[-n_tail - 1] == s[-1]:
+        n_tail += 1
+    head = s[: len(s) - n_tail]
+    parts = [f"{x:.2f}" if x < 1 else "1.0" for x in head]
+    tail = f"{s[-1]:.2f}" if s[-1] < 1 else "1.0"
+    return ", ".join(parts + [tail + (f" x {n_tail}" if n_tail > 1 else "")])
+
+
+def describe(wl):
+    sh = wl.shape
+    lens = sorted(set(wl.chunk_lens))
+    chunks = (f"{len(wl.chunk_lens)}x{lens[0]}-token" if len(lens) == 1
+              else f"{len(wl.chunk_lens)} ragged ({min(lens)}-{max(lens)} token)")
+    return (f"{wl.name}: {sh.name}-shaped blended prefill, {sh.n_layers} layers, d_model {sh.d_model}, "
+            f"{sh.n_q_heads}/{sh.n_kv_heads} heads of {sh.head_dim}, FFN {sh.ffn_dim}, {sh.dtype}; {chunks} cached "
+            f"chunks + {wl.n_query}-token query, recompute {schedule_text(wl.schedule)}, cached KV resident in HBM")
+
+
 def attention_flops(shape, records, n_query):
     """4 * H_q * d_h * sum over kept rows of (position + 1), summed over layers."""
     return [4.0 * shape.n_q_heads * shape.head_dim * float((r.new_sel.astype(np.int64) + 1).sum()) for r in records]
@@ -128,6 +151,158 @@ def run_controller(eng, buf, tokens, offs, wl, fused, host, full_ms, steps):
             "ratio": round(float(plan.ratio), 4), "predicted_ms_per_step": round(plan.t_total * 1e3, 4),
             "measured_ms_per_step": round(ms, 4), "context_tokens_per_s": round(wl.n_ctx / ms * 1e3, 1),
             "schedule": "1.0, then the planned ratio (pinned-host cache fetched two layers ahead)"}
+
+
+def _fetch_layer(eng, buf, host, offs, l, fused):
+    from rag_kv_cache_amd import _lib as L
+    n_chunks = len(offs) - 1
+    L.cb_fetch_layer(eng.ctx, l, [int(host[l][c][0].data_ptr()) for c in range(n_chunks)],
+                     [int(host[l][c][1].data_ptr()) for c in range(n_chunks)], offs, n_chunks,
+                     int(buf.offsets.data_ptr()), int(fused[l][0].data_ptr()), int(fused[l][1].data_ptr()))
+
+
+def run_overlap(eng, buf, tokens, offs, wl, fused, host, reps: int = 5, eps_ms: float = 0.02):
+    """Per-layer T_load, T_recompute and T_overlapped of the pinned-host prefetched prefill, medians
+    over `reps` runs:
+      * T_load[l]: layer l's fetch alone (cached K/V of every chunk over PCIe + position update),
+        HIP events around each launch on the copy stream, every layer fetched back to back with
+        no compute running;
+      * T_recompute[l]: layer l's compute alone (blend + rest), events on the compute stream, the
+        fused buffers already holding the re-rotated cache (no fetch);
+      * T_overlapped[l]: layer l on the compute stream in the pipelined run (fetches two layers
+        ahead on the copy stream), including any wait for its fetch.
+    The pipeline claim is checked per layer as T_overlapped <= max(T_load, T_recompute) + eps."""
+    import torch
+    from rag_kv_cache_amd import _lib as L
+    from rag_kv_cache_amd.pipeline import run_layers
+    nl = wl.shape.n_layers
+    xs, cs = eng.copy, eng.compute
+    loads, recs, ovs = [], [], []
+
+    def layer_times(kw):
+        evs = []
+        run_layers(eng, buf, tokens, offs, wl.n_query, wl.schedule, fused, upload_inputs=False,
+                   layer_events=evs, **kw)
+        cs.synchronize()
+        torch.cuda.synchronize()
+        return [evs[i].elapsed_time(evs[i + 1]) for i in range(nl)]
+
+    for r in range(reps + 1):  # the first round warms up
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(nl + 1)]
+        ev[0].record(xs)
+        for l in range(nl):
+            _fetch_layer(eng, buf, host, offs, l, fused)
+            ev[l + 1].record(xs)
+        for l in range(nl):
+            L.cb_synchronize(eng.ctx, l)
+        xs.synchronize()
+        cs.synchronize()
+        lt = [ev[i].elapsed_time(ev[i + 1]) for i in range(nl)]
+        # the fused buffers now hold every layer's re-rotated cache: compute alone over them
+        rt = layer_times(dict(cache=None))
+        ot = layer_times(dict(host_cache=host))
+        if r:
+            loads.append(lt)
+            recs.append(rt)
+            ovs.append(ot)
+    med = lambda rows: [float(np.median(c)) for c in zip(*rows)]
+    t_load, t_rec, t_ov = med(loads), med(recs), med(ovs)
+    excess = [t_ov[l] - max(t_load[l], t_rec[l]) for l in range(nl)]
+    steady = list(range(3, nl))
+    ok = [l for l in range(nl) if excess[l] <= eps_ms]
+    log(f"overlap (steady medians): load {np.median([t_load[l] for l in steady]):.4f}, recompute "
+        f"{np.median([t_rec[l] for l in steady]):.4f}, overlapped {np.median([t_ov[l] for l in steady]):.4f} ms; "
+        f"{len(ok)}/{nl} layers within max(load, recompute) + {eps_ms} ms")
+    r4 = lambda v: [round(x, 4) for x in v]
+    return {"t_load_ms": r4(t_load), "t_recompute_ms": r4(t_rec), "t_overlapped_ms": r4(t_ov),
+            "steady_median_ms": {"load": round(float(np.median([t_load[l] for l in steady])), 4),
+                                 "recompute": round(float(np.median([t_rec[l] for l in steady])), 4),
+                                 "overlapped": round(float(np.median([t_ov[l] for l in steady])), 4)},
+            "sum_ms": {"load": round(sum(t_load), 4), "recompute": round(sum(t_rec), 4),
+                       "overlapped": round(sum(t_ov), 4),
+                       "max_per_layer": round(sum(max(a, b) for a, b in zip(t_load, t_rec)), 4)},
+            "check": {"eps_ms": eps_ms, "layers_within": len(ok), "layers": nl,
+                      "max_excess_ms": round(max(excess), 4),
+                      "steady_median_excess_ms": round(float(np.median([excess[l] for l in steady])), 4)},
+            "note": "per-layer medians over %d runs; T_load: each layer's fetch alone on the copy stream; "
+                    "T_recompute: compute alone on fused buffers that already hold the cache" % reps}
+
+
+def run_reuse(eng, buf, tokens, offs, wl, fused, cache, steps):
+    """Lower bounds on the same GPU and kernels (HBM-resident cache, eager launches): full KV reuse
+    as ratio 0 from layer 2 (layer 1 recomputes every row, later layers only the query rows), and
+    no context row recomputed at any layer (only the query rows run through the model over the
+    re-rotated caches)."""
+    import torch
+    from rag_kv_cache_amd.pipeline import run_layers
+    sh = wl.shape
+    n = max(3, steps // 2)
+    q_only = list(range(wl.n_ctx, wl.n_tokens))
+
+    def timed(sched, init=None):
+        for r in range(n + 2):
+            if r == 2:
+                eng.compute.synchronize()
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+            run_layers(eng, buf, tokens, offs, wl.n_query, sched, fused, cache=cache, upload_inputs=False,
+                       initial_sel=init)
+        eng.compute.synchronize()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / n * 1e3
+
+    reuse_ms = timed([1.0] + [0.0] * (sh.n_layers - 1))
+    query_ms = timed([1.0] * sh.n_layers, q_only)
+    buf.tokens[: wl.n_tokens].copy_(torch.from_numpy(np.asarray(tokens, np.int32)))
+    torch.cuda.synchronize()
+    log(f"full KV reuse (ratio 0 from layer 2): {reuse_ms:.3f} ms/step; query rows only: {query_ms:.3f} ms/step")
+    return {"ratio0_from_layer2_ms": round(reuse_ms, 4), "query_rows_only_ms": round(query_ms, 4),
+            "note": "eager launches; HBM-resident chunk caches; the position update of every cached row is included"}
+
+
+def run_peaks(eng):
+    """This GPU's own ceilings next to the published ones: a device-to-device copy (torch's copy
+    kernel, read + write bytes), a pinned host-to-device copy (copy engine), and a large bf16
+    product through the vendor BLAS (torch.mm, 8192^3)."""
+    import torch
+    dv = eng.device
+    st = torch.cuda.current_stream(dv)
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            fn()
+        e1.record(st)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    nb = 1 << 30
+    src = torch.empty(nb // 2, dtype=torch.bfloat16, device=dv)
+    dst = torch.empty_like(src)
+    copy_gbs = 2 * nb / timed(lambda: dst.copy_(src), 20) / 1e9
+    del src, dst
+    hb = 256 << 20
+    h = torch.empty(hb, dtype=torch.uint8, pin_memory=True)
+    d = torch.empty(hb, dtype=torch.uint8, device=dv)
+    h2d_gbs = hb / timed(lambda: d.copy_(h, non_blocking=True), 10) / 1e9
+    del h, d
+    m = 8192
+    a = torch.randn(m, m, device=dv, dtype=torch.bfloat16)
+    b = torch.randn(m, m, device=dv, dtype=torch.bfloat16)
+    c = torch.empty(m, m, device=dv, dtype=torch.bfloat16)
+    mm_tf = 2 * m ** 3 / timed(lambda: torch.mm(a, b, out=c), 20) / 1e12
+    del a, b, c
+    torch.cuda.synchronize()
+    log(f"peaks on this GPU: device copy {copy_gbs:.0f} GB/s, pinned H2D {h2d_gbs:.1f} GB/s, "
+        f"bf16 mm {mm_tf:.0f} TFLOP/s")
+    return {"device_copy_GBps": round(copy_gbs, 1), "pinned_h2d_GBps": round(h2d_gbs, 2),
+            "bf16_mm_8192_TFLOPs": round(mm_tf, 1),
+            "published": {"hbm_GBps": PEAK_HBM_GBS, "bf16_dense_TFLOPs": PEAK_BF16_TFLOPS, "pcie5_x16_GBps": 64.0},
+            "note": "torch copy_ (read + write bytes over 1 GiB), torch copy_ from 256 MiB pinned host memory, "
+                    "torch.mm bf16 8192 x 8192 x 8192"}
 
 
 def run_variants(eng, buf, tokens, offs, wl, fused, cache, steps):
@@ -248,50 +423,87 @@ def run_store(eng, buf, tokens, offs, wl, fused, steps):
     return out
 
 
+def _host_info():
+    """CPU model, logical CPUs and the BLAS numpy was built with."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg["Build Dependencies"]["blas"]
+        blas = f"{b.get('name')} {b.get('version', '')}".strip()
+    except Exception:
+        pass
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "blas": blas}
+
+
 def cpu_baseline(wl, budget_s: float = 25.0):
     """The oracle (fp64 NumPy with bf16 rounding points) on a bounded sample of the same
     workload: layer 1 (every row), layer 2 (all rows scored, 30% kept), layer 3 (15% kept)
-    and steady layers until the time budget; tokens/s extrapolated to all layers.  The chunk
-    caches are random bf16-valued arrays of the real shape (their values do not change the
-    oracle's cost); weights and tokens are the fixtures'."""
+    and steady layers until the time budget; tokens/s extrapolated to all layers.  The first
+    steady layer is timed a second time with BLAS limited to one thread.  The chunk caches are
+    random bf16-valued arrays of the real shape (their values do not change the oracle's cost);
+    weights and tokens are the fixtures'."""
     import fixtures as F
     import oracle as O
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
+        threadpool_limits = None
         threads = os.cpu_count() or 1
     sh = wl.shape
     prec = O.Precision("bf16")
     rng = np.random.default_rng(0)
     E = F.embedding(sh)
     tokens = F.all_tokens(wl)
-    offs = F.chunk_offsets(wl)
     n_ctx, n_tok, n_q = wl.n_ctx, wl.n_tokens, wl.n_query
     hidden = np.asarray(E[tokens], np.float64)
     del E
     sel = np.arange(n_tok)
     times = []
+    single = None
     t_start = time.perf_counter()
     for l in range(sh.n_layers):
         w = F.layer_weights(sh, l + 1)
         kc = prec.store(rng.standard_normal((n_ctx, sh.n_kv_heads, sh.head_dim)) * 0.3)
         vc = prec.store(rng.standard_normal((n_ctx, sh.n_kv_heads, sh.head_dim)) * 0.3)
+
+        def one_layer():
+            fk, fv = O.fuse_cache(sh, prec, [(kc, vc)], [0, n_ctx], n_q)
+            r = O.blend_layer(sh, w, prec, hidden, fk, fv, n_ctx, sel, n_q, wl.schedule[l])
+            return O.layer_rest(sh, w, prec, hidden, r["new_local"], r["out"]), r["new_sel"]
+
         t0 = time.perf_counter()
-        fk, fv = O.fuse_cache(sh, prec, [(kc, vc)], [0, n_ctx], n_q)
-        r = O.blend_layer(sh, w, prec, hidden, fk, fv, n_ctx, sel, n_q, wl.schedule[l])
-        hidden = O.layer_rest(sh, w, prec, hidden, r["new_local"], r["out"])
-        sel = r["new_sel"]
+        h_next, s_next = one_layer()
         times.append(time.perf_counter() - t0)
+        if l == 3 and threadpool_limits is not None:
+            with threadpool_limits(limits=1):
+                t0 = time.perf_counter()
+                one_layer()
+                single = time.perf_counter() - t0
+        hidden, sel = h_next, s_next
         if l >= 4 and time.perf_counter() - t_start > budget_s:
             break
     steady = float(np.median(times[3:])) if len(times) > 3 else times[-1]
     total = sum(times[:3]) + steady * (sh.n_layers - 3)
-    return {"value": n_ctx / total, "unit": "context tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"oracle (fp64 NumPy, bf16 rounding emulated) on layers 1-{len(times)} of the same workload "
-                       f"with random-valued chunk caches of the real shape; layer times "
-                       f"{[round(t, 3) for t in times]} s; blended prefill extrapolated as "
-                       f"T1+T2+T3+{sh.n_layers - 3}*median(steady) = {total:.2f} s")}
+    out = {"value": n_ctx / total, "unit": "context tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": (f"oracle (fp64 NumPy, bf16 rounding emulated) on layers 1-{len(times)} of the same workload "
+                      f"with random-valued chunk caches of the real shape; layer times "
+                      f"{[round(t, 3) for t in times]} s; blended prefill extrapolated as "
+                      f"T1+T2+T3+{sh.n_layers - 3}*median(steady) = {total:.2f} s")}
+    out.update(_host_info())
+    if single is not None:
+        out["single_thread_steady_layer_s"] = round(single, 3)
+        out["all_threads_steady_layer_s"] = round(times[3], 3)
+    return out
 
 
 def main() -> int:
@@ -304,6 +516,9 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=25.0)
     ap.add_argument("--only-blend", action="store_true",
                     help="skip the pinned-host and full-recompute passes (profiling runs)")
+    ap.add_argument("--ratios", default="",
+                    help="comma-separated steady ratios: also time the graph-replayed prefill with the schedule "
+                         "1.0, r, r, ... for each (e.g. 0.10,0.15,0.20 for the Mistral-7B-shaped sweep)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain device-to-device copy of 256 MiB, 3 times (counter calibration)")
     args = ap.parse_args()
@@ -379,6 +594,29 @@ def main() -> int:
     value = n_ctx * args.steps / wall
     log(f"blended prefill, graph replay: {ms_step:.3f} ms/step, {value:,.0f} context tokens/s")
 
+    sweep = None
+    if args.ratios:
+        sweep = {}
+        for r in [float(x) for x in args.ratios.split(",") if x]:
+            sched = [1.0] + [r] * (sh.n_layers - 1)
+            g = capture_step(eng, lambda: run_layers(eng, buf, tokens, offs, wl.n_query, sched, fused, cache=cache,
+                                                     upload_inputs=False))
+            with torch.cuda.stream(cs):
+                for _ in range(args.warmup):
+                    g.replay()
+            cs.synchronize()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            with torch.cuda.stream(cs):
+                for _ in range(args.steps):
+                    g.replay()
+            cs.synchronize()
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t0) / args.steps * 1e3
+            sweep[f"{r:.2f}"] = {"ms_per_step": round(ms, 4), "context_tokens_per_s": round(n_ctx / ms * 1e3, 1)}
+            log(f"ratio {r:.2f}: {ms:.3f} ms/step, {n_ctx / ms * 1e3:,.0f} context tokens/s")
+            del g
+
     # the same steps again with a HIP event pair around every launch (per-kernel durations)
     L.cb_profile_enable(eng.ctx, True)
     for _ in range(args.steps):
@@ -403,7 +641,7 @@ def main() -> int:
                          "frac": round(rate / peak, 4)}
     dom = max(kernels, key=lambda k: kernels[k]["ms_total_per_step"])
     dk = kernels[dom]
-    traffic = gate_up_traffic(sh, kept) if dom == "gemm_gate_up" else None
+    traffic = gate_up_traffic(sh, kept) if dom == "gemm_gate_up" and args.config == "qwen" else None
     roofline = {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"],
                 "peak": PEAK_BF16_TFLOPS if dk["bound"] == "mfma" else PEAK_HBM_GBS, "unit": dk["unit"],
                 "frac": dk["frac"], "traffic": None if traffic is None else round(traffic)}
@@ -414,7 +652,7 @@ def main() -> int:
     cs.synchronize()
     per_layer = [evs[i].elapsed_time(evs[i + 1]) for i in range(len(evs) - 1)]
 
-    pcie_ms = full_ms = controller = variants = decode_ms = store_res = None
+    pcie_ms = full_ms = controller = variants = decode_ms = store_res = overlap = reuse = peaks = None
     if not args.only_blend:
         # PCIe-inclusive variant: cached KV in pinned host memory, fetched one layer ahead
         for _ in range(2):
@@ -439,10 +677,13 @@ def main() -> int:
         cs.synchronize()
         full_ms = (time.perf_counter() - t0) / n_full * 1e3
         log(f"pinned-host prefetch: {pcie_ms:.3f} ms/step; full recompute: {full_ms:.3f} ms/step")
+        overlap = run_overlap(eng, buf, tokens, offs, wl, fused, host)
+        reuse = run_reuse(eng, buf, tokens, offs, wl, fused, cache, args.steps)
         controller = run_controller(eng, buf, tokens, offs, wl, fused, host, full_ms, args.steps)
         variants = run_variants(eng, buf, tokens, offs, wl, fused, cache, args.steps)
         decode_ms = run_decode(eng, buf, tokens, offs, wl, fused, cache)
         store_res = run_store(eng, buf, tokens, offs, wl, fused, args.steps)
+        peaks = run_peaks(eng)
     if args.calib_copy:
         src = torch.empty(128 << 20, dtype=torch.bfloat16, device=eng.device)
         dst = torch.empty_like(src)
@@ -460,10 +701,9 @@ def main() -> int:
         "metric": "blended-prefill context tokens/s @ r=15% + per-layer ms; % HBM/MFMA peak",
         "value": round(value, 1), "unit": "context tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"{wl.name}: Qwen2.5-1.5B-shaped blended prefill, 28 layers, 10x512-token cached "
-                               f"chunks + 64-token query, recompute 100% -> 30% -> 15%, cached KV resident in HBM",
-                   "n_ctx": n_ctx, "n_query": wl.n_query, "schedule": "1.0, 0.30, 0.15 x 26"},
+        "vs_baseline": None, "dtype": sh.dtype, "data": "synthetic",
+        "config": {"workload": describe(wl), "n_ctx": n_ctx, "n_query": wl.n_query,
+                   "schedule": schedule_text(wl.schedule)},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "per_layer_ms": {"layer1": round(per_layer[0], 4), "layer2": round(per_layer[1], 4),
@@ -474,12 +714,16 @@ def main() -> int:
         "pcie_prefetch": None if pcie_ms is None else {
             "ms_per_step": round(pcie_ms, 4), "context_tokens_per_s": round(n_ctx / pcie_ms * 1e3, 1),
             "host_kv_bytes_per_step": int(2 * sh.n_layers * n_ctx * sh.n_kv_heads * sh.head_dim * 2)},
+        "prefetch_per_layer": overlap,
         "eager_ms_per_step": round(eager_ms, 4),
         "full_recompute_ms": None if full_ms is None else round(full_ms, 4),
+        "full_reuse": reuse,
+        "peaks_measured": peaks,
         "loading_controller": controller,
         "selection_variants": variants,
         "decode": decode_ms,
         "chunk_store": store_res,
+        "ratio_sweep": sweep,
         "speedup_vs_full_recompute": None if full_ms is None else round(full_ms / ms_step, 3),
     }
     print(json.dumps(out), flush=True)

@@ -20,6 +20,8 @@ bf16 numbers.  RMSNorm gains are ones.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field, replace
 from typing import Dict, List, Tuple
 
@@ -114,15 +116,28 @@ def rng(stream: int, i: int = 0, j: int = 0) -> np.random.Generator:
 
 def to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """float32 -> bfloat16 bit patterns (uint16), round to nearest, ties to even."""
-    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return u.astype(np.uint16)
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    if not np.isfinite(u.view(np.float32)).all():
+        w = u.astype(np.uint64)
+        return ((w + 0x7FFF + ((w >> 16) & 1)) >> 16).astype(np.uint16)
+    # finite inputs: u + 0x8000 <= 0xFF807FFF, so the sum fits in 32 bits
+    r = (u >> 16) & 1
+    r += 0x7FFF
+    r += u
+    r >>= 16
+    return r.astype(np.uint16)
 
 
 def to_bf16_values(a: np.ndarray) -> np.ndarray:
     """float32 array whose values are the bfloat16 roundings of `a`."""
-    bits = to_bf16_bits(a).astype(np.uint32) << 16
-    return bits.view(np.float32)
+    u = np.array(a, dtype=np.float32, copy=True).view(np.uint32)
+    if not np.isfinite(u.view(np.float32)).all():
+        return (to_bf16_bits(a).astype(np.uint32) << 16).view(np.float32)
+    r = (u >> 16) & 1
+    r += 0x7FFF
+    u += r
+    u &= np.uint32(0xFFFF0000)
+    return u.view(np.float32)
 
 
 def _draw(shape: ModelShape, i: int, j: int, dims: Tuple[int, int]) -> np.ndarray:
@@ -139,7 +154,11 @@ def layer_weights(shape: ModelShape, layer: int) -> Dict[str, np.ndarray]:
     d, hq, hkv, dh, f = shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.ffn_dim
     dims = {"q": (hq * dh, d), "k": (hkv * dh, d), "v": (hkv * dh, d), "o": (d, hq * dh),
             "gate": (f, d), "up": (f, d), "down": (d, f)}
-    out = {"w_" + n: _draw(shape, layer, _TENSOR_ID[n], dims[n]) for n in dims}
+    # one generator per tensor: the draws are independent, so they run on a thread pool (numpy
+    # fills arrays without holding the interpreter lock) with the same values as a serial loop
+    with ThreadPoolExecutor(max_workers=min(len(dims), os.cpu_count() or 1)) as ex:
+        drawn = list(ex.map(lambda n: _draw(shape, layer, _TENSOR_ID[n], dims[n]), dims))
+    out = {"w_" + n: w for n, w in zip(dims, drawn)}
     out["g_attn"] = np.ones(d, np.float32)
     out["g_ffn"] = np.ones(d, np.float32)
     return out

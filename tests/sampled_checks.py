@@ -1,0 +1,98 @@
+"""Sampled, teacher-forced checks of one layer of a large blended prefill against the oracle.
+
+At sizes the oracle cannot run whole, each sampled layer is checked with the GPU's own inputs
+of that layer (the residual rows entering it and the fused cache it attends over):
+  * the kept set is exactly the top-k of the GPU's deviations (float32, ties to the lower
+    position) and ends with every query row;
+  * the deviation of sampled candidate rows equals the oracle's (fresh K/V against the
+    re-rotated GPU cache row);
+  * sampled recomputed rows of the fused cache hold the oracle's fresh K/V, sampled rows that
+    were not recomputed hold the re-rotated chunk cache (V bit for bit);
+  * the attention output and the layer output of sampled kept rows (always some query rows).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import fixtures as F
+import oracle as O
+from parity_util import assert_close
+
+
+def to_np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def check_layer(wl, layer, w, rec, h, cache_kv, fused_kv, n_sample=24, seed=100):
+    """wl: the workload; layer: 0-based; w: the oracle's weights of that layer; rec: the GPU's
+    LayerRecord; h: [len(rec.sel), d] residual rows entering the layer (GPU values);
+    cache_kv / fused_kv: (K, V) device tensors of the chunk cache and fused cache of the layer."""
+    sh = wl.shape
+    prec = O.Precision("bf16")
+    sel, new = rec.sel, rec.new_sel
+    n_ctx, n_q = wl.n_ctx, wl.n_query
+    n_cand = len(sel) - n_q
+    k = O.k_for_ratio(wl.schedule[layer], n_ctx, n_cand)
+    offs = F.chunk_offsets(wl)
+    rng = np.random.default_rng(seed + layer)
+    hq, hkv, dh = sh.n_q_heads, sh.n_kv_heads, sh.head_dim
+    assert h.shape[0] == len(sel)
+
+    # 1. kept set
+    dev = rec.deviation.astype(np.float32)
+    assert len(new) == k + n_q
+    assert np.array_equal(new[k:], np.arange(n_ctx, n_ctx + n_q))
+    assert np.array_equal(new[:k], np.sort(sel[:n_cand][O.topk_select(dev, k)]))
+
+    # 2. deviation of sampled candidate rows
+    ck, cv = to_np(cache_kv[0]), to_np(cache_kv[1])
+    rows = rng.choice(n_cand, size=min(n_sample, n_cand), replace=False)
+    pos = sel[rows]
+    chunk_of = np.searchsorted(offs, pos, side="right") - 1
+    k_rot = prec.store(O.rope_rotate(ck[pos], offs[chunk_of], sh.rope_base))
+    x = prec.store(O.rmsnorm(h[rows], w["g_attn"], sh.rms_eps))
+    k_new = prec.store(O.rope_rotate(O.project(x, w["w_k"]).reshape(-1, hkv, dh), pos, sh.rope_base))
+    v_new = prec.store(O.project(x, w["w_v"]).reshape(-1, hkv, dh))
+    d_ref = O.kv_deviation(k_new, v_new, k_rot, cv[pos])
+    err = np.abs(dev[rows] - d_ref) - 1e-3 * d_ref
+    assert err.max() <= 1e-3, f"layer {layer + 1}: deviation err {err.max():.3e}"
+
+    # 3. fused cache
+    fk, fv = to_np(fused_kv[0]), to_np(fused_kv[1])
+    assert_close(fk[pos], k_new, "bf16", f"layer {layer + 1}: fused K of recomputed rows")
+    assert_close(fv[pos], v_new, "bf16", f"layer {layer + 1}: fused V of recomputed rows")
+    untouched = np.setdiff1d(np.arange(n_ctx), sel)
+    if len(untouched):
+        urows = rng.choice(untouched, size=min(n_sample, len(untouched)), replace=False)
+        uchunk = np.searchsorted(offs, urows, side="right") - 1
+        rot = prec.store(O.rope_rotate(ck[urows], offs[uchunk], sh.rope_base))
+        assert_close(fk[urows], rot, "bf16", f"layer {layer + 1}: re-rotated K of untouched rows")
+        assert np.array_equal(fv[urows], cv[urows])
+
+    # 4. attention output and layer output of sampled kept rows
+    loc = {int(p): i for i, p in enumerate(sel)}
+    tail = min(8, len(new))
+    kept_rows = np.unique(np.concatenate([rng.choice(len(new), size=min(n_sample - 8, len(new)), replace=False),
+                                          np.arange(len(new) - tail, len(new))]))
+    kpos = new[kept_rows]
+    kloc = np.array([loc[int(p)] for p in kpos])
+    xq = prec.store(O.rmsnorm(h[kloc], w["g_attn"], sh.rms_eps))
+    q = prec.store(O.rope_rotate(O.project(xq, w["w_q"]).reshape(-1, hq, dh), kpos, sh.rope_base))
+    att = prec.store(O.causal_attention(q, fk, fv, kpos)).reshape(len(kpos), hq * dh)
+    assert_close(rec.out_sel[kept_rows], att, "bf16", f"attention output layer {layer + 1}")
+    h_next = O.layer_rest(sh, w, prec, h, kloc, rec.out_sel[kept_rows])
+    assert_close(rec.hidden_out[kept_rows], h_next, "bf16", f"layer output layer {layer + 1}")
+
+
+def check_chunk_cache(wl, layer, w, h, k_dev, v_dev):
+    """A chunk's cache is its own prefill at positions 0..: K/V of every row of the chunk at
+    `layer` against the oracle fed with the GPU's input rows h of that layer."""
+    sh = wl.shape
+    prec = O.Precision("bf16")
+    n = h.shape[0]
+    x = prec.store(O.rmsnorm(h, w["g_attn"], sh.rms_eps))
+    pos = np.arange(n)
+    k = prec.store(O.rope_rotate(O.project(x, w["w_k"]).reshape(n, sh.n_kv_heads, sh.head_dim), pos, sh.rope_base))
+    v = prec.store(O.project(x, w["w_v"]).reshape(n, sh.n_kv_heads, sh.head_dim))
+    assert_close(to_np(k_dev), k, "bf16", f"chunk-0 cache K layer {layer + 1}")
+    assert_close(to_np(v_dev), v, "bf16", f"chunk-0 cache V layer {layer + 1}")

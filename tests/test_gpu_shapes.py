@@ -1,0 +1,92 @@
+"""Parity at the larger model shapes' real per-layer sizes: Mistral-7B (4,096 context rows in 6
+chunks of 640 + 256 query rows, GQA group 4; recompute ratios 10%, 15% and 20%), Yi-34B (8 x 480
++ 256, group 7, d_model 7,168) and Llama-70B (group 8, d_model 8,192, FFN 28,672) at 4K and at
+16K context (32 x 512 + 256 rows: the largest prompt, 16,640 rows through layer 1).
+
+The first three decoder layers of each shape run (layer 1 at ratio 1, layer 2 narrowing to the
+ratio, layer 3 at the steady ratio); every kernel sees the same sizes at any depth, so these
+layers cover the whole model's launch shapes.  Each layer is checked against the oracle with the
+GPU's own inputs of that layer (teacher-forced, sampled rows), as at the benchmark's size."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import fixtures as F
+from sampled_checks import check_chunk_cache, check_layer
+
+pytestmark = pytest.mark.gpu
+
+N_LAYERS = 3
+CASES = ("mistral_r10", "mistral_r15", "mistral_r20", "yi_r15", "l70_4k", "l70_16k")
+
+_state = {"shape": None}
+
+
+def _reduced(name):
+    wl = F.get_config(name)
+    return replace(wl, shape=replace(wl.shape, n_layers=N_LAYERS), schedule=wl.schedule[:N_LAYERS])
+
+
+def _engine(wl):
+    """One engine per model shape (weights of the first layers), kept while its cases run."""
+    from rag_kv_cache_amd.pipeline import Engine
+    sh = wl.shape
+    if _state["shape"] != sh.name:
+        if _state.get("eng") is not None:
+            _state["eng"].close()
+        _state.clear()
+        _state["shape"] = None
+        max_tok = max(_reduced(c).n_tokens for c in CASES if F.get_config(c).shape.name == sh.name)
+        print(f"[shapes] loading {sh.name}: d {sh.d_model}, heads {sh.n_q_heads}/{sh.n_kv_heads}, "
+              f"ffn {sh.ffn_dim}, {N_LAYERS} layers, up to {max_tok} rows", flush=True)
+        W = [F.layer_weights(sh, l) for l in range(1, N_LAYERS + 1)]
+        emb = F.embedding(sh)
+        eng = Engine(sh, max_tokens=max_tok)
+        eng.load_all(lambda l: W[l - 1], emb)
+        _state.update(shape=sh.name, eng=eng, W=W, emb=emb)
+    return _state["eng"], _state["W"], _state["emb"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _release():
+    yield
+    if _state.get("eng") is not None:
+        _state["eng"].close()
+    _state.clear()
+
+
+@pytest.mark.parametrize("name", CASES)
+def test_shape_teacher_forced(name):
+    from rag_kv_cache_amd.pipeline import build_chunk_caches, make_buffers, run_layers
+    wl = _reduced(name)
+    sh = wl.shape
+    eng, W, emb = _engine(wl)
+    print(f"[shapes] {name}: {wl.n_ctx} context + {wl.n_query} query rows, schedule {wl.schedule}", flush=True)
+    chunks = F.chunk_tokens(wl)
+    tokens = F.all_tokens(wl)
+    cache, _ = build_chunk_caches(eng, chunks)
+    buf = make_buffers(eng, wl.n_tokens, len(chunks))
+    fused = [(eng.kv_empty(wl.n_tokens), eng.kv_empty(wl.n_tokens)) for _ in range(N_LAYERS)]
+    res = run_layers(eng, buf, tokens, F.chunk_offsets(wl), wl.n_query, wl.schedule, fused,
+                     cache=cache, record=True)
+    eng.compute.synchronize()
+    k = int(np.floor(float(np.float32(wl.schedule[-1])) * wl.n_ctx + 0.5))
+    assert res.n_final == k + wl.n_query
+    hidden_in = [np.asarray(emb[tokens], np.float64)] + [r.hidden_out for r in res.records[:-1]]
+    for layer in range(N_LAYERS):
+        print(f"[shapes] {name}: layer {layer + 1}, {len(res.records[layer].sel)} -> "
+              f"{len(res.records[layer].new_sel)} rows", flush=True)
+        check_layer(wl, layer, W[layer], res.records[layer], hidden_in[layer], cache[layer], fused[layer])
+
+    # chunk 0's cache at the last layer: its own prefill at positions 0..
+    toks = chunks[0]
+    n = len(toks)
+    cbuf = make_buffers(eng, n, 0)
+    tmp = [(eng.kv_empty(n), eng.kv_empty(n)) for _ in range(N_LAYERS)]
+    rec = run_layers(eng, cbuf, toks, [0], n, [1.0] * N_LAYERS, tmp, record=True).records
+    eng.compute.synchronize()
+    last = N_LAYERS - 1
+    check_chunk_cache(wl, last, W[last], rec[last - 1].hidden_out.astype(np.float64),
+                      cache[last][0][:n], cache[last][1][:n])
+    del cache, fused, buf
