@@ -14,7 +14,8 @@ From the pages:
   token (a fixed latency left aside); below it, recompute.
 
 Readings: a layer's recompute time is linear in the ratio (the explainer's equation applied
-per layer, T_prefill split evenly over the layers); the planned ratio is the largest one whose
+per layer, T_prefill split evenly over the layers; plan_ratio_measured adds a measured
+ratio-independent part and the full first layer); the planned ratio is the largest one whose
 recompute still hides under the layer's load, kept inside [r_min, r_max] (the quality floor
 and the point past which recompute cannot hide); when the bandwidth is at or below break-even
 the plan is to recompute everything and load nothing.
@@ -65,3 +66,32 @@ def plan_ratio(n_ctx: int, n_layers: int, kv_bytes_per_token_layer: float, bandw
     r = min(max(r, r_min), r_max)
     tr = t_recompute(r, t_pre_layer)
     return Plan(True, r, tl, tr, t_layer(tl, tr), n_layers * t_layer(tl, tr), be)
+
+
+def plan_ratio_measured(n_layers: int, kv_bytes_layer: float, bandwidth: float, t_first_layer: float,
+                        t_full_layer: float, t_fixed_layer: float, r_min: float, r_max: float,
+                        latency_layer: float = 0.0) -> Plan:
+    """The same policy with a layer's recompute time measured on the GPU instead of an even
+    split of the full prefill.  Reading: the explainer's T_recompute = r * T_prefill, taken per
+    layer with a ratio-independent part added, T_recompute(r) = t_fixed + r (t_full - t_fixed)
+    (t_full: a layer recomputing every row; t_fixed: a layer recomputing none, i.e. the query
+    rows, norms, attention over the cache and the fixed kernel costs); t_fixed = 0 is the
+    explainer's model.  Loading pays when a layer's load, and the least recompute allowed,
+    both take less than recomputing the layer: max(T_load, T_recompute(r_min)) < t_full.  The
+    first layer recomputes every row whatever the plan (layer 1 scores all tokens), so the step
+    is t_first + (L - 1) T_layer.  break_even: the bandwidth at which a layer's load (latency
+    aside) takes t_full."""
+    be = kv_bytes_layer / t_full_layer
+    tl = t_load(1, kv_bytes_layer, bandwidth, latency_layer)
+    slope = t_full_layer - t_fixed_layer
+
+    def rec(r):
+        return t_fixed_layer + r * slope
+
+    if max(tl, rec(r_min)) >= t_full_layer:
+        return Plan(False, 1.0, 0.0, t_full_layer, t_full_layer,
+                    t_first_layer + (n_layers - 1) * t_full_layer, be)
+    r = (tl - t_fixed_layer) / slope
+    r = min(max(r, r_min), r_max)
+    tr = rec(r)
+    return Plan(True, r, tl, tr, t_layer(tl, tr), t_first_layer + (n_layers - 1) * t_layer(tl, tr), be)

@@ -75,3 +75,63 @@ def test_plan_hides_recompute_under_load_and_falls_with_bandwidth():
     # unclamped, the ratio is the load / prefill time ratio of a layer: at 10x break-even, 0.1
     p = C.plan_ratio(n_ctx, L, per_tok_layer, 10 * be, pre, 0.01, 1.0)
     assert abs(p.ratio - 0.1) < 1e-12
+
+
+def test_measured_plan_reduces_to_the_explainers_model():
+    # t_fixed = 0 and the full prefill split evenly over the layers: the measured plan takes the
+    # same decision, ratio and per-layer times as plan_ratio (pinned above to the pages' numbers);
+    # only the total differs, by counting the first layer at its full cost
+    rng = np.random.default_rng(4)
+    for _ in range(300):
+        n_ctx, L = int(rng.integers(64, 20000)), int(rng.integers(2, 90))
+        kvb = float(rng.uniform(256, 40000))
+        pre = float(10 ** rng.uniform(-6.5, -3.5))
+        bw = float(10 ** rng.uniform(7, 12))
+        r_min = float(rng.uniform(0, 0.3))
+        r_max = float(rng.uniform(r_min, 1.0))
+        a = C.plan_ratio(n_ctx, L, kvb, bw, pre, r_min, r_max)
+        t_full = n_ctx * pre / L
+        b = C.plan_ratio_measured(L, n_ctx * kvb, bw, t_full, t_full, 0.0, r_min, r_max)
+        if abs(bw / a.break_even - 1) < 1e-9:
+            continue                                   # the tie itself may go either way in rounding
+        assert a.load == b.load
+        assert abs(a.ratio - b.ratio) <= 1e-12 * max(1, a.ratio)
+        for f in ("t_load_layer", "t_recompute_layer", "t_layer"):
+            assert abs(getattr(a, f) - getattr(b, f)) <= 1e-12 * max(1e-9, getattr(a, f))
+        assert abs(a.break_even / b.break_even - 1) < 1e-12
+        assert abs(b.t_total - (t_full + (L - 1) * b.t_layer)) <= 1e-12 * b.t_total
+
+
+def test_measured_plan_against_a_grid_search():
+    # the largest ratio on a fine grid whose recompute still fits under the load
+    rng = np.random.default_rng(5)
+    grid = np.linspace(0.0, 1.0, 100001)
+    for _ in range(200):
+        t_full = float(rng.uniform(0.2e-3, 2e-3))
+        t_fix = float(rng.uniform(0, 0.6)) * t_full
+        tl = float(rng.uniform(0.3, 1.2)) * t_full
+        r_min, r_max = 0.05, 0.8
+        p = C.plan_ratio_measured(28, tl * 40e9, 40e9, 1e-3, t_full, t_fix, r_min, r_max)
+        rec = t_fix + grid * (t_full - t_fix)
+        if max(tl, t_fix + r_min * (t_full - t_fix)) >= t_full:
+            assert not p.load and p.ratio == 1.0 and p.t_layer == t_full
+            continue
+        ok = grid[(rec <= tl) & (grid >= r_min) & (grid <= r_max)]
+        want = ok.max() if len(ok) else r_min
+        assert p.load and abs(p.ratio - want) <= 1.01e-5
+        assert abs(p.t_load_layer - tl) <= 1e-12 * tl
+        assert p.t_layer == max(p.t_load_layer, p.t_recompute_layer)
+        assert abs(p.t_total - (1e-3 + 27 * p.t_layer)) <= 1e-15 + 1e-12 * p.t_total
+
+
+def test_measured_plan_special_cases():
+    # a fixed recompute cost above the load: nothing more can hide, the ratio floor is used
+    p = C.plan_ratio_measured(10, 1e6, 1e10, 2e-3, 1e-3, 0.5e-3, 0.1, 0.9)   # load 0.1 ms
+    assert p.load and p.ratio == 0.1 and abs(p.t_layer - (0.5e-3 + 0.1 * 0.5e-3)) < 1e-15
+    # load slower than recomputing the layer: recompute everything
+    p = C.plan_ratio_measured(10, 1e6, 0.5e9, 2e-3, 1e-3, 0.2e-3, 0.1, 0.9)  # load 2 ms
+    assert not p.load and p.ratio == 1.0 and abs(p.t_total - (2e-3 + 9e-3)) < 1e-15
+    # the review's Llama-7B example (load 16 ms against 3 ms of recompute): load-bound, the plan
+    # raises the ratio to its ceiling and the layer takes the load time
+    p = C.plan_ratio_measured(32, 16e-3 * 1e9, 1e9, 20e-3, 20e-3, 0.0, 0.15, 0.5)
+    assert p.load and p.ratio == 0.5 and abs(p.t_layer - 16e-3) < 1e-15
