@@ -102,55 +102,85 @@ def gate_up_traffic(shape, kept_rows):
     return total / len(kept_rows)
 
 
-def run_controller(eng, buf, tokens, offs, wl, fused, host, full_ms, steps):
-    """The loading controller on this GPU: the pinned-host load bandwidth measured by fetching a
-    whole step's cached KV alone, the prefill time per token from the full recompute, the ratio
-    cb_plan_ratio chooses (layer 1 stays at 1), and the pinned-host blended prefill run at it."""
+def run_controller(eng, buf, tokens, offs, wl, fused, host, full_ms, overlap, steps):
+    """The loading controller on this GPU, two ways, each followed by the pinned-host prefill run
+    at the ratio it plans (layer 1 stays at 1):
+      * cb_plan_ratio (the explainer's model): the load bandwidth of a whole step's cached KV
+        fetched alone, and the full prefill split evenly over the layers and tokens;
+      * cb_plan_ratio_measured: a layer's load time from the per-layer fetch measurement, and a
+        layer's recompute time measured at ratio 1 (every row) and at ratio 0 (no context row:
+        the fixed part), layer 1 counted at its own measured time.
+    Both with a ratio floor of 5% (below the workload's 15%, so that the plan is not just the
+    floor) and no ceiling."""
     import torch
     from rag_kv_cache_amd import _lib as L
     from rag_kv_cache_amd.pipeline import run_layers
     sh = wl.shape
-    n_chunks = len(offs) - 1
+    nl = sh.n_layers
     kv_layer_tok = 2 * sh.n_kv_heads * sh.head_dim * 2
+    kv_layer = wl.n_ctx * kv_layer_tok
+    r_min, r_max = 0.05, 1.0
 
-    def fetch_all():
-        for l in range(sh.n_layers):
-            L.cb_fetch_layer(eng.ctx, l, [int(host[l][c][0].data_ptr()) for c in range(n_chunks)],
-                             [int(host[l][c][1].data_ptr()) for c in range(n_chunks)], offs, n_chunks,
-                             int(buf.offsets.data_ptr()), int(fused[l][0].data_ptr()), int(fused[l][1].data_ptr()))
-        for l in range(sh.n_layers):
-            L.cb_synchronize(eng.ctx, l)
+    def layer_times(sched, reps=3):
+        rows = []
+        for r in range(reps + 1):
+            evs = []
+            run_layers(eng, buf, tokens, offs, wl.n_query, sched, fused, upload_inputs=False, cache=None,
+                       layer_events=evs)
+            eng.compute.synchronize()
+            if r:
+                rows.append([evs[i].elapsed_time(evs[i + 1]) for i in range(nl)])
+        return np.median(np.array(rows), axis=0) * 1e-3
+
+    def run_plan(plan):
+        sched = [1.0] + [float(plan.ratio) if plan.load else 1.0] * (nl - 1)
+        kw = dict(host_cache=host) if plan.load else dict(cache=None)
+        n = max(3, steps // 2)
+        for r in range(n + 2):
+            if r == 2:
+                eng.compute.synchronize()
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+            run_layers(eng, buf, tokens, offs, wl.n_query, sched, fused, upload_inputs=False, **kw)
         eng.compute.synchronize()
-        eng.copy.synchronize()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / n * 1e3
 
-    fetch_all()
-    t0 = time.perf_counter()
-    for _ in range(3):
-        fetch_all()
-    load_s = (time.perf_counter() - t0) / 3
-    bw = sh.n_layers * wl.n_ctx * kv_layer_tok / load_s
+    def summary(plan, ms):
+        return {"load": bool(plan.load), "ratio": round(float(plan.ratio), 4),
+                "t_load_layer_ms": round(plan.t_load_layer * 1e3, 4),
+                "t_recompute_layer_ms": round(plan.t_recompute_layer * 1e3, 4),
+                "break_even_GBps": round(plan.break_even_bandwidth / 1e9, 2),
+                "predicted_ms_per_step": round(plan.t_total * 1e3, 4), "measured_ms_per_step": round(ms, 4),
+                "context_tokens_per_s": round(wl.n_ctx / ms * 1e3, 1)}
+
+    # the explainer's model
+    load_s = sum(overlap["t_load_ms"]) * 1e-3
+    bw = nl * kv_layer / load_s
     pre = full_ms * 1e-3 / wl.n_tokens
-    plan = L.cb_plan_ratio(wl.n_ctx, sh.n_layers, kv_layer_tok, bw, pre, 0.0, 0.05, 1.0)
-    sched = [1.0] + [float(plan.ratio) if plan.load else 1.0] * (sh.n_layers - 1)
-    kw = dict(host_cache=host) if plan.load else dict(cache=None)
-    for _ in range(2):
-        run_layers(eng, buf, tokens, offs, wl.n_query, sched, fused, upload_inputs=False, **kw)
-    eng.compute.synchronize()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    n = max(3, steps // 2)
-    for _ in range(n):
-        run_layers(eng, buf, tokens, offs, wl.n_query, sched, fused, upload_inputs=False, **kw)
-    eng.compute.synchronize()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) / n * 1e3
-    log(f"controller: load {bw / 1e9:.1f} GB/s, break-even {plan.break_even_bandwidth / 1e9:.1f} GB/s, "
-        f"ratio {plan.ratio:.3f} (load={plan.load}), predicted {plan.t_total * 1e3:.3f} ms, measured {ms:.3f} ms/step")
-    return {"load_bandwidth_GBps": round(bw / 1e9, 2), "prefill_us_per_token": round(pre * 1e6, 4),
-            "break_even_GBps": round(plan.break_even_bandwidth / 1e9, 2), "load": bool(plan.load),
-            "ratio": round(float(plan.ratio), 4), "predicted_ms_per_step": round(plan.t_total * 1e3, 4),
-            "measured_ms_per_step": round(ms, 4), "context_tokens_per_s": round(wl.n_ctx / ms * 1e3, 1),
-            "schedule": "1.0, then the planned ratio (pinned-host cache fetched two layers ahead)"}
+    even = L.cb_plan_ratio(wl.n_ctx, nl, kv_layer_tok, bw, pre, 0.0, r_min, r_max)
+    even_ms = run_plan(even)
+    # the measured model (the fused buffers hold every layer's re-rotated cache after a fetch pass)
+    t_full = layer_times([1.0] * nl)
+    t_zero = layer_times([1.0] + [0.0] * (nl - 1))
+    t_first = float(t_full[0])
+    t_full_l = float(np.median(t_full[1:]))
+    t_fixed_l = min(float(np.median(t_zero[2:])), t_full_l)
+    t_load_l = float(np.median(overlap["t_load_ms"])) * 1e-3
+    meas = L.cb_plan_ratio_measured(nl, kv_layer, kv_layer / t_load_l, 0.0, t_first, t_full_l, t_fixed_l, r_min, r_max)
+    meas_ms = run_plan(meas)
+    log(f"controller (even split): load {bw / 1e9:.1f} GB/s, ratio {even.ratio:.3f}, predicted "
+        f"{even.t_total * 1e3:.3f} ms, measured {even_ms:.3f} ms/step")
+    log(f"controller (measured layer times: first {t_first * 1e3:.3f}, full {t_full_l * 1e3:.3f}, fixed "
+        f"{t_fixed_l * 1e3:.3f}, load {t_load_l * 1e3:.3f} ms): ratio {meas.ratio:.3f} (load={meas.load}), "
+        f"predicted {meas.t_total * 1e3:.3f} ms, measured {meas_ms:.3f} ms/step")
+    return {"r_min": r_min, "r_max": r_max,
+            "even_split": dict(summary(even, even_ms), load_bandwidth_GBps=round(bw / 1e9, 2),
+                               prefill_us_per_token=round(pre * 1e6, 4)),
+            "measured_layers": dict(summary(meas, meas_ms), t_first_ms=round(t_first * 1e3, 4),
+                                    t_full_layer_ms=round(t_full_l * 1e3, 4),
+                                    t_fixed_layer_ms=round(t_fixed_l * 1e3, 4)),
+            "schedule": "1.0, then the planned ratio (pinned-host cache fetched two layers ahead; eager launches)"}
 
 
 def _fetch_layer(eng, buf, host, offs, l, fused):
@@ -229,35 +259,42 @@ def run_overlap(eng, buf, tokens, offs, wl, fused, host, reps: int = 5, eps_ms: 
 
 
 def run_reuse(eng, buf, tokens, offs, wl, fused, cache, steps):
-    """Lower bounds on the same GPU and kernels (HBM-resident cache, eager launches): full KV reuse
-    as ratio 0 from layer 2 (layer 1 recomputes every row, later layers only the query rows), and
-    no context row recomputed at any layer (only the query rows run through the model over the
-    re-rotated caches)."""
+    """Lower bounds on the same GPU and kernels (HBM-resident cache, graph replay as for value):
+    full KV reuse as ratio 0 from layer 2 (layer 1 recomputes every row, later layers only the
+    query rows), and no context row recomputed at any layer (only the query rows run through
+    the model over the re-rotated caches)."""
     import torch
-    from rag_kv_cache_amd.pipeline import run_layers
+    from rag_kv_cache_amd.pipeline import capture_step, run_layers
     sh = wl.shape
-    n = max(3, steps // 2)
+    cs = eng.compute
     q_only = list(range(wl.n_ctx, wl.n_tokens))
 
     def timed(sched, init=None):
-        for r in range(n + 2):
-            if r == 2:
-                eng.compute.synchronize()
-                torch.cuda.synchronize()
-                t0 = time.perf_counter()
-            run_layers(eng, buf, tokens, offs, wl.n_query, sched, fused, cache=cache, upload_inputs=False,
-                       initial_sel=init)
-        eng.compute.synchronize()
+        run_layers(eng, buf, tokens, offs, wl.n_query, sched, fused, cache=cache, upload_inputs=init is None,
+                   initial_sel=init)
+        g = capture_step(eng, lambda: run_layers(eng, buf, tokens, offs, wl.n_query, sched, fused, cache=cache,
+                                                 upload_inputs=False, initial_sel=init, sel_uploaded=True))
+        with torch.cuda.stream(cs):
+            for _ in range(3):
+                g.replay()
+        cs.synchronize()
         torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / n * 1e3
+        t0 = time.perf_counter()
+        with torch.cuda.stream(cs):
+            for _ in range(steps):
+                g.replay()
+        cs.synchronize()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps * 1e3
 
     reuse_ms = timed([1.0] + [0.0] * (sh.n_layers - 1))
     query_ms = timed([1.0] * sh.n_layers, q_only)
     buf.tokens[: wl.n_tokens].copy_(torch.from_numpy(np.asarray(tokens, np.int32)))
+    buf.offsets[: len(offs)].copy_(torch.tensor(offs, dtype=torch.int32))
     torch.cuda.synchronize()
     log(f"full KV reuse (ratio 0 from layer 2): {reuse_ms:.3f} ms/step; query rows only: {query_ms:.3f} ms/step")
     return {"ratio0_from_layer2_ms": round(reuse_ms, 4), "query_rows_only_ms": round(query_ms, 4),
-            "note": "eager launches; HBM-resident chunk caches; the position update of every cached row is included"}
+            "note": "graph replay; HBM-resident chunk caches; the position update of every cached row is included"}
 
 
 def run_peaks(eng):
@@ -679,7 +716,7 @@ def main() -> int:
         log(f"pinned-host prefetch: {pcie_ms:.3f} ms/step; full recompute: {full_ms:.3f} ms/step")
         overlap = run_overlap(eng, buf, tokens, offs, wl, fused, host)
         reuse = run_reuse(eng, buf, tokens, offs, wl, fused, cache, args.steps)
-        controller = run_controller(eng, buf, tokens, offs, wl, fused, host, full_ms, args.steps)
+        controller = run_controller(eng, buf, tokens, offs, wl, fused, host, full_ms, overlap, args.steps)
         variants = run_variants(eng, buf, tokens, offs, wl, fused, cache, args.steps)
         decode_ms = run_decode(eng, buf, tokens, offs, wl, fused, cache)
         store_res = run_store(eng, buf, tokens, offs, wl, fused, args.steps)

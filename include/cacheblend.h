@@ -129,6 +129,14 @@ cb_status cb_embed(cb_ctx* ctx, const int32_t* tokens, int32_t n, const void* ta
 typedef enum { CB_FETCH_COPY = 0, CB_FETCH_KERNEL = 1 } cb_fetch_mode;
 cb_status cb_set_fetch_mode(cb_ctx* ctx, int32_t mode);
 
+/* Launch shape of the CB_FETCH_KERNEL path: `blocks` workgroups of `threads` threads (a
+ * multiple of 64, at most 1024), each thread keeping `unroll` (1, 2 or 4) row pieces of 16
+ * bytes of K and V in flight.  The reads cross PCIe, so a few requests in flight already reach
+ * the link's rate; more only queue in the memory system that the compute stream's kernels
+ * share.  Results do not depend on the shape.  (0, 0, 0) restores the library's default
+ * shape.  CB_EINVAL outside these ranges. */
+cb_status cb_set_fetch_launch(cb_ctx* ctx, int32_t blocks, int32_t threads, int32_t unroll);
+
 cb_status cb_fetch_layer(cb_ctx* ctx, int32_t layer, const void* const* host_k,
                          const void* const* host_v, const int32_t* chunk_offsets_host,
                          int32_t n_chunks, const int32_t* chunk_offsets_dev, void* fused_k,
@@ -279,6 +287,23 @@ typedef struct {
 cb_status cb_plan_ratio(int32_t n_ctx, int32_t n_layers, double kv_bytes_per_token_layer, double bandwidth,
                         double prefill_s_per_token, double latency_layer_s, float r_min, float r_max,
                         cb_ratio_plan* out);
+
+/* The same policy with a layer's recompute time measured on this GPU (seconds) instead of an
+ * even split of the full prefill: T_recompute(r) = t_fixed_layer + r * (t_full_layer -
+ * t_fixed_layer), where t_full_layer is a layer recomputing every row and t_fixed_layer a layer
+ * recomputing none (query rows, attention over the cache, fixed kernel costs); t_fixed_layer = 0
+ * is the explainer's linear model.  Per layer T_load = kv_bytes_layer / bandwidth +
+ * latency_layer_s.  Loading pays when max(T_load, T_recompute(r_min)) < t_full_layer; then
+ * ratio = (T_load - t_fixed_layer) / (t_full_layer - t_fixed_layer) clamped to [r_min, r_max]
+ * and T_layer = max(T_load, T_recompute(ratio)); otherwise load = 0, ratio = 1, T_layer =
+ * t_full_layer, t_load_layer = 0.  The first layer recomputes every row in either case:
+ * t_total = t_first_layer + (n_layers - 1) * T_layer.  break_even_bandwidth =
+ * kv_bytes_layer / t_full_layer.  CB_EINVAL for non-positive sizes, bandwidth or t_full_layer,
+ * negative latency or t_first_layer, t_fixed_layer outside [0, t_full_layer], or ratios outside
+ * 0 <= r_min <= r_max <= 1. */
+cb_status cb_plan_ratio_measured(int32_t n_layers, double kv_bytes_layer, double bandwidth, double latency_layer_s,
+                                 double t_first_layer, double t_full_layer, double t_fixed_layer, float r_min,
+                                 float r_max, cb_ratio_plan* out);
 
 /* ---------------------------------------------------------------- chunk KV store
  * The offline side of the path: every chunk is prefilled alone at positions 0.. (CacheBlend

@@ -62,6 +62,7 @@ _SIGS = {
     "cb_fetch_layer": [_P, _I, C.POINTER(_P), C.POINTER(_P), C.POINTER(_I), _I, _P, _P, _P],
     "cb_fetch_layer_device": [_P, _I, _P, _P, C.POINTER(_I), _I, _P, _P, _P],
     "cb_set_fetch_mode": [_P, _I],
+    "cb_set_fetch_launch": [_P, _I, _I, _I],
     "cb_rotate_layers": [_P, _I, _I, C.POINTER(_P), C.POINTER(_P), C.POINTER(_I), _I, _P, C.POINTER(_P), C.POINTER(_P)],
     "cb_synchronize": [_P, _I],
     "cb_blend_layer": [_P, _I, _P, _P, _P, _P, _P, _P, _P, C.POINTER(_I), _I, _P, _I, _I, C.c_float, _P, _P,
@@ -71,6 +72,8 @@ _SIGS = {
     "cb_set_score_mode": [_P, _I],
     "cb_seam_select": [C.POINTER(_I), _I, _I, _I, C.POINTER(_I), _I, C.POINTER(_I)],
     "cb_plan_ratio": [_I, _I, C.c_double, C.c_double, C.c_double, C.c_double, C.c_float, C.c_float, _P],
+    "cb_plan_ratio_measured": [_I, C.c_double, C.c_double, C.c_double, C.c_double, C.c_double, C.c_double,
+                               C.c_float, C.c_float, _P],
     "cb_sha256": [_P, C.c_size_t, _P],
     "cb_chunk_key": [_P, _I, _P, _I, C.POINTER(C.c_uint64)],
     "cb_store_create": [C.POINTER(cb_model_desc), _I, _I, _I, C.POINTER(_P)],
@@ -152,6 +155,10 @@ def cb_set_fetch_mode(ctx: int, mode: int) -> None:
     _check(_L.cb_set_fetch_mode(ctx, mode))
 
 
+def cb_set_fetch_launch(ctx: int, blocks: int, threads: int, unroll: int) -> None:
+    _check(_L.cb_set_fetch_launch(ctx, blocks, threads, unroll))
+
+
 def cb_rotate_layers(ctx: int, first_layer: int, cache_k: Sequence[int], cache_v: Sequence[int],
                      chunk_offsets: Sequence[int], n_chunks: int, chunk_offsets_dev: int, fused_k: Sequence[int],
                      fused_v: Sequence[int]) -> None:
@@ -219,6 +226,15 @@ def cb_plan_ratio(n_ctx: int, n_layers: int, kv_bytes_per_token_layer: float, ba
     out = cb_ratio_plan()
     _check(_L.cb_plan_ratio(n_ctx, n_layers, kv_bytes_per_token_layer, bandwidth, prefill_s_per_token,
                             latency_layer_s, r_min, r_max, C.byref(out)))
+    return out
+
+
+def cb_plan_ratio_measured(n_layers: int, kv_bytes_layer: float, bandwidth: float, latency_layer_s: float,
+                           t_first_layer: float, t_full_layer: float, t_fixed_layer: float, r_min: float,
+                           r_max: float) -> cb_ratio_plan:
+    out = cb_ratio_plan()
+    _check(_L.cb_plan_ratio_measured(n_layers, kv_bytes_layer, bandwidth, latency_layer_s, t_first_layer,
+                                     t_full_layer, t_fixed_layer, r_min, r_max, C.byref(out)))
     return out
 
 

@@ -68,9 +68,14 @@ struct FetchChunks {
   int offs[kFetchMaxChunks + 1];
   int n;
 };
-// Read them, rotate K by R(o_c), copy V, into kf / vf (device); n_blocks workgroups.
+// Launch shape of the fetch: workgroups, threads per workgroup (a multiple of 64, <= 1024) and
+// 16-byte row pieces each thread keeps in flight (1, 2 or 4; four loads each).
+struct FetchLaunch {
+  int blocks, threads, unroll;
+};
+// Read them, rotate K by R(o_c), copy V, into kf / vf (device).
 hipError_t fetch_rope(const FetchChunks& F, void* kf, void* vf, int hkv, int dh, const float2* table, int table_rows,
-                      int bf16, int n_blocks, hipStream_t s);
+                      int bf16, const FetchLaunch& fl, hipStream_t s);
 // table: [table_rows][dh / 2] cos/sin; a chunk offset outside [0, table_rows) is clamped.
 hipError_t rope_delta(const void* kc, const void* vc, void* kf, void* vf, int n_ctx, int hkv, int dh,
                       const int32_t* offs, int n_chunks, const float2* table, int table_rows, int bf16,

@@ -246,11 +246,10 @@ __device__ __forceinline__ void unpack16<bf16_t>(const uint4 v, float* o) {
   }
 }
 
-template <typename T>
+template <typename T, int FU>
 __global__ __launch_bounds__(1024) void fetch_rope_kernel(FetchChunks F, T* kf, T* vf, int hkv, int dh,
                                                          const float2* table, int table_rows) {
   constexpr int VE = Vec16<T>::N;
-  constexpr int FU = 4;
   const int half = dh >> 1;
   const int vph = half / VE;
   const int vpr = hkv * vph;
@@ -432,17 +431,26 @@ hipError_t rope_delta_layers(const RopeLayers& L, int n_layers, int n_ctx, int h
   return hipGetLastError();
 }
 
-hipError_t fetch_rope(const FetchChunks& F, void* kf, void* vf, int hkv, int dh, const float2* table, int table_rows,
-                      int bf16, int n_blocks, hipStream_t s) {
-  if (F.n <= 0 || F.offs[F.n] <= F.offs[0]) return hipSuccess;
-  if (F.n > kFetchMaxChunks) return hipErrorInvalidValue;
-  if (bf16)
-    hipLaunchKernelGGL(fetch_rope_kernel<bf16_t>, dim3(n_blocks), dim3(1024), 0, s, F, (bf16_t*)kf, (bf16_t*)vf, hkv,
-                       dh, table, table_rows);
-  else
-    hipLaunchKernelGGL(fetch_rope_kernel<float>, dim3(n_blocks), dim3(1024), 0, s, F, (float*)kf, (float*)vf, hkv, dh,
-                       table, table_rows);
+template <typename T>
+hipError_t launch_fetch(const FetchChunks& F, T* kf, T* vf, int hkv, int dh, const float2* table, int table_rows,
+                        const FetchLaunch& fl, hipStream_t s) {
+  const dim3 grid(fl.blocks), block(fl.threads);
+  switch (fl.unroll) {
+    case 1: hipLaunchKernelGGL((fetch_rope_kernel<T, 1>), grid, block, 0, s, F, kf, vf, hkv, dh, table, table_rows); break;
+    case 2: hipLaunchKernelGGL((fetch_rope_kernel<T, 2>), grid, block, 0, s, F, kf, vf, hkv, dh, table, table_rows); break;
+    case 4: hipLaunchKernelGGL((fetch_rope_kernel<T, 4>), grid, block, 0, s, F, kf, vf, hkv, dh, table, table_rows); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
+}
+
+hipError_t fetch_rope(const FetchChunks& F, void* kf, void* vf, int hkv, int dh, const float2* table, int table_rows,
+                      int bf16, const FetchLaunch& fl, hipStream_t s) {
+  if (F.n <= 0 || F.offs[F.n] <= F.offs[0]) return hipSuccess;
+  if (F.n > kFetchMaxChunks || fl.blocks < 1 || fl.threads < 64 || fl.threads > 1024 || fl.threads % 64)
+    return hipErrorInvalidValue;
+  if (bf16) return launch_fetch(F, (bf16_t*)kf, (bf16_t*)vf, hkv, dh, table, table_rows, fl, s);
+  return launch_fetch(F, (float*)kf, (float*)vf, hkv, dh, table, table_rows, fl, s);
 }
 
 hipError_t dev_scatter(const void* fresh, long ld_fresh, void* fk, void* fv, const int32_t* sel, int n_sel,

@@ -164,7 +164,8 @@ def run_layers(eng: Engine, buf: RunBuffers, tokens: np.ndarray, offsets: Sequen
                host_cache: Optional[List[List[Sequence[torch.Tensor]]]] = None,
                record: bool = False, upload_inputs: bool = True,
                layer_events: Optional[list] = None, rotate_on_copy_stream: bool = False,
-               initial_sel: Optional[Sequence[int]] = None, batch_rotation: bool = True) -> RunResult:
+               initial_sel: Optional[Sequence[int]] = None, batch_rotation: bool = True,
+               sel_uploaded: bool = False) -> RunResult:
     """Blended prefill over every layer.
 
     fused[l] = (K, V) device buffers [N, H_kv, d_h] of layer l (the fused cache, output).
@@ -182,7 +183,8 @@ def run_layers(eng: Engine, buf: RunBuffers, tokens: np.ndarray, offsets: Sequen
     batch_rotation (HBM mode, otherwise): the position update of every layer in one launch
     before the first layer (cb_rotate_layers); False runs it inside each cb_blend_layer.
     upload_inputs=False reuses the token ids and offsets already on the device (a repeated
-    step then enqueues no host-to-device copy).  layer_events, if given, receives a CUDA event
+    step then enqueues no host-to-device copy); with initial_sel, sel_uploaded=True likewise
+    reuses the rows and their token ids uploaded by an earlier call with the same initial_sel.  layer_events, if given, receives a CUDA event
     recorded on the compute stream before the first layer and after every layer.
     """
     s = eng.shape
@@ -195,12 +197,14 @@ def run_layers(eng: Engine, buf: RunBuffers, tokens: np.ndarray, offsets: Sequen
     ctx = eng.ctx
     with torch.cuda.stream(cs):
         if initial_sel is not None:  # layer 1 embeds the selected rows only
-            init = np.asarray(initial_sel, np.int32)
-            buf.init_sel[: len(init)].copy_(torch.from_numpy(init), non_blocking=False)
-            buf.tokens[: len(init)].copy_(torch.from_numpy(np.asarray(tokens, np.int32)[init]), non_blocking=False)
+            if not sel_uploaded:
+                init = np.asarray(initial_sel, np.int32)
+                buf.init_sel[: len(init)].copy_(torch.from_numpy(init), non_blocking=False)
+                buf.tokens[: len(init)].copy_(torch.from_numpy(np.asarray(tokens, np.int32)[init]),
+                                              non_blocking=False)
         elif upload_inputs:
             buf.tokens[:n_tok].copy_(torch.from_numpy(np.asarray(tokens, np.int32)), non_blocking=False)
-        if upload_inputs or initial_sel is not None:
+        if upload_inputs or (initial_sel is not None and not sel_uploaded):
             buf.offsets[: n_chunks + 1].copy_(torch.tensor(offs, dtype=torch.int32))
     prefetch = host_cache is not None
     fetched = prefetch or (cache is not None and n_ctx > 0 and rotate_on_copy_stream)

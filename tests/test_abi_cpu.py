@@ -102,3 +102,34 @@ def test_plan_ratio_matches_oracle():
                 (10, 28, 1024.0, 1e9, 1e-6, 0.0, 0.6, 0.5), (10, 28, 1024.0, 1e9, 1e-6, 0.0, 0.1, 1.5)]:
         with pytest.raises(L.CbError):
             L.cb_plan_ratio(*bad)
+
+
+def test_plan_ratio_measured_matches_oracle():
+    """cb_plan_ratio_measured against the oracle's plan on random measured layer times, on both
+    sides of break-even, plus its argument checks."""
+    import numpy as np
+    from oracle import controller as C
+    from rag_kv_cache_amd import _lib as L
+    rng = np.random.default_rng(10)
+    for _ in range(500):
+        nl = int(rng.integers(1, 100))
+        t_full = float(10 ** rng.uniform(-5, -2))
+        t_fix = float(rng.uniform(0, 1)) * t_full
+        t_first = float(rng.uniform(1, 4)) * t_full
+        kvb = float(10 ** rng.uniform(4, 8))
+        bw = float(10 ** rng.uniform(8, 12))
+        lat = float(rng.choice([0.0, 1e-5]))
+        r_min = float(np.float32(rng.uniform(0, 0.3)))
+        r_max = float(np.float32(rng.uniform(r_min, 1.0)))
+        got = L.cb_plan_ratio_measured(nl, kvb, bw, lat, t_first, t_full, t_fix, r_min, r_max)
+        ref = C.plan_ratio_measured(nl, kvb, bw, t_first, t_full, t_fix, r_min, r_max, latency_layer=lat)
+        assert bool(got.load) == ref.load
+        assert abs(got.ratio - ref.ratio) <= 1e-6 * max(1.0, ref.ratio)
+        for f in ("t_load_layer", "t_recompute_layer", "t_layer", "t_total"):
+            assert abs(getattr(got, f) - getattr(ref, f)) <= 1e-6 * max(1e-9, abs(getattr(ref, f))), f
+        assert abs(got.break_even_bandwidth - ref.break_even) <= 1e-9 * ref.break_even
+    for bad in [(0, 1e6, 1e9, 0.0, 1e-3, 1e-3, 0.0, 0.1, 0.5), (4, 1e6, 1e9, 0.0, 1e-3, 1e-3, 2e-3, 0.1, 0.5),
+                (4, 1e6, 1e9, 0.0, 1e-3, 0.0, 0.0, 0.1, 0.5), (4, 1e6, 1e9, -1.0, 1e-3, 1e-3, 0.0, 0.1, 0.5),
+                (4, 1e6, 1e9, 0.0, 1e-3, 1e-3, 0.0, 0.6, 0.5)]:
+        with pytest.raises(L.CbError):
+            L.cb_plan_ratio_measured(*bad)

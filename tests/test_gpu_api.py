@@ -66,6 +66,14 @@ def test_status_codes(tiny):
         L.cb_workspace_size(eng.ctx, 10, 20)
     assert e.value.status == L.CB_ESHAPE
     assert "n_sel_max" in L.cb_last_error()
+    for bad in ((0, 256, 1), (8, 100, 1), (8, 2048, 1), (8, 256, 3), (2000, 64, 1), (0, 0, 1)):
+        with pytest.raises(L.CbError) as e:
+            L.cb_set_fetch_launch(eng.ctx, *bad)
+        assert e.value.status == L.CB_EINVAL
+    with pytest.raises(L.CbError) as e:
+        L.cb_set_fetch_mode(eng.ctx, 7)
+    assert e.value.status == L.CB_EINVAL
+    L.cb_set_fetch_launch(eng.ctx, 0, 0, 0)
     assert _blend(eng, wl, ratio=0.3) == 77 + wl.n_query
     assert _blend(eng, wl, ratio=5.0) == wl.n_tokens          # k clamped to the candidates
     assert _blend(eng, wl, ratio=0.0) == wl.n_query

@@ -107,7 +107,8 @@ def test_repeat_runs_are_bit_identical():
 
 def test_prefetch_path_equals_hbm_path():
     """Pinned-host cache fetched two layers ahead on the copy stream (read over PCIe and
-    rotated by one kernel, or copied by the copy engine and rotated in place, or from pageable
+    rotated by one kernel, at the default launch shape and at others down to one wavefront, or
+    copied by the copy engine and rotated in place, or from pageable
     memory, which falls back to the copy engine), the HBM-resident cache re-rotated by copy on
     the copy stream, and re-rotated inside each cb_blend_layer, all give bit-identical results
     to the HBM-resident cache re-rotated for every layer in one launch (cb_rotate_layers)."""
@@ -121,17 +122,21 @@ def test_prefetch_path_equals_hbm_path():
     pageable = [[(k.clone(), v.clone()) for k, v in layer] for layer in host]  # not page-locked
     assert not pageable[0][0][0].is_pinned()
     outs = []
-    for mode in ("hbm", "prefetch", "prefetch_copy", "prefetch_pageable", "hbm_copy_stream", "hbm_per_layer"):
+    shapes = {"prefetch_3x192x2": (3, 192, 2), "prefetch_1x64x1": (1, 64, 1), "prefetch_40x1024x4": (40, 1024, 4)}
+    for mode in ("hbm", "prefetch", "prefetch_copy", "prefetch_pageable", "hbm_copy_stream", "hbm_per_layer",
+                 *shapes):
         buf = make_buffers(eng, wl.n_tokens, len(chunks))
         fused = fused_buffers(eng, wl.n_tokens)
         pre = mode.startswith("prefetch")
         L.cb_set_fetch_mode(eng.ctx, L.CB_FETCH_COPY if mode == "prefetch_copy" else L.CB_FETCH_KERNEL)
+        L.cb_set_fetch_launch(eng.ctx, *shapes.get(mode, (0, 0, 0)))
         res = run_layers(eng, buf, F.all_tokens(wl), F.chunk_offsets(wl), wl.n_query, wl.schedule, fused,
                          cache=None if pre else cache,
                          host_cache=(pageable if mode == "prefetch_pageable" else host) if pre else None,
                          rotate_on_copy_stream=mode == "hbm_copy_stream", batch_rotation=mode != "hbm_per_layer")
         eng.compute.synchronize()
         L.cb_set_fetch_mode(eng.ctx, L.CB_FETCH_KERNEL)
+        L.cb_set_fetch_launch(eng.ctx, 0, 0, 0)
         outs.append((res.hidden[: res.n_final].cpu().numpy().copy(), res.sel[: res.n_final].cpu().numpy().copy(),
                      [(bits(k), bits(v)) for k, v in fused]))
     h0, s0, f0 = outs[0]
