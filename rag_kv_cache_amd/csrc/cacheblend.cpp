@@ -58,11 +58,13 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 }  // namespace
 
-// Launch shape of the fetch kernel unless the caller sets one: 32 single-wavefront workgroups,
-// one 16-byte piece in flight per lane (128 KiB in flight).  Measured on MI355X with ten 512-row
-// chunks per layer: 43 GB/s alone against 35 GB/s for 8 x 1024 threads x 4 pieces (2 MiB in
-// flight), the same prefetched prefill time; fewer requests in flight fall below the link rate.
-constexpr cb::FetchLaunch kFetchLaunchDefault{32, 64, 1};
+// Launch shape of the fetch kernel unless the caller sets one: 8 workgroups of 512 threads, two
+// 16-byte pieces in flight per thread (512 KiB in flight).  Measured on MI355X, Qwen2.5-1.5B
+// shape, blended prefills back to back (each prefetching while the previous one computes):
+// 6.74 ms per prefill against 6.93 for 8 x 1024 x 4 and 7.25 for 32 x 64 x 1, although the last
+// loads fastest alone (43 against 31 GB/s): the fetch slows the compute kernels while it runs,
+// and spread over more CUs it slows them more.
+constexpr cb::FetchLaunch kFetchLaunchDefault{8, 512, 2};
 
 struct cb_ctx {
   cb_model_desc d{};

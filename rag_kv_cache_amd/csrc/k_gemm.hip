@@ -733,18 +733,50 @@ hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
 
 }  // namespace
 
+// Tile for the SwiGLU (gate/up) product, which does not split K.  Model: a workgroup of tile
+// cfg takes about t(cfg) per 64-wide K-step whatever the shape, and the grid runs in
+// ceil(workgroups / 256) waves; the tile with the fewest wave-steps wins.  t measured on MI355X
+// (K = 1536, one wave of workgroups): 64x128 0.72 us, 128x128 0.83, 64x256 1.04, 128x256 1.13,
+// 256x256 1.75, 128x512 2.10.  The model ranks the measured tiles of the gate/up products of the
+// Qwen2.5-1.5B shape at 64..5184 rows and of the Mistral-7B shape at 640..1024 rows within 10%
+// of the best.
+GemmCfg swiglu_cfg(int M, int N) {
+  struct Cand {
+    GemmCfg cfg;
+    int bm, bn;
+    float t;
+  };
+  constexpr Cand cands[] = {{GEMM_64x128, 64, 128, 0.72f},   {GEMM_128x128, 128, 128, 0.83f},
+                            {GEMM_64x256, 64, 256, 1.04f},   {GEMM_128x256, 128, 256, 1.13f},
+                            {GEMM_256x256, 256, 256, 1.75f}, {GEMM_128x512, 128, 512, 2.10f}};
+  GemmCfg best = GEMM_64x128;
+  float best_cost = 3.4e38f;
+  for (const Cand& c : cands) {
+    if (N % c.bn) continue;
+    const long wgs = (long)((M + c.bm - 1) / c.bm) * (N / c.bn);
+    const float cost = (float)((wgs + 255) / 256) * c.t;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = c.cfg;
+    }
+  }
+  return best;
+}
+
 // Tile configuration and split-K factor for an M x N x K product (measured on MI355X at the
 // fusion step's shapes):
 //   * M <= 4 rows (a decode step): the skinny product, no split;
 //   * large M (>= 2048 rows, e.g. the first layer's full prompt) with a bf16 output and
 //     N % 256 == 0: 256 x 256 tiles of 8 wavefronts, no split (the fewest operand bytes per
 //     flop: 7-18% faster than the next best there);
-//   * SwiGLU (gate/up, widest output): 128 x 512 tiles of 8 wavefronts, no split;
+//   * SwiGLU (gate/up, widest output): no split, the tile swiglu_cfg's model ranks first
+//     (64 x 128 at 64 rows, 128 x 256 at 320, 256 x 256 at 640, 128 x 512 at 832 for Qwen);
 //   * problems with >= 200 tiles of 128 x 256: those tiles (8 wavefronts), no split;
 //   * short reductions (K <= 2048: the Q/K/V and o-projections of the kept rows): 64 x 128
 //     tiles of 4 wavefronts with a 4-stage ring, split only while fewer than ~150 tiles;
-//   * long reductions (the FFN down-projection): 128 x 256 tiles, K split so that about 210
-//     workgroups run;
+//   * long reductions (the FFN down-projection): up to 320 rows, 64 x 128 tiles with K split
+//     so that at most 256 workgroups run (64 rows: 15 against 20 us with 64 x 256); above,
+//     128 x 256 tiles, K split so that about 210 workgroups run;
 //   each split keeps at least two 64-wide K-steps and its partials fit the buffer.
 GemmPlan gemm_plan(int M, int N, int K, int epi, long partial_cap_elems) {
   GemmPlan p{GEMM_128x128, 1};
@@ -756,13 +788,12 @@ GemmPlan gemm_plan(int M, int N, int K, int epi, long partial_cap_elems) {
     p.cfg = GEMM_256x256;
     return p;
   }
-  if (epi == EPI_SWIGLU) {
-    const int ffn = N / 2;
-    if (ffn % 256 == 0) p.cfg = GEMM_128x512;
-    else if (ffn % 128 == 0) p.cfg = M <= 64 ? GEMM_64x256 : GEMM_128x256;
+  if (epi == EPI_SWIGLU) {  // no split (the epilogue needs whole sums): the cheapest tile by model
+    p.cfg = swiglu_cfg(M, N);
     return p;
   }
   int bm = 128, bn = 128, target = 210;
+  bool one_wave = false;  // split only as far as one wave of 256 workgroups
   if (N % 256 == 0 && ((M + 127) / 128) * (N / 256) >= 200) {
     p.cfg = GEMM_128x256;
     return p;
@@ -771,16 +802,20 @@ GemmPlan gemm_plan(int M, int N, int K, int epi, long partial_cap_elems) {
     p.cfg = GEMM_64x128;
     bm = 64;
     target = 150;
+  } else if (M <= 320) {  // a long reduction over few rows: small tiles, K split up to 8 ways
+    p.cfg = GEMM_64x128;
+    bm = 64;
+    target = 256;
+    one_wave = true;
   } else if (N % 256 == 0) {
-    p.cfg = M <= 64 ? GEMM_64x256 : GEMM_128x256;
-    bm = M <= 64 ? 64 : 128;
+    p.cfg = GEMM_128x256;
     bn = 256;
   }
   const int tiles = ((M + bm - 1) / bm) * (N / bn);
   if (tiles >= target) return p;
   const int nk = K / 64;
-  int sp = (target + tiles - 1) / tiles;
-  sp = sp > 8 ? 8 : sp;
+  int sp = one_wave ? target / tiles : (target + tiles - 1) / tiles;
+  sp = sp > 8 ? 8 : (sp < 1 ? 1 : sp);
   while (sp > 1 && (nk / sp < 2 || (long)sp * M * N > partial_cap_elems)) --sp;
   p.splits = sp;
   return p;
