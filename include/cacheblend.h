@@ -229,7 +229,9 @@ cb_status cb_blend_layer(cb_ctx* ctx, int32_t layer, const float* hidden_sel, co
  * positions by n_past + n_new).  Then cb_layer_rest on the same rows with new_sel_local =
  * 0 .. n_new - 1.  The workspace is cb_workspace_size(n_past + n_new, n_new).  It is
  * cb_blend_layer with the past rows as one already-fused context span and the new rows as
- * query rows; few rows split the key range finely (256-key ranges) to fill the chip. */
+ * query rows.  Up to 4 new rows whose count (taken as 1, 2 or 4) times the GQA group is at
+ * most 8 run a few-row attention on the vector ALUs over 64-key ranges (at most 64 ranges) and
+ * a combine of the ranges; other counts take the prefill attention with 256-key ranges. */
 cb_status cb_decode_layer(cb_ctx* ctx, int32_t layer, const float* hidden_new, const void* x_new,
                           void* kv_fused_k, void* kv_fused_v, int32_t n_past, int32_t n_new,
                           const int32_t* pos_dev, void* out_sel, void* workspace, size_t workspace_bytes);

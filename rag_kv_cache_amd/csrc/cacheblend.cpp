@@ -142,15 +142,17 @@ void plan_gemm(cb::GemmArgs& g, bool bf, long cap_elems) {
 // Split-KV: key ranges of 256 keys for the few rows of a decode step, 1024 keys for small kept
 // sets, 2048 for large ones (measured best for
 // the causal row-length mix of the fused prompt), bounded by the partial buffer.
-void attn_splits(int n_q, int n_tok, long cap_rows, int& splits, int& split_len) {
+void attn_splits(int n_q, int n_tok, int group, long cap_rows, int& splits, int& split_len) {
   const bool small = n_q <= kAttnSmallRows;
-  int len = small ? 256 : (n_q < 1200 ? 1024 : 2048);
+  const bool few = cb::attn_decode_fits(n_q, group);  // the decode kernel: 64-key ranges, any multiple of 16
+  int len = few ? 64 : (small ? 256 : (n_q < 1200 ? 1024 : 2048));
   int s = (n_tok + len - 1) / len;
   s = std::min(s, small ? kAttnSmallSplits : kAttnMaxSplits);
   while (s > 1 && (long)s * n_q > cap_rows) --s;
+  const int gran = few ? 16 : 64;
   len = (n_tok + s - 1) / s;
-  len = (len + 63) / 64 * 64;
-  if (len <= 0) len = 64;
+  len = (len + gran - 1) / gran * gran;
+  if (len <= 0) len = gran;
   splits = std::max(1, (n_tok + len - 1) / len);
   split_len = len;
 }
@@ -642,7 +644,7 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
     a.dh = d.head_dim; a.out = out_sel; a.ldo = qd;
     a.part_o = (float*)(ws + wp.attn_o); a.part_ml = (float*)(ws + wp.attn_ml);
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
-    if (bf) attn_splits(nn, (int)n_tok, wp.attn_cap_rows, a.splits, a.split_len);
+    if (bf) attn_splits(nn, (int)n_tok, d.n_q_heads / d.n_kv_heads, wp.attn_cap_rows, a.splits, a.split_len);
     else { a.splits = 1; a.split_len = (int)std::max<long>(n_tok, 1); }
     // causal flops of the kept rows are not known on the host; the row count bounds them
     Timed t(c, CB_K_ATTN, 0.0);

@@ -42,6 +42,9 @@ struct AttnArgs {
 hipError_t attn_bf16(const AttnArgs& a, hipStream_t s);
 // Query rows per workgroup of the bf16 attention for a GQA group of `group` query heads.
 int attn_rows_per_wg(int group);
+// Whether n_q query rows of a group of `group` heads run on the few-row (decode) kernel, whose
+// key ranges may be any multiple of 16 keys (other kernels: multiples of 64), at most 64 ranges.
+bool attn_decode_fits(int n_q, int group);
 hipError_t attn_f32(const AttnArgs& a, hipStream_t s);
 
 hipError_t embed(const int32_t* tok, int n, const void* table, int vocab, int d, int bf16, float* out,

@@ -332,6 +332,252 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   for (int i = 0; i < 4; ++i) Elem<TO>::st(out + i, acc[i] * inv);
 }
 
+// ---------------------------------------------------------------- decode (few query rows)
+// A decode step has 1..4 query rows: 16-row MFMA tiles would be almost empty, so the few rows
+// run on the vector ALUs with the key range split finely.  One workgroup per (KV head g, key
+// range sp), 4 wavefronts; 16 lanes hold one key row (8 of its 128 dims each), so a wavefront
+// takes 4 keys per step and the workgroup 16.  Every lane keeps, for each of the MR rows x G
+// query heads of the group, the online-softmax state (max, sum, 8 dims of O) of the keys its
+// 16-lane row sees; the states are merged across the 4 rows of a wavefront with lane swaps and
+// across wavefronts in LDS, and written as the split's partial (O, max, sum) for the combine.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Sum over each row of 16 lanes, every lane getting the row's sum.
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+  v += dpp_f<0x141>(v);  // row_half_mirror: lane i of 8 reads 7 - i, i.e. the other quad
+  v += dpp_f<0x140>(v);  // row_mirror: lane i of 16 reads 15 - i, i.e. the other 8 lanes
+  return v;
+}
+
+__device__ __forceinline__ void unpack_bf16x8(const uint4 v, float* o) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = __uint_as_float(w[i] << 16);
+    o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+template <int G, int MR>
+__global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
+  constexpr int DH = 128, RH = MR * G;
+  __shared__ float s_o[4][RH][DH];
+  __shared__ float s_m[4][RH], s_l[4][RH];
+  const int g = blockIdx.x, sp = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kl = lane >> 4, dl = (lane & 15) * 8;
+  const int k0 = sp * a.split_len;
+  const int kend0 = min(k0 + a.split_len, a.n_tok);
+  const long rs = (long)a.hkv * DH;  // elements per fused row
+  const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + g * DH + dl;
+  const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + g * DH + dl;
+  // Every load of the first DU steps is issued before any is used (K/V rows, Q, positions), so
+  // the workgroup waits for memory once; rows' causal bounds are applied afterwards.
+  // The 16 lanes of a row share kb, so a row is wholly active or inactive (DPP stays in rows).
+  constexpr int DU = 8;
+  int kb0 = k0 + wave * 4 + kl;
+  uint4 kr[DU], vr[DU];
+#pragma unroll
+  for (int u = 0; u < DU; ++u) {
+    const int kb = kb0 + 16 * u;
+    if (kb < kend0) {
+      kr[u] = *reinterpret_cast<const uint4*>(K + kb * rs);
+      vr[u] = *reinterpret_cast<const uint4*>(V + kb * rs);
+    }
+  }
+  uint4 qraw[MR][G];
+#pragma unroll
+  for (int r = 0; r < MR; ++r)
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      if (r < a.n_q)
+        qraw[r][h] = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.q) + (long)r * a.ldq +
+                                                     (g * G + h) * DH + dl);
+  int qp[MR];
+  int qmax = -1;
+#pragma unroll
+  for (int r = 0; r < MR; ++r) {
+    qp[r] = r < a.n_q ? a.qpos[r] : -1;
+    qmax = max(qmax, qp[r]);
+  }
+  const int kend = min(kend0, qmax + 1);
+  if (k0 >= kend) return;  // no row attends to this key range (uniform over the workgroup)
+
+  float q[MR][G][8];
+#pragma unroll
+  for (int r = 0; r < MR; ++r)
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (r < a.n_q) {
+        unpack_bf16x8(qraw[r][h], q[r][h]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q[r][h][e] *= a.scale_log2;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q[r][h][e] = 0.f;
+      }
+    }
+  float m[MR][G], l[MR][G], o[MR][G][8];
+#pragma unroll
+  for (int r = 0; r < MR; ++r)
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m[r][h] = NEG_INF;
+      l[r][h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[r][h][e] = 0.f;
+    }
+  for (;;) {
+#pragma unroll
+    for (int u = 0; u < DU; ++u) {
+      const int kb = kb0 + 16 * u;
+      if (kb >= kend) break;
+      float kf[8], vf[8];
+      unpack_bf16x8(kr[u], kf);
+      unpack_bf16x8(vr[u], vf);
+#pragma unroll
+      for (int r = 0; r < MR; ++r) {
+        const bool live = kb <= qp[r];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float sc = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sc = fmaf(q[r][h][e], kf[e], sc);
+          sc = sum16(sc);
+          if (live) {
+            const float mn = fmaxf(m[r][h], sc);
+            const float al = __builtin_amdgcn_exp2f(m[r][h] - mn);  // exp2(-inf) = 0
+            const float p = __builtin_amdgcn_exp2f(sc - mn);
+            l[r][h] = l[r][h] * al + p;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[r][h][e] = fmaf(p, vf[e], o[r][h][e] * al);
+            m[r][h] = mn;
+          }
+        }
+      }
+    }
+    kb0 += 16 * DU;
+    if (kb0 >= kend) break;
+    // key ranges longer than 16 DU keys: the next DU steps
+#pragma unroll
+    for (int u = 0; u < DU; ++u) {
+      const int kb = kb0 + 16 * u;
+      if (kb < kend) {
+        kr[u] = *reinterpret_cast<const uint4*>(K + kb * rs);
+        vr[u] = *reinterpret_cast<const uint4*>(V + kb * rs);
+      }
+    }
+  }
+  // merge the 4 key rows of the wavefront (lanes l, l^16, l^32, l^48 hold the same dims)
+#pragma unroll
+  for (int r = 0; r < MR; ++r)
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float M = max4_rows(m[r][h]);
+      const float w = m[r][h] == NEG_INF ? 0.f : exp2f(m[r][h] - M);
+      const float L = sum4_rows(l[r][h] * w);
+      float od[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) od[e] = sum4_rows(o[r][h][e] * w);
+      if (kl == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s_o[wave][r * G + h][dl + e] = od[e];
+        if (lane == 0) {
+          s_m[wave][r * G + h] = M;
+          s_l[wave][r * G + h] = L;
+        }
+      }
+    }
+  __syncthreads();
+  // merge the wavefronts and write the split's partial of every row that reads this split
+  for (int i = threadIdx.x; i < RH * DH; i += 256) {
+    const int rh = i / DH, d = i - rh * DH;
+    const int r = rh / G, h = rh - r * G;
+    if (r >= a.n_q || qp[r] < k0) continue;
+    float M = NEG_INF;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][rh]);
+    float O = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float wt = s_m[w][rh] == NEG_INF ? 0.f : exp2f(s_m[w][rh] - M);
+      O = fmaf(wt, s_o[w][rh][d], O);
+      L = fmaf(wt, s_l[w][rh], L);
+    }
+    const long pi = ((long)sp * a.n_q + r) * a.hq + g * G + h;
+    a.part_o[pi * DH + d] = O;
+    if (d == 0) {
+      a.part_ml[pi * 2] = M;
+      a.part_ml[pi * 2 + 1] = L;
+    }
+  }
+}
+
+// Combine of the decode partials: one workgroup of DH threads per (row, query head); the
+// splits' (max, sum) go through LDS, then each thread sums its dim over the row's splits with
+// every load in flight at once (at most kDecodeMaxSplits).
+constexpr int kDecodeMaxSplits = 64;
+template <typename TO>
+__global__ __launch_bounds__(128) void attn_combine_few_kernel(AttnArgs a) {
+  __shared__ float s_w[kDecodeMaxSplits];
+  __shared__ float s_inv;
+  const int row = blockIdx.x / a.hq, h = blockIdx.x - row * a.hq;
+  const int t = threadIdx.x;
+  const int nsp = min(a.splits, kDecodeMaxSplits);
+  // every load at once (positions, the splits' (max, sum), this thread's dim of every split's O);
+  // splits past the row's last one are not read further (their buffers may hold anything)
+  float v[kDecodeMaxSplits];
+#pragma unroll
+  for (int sidx = 0; sidx < kDecodeMaxSplits; ++sidx)
+    if (sidx < nsp) v[sidx] = a.part_o[(((long)sidx * a.n_q + row) * a.hq + h) * a.dh + t];
+  float2 mlv = make_float2(NEG_INF, 0.f);
+  if (t < nsp) mlv = *reinterpret_cast<const float2*>(a.part_ml + (((long)t * a.n_q + row) * a.hq + h) * 2);
+  const int ns = min(a.qpos[row] / a.split_len + 1, nsp);
+  if (t < 64) {  // wavefront 0 holds every split's (max, sum)
+    const float mv = t < ns ? mlv.x : NEG_INF, lv = t < ns ? mlv.y : 0.f;
+    float M = mv;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float w = mv == NEG_INF ? 0.f : exp2f(mv - M);
+    const float L = wave_sum(lv * w);
+    s_w[t] = w;
+    if (t == 0) s_inv = L > 0.f ? 1.f / L : 0.f;
+  }
+  __syncthreads();
+  float acc = 0.f;
+#pragma unroll
+  for (int sidx = 0; sidx < kDecodeMaxSplits; ++sidx)
+    if (sidx < ns) acc = fmaf(s_w[sidx], v[sidx], acc);
+  Elem<TO>::st(reinterpret_cast<TO*>(a.out) + (long)row * a.ldo + h * a.dh + t, acc * s_inv);
+}
+
+template <int G, int MR>
+hipError_t launch_decode(const AttnArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((attn_decode_kernel<G, MR>), dim3(a.hkv, a.splits), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_combine_few_kernel<bf16_t>, dim3(a.n_q * a.hq), dim3(128), 0, s, a);
+  return hipGetLastError();
+}
+
+// The decode kernel for n_q query rows of group G when its registers allow (MR x G <= 8, MR
+// the row count rounded up to 1, 2 or 4); hipErrorNotSupported otherwise.
+template <int G>
+hipError_t launch_decode_g(const AttnArgs& a, hipStream_t s) {
+  if (a.n_q == 1 && G <= 8) return launch_decode<G, 1>(a, s);
+  if constexpr (2 * G <= 8) {
+    if (a.n_q == 2) return launch_decode<G, 2>(a, s);
+  }
+  if constexpr (4 * G <= 8) {
+    if (a.n_q <= 4) return launch_decode<G, 4>(a, s);
+  }
+  return hipErrorNotSupported;
+}
+
 // fp32 path (correctness configurations): one thread per (query row, query head), online
 // softmax over keys 0 .. qpos[row], head_dim DH in registers.
 template <int DH>
@@ -395,9 +641,27 @@ hipError_t launch_g(const AttnArgs& a, hipStream_t s) {
 
 int attn_rows_per_wg(int group) { return group <= 6 ? 32 : 16; }
 
+// Whether the vector-ALU decode kernel takes n_q query rows of a GQA group of `group` heads.
+bool attn_decode_fits(int n_q, int group) {
+  if (n_q < 1 || n_q > 4) return false;
+  const int mr = n_q == 1 ? 1 : (n_q == 2 ? 2 : 4);
+  return mr * group <= 8;
+}
+
 hipError_t attn_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.n_q <= 0) return hipSuccess;
   hipError_t e;
+  if (a.dh == 128 && attn_decode_fits(a.n_q, a.hq / a.hkv) && a.splits <= kDecodeMaxSplits) {
+    switch (a.hq / a.hkv) {
+      case 1: return launch_decode_g<1>(a, s);
+      case 2: return launch_decode_g<2>(a, s);
+      case 4: return launch_decode_g<4>(a, s);
+      case 6: return launch_decode_g<6>(a, s);
+      case 7: return launch_decode_g<7>(a, s);
+      case 8: return launch_decode_g<8>(a, s);
+      default: break;
+    }
+  }
   switch (a.hq / a.hkv) {
     case 1: e = launch_g<1>(a, s); break;
     case 2: e = launch_g<2>(a, s); break;

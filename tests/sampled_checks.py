@@ -8,7 +8,8 @@ of that layer (the residual rows entering it and the fused cache it attends over
     re-rotated GPU cache row);
   * sampled recomputed rows of the fused cache hold the oracle's fresh K/V, sampled rows that
     were not recomputed hold the re-rotated chunk cache (V bit for bit);
-  * the attention output and the layer output of sampled kept rows (always some query rows).
+  * the attention output and the layer output of sampled kept rows (always some query rows);
+and a decode step on the fused KV is checked layer by layer the same way.
 """
 from __future__ import annotations
 
@@ -107,3 +108,43 @@ def check_chunk_cache(wl, layer, w, h, k_dev, v_dev):
     v = prec.store(O.project(x, w["w_v"]).reshape(n, sh.n_kv_heads, sh.head_dim))
     assert_close(to_np(k_dev), k, "bf16", f"chunk-0 cache K layer {layer + 1}")
     assert_close(to_np(v_dev), v, "bf16", f"chunk-0 cache V layer {layer + 1}")
+
+
+def check_decode_teacher_forced(eng, buf, fused, wl, W, emb, tok):
+    """One decode step of token `tok` at position N (after a blended prefill of N rows whose
+    fused K/V sit in `fused`), run layer by layer; at every layer the attention output, the
+    appended K/V row and the layer output of the new row are checked against the oracle's
+    decode layer fed the GPU's input row of that layer and the GPU's fused rows."""
+    import torch
+    from rag_kv_cache_amd import _lib as L
+    from rag_kv_cache_amd.pipeline import _ptr
+    sh = wl.shape
+    prec = O.Precision("bf16")
+    n = wl.n_tokens
+    cs = eng.compute
+    with torch.cuda.stream(cs):
+        buf.tokens[:1].copy_(torch.tensor([tok], dtype=torch.int32))
+        buf.init_sel[:1].copy_(torch.tensor([n], dtype=torch.int32))
+    L.cb_embed(eng.ctx, _ptr(buf.tokens), 1, _ptr(eng.emb), _ptr(buf.hidden[0]))
+    ws = buf.ws
+    cur = 0
+    for l in range(sh.n_layers):
+        h_in, h_out = buf.hidden[cur], buf.hidden[1 - cur]
+        cs.synchronize()
+        hin = h_in[:1].cpu().numpy().astype(np.float64)
+        fk, fv = to_np(fused[l][0][:n]), to_np(fused[l][1][:n])
+        L.cb_decode_layer(eng.ctx, l, _ptr(h_in), _ptr(fused[l][0]), _ptr(fused[l][1]), n, 1, _ptr(buf.init_sel),
+                          _ptr(buf.out_sel), _ptr(ws), ws.numel())
+        L.cb_layer_rest(eng.ctx, l, _ptr(h_in), 1, _ptr(buf.iota), 1, _ptr(buf.out_sel), _ptr(h_out), _ptr(ws),
+                        ws.numel())
+        cs.synchronize()
+        zero = np.zeros((1,) + fk.shape[1:])
+        r = O.blend_layer(sh, W[l], prec, hin, np.concatenate([fk, zero]), np.concatenate([fv, zero]), n,
+                          np.array([n]), 1, 0.0)
+        out = to_np(buf.out_sel[:1])
+        assert_close(out, r["out"].reshape(1, -1), "bf16", f"decode attention output layer {l + 1}")
+        assert_close(to_np(fused[l][0][n:n + 1]), r["fused_k"][n:n + 1], "bf16", f"decode K layer {l + 1}")
+        assert_close(to_np(fused[l][1][n:n + 1]), r["fused_v"][n:n + 1], "bf16", f"decode V layer {l + 1}")
+        ref_h = O.layer_rest(sh, W[l], prec, hin, [0], out)
+        assert_close(h_out[:1].cpu().numpy().astype(np.float64), ref_h, "bf16", f"decode layer output {l + 1}")
+        cur = 1 - cur

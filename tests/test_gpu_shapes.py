@@ -6,14 +6,16 @@ chunks of 640 + 256 query rows, GQA group 4; recompute ratios 10%, 15% and 20%),
 The first three decoder layers of each shape run (layer 1 at ratio 1, layer 2 narrowing to the
 ratio, layer 3 at the steady ratio); every kernel sees the same sizes at any depth, so these
 layers cover the whole model's launch shapes.  Each layer is checked against the oracle with the
-GPU's own inputs of that layer (teacher-forced, sampled rows), as at the benchmark's size."""
+GPU's own inputs of that layer (teacher-forced, sampled rows), as at the benchmark's size; then
+one decode step on the fused KV, each layer against the oracle's decode layer fed the GPU's input
+row and fused rows of that layer."""
 from dataclasses import replace
 
 import numpy as np
 import pytest
 
 import fixtures as F
-from sampled_checks import check_chunk_cache, check_layer
+from sampled_checks import check_chunk_cache, check_decode_teacher_forced, check_layer
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +39,7 @@ def _engine(wl):
             _state["eng"].close()
         _state.clear()
         _state["shape"] = None
-        max_tok = max(_reduced(c).n_tokens for c in CASES if F.get_config(c).shape.name == sh.name)
+        max_tok = max(_reduced(c).n_tokens for c in CASES if F.get_config(c).shape.name == sh.name) + 2
         print(f"[shapes] loading {sh.name}: d {sh.d_model}, heads {sh.n_q_heads}/{sh.n_kv_heads}, "
               f"ffn {sh.ffn_dim}, {N_LAYERS} layers, up to {max_tok} rows", flush=True)
         W = [F.layer_weights(sh, l) for l in range(1, N_LAYERS + 1)]
@@ -66,8 +68,8 @@ def test_shape_teacher_forced(name):
     chunks = F.chunk_tokens(wl)
     tokens = F.all_tokens(wl)
     cache, _ = build_chunk_caches(eng, chunks)
-    buf = make_buffers(eng, wl.n_tokens, len(chunks))
-    fused = [(eng.kv_empty(wl.n_tokens), eng.kv_empty(wl.n_tokens)) for _ in range(N_LAYERS)]
+    buf = make_buffers(eng, wl.n_tokens + 1, len(chunks))
+    fused = [(eng.kv_empty(wl.n_tokens + 1), eng.kv_empty(wl.n_tokens + 1)) for _ in range(N_LAYERS)]
     res = run_layers(eng, buf, tokens, F.chunk_offsets(wl), wl.n_query, wl.schedule, fused,
                      cache=cache, record=True)
     eng.compute.synchronize()
@@ -78,6 +80,9 @@ def test_shape_teacher_forced(name):
         print(f"[shapes] {name}: layer {layer + 1}, {len(res.records[layer].sel)} -> "
               f"{len(res.records[layer].new_sel)} rows", flush=True)
         check_layer(wl, layer, W[layer], res.records[layer], hidden_in[layer], cache[layer], fused[layer])
+
+    # one decode step on the fused KV, layer by layer (the few-row attention over every fused row)
+    check_decode_teacher_forced(eng, buf, fused, wl, W, emb, 11)
 
     # chunk 0's cache at the last layer: its own prefill at positions 0..
     toks = chunks[0]
