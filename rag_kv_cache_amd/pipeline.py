@@ -33,14 +33,20 @@ def _ptr(t) -> int:
 class Engine:
     """A library context plus the device weights of one model."""
 
-    def __init__(self, shape, max_tokens: int, device: int = 0, copy_stream: bool = True):
+    def __init__(self, shape, max_tokens: int, device: int = 0, copy_stream: bool = True,
+                 streams: Optional[tuple] = None):
+        """streams: optional (compute, copy) torch streams to use instead of new ones (e.g.
+        torch.cuda.ExternalStream wrapping streams made elsewhere); copy may be None."""
         if not torch.cuda.is_available():
             raise RuntimeError("a ROCm GPU is required: the fusion step runs only in the HIP library")
         self.shape = shape
         self.device = torch.device("cuda", device)
         self.dtype = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
-        self.compute = torch.cuda.Stream(self.device)
-        self.copy = torch.cuda.Stream(self.device) if copy_stream else None
+        if streams is not None:
+            self.compute, self.copy = streams
+        else:
+            self.compute = torch.cuda.Stream(self.device)
+            self.copy = torch.cuda.Stream(self.device) if copy_stream else None
         desc = L.cb_model_desc(shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads,
                                shape.head_dim, shape.ffn_dim, shape.vocab, max_tokens,
                                float(shape.rope_base), float(shape.rms_eps),
@@ -165,7 +171,7 @@ def run_layers(eng: Engine, buf: RunBuffers, tokens: np.ndarray, offsets: Sequen
                record: bool = False, upload_inputs: bool = True,
                layer_events: Optional[list] = None, rotate_on_copy_stream: bool = False,
                initial_sel: Optional[Sequence[int]] = None, batch_rotation: bool = True,
-               sel_uploaded: bool = False) -> RunResult:
+               sel_uploaded: bool = False, paced: bool = False) -> RunResult:
     """Blended prefill over every layer.
 
     fused[l] = (K, V) device buffers [N, H_kv, d_h] of layer l (the fused cache, output).
@@ -184,7 +190,9 @@ def run_layers(eng: Engine, buf: RunBuffers, tokens: np.ndarray, offsets: Sequen
     before the first layer (cb_rotate_layers); False runs it inside each cb_blend_layer.
     upload_inputs=False reuses the token ids and offsets already on the device (a repeated
     step then enqueues no host-to-device copy); with initial_sel, sel_uploaded=True likewise
-    reuses the rows and their token ids uploaded by an earlier call with the same initial_sel.  layer_events, if given, receives a CUDA event
+    reuses the rows and their token ids uploaded by an earlier call with the same initial_sel.
+    paced (prefetch modes): layer l+2's fetch waits until the compute stream has reached layer l,
+    so that the fetches spread over the step instead of running back to back at its start.  layer_events, if given, receives a CUDA event
     recorded on the compute stream before the first layer and after every layer.
     """
     s = eng.shape
@@ -243,6 +251,10 @@ def run_layers(eng: Engine, buf: RunBuffers, tokens: np.ndarray, offsets: Sequen
     for l in range(s.n_layers):
         if fetched:  # the fused buffer already holds the re-rotated cache
             L.cb_synchronize(ctx, l)
+            if paced and l + 2 < s.n_layers:
+                ev = torch.cuda.Event()
+                ev.record(cs)
+                eng.copy.wait_event(ev)
             fetch(l + 2)
             ck, cv = None, None
         elif cache is not None and not batched:  # position update inside cb_blend_layer (copy from the cache)
