@@ -7,5 +7,5 @@ CPU oracle and the HIP path stay independent of each other.
 from .synth import (  # noqa: F401
     SEED, ModelShape, Workload, CONFIGS, get_config, rng, layer_weights, embedding,
     chunk_tokens, query_tokens, all_tokens, chunk_offsets, perturbation, to_bf16_values,
-    to_bf16_bits, kv_bytes_per_element,
+    to_bf16_bits, kv_bytes_per_element, quantize_int8_rows, layer_weights_int8,
 )

@@ -164,6 +164,42 @@ def layer_weights(shape: ModelShape, layer: int) -> Dict[str, np.ndarray]:
     return out
 
 
+def quantize_int8_rows(w: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Symmetric int8 per output channel (row of an nn.Linear weight): s = max|w| / 127 and
+    q = rint(w / s) (half to even) clamped to [-127, 127], in float32; an all-zero row gets
+    s = 0 and q = 0.  Returns (q int8 [out, in], s float32 [out])."""
+    w = np.asarray(w, np.float32)
+    s = (np.abs(w).max(axis=1) / np.float32(127)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1)).astype(np.float32)
+    q = np.clip(np.rint(w / safe[:, None]), -127, 127).astype(np.int8)
+    return q, s
+
+
+def layer_weights_int8(shape: ModelShape, layer: int) -> Dict[str, np.ndarray]:
+    """Weights of decoder layer `layer` for the int8-weight run: the same float32 draws as
+    layer_weights (before any bf16 rounding), each linear weight quantized per output row:
+    q_<name> int8 [out, in] and s_<name> float32 [out]; norm gains are ones."""
+    assert 1 <= layer <= shape.n_layers
+    d, hq, hkv, dh, f = shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.ffn_dim
+    dims = {"q": (hq * dh, d), "k": (hkv * dh, d), "v": (hkv * dh, d), "o": (d, hq * dh),
+            "gate": (f, d), "up": (f, d), "down": (d, f)}
+
+    def one(n):
+        w = rng(_STREAM_WEIGHTS, layer, _TENSOR_ID[n]).standard_normal(dims[n], dtype=np.float32)
+        w *= np.float32(0.02)
+        return quantize_int8_rows(w)
+
+    with ThreadPoolExecutor(max_workers=min(len(dims), os.cpu_count() or 1)) as ex:
+        drawn = list(ex.map(one, dims))
+    out = {}
+    for n, (q, sc) in zip(dims, drawn):
+        out["q_" + n] = q
+        out["s_" + n] = sc
+    out["g_attn"] = np.ones(d, np.float32)
+    out["g_ffn"] = np.ones(d, np.float32)
+    return out
+
+
 def embedding(shape: ModelShape) -> np.ndarray:
     """Token embedding table [vocab, d] (float32 array; bf16-valued for bf16 shapes)."""
     return _draw(shape, 0, 0, (shape.vocab, shape.d_model))

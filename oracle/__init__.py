@@ -37,12 +37,13 @@ Parity status per function (what pins each one, see tests/test_oracle_*.py):
   store ............. FIPS 180-2 SHA-256 examples rebuilt from token and key bytes, the
                       LRU cyclic-scan trap the LMCache page measures, LRU's stack property,
                       a hand-worked eviction sequence
+  dequantize ........ q * s per output row in float32 against hand-worked rows
   which rows are HKVD on random weights ... parity unpinned (the pages print no
                       worked example; only the invariants above constrain it)
 """
 from .model import (  # noqa: F401
     Precision, F64, round_bf16, rope_cos_sin, rope_rotate, rope_delta, rmsnorm, project,
-    causal_attention, mlp, full_prefill, chunk_caches, cache_nbytes,
+    causal_attention, mlp, full_prefill, chunk_caches, cache_nbytes, dequantize,
 )
 from .blend import (  # noqa: F401
     k_for_ratio, topk_select, kv_deviation, cosine_deviation, seam_positions, blend_layer,

@@ -139,6 +139,16 @@ def mlp(h1: np.ndarray, w: Dict[str, np.ndarray], eps: float, prec: Precision) -
 
 
 # ---------------------------------------------------------------- full prefill (ground truth)
+def dequantize(wq: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
+    """The int8-weight model as the oracle runs it: every linear weight is q * s in float32
+    (q int8 [out, in], s float32 per output row), the norm gains as given.  Reading (no page
+    fixes a weight format): symmetric per-output-channel int8 of the same float32 draws."""
+    out = {"g_attn": np.asarray(wq["g_attn"], np.float32), "g_ffn": np.asarray(wq["g_ffn"], np.float32)}
+    for n in ("q", "k", "v", "o", "gate", "up", "down"):
+        out["w_" + n] = np.asarray(wq["q_" + n], np.float32) * np.asarray(wq["s_" + n], np.float32)[:, None]
+    return out
+
+
 def full_prefill(shape, weights: List[Dict[str, np.ndarray]], emb: np.ndarray, tokens: np.ndarray,
                  prec: Precision = F64, start_pos: int = 0):
     """Ordinary prefill of `tokens` at positions start_pos.. (every row, every layer).

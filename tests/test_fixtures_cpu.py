@@ -71,3 +71,48 @@ def test_threaded_layer_weights_equal_a_serial_draw(cfg):
                 ref = (_round_u64(ref).astype(np.uint32) << 16).view(np.float32)
             assert np.array_equal(w["w_" + n], ref), (cfg, layer, n)
     assert S._TENSOR_ID == {n: j for j, n in enumerate(dims)}
+
+
+def test_int8_quantizer_hand_worked_rows():
+    # row 0: max |w| = 1.27 -> s = 0.01; 0.025 / 0.01 = 2.5 exactly in binary? it is not, so use
+    # a power-of-two scale: row 1 has max 127 -> s = 1 and exact halves round to even
+    w = np.array([[1.27, -0.5, 0.004, 0.0],
+                  [127.0, 2.5, 3.5, -2.5],
+                  [0.0, 0.0, 0.0, 0.0],
+                  [-63.5, 0.25, 0.75, 1.0]], np.float32)
+    q, s = F.quantize_int8_rows(w)
+    assert q.dtype == np.int8 and s.dtype == np.float32
+    assert s[1] == 1.0 and q[1].tolist() == [127, 2, 4, -2]          # ties to even
+    assert q[0, 0] == 127 and q[0, 1] == -50 and q[0, 2] == 0 and q[0, 3] == 0
+    assert s[2] == 0.0 and q[2].tolist() == [0, 0, 0, 0]              # an all-zero row
+    assert s[3] == np.float32(63.5) / np.float32(127) and q[3, 0] == -127
+    assert q[3].tolist() == [-127, 0, 2, 2]                           # 0.5 -> 0, 1.5 -> 2, 2.0 -> 2
+
+
+def test_int8_quantizer_bounds_on_random_rows():
+    rng = np.random.default_rng(0)
+    w = rng.standard_normal((300, 97)).astype(np.float32) * np.float32(0.02)
+    q, s = F.quantize_int8_rows(w)
+    assert np.abs(q).max() == 127
+    assert (np.abs(q).max(axis=1) == 127).all()                        # every row's max maps to +-127
+    err = np.abs(w - q.astype(np.float64) * s[:, None])
+    assert (err <= s[:, None] * (0.5 + 1e-6)).all()                    # within half a step
+
+
+def test_int8_layer_weights_quantize_the_float32_draws():
+    sh = F.get_config("small_bf16").shape
+    wq = F.layer_weights_int8(sh, 2)
+    ref = F.rng(1, 2, 4).standard_normal((sh.ffn_dim, sh.d_model), dtype=np.float32) * np.float32(0.02)
+    q, s = F.quantize_int8_rows(ref)
+    assert np.array_equal(wq["q_gate"], q) and np.array_equal(wq["s_gate"], s)
+    assert wq["q_q"].shape == (sh.n_q_heads * sh.head_dim, sh.d_model)
+    assert wq["q_down"].shape == (sh.d_model, sh.ffn_dim) and wq["s_down"].shape == (sh.d_model,)
+
+
+def test_oracle_dequantize():
+    import oracle as O
+    wq = {"q_" + n: np.array([[127, -2], [0, 5]], np.int8) for n in ("q", "k", "v", "o", "gate", "up", "down")}
+    wq.update({"s_" + n: np.array([0.5, 0.25], np.float32) for n in ("q", "k", "v", "o", "gate", "up", "down")})
+    wq["g_attn"] = wq["g_ffn"] = np.ones(2, np.float32)
+    w = O.dequantize(wq)
+    assert w["w_gate"].tolist() == [[63.5, -1.0], [0.0, 1.25]] and w["w_down"].dtype == np.float32
