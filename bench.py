@@ -342,6 +342,52 @@ def run_peaks(eng):
                     "torch.mm bf16 8192 x 8192 x 8192"}
 
 
+def run_int8(wl, steps, warmup):
+    """The same blended prefill with int8 weights (per-output-channel scales; the same float32
+    draws quantized), HBM-resident caches, graph replay: ms per step and the gate/up product's
+    share."""
+    import torch
+    import fixtures as F
+    from rag_kv_cache_amd import _lib as L
+    from rag_kv_cache_amd.pipeline import Engine, build_chunk_caches, capture_step, make_buffers, run_layers
+    sh = wl.shape
+    eng = Engine(sh, max_tokens=wl.n_tokens + 8)
+    for l in range(sh.n_layers):
+        eng.load_layer_int8(l, F.layer_weights_int8(sh, l + 1))
+    eng.load_embedding(F.embedding(sh))
+    chunks = F.chunk_tokens(wl)
+    tokens = F.all_tokens(wl)
+    offs = [int(o) for o in F.chunk_offsets(wl)]
+    cache, _ = build_chunk_caches(eng, chunks)
+    buf = make_buffers(eng, wl.n_tokens, len(chunks))
+    fused = [(eng.kv_empty(wl.n_tokens), eng.kv_empty(wl.n_tokens)) for _ in range(sh.n_layers)]
+    run_layers(eng, buf, tokens, offs, wl.n_query, wl.schedule, fused, cache=cache)
+    g = capture_step(eng, lambda: run_layers(eng, buf, tokens, offs, wl.n_query, wl.schedule, fused, cache=cache,
+                                             upload_inputs=False))
+    cs = eng.compute
+    with torch.cuda.stream(cs):
+        for _ in range(warmup):
+            g.replay()
+    cs.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(cs):
+        for _ in range(steps):
+            g.replay()
+    cs.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    L.cb_profile_enable(eng.ctx, True)
+    run_layers(eng, buf, tokens, offs, wl.n_query, wl.schedule, fused, cache=cache, upload_inputs=False)
+    cs.synchronize()
+    L.cb_profile_enable(eng.ctx, False)
+    gu_ms, gu_n, _ = L.cb_profile_read(eng.ctx, L.CB_K_GEMM_GATE_UP)
+    del g
+    eng.close()
+    log(f"int8 weights: {ms:.3f} ms/step, gate/up {gu_ms * 1e3 / max(gu_n, 1):.1f} us per launch")
+    return {"ms_per_step": round(ms, 4), "context_tokens_per_s": round(wl.n_ctx / ms * 1e3, 1),
+            "gate_up_us_per_launch": round(gu_ms * 1e3 / max(gu_n, 1), 2),
+            "note": "int8 weights, one float32 scale per output channel, bf16 activations; graph replay"}
+
+
 def run_variants(eng, buf, tokens, offs, wl, fused, cache, steps):
     """The selection variants of the KVBoost page on the same workload (HBM-resident cache,
     eager launches): the cosine deviation score with the same schedule, and the spatial seam
@@ -689,7 +735,7 @@ def main() -> int:
     cs.synchronize()
     per_layer = [evs[i].elapsed_time(evs[i + 1]) for i in range(len(evs) - 1)]
 
-    pcie_ms = full_ms = controller = variants = decode_ms = store_res = overlap = reuse = peaks = None
+    pcie_ms = full_ms = controller = variants = decode_ms = store_res = overlap = reuse = peaks = int8 = None
     if not args.only_blend:
         # PCIe-inclusive variant: cached KV in pinned host memory, fetched one layer ahead
         for _ in range(2):
@@ -721,6 +767,7 @@ def main() -> int:
         decode_ms = run_decode(eng, buf, tokens, offs, wl, fused, cache)
         store_res = run_store(eng, buf, tokens, offs, wl, fused, args.steps)
         peaks = run_peaks(eng)
+        int8 = run_int8(wl, args.steps, args.warmup) if wl.shape.dtype == "bf16" else None
     if args.calib_copy:
         src = torch.empty(128 << 20, dtype=torch.bfloat16, device=eng.device)
         dst = torch.empty_like(src)
@@ -761,6 +808,7 @@ def main() -> int:
         "decode": decode_ms,
         "chunk_store": store_res,
         "ratio_sweep": sweep,
+        "int8_weights": int8,
         "speedup_vs_full_recompute": None if full_ms is None else round(full_ms / ms_step, 3),
     }
     print(json.dumps(out), flush=True)

@@ -98,6 +98,28 @@ cb_status cb_destroy(cb_ctx* ctx);
 /* Register the weights of `layer`.  Must precede cb_blend_layer / cb_layer_rest on it. */
 cb_status cb_set_layer_weights(cb_ctx* ctx, int32_t layer, const cb_layer_weights* w);
 
+/* The int8-weight variant of a layer (bf16 contexts only): every linear weight as int8 q with
+ * one fp32 scale per output channel (row), the layer's products computing
+ * sum_k bf16(x_k) * q[n][k] in fp32 (exact products, |q| <= 127) times s[n].  Same shapes and
+ * row orders as cb_layer_weights; the scales are fp32 device arrays of one entry per weight
+ * row (s_qkv [(n_q_heads + 2 n_kv_heads) * head_dim], s_o [d_model], s_gate_up [2 ffn_dim],
+ * s_down [d_model]).  Row strides (d_model, n_q_heads * head_dim, ffn_dim) must be multiples
+ * of 16 bytes.  Replaces any weights set before for the layer.  CB_EUNSUPPORTED on an fp32
+ * context; CB_EINVAL for NULL pointers. */
+typedef struct {
+  const int8_t* w_qkv;
+  const int8_t* w_o;
+  const int8_t* w_gate_up;
+  const int8_t* w_down;
+  const float* s_qkv;
+  const float* s_o;
+  const float* s_gate_up;
+  const float* s_down;
+  const float* g_attn;
+  const float* g_ffn;
+} cb_layer_weights_i8;
+cb_status cb_set_layer_weights_i8(cb_ctx* ctx, int32_t layer, const cb_layer_weights_i8* w);
+
 /* Bytes of workspace that cb_blend_layer and cb_layer_rest need for fused prompts of at
  * most n_tokens rows and selected sets of at most n_sel_max rows. */
 cb_status cb_workspace_size(const cb_ctx* ctx, int32_t n_tokens, int32_t n_sel_max, size_t* bytes);

@@ -42,6 +42,12 @@ class cb_layer_weights(C.Structure):
                 ("w_down", C.c_void_p), ("g_attn", C.c_void_p), ("g_ffn", C.c_void_p)]
 
 
+class cb_layer_weights_i8(C.Structure):
+    _fields_ = [("w_qkv", C.c_void_p), ("w_o", C.c_void_p), ("w_gate_up", C.c_void_p), ("w_down", C.c_void_p),
+                ("s_qkv", C.c_void_p), ("s_o", C.c_void_p), ("s_gate_up", C.c_void_p), ("s_down", C.c_void_p),
+                ("g_attn", C.c_void_p), ("g_ffn", C.c_void_p)]
+
+
 def _load() -> C.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"HIP library {LIB_PATH} is not built; run `python -m rag_kv_cache_amd.build`")
@@ -57,6 +63,7 @@ _SIGS = {
     "cb_create": [C.POINTER(cb_model_desc), _I, _P, _P, C.POINTER(_P)],
     "cb_destroy": [_P],
     "cb_set_layer_weights": [_P, _I, C.POINTER(cb_layer_weights)],
+    "cb_set_layer_weights_i8": [_P, _I, C.POINTER(cb_layer_weights_i8)],
     "cb_workspace_size": [_P, _I, _I, C.POINTER(C.c_size_t)],
     "cb_embed": [_P, _P, _I, _P, _P],
     "cb_fetch_layer": [_P, _I, C.POINTER(_P), C.POINTER(_P), C.POINTER(_I), _I, _P, _P, _P],
@@ -121,6 +128,12 @@ def cb_set_layer_weights(ctx: int, layer: int, w_qkv: int, w_o: int, w_gate_up: 
                          g_attn: int, g_ffn: int) -> None:
     w = cb_layer_weights(w_qkv, w_o, w_gate_up, w_down, g_attn, g_ffn)
     _check(_L.cb_set_layer_weights(ctx, layer, C.byref(w)))
+
+
+def cb_set_layer_weights_i8(ctx: int, layer: int, w_qkv: int, w_o: int, w_gate_up: int, w_down: int,
+                            s_qkv: int, s_o: int, s_gate_up: int, s_down: int, g_attn: int, g_ffn: int) -> None:
+    w = cb_layer_weights_i8(w_qkv, w_o, w_gate_up, w_down, s_qkv, s_o, s_gate_up, s_down, g_attn, g_ffn)
+    _check(_L.cb_set_layer_weights_i8(ctx, layer, C.byref(w)))
 
 
 def cb_workspace_size(ctx: int, n_tokens: int, n_sel_max: int) -> int:

@@ -73,6 +73,11 @@ struct cb_ctx {
   float2* rope = nullptr;  // [max_tokens][head_dim / 2]
   std::vector<cb_layer_weights> w;
   std::vector<char> have_w;
+  // int8 layers: per-output-channel scales of w_qkv, w_o, w_gate_up, w_down (NULL: bf16 layer)
+  struct Scales {
+    const float *qkv, *o, *gate_up, *down;
+  };
+  std::vector<Scales> ws8;
   std::vector<hipEvent_t> fetch_ev;
   std::vector<hipEvent_t> release_ev;  // per layer: the compute stream is done with its fused K/V
   std::vector<int> state;
@@ -250,6 +255,7 @@ cb_status cb_create(const cb_model_desc* desc, int32_t device, void* compute_str
   c->xs = copy_stream ? (hipStream_t)copy_stream : c->cs;
   c->w.resize(d.n_layers);
   c->have_w.assign(d.n_layers, 0);
+  c->ws8.assign(d.n_layers, cb_ctx::Scales{nullptr, nullptr, nullptr, nullptr});
   c->state.assign(d.n_layers, LS_IDLE);
   c->fetch_ev.assign(d.n_layers, nullptr);
   for (int l = 0; l < d.n_layers; ++l) {
@@ -303,6 +309,24 @@ cb_status cb_set_layer_weights(cb_ctx* c, int32_t layer, const cb_layer_weights*
     return fail(CB_EINVAL, "a weight pointer of layer %d is NULL", layer);
   c->w[layer] = *w;
   c->have_w[layer] = 1;
+  c->ws8[layer] = cb_ctx::Scales{nullptr, nullptr, nullptr, nullptr};
+  return CB_OK;
+}
+
+cb_status cb_set_layer_weights_i8(cb_ctx* c, int32_t layer, const cb_layer_weights_i8* w) {
+  cb_status st = check_ctx(c);
+  if (st) return st;
+  if ((st = check_layer(c, layer, false))) return st;
+  if (!c->bf16()) return fail(CB_EUNSUPPORTED, "int8 weights need a bf16 context");
+  if (!w || !w->w_qkv || !w->w_o || !w->w_gate_up || !w->w_down || !w->s_qkv || !w->s_o || !w->s_gate_up ||
+      !w->s_down || !w->g_attn || !w->g_ffn)
+    return fail(CB_EINVAL, "a weight or scale pointer of layer %d is NULL", layer);
+  const cb_model_desc& d = c->d;
+  if (d.d_model % 16 || (d.n_q_heads * d.head_dim) % 16 || d.ffn_dim % 16)
+    return fail(CB_EUNSUPPORTED, "int8 weight rows must be multiples of 16 bytes");
+  c->w[layer] = cb_layer_weights{w->w_qkv, w->w_o, w->w_gate_up, w->w_down, w->g_attn, w->g_ffn};
+  c->have_w[layer] = 1;
+  c->ws8[layer] = cb_ctx::Scales{w->s_qkv, w->s_o, w->s_gate_up, w->s_down};
   return CB_OK;
 }
 
@@ -563,6 +587,7 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
   const int qd = d.n_q_heads * d.head_dim;
   const int dm = d.d_model;
   const cb_layer_weights& W = c->w[layer];
+  const cb_ctx::Scales& S8 = c->ws8[layer];
   hipError_t e;
 
   // 1. position update of the cached K (and copy of V) into the fused buffer
@@ -592,7 +617,9 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
   {
     cb::GemmArgs g{};
     g.A = x; g.lda = dm; g.a_rows = nullptr;
-    g.B = fuse_q ? W.w_qkv : (const char*)W.w_qkv + (size_t)qd * dm * es; g.ldb = dm;
+    const size_t wes = S8.qkv ? 1 : es;  // bytes per weight
+    g.B = fuse_q ? W.w_qkv : (const char*)W.w_qkv + (size_t)qd * dm * wes; g.ldb = dm;
+    g.b_i8 = S8.qkv != nullptr; g.bscale = S8.qkv ? S8.qkv + (fuse_q ? 0 : qd) : nullptr;
     g.M = n_sel; g.N = fresh_ld; g.K = dm;
     g.partial = (float*)(ws + wp.gpart);
     g.epi = cb::EPI_ROPE; g.out = fresh; g.ldo = fresh_ld;
@@ -627,6 +654,7 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
     cb::GemmArgs g{};
     g.A = x; g.lda = dm; g.a_rows = new_sel_local; g.a_rows_total = n_sel;
     g.B = W.w_qkv; g.ldb = dm;
+    g.b_i8 = S8.qkv != nullptr; g.bscale = S8.qkv;
     g.M = nn; g.N = qd; g.K = dm;
     g.partial = (float*)(ws + wp.gpart);
     g.epi = cb::EPI_ROPE; g.out = q; g.ldo = qd;
@@ -695,6 +723,7 @@ cb_status cb_layer_rest(cb_ctx* c, int32_t layer, const float* hidden_sel, int32
   const int es = c->esize();
   const int dm = d.d_model, qd = d.n_q_heads * d.head_dim, ff = d.ffn_dim;
   const cb_layer_weights& W = c->w[layer];
+  const cb_ctx::Scales& S8 = c->ws8[layer];
   float* h1 = (float*)(ws + wp.h1);
   void* mn = ws + wp.mnorm;
   void* act = ws + wp.act;
@@ -702,6 +731,7 @@ cb_status cb_layer_rest(cb_ctx* c, int32_t layer, const float* hidden_sel, int32
   {  // h1 = hidden_sel[new_sel_local] + out_sel W_o^T, and mn = RMSNorm(h1) (fused for bf16)
     cb::GemmArgs g{};
     g.A = out_sel; g.lda = qd; g.B = W.w_o; g.ldb = qd;
+    g.b_i8 = S8.o != nullptr; g.bscale = S8.o;
     g.M = n_new; g.N = dm; g.K = qd;
     g.partial = (float*)(ws + wp.gpart);
     g.epi = cb::EPI_RESID; g.out = h1; g.ldo = dm; g.resid = hidden_sel; g.ldr = dm; g.resid_rows = new_sel_local;
@@ -719,6 +749,7 @@ cb_status cb_layer_rest(cb_ctx* c, int32_t layer, const float* hidden_sel, int32
   {  // act = silu(m W_gate^T) * (m W_up^T)
     cb::GemmArgs g{};
     g.A = mn; g.lda = dm; g.B = W.w_gate_up; g.ldb = dm; g.swiglu_ffn = ff;
+    g.b_i8 = S8.gate_up != nullptr; g.bscale = S8.gate_up;
     g.M = n_new; g.N = 2 * ff; g.K = dm;
     g.epi = cb::EPI_SWIGLU; g.out = act; g.ldo = ff;
     plan_gemm(g, bf, 0);
@@ -729,6 +760,7 @@ cb_status cb_layer_rest(cb_ctx* c, int32_t layer, const float* hidden_sel, int32
   {  // hidden_next = h1 + act W_down^T
     cb::GemmArgs g{};
     g.A = act; g.lda = ff; g.B = W.w_down; g.ldb = ff;
+    g.b_i8 = S8.down != nullptr; g.bscale = S8.down;
     g.M = n_new; g.N = dm; g.K = ff;
     g.partial = (float*)(ws + wp.gpart);
     g.epi = cb::EPI_RESID; g.out = hidden_next; g.ldo = dm; g.resid = h1; g.ldr = dm;

@@ -21,6 +21,8 @@ struct GemmArgs {
   const float* resid; long ldr; const int32_t* resid_rows;                  // RESID
   const float* norm_g; float norm_eps; void* norm_out;  // RESID: also RMSNorm(out) -> bf16 [M][N]
   int cfg;               // bf16 tile configuration (GemmCfg), from gemm_plan
+  int b_i8;              // B is int8 [N][ldb] with per-row (output channel) scales bscale[N]
+  const float* bscale;
 };
 hipError_t gemm_bf16(const GemmArgs& g, hipStream_t s);
 enum GemmCfg { GEMM_128x512 = 0, GEMM_128x256 = 1, GEMM_64x256 = 2, GEMM_128x128 = 3, GEMM_64x128 = 4, GEMM_256x256 = 5, GEMM_GEMV = 6 };

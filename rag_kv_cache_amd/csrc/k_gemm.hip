@@ -127,7 +127,23 @@ __device__ __forceinline__ void wait_vm_steps(int ahead) {
 
 // amdgpu_waves_per_eu(2): a register budget of 256 arch VGPRs; with more, the 4-wave tiles
 // get their accumulators in AGPRs and copy them around in the main loop.
-template <int BM, int BN, int WM, int WN, int NS, int EPI>
+// Eight int8 weights (two dwords) as eight bf16 (exact for |q| <= 127) in a 16-byte chunk.
+__device__ __forceinline__ uint4 i8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  float f[8];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    f[b] = (float)(int8_t)(lo >> (8 * b));
+    f[4 + b] = (float)(int8_t)(hi >> (8 * b));
+  }
+  return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+}
+
+// BT = 0: bf16 weights, global -> LDS by DMA like the activations.  BT = 1: int8 weights with a
+// per-output-channel scale (g.bscale): a K-step's weight tile goes global -> registers one
+// K-step ahead, is converted to bf16 (exact) and written to the same LDS layout, so the MFMA
+// loop is unchanged; the scale multiplies the fp32 sums before the epilogue (split-K: in the
+// reduce).
+template <int BM, int BN, int WM, int WN, int NS, int EPI, int BT>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2))) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -177,19 +193,54 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
     const long grow = g.a_rows ? (long)g.a_rows[m] : (long)m;
     a_vo[i] = (uint32_t)((grow * g.lda + (long)kb0 * BK + chunk * 8) * 2);
   }
+  if constexpr (BT == 0) {
 #pragma unroll
-  for (int i = 0; i < B_PW; ++i) {
-    const int row = (wave * B_PW + i) * 8 + r8;
-    b_vo[i] = (uint32_t)(((long)logical_col<EPI, BN>(g, tn, row) * g.ldb + (long)kb0 * BK + chunk * 8) * 2);
+    for (int i = 0; i < B_PW; ++i) {
+      const int row = (wave * B_PW + i) * 8 + r8;
+      b_vo[i] = (uint32_t)(((long)logical_col<EPI, BN>(g, tn, row) * g.ldb + (long)kb0 * BK + chunk * 8) * 2);
+    }
   }
+  // int8 weights: thread tid owns 16-byte pieces ci = tid + j * threads of the tile's 64-byte
+  // K-step rows (row ci / 4, piece ci % 4), i.e. bf16 chunks 2 (ci % 4) and 2 (ci % 4) + 1
+  constexpr int CPT = BT ? BN * 4 / (64 * NW) : 1;
+  static_assert(!BT || (BN * 4) % (64 * NW) == 0, "int8 weight pieces per thread");
+  long b8_off[CPT];
+  int b8_lds[CPT];
+  uint4 rb[CPT];
+  if constexpr (BT) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int ci = tid + j * 64 * NW;
+      const int row = ci >> 2, pc = ci & 3;
+      b8_off[j] = (long)logical_col<EPI, BN>(g, tn, row) * g.ldb + (long)kb0 * BK + pc * 16;
+      b8_lds[j] = BM * ROWB + row * ROWB;
+      rb[j] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  auto load_b8 = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) rb[j] = *reinterpret_cast<const uint4*>((const char*)g.B + b8_off[j] + (long)kt * BK);
+  };
+  auto store_b8 = [&](int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int ci = tid + j * 64 * NW;
+      const int row = ci >> 2, pc = ci & 3;
+      unsigned char* rp = smem + st * STAGE_B + b8_lds[j];
+      *reinterpret_cast<uint4*>(rp + (((2 * pc) ^ (row & 7)) << 4)) = i8x8_to_bf16(rb[j].x, rb[j].y);
+      *reinterpret_cast<uint4*>(rp + (((2 * pc + 1) ^ (row & 7)) << 4)) = i8x8_to_bf16(rb[j].z, rb[j].w);
+    }
+  };
   auto issue = [&](int kt, int st) __attribute__((always_inline)) {
     unsigned char* base = smem + st * STAGE_B;
     const int koff = kt * BK * 2;
 #pragma unroll
     for (int i = 0; i < A_PW; ++i) buffer_load_lds16(g.A, a_bytes, base + (wv * A_PW + i) * 1024, a_vo[i], koff);
+    if constexpr (BT == 0) {
 #pragma unroll
-    for (int i = 0; i < B_PW; ++i)
-      buffer_load_lds16(g.B, b_bytes, base + BM * ROWB + (wv * B_PW + i) * 1024, b_vo[i], koff);
+      for (int i = 0; i < B_PW; ++i)
+        buffer_load_lds16(g.B, b_bytes, base + BM * ROWB + (wv * B_PW + i) * 1024, b_vo[i], koff);
+    }
   };
 
   f32x4_t acc[FM][FN];
@@ -227,20 +278,49 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
   // of the other.  At the one barrier per K-step every wave has (a) waited for its own loads of
   // K-step t+1 and (b) finished reading stage t, which is then refilled with K-step t+NS.  The
   // steady loop has a constant wait and no branch; the last NS-1 K-steps drain separately.
+  // int8 weights: the tile of K-step t+NS is loaded into registers after the barrier of
+  // iteration t (before that step's DMA, so that one wait leaves only the DMA in flight) and
+  // written to its stage, converted, in iteration t+1 before that iteration's barrier; the
+  // stage was read for the last time before iteration t's barrier and is next read in
+  // iteration t+NS > t+1.
+  constexpr int LPWD = BT ? A_PW : LPW;  // DMA instructions per wave per K-step
 #pragma unroll
   for (int s = 0; s < NS; ++s)
     if (s < nk) issue(s, s);
-  wait_vm_steps<LPW>(min(NS - 1, nk - 1));  // K-step 0 landed; later K-steps may be in flight
+  if constexpr (BT == 0) {
+    wait_vm_steps<LPW>(min(NS - 1, nk - 1));  // K-step 0 landed; later K-steps may be in flight
+  } else {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {  // the first stages' weights, one stage at a time
+      if (s < nk) {
+        load_b8(s);
+        wait_vm<0>();
+        store_b8(s);
+      }
+    }
+    wait_lgkm0();
+  }
   barrier();
   bf16x8_t a0[FM], b0[FN], a1[FM], b1[FN];
   read(0, 0, a0, b0);
   int st = 0, t = 0;
+  int pst = -1;  // stage whose int8 weights wait in registers (none: -1)
   for (; t + NS < nk; ++t) {
     read(st, 1, a1, b1);
     mma(a0, b0);
-    wait_lgkm0();                        // this wave is done reading stage st
-    wait_vm<Sat63<(NS - 2) * LPW>::v>();  // K-step t+1 landed (t+2 .. t+NS-1 may be in flight)
+    if constexpr (BT) {
+      if (pst >= 0) {
+        wait_vm<Sat63<A_PW>::v>();  // only the last K-step's DMA may still be in flight
+        store_b8(pst);
+      }
+    }
+    wait_lgkm0();                         // this wave is done reading stage st
+    wait_vm<Sat63<(NS - 2) * LPWD>::v>();  // K-step t+1 landed (t+2 .. t+NS-1 may be in flight)
     barrier();
+    if constexpr (BT) {
+      load_b8(t + NS);
+      pst = st;
+    }
     issue(t + NS, st);
     st = st + 1 == NS ? 0 : st + 1;
     read(st, 0, a0, b0);
@@ -249,8 +329,15 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
   for (; t + 1 < nk; ++t) {
     read(st, 1, a1, b1);
     mma(a0, b0);
+    if constexpr (BT) {
+      if (pst >= 0) {
+        wait_vm<Sat63<A_PW>::v>();
+        store_b8(pst);
+        pst = -1;
+      }
+    }
     wait_lgkm0();
-    wait_vm_steps<LPW>(nk - 2 - t);  // K-step t+1 landed
+    wait_vm_steps<LPWD>(nk - 2 - t);  // K-step t+1 landed
     barrier();
     st = st + 1 == NS ? 0 : st + 1;
     read(st, 0, a0, b0);
@@ -259,6 +346,23 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
   read(st, 1, a1, b1);
   mma(a0, b0);
   mma(a1, b1);
+  if constexpr (BT) {  // per-output-channel weight scales (split-K partials stay unscaled)
+    if (g.splits == 1) {
+#pragma unroll
+      for (int q = 0; q < FN / 2; ++q) {
+        const int tc = wn * WTN + q * 32 + (lane & 15);
+        const float sa = g.bscale[logical_col<EPI, BN>(g, tn, tc)];
+        const float sb = g.bscale[logical_col<EPI, BN>(g, tn, tc + 16)];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            acc[i][2 * q][r] *= sa;
+            acc[i][2 * q + 1][r] *= sb;
+          }
+      }
+    }
+  }
 
   // Epilogue.  The pair math (RoPE rotation, SwiGLU) runs on the fp32 accumulators in
   // registers; the results are staged in LDS (the operand stages are free by now) in output
@@ -376,7 +480,7 @@ constexpr int gemm_lds_bytes(bool f32_out) {
   return ring > stage ? ring : stage;
 }
 
-template <int BM, int BN, int WM, int WN, int NS, int EPI>
+template <int BM, int BN, int WM, int WN, int NS, int EPI, int BT>
 hipError_t launch_dma(const GemmArgs& g, hipStream_t s) {
   constexpr int kMaxLds = 160 * 1024;
   static_assert(NS * (BM + BN) * BK * 2 <= kMaxLds, "LDS");
@@ -384,17 +488,18 @@ hipError_t launch_dma(const GemmArgs& g, hipStream_t s) {
   if (lds > kMaxLds || g.N % BN != 0 || g.splits < 1 || g.splits > g.K / BK) return hipErrorInvalidValue;
   // operand byte offsets are 32-bit buffer offsets
   const long a_rows = g.a_rows_total ? g.a_rows_total : g.M;
-  if (a_rows * g.lda * 2 >= (1L << 31) || (long)g.N * g.ldb * 2 >= (1L << 31)) return hipErrorInvalidValue;
+  if (a_rows * g.lda * 2 >= (1L << 31) || (long)g.N * g.ldb * (BT ? 1 : 2) >= (1L << 31)) return hipErrorInvalidValue;
+  if (BT && (!g.bscale || g.ldb % 16 != 0)) return hipErrorInvalidValue;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<BM, BN, WM, WN, NS, EPI>,
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<BM, BN, WM, WN, NS, EPI, BT>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int tiles = ((g.M + BM - 1) / BM) * (g.N / BN);
   const int grid_x = 8 * ((tiles + 7) / 8);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, NS, EPI>), dim3(grid_x, g.splits), dim3(64 * WM * WN), lds, s, g);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, NS, EPI, BT>), dim3(grid_x, g.splits), dim3(64 * WM * WN), lds, s, g);
   return hipGetLastError();
 }
 
@@ -426,6 +531,11 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
     const float4 b = *reinterpret_cast<const float4*>(p + s * stride + n_b);
     va.x += a.x; va.y += a.y; va.z += a.z; va.w += a.w;
     vb.x += b.x; vb.y += b.y; vb.z += b.z; vb.w += b.w;
+  }
+  if (g.bscale) {  // int8 weights: per-output-channel scale of the summed partials
+    const float4 sa = *reinterpret_cast<const float4*>(g.bscale + n_a), sb = *reinterpret_cast<const float4*>(g.bscale + n_b);
+    va.x *= sa.x; va.y *= sa.y; va.z *= sa.z; va.w *= sa.w;
+    vb.x *= sb.x; vb.y *= sb.y; vb.z *= sb.z; vb.w *= sb.w;
   }
   epi_pair<EPI, bf16_t>(g, m, n_a + 0, n_b + 0, va.x, vb.x);
   epi_pair<EPI, bf16_t>(g, m, n_a + 1, n_b + 1, va.y, vb.y);
@@ -470,6 +580,10 @@ __global__ __launch_bounds__(64 * kResidWavesMax) void splitk_resid_norm_kernel(
 #pragma unroll
       for (int sp = 1; sp < 8; ++sp)
         if (sp < g.splits) { v.x += a[sp].x; v.y += a[sp].y; v.z += a[sp].z; v.w += a[sp].w; }
+      if (g.bscale) {  // int8 weights: per-output-channel scale of the summed partials
+        const float4 sc = *reinterpret_cast<const float4*>(g.bscale + e);
+        v.x *= sc.x; v.y *= sc.y; v.z *= sc.z; v.w *= sc.w;
+      }
       w[j] = make_float4(rv.x + v.x, rv.y + v.y, rv.z + v.z, rv.w + v.w);
       *reinterpret_cast<float4*>(o + e) = w[j];
       q = w[j].x * w[j].x + w[j].y * w[j].y + w[j].z * w[j].z + w[j].w * w[j].w;
@@ -538,7 +652,21 @@ __device__ __forceinline__ float dot8_bf16(const uint4 a, const uint4 w) {
   return s;
 }
 
-template <int EPI, int MR>
+// Dot product of 8 bf16 activations with 8 int8 weights (two dwords).
+__device__ __forceinline__ float dot8_bf16_i8(const uint4 a, uint32_t wlo, uint32_t whi) {
+  const uint32_t av[4] = {a.x, a.y, a.z, a.w};
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = i < 2 ? wlo : whi;
+    const int sh = (i & 1) * 16;
+    s = fmaf(__uint_as_float(av[i] << 16), (float)(int8_t)(w >> sh), s);
+    s = fmaf(__uint_as_float(av[i] & 0xffff0000u), (float)(int8_t)(w >> (sh + 8)), s);
+  }
+  return s;
+}
+
+template <int EPI, int MR, int BT>
 __global__ __launch_bounds__(256) void gemv_bf16_kernel(GemmArgs g) {
   constexpr int NR = 2 * GV_P;  // weight rows of the workgroup
   __shared__ float part[4][MR][NR];
@@ -546,14 +674,15 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(GemmArgs g) {
   const int j0 = blockIdx.x * GV_P;
   const int n_pairs = g.N / 2;
   const bf16_t* A = reinterpret_cast<const bf16_t*>(g.A);
-  const bf16_t* B = reinterpret_cast<const bf16_t*>(g.B);
-  const bf16_t* wrow[NR];
+  const char* B = reinterpret_cast<const char*>(g.B);
+  constexpr int WB = BT ? 1 : 2;  // bytes per weight
+  const char* wrow[NR];
 #pragma unroll
   for (int q = 0; q < GV_P; ++q) {
     int n_a, n_b;
     gv_pair_cols(g, EPI, min(j0 + q, n_pairs - 1), n_a, n_b);
-    wrow[2 * q] = B + (long)n_a * g.ldb;
-    wrow[2 * q + 1] = B + (long)n_b * g.ldb;
+    wrow[2 * q] = B + (long)n_a * g.ldb * WB;
+    wrow[2 * q + 1] = B + (long)n_b * g.ldb * WB;
   }
   const bf16_t* arow[MR];
 #pragma unroll
@@ -568,15 +697,26 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int r = 0; r < NR; ++r) acc[m][r] = 0.f;
   for (int k = wave * kq + lane * 8; k < (wave + 1) * kq; k += 512) {
-    uint4 w[NR], a[MR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r) w[r] = *reinterpret_cast<const uint4*>(wrow[r] + k);
+    uint4 a[MR];
 #pragma unroll
     for (int m = 0; m < MR; ++m) a[m] = *reinterpret_cast<const uint4*>(arow[m] + k);
+    if constexpr (BT) {
+      uint2 w[NR];
 #pragma unroll
-    for (int m = 0; m < MR; ++m)
+      for (int r = 0; r < NR; ++r) w[r] = *reinterpret_cast<const uint2*>(wrow[r] + k);
 #pragma unroll
-      for (int r = 0; r < NR; ++r) acc[m][r] += dot8_bf16(a[m], w[r]);
+      for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int r = 0; r < NR; ++r) acc[m][r] += dot8_bf16_i8(a[m], w[r].x, w[r].y);
+    } else {
+      uint4 w[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) w[r] = *reinterpret_cast<const uint4*>(wrow[r] + (long)k * 2);
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int r = 0; r < NR; ++r) acc[m][r] += dot8_bf16(a[m], w[r]);
+    }
   }
 #pragma unroll
   for (int m = 0; m < MR; ++m)
@@ -599,21 +739,26 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(GemmArgs g) {
       }
       int n_a, n_b;
       gv_pair_cols(g, EPI, j, n_a, n_b);
+      if (BT) {  // int8 weights: per-output-channel scales
+        va *= g.bscale[n_a];
+        vb *= g.bscale[n_b];
+      }
       epi_pair<EPI, bf16_t>(g, m, n_a, n_b, va, vb);
     }
   }
 }
 
-template <int EPI>
+template <int EPI, int BT>
 hipError_t launch_gemv(const GemmArgs& g, hipStream_t s) {
   if (g.M > 4 || g.K % 32 != 0 || g.N % 2 != 0) return hipErrorInvalidValue;
+  if (BT && !g.bscale) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((g.N / 2 + GV_P - 1) / GV_P));
   if (g.M == 1)
-    hipLaunchKernelGGL((gemv_bf16_kernel<EPI, 1>), grid, dim3(256), 0, s, g);
+    hipLaunchKernelGGL((gemv_bf16_kernel<EPI, 1, BT>), grid, dim3(256), 0, s, g);
   else if (g.M == 2)
-    hipLaunchKernelGGL((gemv_bf16_kernel<EPI, 2>), grid, dim3(256), 0, s, g);
+    hipLaunchKernelGGL((gemv_bf16_kernel<EPI, 2, BT>), grid, dim3(256), 0, s, g);
   else
-    hipLaunchKernelGGL((gemv_bf16_kernel<EPI, 4>), grid, dim3(256), 0, s, g);
+    hipLaunchKernelGGL((gemv_bf16_kernel<EPI, 4, BT>), grid, dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
@@ -700,24 +845,24 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 }
 
 // ------------------------------------------------------------------ launch
-template <int EPI>
+template <int EPI, int BT>
 hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
   hipError_t e;
   switch (g.cfg) {
     case GEMM_GEMV:
-      return launch_gemv<EPI>(g, s);
+      return launch_gemv<EPI, BT>(g, s);
     case GEMM_128x512:  // planned for the SwiGLU epilogue only
-      if constexpr (EPI == EPI_SWIGLU) { e = launch_dma<128, 512, 2, 4, 2, EPI>(g, s); break; }
+      if constexpr (EPI == EPI_SWIGLU) { e = launch_dma<128, 512, 2, 4, 2, EPI, BT>(g, s); break; }
       return hipErrorInvalidValue;
     case GEMM_256x256:  // bf16 output, no split (the fp32 staged tile would not fit in LDS)
       if constexpr (EPI != EPI_RESID) {
-        if (g.splits == 1) { e = launch_dma<256, 256, 2, 4, 2, EPI>(g, s); break; }
+        if (g.splits == 1) { e = launch_dma<256, 256, 2, 4, 2, EPI, BT>(g, s); break; }
       }
       return hipErrorInvalidValue;
-    case GEMM_128x256: e = launch_dma<128, 256, 2, 4, 3, EPI>(g, s); break;
-    case GEMM_64x256: e = launch_dma<64, 256, 1, 4, 3, EPI>(g, s); break;
-    case GEMM_128x128: e = launch_dma<128, 128, 2, 2, 3, EPI>(g, s); break;
-    case GEMM_64x128: e = launch_dma<64, 128, 2, 2, 4, EPI>(g, s); break;
+    case GEMM_128x256: e = launch_dma<128, 256, 2, 4, 3, EPI, BT>(g, s); break;
+    case GEMM_64x256: e = launch_dma<64, 256, 1, 4, 3, EPI, BT>(g, s); break;
+    case GEMM_128x128: e = launch_dma<128, 128, 2, 2, 3, EPI, BT>(g, s); break;
+    case GEMM_64x128: e = launch_dma<64, 128, 2, 2, 4, EPI, BT>(g, s); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || g.splits <= 1) return e;
@@ -825,10 +970,10 @@ hipError_t gemm_bf16(const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0) return hipSuccess;
   hipError_t e;
   switch (g.epi) {
-    case EPI_ROPE: e = launch_epi<EPI_ROPE>(g, s); break;
-    case EPI_SWIGLU: e = launch_epi<EPI_SWIGLU>(g, s); break;
-    case EPI_RESID: e = launch_epi<EPI_RESID>(g, s); break;
-    default: e = launch_epi<EPI_STORE>(g, s); break;
+    case EPI_ROPE: e = g.b_i8 ? launch_epi<EPI_ROPE, 1>(g, s) : launch_epi<EPI_ROPE, 0>(g, s); break;
+    case EPI_SWIGLU: e = g.b_i8 ? launch_epi<EPI_SWIGLU, 1>(g, s) : launch_epi<EPI_SWIGLU, 0>(g, s); break;
+    case EPI_RESID: e = g.b_i8 ? launch_epi<EPI_RESID, 1>(g, s) : launch_epi<EPI_RESID, 0>(g, s); break;
+    default: e = g.b_i8 ? launch_epi<EPI_STORE, 1>(g, s) : launch_epi<EPI_STORE, 0>(g, s); break;
   }
   // the RMSNorm of a residual output that was written directly (no split-K reduce)
   if (e == hipSuccess && g.epi == EPI_RESID && g.norm_out && g.splits <= 1)

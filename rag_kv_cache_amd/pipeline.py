@@ -88,6 +88,32 @@ class Engine:
         L.cb_set_layer_weights(self.ctx, layer, _ptr(t["w_qkv"]), _ptr(t["w_o"]), _ptr(t["w_gate_up"]),
                                _ptr(t["w_down"]), _ptr(t["g_attn"]), _ptr(t["g_ffn"]))
 
+    def load_layer_int8(self, layer: int, wq: Dict[str, np.ndarray]) -> None:
+        """wq: int8 q_q, q_k, q_v, q_o, q_gate, q_up, q_down [out, in], their float32 per-row
+        scales s_<name> [out], and the float32 gains g_attn, g_ffn (bf16 engines only)."""
+        def dev8(a):
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int8)).to(self.device)
+
+        def dev32(a):
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(self.device)
+
+        t = {
+            "w_qkv": dev8(np.concatenate([wq["q_q"], wq["q_k"], wq["q_v"]])),
+            "w_o": dev8(wq["q_o"]),
+            "w_gate_up": dev8(np.concatenate([wq["q_gate"], wq["q_up"]])),
+            "w_down": dev8(wq["q_down"]),
+            "s_qkv": dev32(np.concatenate([wq["s_q"], wq["s_k"], wq["s_v"]])),
+            "s_o": dev32(wq["s_o"]),
+            "s_gate_up": dev32(np.concatenate([wq["s_gate"], wq["s_up"]])),
+            "s_down": dev32(wq["s_down"]),
+            "g_attn": dev32(wq["g_attn"]),
+            "g_ffn": dev32(wq["g_ffn"]),
+        }
+        self.weights[layer] = t
+        L.cb_set_layer_weights_i8(self.ctx, layer, _ptr(t["w_qkv"]), _ptr(t["w_o"]), _ptr(t["w_gate_up"]),
+                                  _ptr(t["w_down"]), _ptr(t["s_qkv"]), _ptr(t["s_o"]), _ptr(t["s_gate_up"]),
+                                  _ptr(t["s_down"]), _ptr(t["g_attn"]), _ptr(t["g_ffn"]))
+
     def load_embedding(self, emb: np.ndarray) -> None:
         self.emb = self._dev(emb)
 
