@@ -5,7 +5,8 @@ chunks of 640 + 256 query rows, GQA group 4; recompute ratios 10%, 15% and 20%),
 
 The first three decoder layers of each shape run (layer 1 at ratio 1, layer 2 narrowing to the
 ratio, layer 3 at the steady ratio); every kernel sees the same sizes at any depth, so these
-layers cover the whole model's launch shapes.  Each layer is checked against the oracle with the
+layers cover the whole model's launch shapes.  The Llama-70B cases, whose cached KV streams
+from pinned host memory, also run the prefetched path and must give the same bits.  Each layer is checked against the oracle with the
 GPU's own inputs of that layer (teacher-forced, sampled rows), as at the benchmark's size; then
 one decode step on the fused KV, each layer against the oracle's decode layer fed the GPU's input
 row and fused rows of that layer."""
@@ -13,6 +14,7 @@ from dataclasses import replace
 
 import numpy as np
 import pytest
+import torch
 
 import fixtures as F
 from sampled_checks import check_chunk_cache, check_decode_teacher_forced, check_layer
@@ -67,7 +69,8 @@ def test_shape_teacher_forced(name):
     print(f"[shapes] {name}: {wl.n_ctx} context + {wl.n_query} query rows, schedule {wl.schedule}", flush=True)
     chunks = F.chunk_tokens(wl)
     tokens = F.all_tokens(wl)
-    cache, _ = build_chunk_caches(eng, chunks)
+    streamed = name.startswith("l70")  # these shapes stream the cached KV from pinned host memory
+    cache, host = build_chunk_caches(eng, chunks, pinned_host=streamed)
     buf = make_buffers(eng, wl.n_tokens + 1, len(chunks))
     fused = [(eng.kv_empty(wl.n_tokens + 1), eng.kv_empty(wl.n_tokens + 1)) for _ in range(N_LAYERS)]
     res = run_layers(eng, buf, tokens, F.chunk_offsets(wl), wl.n_query, wl.schedule, fused,
@@ -80,6 +83,18 @@ def test_shape_teacher_forced(name):
         print(f"[shapes] {name}: layer {layer + 1}, {len(res.records[layer].sel)} -> "
               f"{len(res.records[layer].new_sel)} rows", flush=True)
         check_layer(wl, layer, W[layer], res.records[layer], hidden_in[layer], cache[layer], fused[layer])
+
+    if streamed:  # the pinned-host prefetch path gives the same bits as the HBM-resident one
+        buf2 = make_buffers(eng, wl.n_tokens + 1, len(chunks))
+        fused2 = [(eng.kv_empty(wl.n_tokens + 1), eng.kv_empty(wl.n_tokens + 1)) for _ in range(N_LAYERS)]
+        res2 = run_layers(eng, buf2, tokens, F.chunk_offsets(wl), wl.n_query, wl.schedule, fused2, host_cache=host)
+        eng.compute.synchronize()
+        assert res2.n_final == res.n_final
+        assert np.array_equal(res2.hidden[: res2.n_final].cpu().numpy(), res.hidden[: res.n_final].cpu().numpy())
+        for (a, b), (c, d) in zip(fused, fused2):
+            assert np.array_equal(a.view(torch.int16).cpu().numpy(), c.view(torch.int16).cpu().numpy())
+            assert np.array_equal(b.view(torch.int16).cpu().numpy(), d.view(torch.int16).cpu().numpy())
+        del buf2, fused2, host
 
     # one decode step on the fused KV, layer by layer (the few-row attention over every fused row)
     check_decode_teacher_forced(eng, buf, fused, wl, W, emb, 11)
