@@ -23,6 +23,20 @@ namespace {
 
 constexpr float NEG_INF = -__builtin_huge_valf();
 
+typedef _Float16 half_t;
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+// Two floats as packed fp16 (round to nearest even), low half = lo.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f16x2_t v = {(half_t)lo, (half_t)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float4 unpack_f16x4(const u32x2_t p) {
+  // through scalar temporaries: a bit cast of a vector element subscript (p[1]) reads element 0
+  const uint32_t lo = p.x, hi = p.y;
+  const f16x2_t a = __builtin_bit_cast(f16x2_t, lo), b = __builtin_bit_cast(f16x2_t, hi);
+  return make_float4((float)a[0], (float)a[1], (float)b[0], (float)b[1]);
+}
+
 typedef __attribute__((address_space(1))) void gvoid_t;
 typedef __attribute__((address_space(3))) void lvoid_t;
 
@@ -271,12 +285,14 @@ __global__ __launch_bounds__(64 * G * QT) void attn_bf16_kernel(AttnArgs a) {
       for (int d = 0; d < 8; ++d)
         *reinterpret_cast<u32x2_t*>(out + d * 16) =
             u32x2_t{pack_bf16x2(o[rb][d][0] * inv, o[rb][d][1] * inv), pack_bf16x2(o[rb][d][2] * inv, o[rb][d][3] * inv)};
-    } else {
+    } else {  // the split's O normalized by its own sum, as fp16 (|O| <= max |V|), and (max, sum)
+      const float inv = l_i[rb] > 0.f ? 1.f / l_i[rb] : 0.f;
       const long idx = ((long)split * a.n_q + my_row) * a.hq + h;
-      float* po = a.part_o + idx * DH + lg * 4;
+      half_t* po = reinterpret_cast<half_t*>(a.part_o) + idx * DH + lg * 4;
 #pragma unroll
       for (int d = 0; d < 8; ++d)
-        *reinterpret_cast<float4*>(po + d * 16) = make_float4(o[rb][d][0], o[rb][d][1], o[rb][d][2], o[rb][d][3]);
+        *reinterpret_cast<u32x2_t*>(po + d * 16) =
+            u32x2_t{pack_f16x2(o[rb][d][0] * inv, o[rb][d][1] * inv), pack_f16x2(o[rb][d][2] * inv, o[rb][d][3] * inv)};
       if (lg == 0) *reinterpret_cast<float2*>(a.part_ml + idx * 2) = make_float2(m_i[rb] * c, l_i[rb]);
     }
   }
@@ -297,33 +313,52 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int rem = (int)(idx - (long)row * a.hq * d4n);
   const int h = rem / d4n, d0 = (rem - h * d4n) * 4;
   const int ns = min(a.qpos[row] / a.split_len + 1, a.splits);
-  float M = NEG_INF;
-  for (int s0 = 0; s0 < ns; s0 += NSB) {
-    float mv[NSB];
-#pragma unroll
-    for (int j = 0; j < NSB; ++j)
-      mv[j] = s0 + j < ns ? a.part_ml[(((long)(s0 + j) * a.n_q + row) * a.hq + h) * 2] : NEG_INF;
-#pragma unroll
-    for (int j = 0; j < NSB; ++j) M = fmaxf(M, mv[j]);
-  }
-  float L = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < ns; s0 += NSB) {
-    float2 ml[NSB];
-    float4 v[NSB];
+  const half_t* part = reinterpret_cast<const half_t*>(a.part_o);
+  float M = NEG_INF, L = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+  auto load = [&](int s0, float2 (&ml)[NSB], float4 (&v)[NSB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < NSB; ++j) {
       if (s0 + j < ns) {
         const long pi = ((long)(s0 + j) * a.n_q + row) * a.hq + h;
         ml[j] = *reinterpret_cast<const float2*>(a.part_ml + pi * 2);
-        v[j] = *reinterpret_cast<const float4*>(a.part_o + pi * a.dh + d0);
+        const u32x2_t hv = *reinterpret_cast<const u32x2_t*>(part + pi * a.dh + d0);
+        v[j] = unpack_f16x4(hv);
+      } else {
+        ml[j] = make_float2(NEG_INF, 0.f);
       }
     }
+  };
+  // O_s holds the split's sum-normalized output: the weight of split s is l_s 2^(m_s - M)
+  auto add = [&](const float2 (&ml)[NSB], const float4 (&v)[NSB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < NSB; ++j) {
-      if (s0 + j >= ns || ml[j].x == NEG_INF) continue;
-      const float w = exp2f(ml[j].x - M);
-      L += ml[j].y * w;
+      if (ml[j].x == NEG_INF) continue;
+      const float w = ml[j].y * exp2f(ml[j].x - M);
+      L += w;
       acc[0] += v[j].x * w; acc[1] += v[j].y * w; acc[2] += v[j].z * w; acc[3] += v[j].w * w;
+    }
+  };
+  if (ns <= NSB) {  // one round of loads
+    float2 ml[NSB];
+    float4 v[NSB];
+    load(0, ml, v);
+#pragma unroll
+    for (int j = 0; j < NSB; ++j) M = fmaxf(M, ml[j].x);
+    add(ml, v);
+  } else {
+    for (int s0 = 0; s0 < ns; s0 += NSB) {  // the splits' maxima, a batch of loads at a time
+      float mv[NSB];
+#pragma unroll
+      for (int j = 0; j < NSB; ++j)
+        mv[j] = s0 + j < ns ? a.part_ml[(((long)(s0 + j) * a.n_q + row) * a.hq + h) * 2] : NEG_INF;
+#pragma unroll
+      for (int j = 0; j < NSB; ++j) M = fmaxf(M, mv[j]);
+    }
+    for (int s0 = 0; s0 < ns; s0 += NSB) {
+      float2 ml[NSB];
+      float4 v[NSB];
+      load(s0, ml, v);
+      add(ml, v);
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
