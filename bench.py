@@ -69,17 +69,41 @@ def attention_flops(shape, records, n_query):
     return [4.0 * shape.n_q_heads * shape.head_dim * float((r.new_sel.astype(np.int64) + 1).sum()) for r in records]
 
 
+# The gate/up product's tile choice: (rows, cols, wavefronts, modelled microseconds per K-step
+# of a workgroup) for each candidate; a launch costs ceil(workgroups / 256) K-step times, the
+# cheapest candidate wins, and from 2,048 rows up the 256 x 256 tile is taken outright.
+_SWIGLU_TILES = ((64, 128, 4, 0.72), (128, 128, 4, 0.83), (64, 256, 4, 1.04), (128, 256, 8, 1.13),
+                 (256, 256, 8, 1.75), (128, 512, 8, 2.10))
+
+
+def swiglu_tile(rows, n):
+    """(bm, bn, wavefronts, workgroups) of the gate/up launch over `rows` rows and n = 2 ffn
+    output columns, as the library plans it."""
+    if rows >= 2048 and n % 256 == 0:
+        bm, bn, nw = 256, 256, 8
+    else:
+        best = None
+        for bm_, bn_, nw_, t in _SWIGLU_TILES:
+            if n % bn_:
+                continue
+            cost = -(-(-(-rows // bm_) * (n // bn_)) // 256) * t
+            if best is None or cost < best[0]:
+                best = (cost, bm_, bn_, nw_)
+        _, bm, bn, nw = best
+    tiles = -(-rows // bm) * (n // bn)
+    return bm, bn, nw, 8 * (-(-tiles // 8))  # workgroups: tiles rounded up to a multiple of 8
+
+
 def gate_up_traffic(shape, kept_rows):
     """Mean HBM bytes per launch of the FFN gate/up GEMM over one step, from the committed
     rocprofv3 counter summary (FETCH_SIZE / WRITE_SIZE, scaled by a plain copy's reading),
-    or None if that summary is missing or was taken on another version of the kernel source.
-    A launch on M rows runs ceil(M/128) x (2 ffn / 512) tiles of 512 threads, rounded up to a
-    multiple of 8 workgroups: that grid size identifies its counter line.  (At M >= 2048 rows
-    the launch uses 256 x 256 tiles of 512 threads instead: ceil(M/256) x (2 ffn / 256).)"""
+    or None if that summary is missing, lacks one of the step's launches, or was taken on
+    another version of the kernel source.  A launch is identified by its tile (in the kernel's
+    name) and its grid size in threads (workgroups x 64 x wavefronts)."""
     import hashlib
     import re
     path = os.path.join(ROOT, "profiles", "gemm_gate_up_qwen_traffic.txt")
-    if not os.path.exists(path) or (2 * shape.ffn_dim) % 512:
+    if not os.path.exists(path):
         return None
     text = open(path).read()
     m = re.search(r"source_sha256 (\S+): ([0-9a-f]{64})", text)
@@ -88,17 +112,15 @@ def gate_up_traffic(shape, kept_rows):
     src = os.path.join(ROOT, m.group(1))
     if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != m.group(2):
         return None
-    per_grid = {int(g): float(mb) for g, mb in re.findall(r"^\s*(\d+)\s+\d+\s+[\d.]+\s+[\d.]+\s+([\d.]+)\s+gemm", text, re.M)}
+    per_launch = {(int(bm), int(bn), int(g)): float(mb) for g, mb, bm, bn in re.findall(
+        r"^\s*(\d+)\s+\d+\s+[\d.]+\s+[\d.]+\s+([\d.]+)\s+gemm_bf16_kernel<(\d+), (\d+),", text, re.M)}
     total = 0.0
     for rows in kept_rows:
-        if rows >= 2048:
-            tiles = -(-rows // 256) * (2 * shape.ffn_dim // 256)
-        else:
-            tiles = -(-rows // 128) * (2 * shape.ffn_dim // 512)
-        grid = 8 * (-(-tiles // 8)) * 512
-        if grid not in per_grid:
+        bm, bn, nw, wgs = swiglu_tile(rows, 2 * shape.ffn_dim)
+        key = (bm, bn, wgs * 64 * nw)
+        if key not in per_launch:
             return None
-        total += per_grid[grid] * 1e6
+        total += per_launch[key] * 1e6
     return total / len(kept_rows)
 
 

@@ -3,18 +3,21 @@
 //
 // Query rows are the kept rows of the layer (ascending positions qpos); keys are every fused
 // K/V row 0 .. qpos[row].  bf16 path (head_dim 128):
-//   workgroup = 16 consecutive query rows x all G query heads of one KV head (one
-//   wavefront per query head, so the K/V tile in LDS serves the whole GQA group);
-//   64-key tiles: K stored row-major, V stored transposed (V^T[dim][key]) in LDS;
+//   workgroup = 16 x QT consecutive query rows x all G query heads of one KV head (one
+//   wavefront per query head and 16-row block, so the K/V tile in LDS serves the whole GQA
+//   group; QT = 2 up to 6 heads, else 1);
+//   64-key tiles of K and V, row-major in a 4-stage LDS ring (loaded global -> LDS directly,
+//   16-byte chunks swizzled by row);
 //   S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (K as the A operand, the wave's Q rows held
 //   in registers as the B operand), so every lane owns one query row's scores: lane l has
 //   row (l & 15) and keys 4*(l >> 4) + r of each 16-key block;
 //   online softmax in fp32 (exp2 with log2(e)/sqrt(d) folded into the scale), row max and
 //   sum over the four lanes of a row by two lane swaps (permlane16/32);
-//   O^T += V^T P^T: P (rounded to bf16) is already in B-operand layout, V^T is read as two
-//   8-byte pieces per lane with the matching key order;
-//   split-KV: grid.y splits the key range so short query sets still fill the chip; partial
-//   (O, max, sum) go to fp32 buffers merged by attn_combine_kernel.
+//   O^T += V^T P^T: P (rounded to bf16) is already in B-operand layout, V^T fragments come
+//   from LDS transpose reads of the row-major V tile;
+//   split-KV: grid.y splits the key range so short query sets still fill the chip; a split
+//   writes its output divided by its own softmax sum, in fp16, and its (max, sum) in fp32;
+//   attn_combine_kernel merges the splits of each row.
 #include "cb_common.h"
 #include "cb_kernels.h"
 
@@ -345,6 +348,17 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < NSB; ++j) M = fmaxf(M, ml[j].x);
     add(ml, v);
+  } else if (ns <= 4 * NSB) {  // four batches, every load issued before any is used
+    float2 ml[4][NSB];
+    float4 v[4][NSB];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) load(b * NSB, ml[b], v[b]);
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int j = 0; j < NSB; ++j) M = fmaxf(M, ml[b][j].x);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) add(ml[b], v[b]);
   } else {
     for (int s0 = 0; s0 < ns; s0 += NSB) {  // the splits' maxima, a batch of loads at a time
       float mv[NSB];

@@ -878,14 +878,14 @@ hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
 
 }  // namespace
 
-// Tile for the SwiGLU (gate/up) product, which does not split K.  Model: a workgroup of tile
-// cfg takes about t(cfg) per 64-wide K-step whatever the shape, and the grid runs in
-// ceil(workgroups / 256) waves; the tile with the fewest wave-steps wins.  t measured on MI355X
-// (K = 1536, one wave of workgroups): 64x128 0.72 us, 128x128 0.83, 64x256 1.04, 128x256 1.13,
-// 256x256 1.75, 128x512 2.10.  The model ranks the measured tiles of the gate/up products of the
-// Qwen2.5-1.5B shape at 64..5184 rows and of the Mistral-7B shape at 640..1024 rows within 10%
-// of the best.
-GemmCfg swiglu_cfg(int M, int N) {
+// Tile of a product that does not split K.  Model: a workgroup of tile cfg takes about t(cfg)
+// per 64-wide K-step whatever the shape, and the grid runs in ceil(workgroups / 256) waves; the
+// tile with the fewest wave-steps wins.  t measured on MI355X (K = 1536, one wave of
+// workgroups): 64x128 0.72 us, 128x128 0.83, 64x256 1.04, 128x256 1.13, 256x256 1.75, 128x512
+// 2.10.  The model ranks the measured tiles of the gate/up products of the Qwen2.5-1.5B shape at
+// 64..5184 rows and of the Mistral-7B shape at 640..1024 rows within 10% of the best.  128 x 512
+// is built for the SwiGLU epilogue only and 256 x 256 for every epilogue but the residual add.
+GemmCfg tile_by_model(int M, int N, int epi, long* workgroups) {
   struct Cand {
     GemmCfg cfg;
     int bm, bn;
@@ -896,31 +896,39 @@ GemmCfg swiglu_cfg(int M, int N) {
                             {GEMM_256x256, 256, 256, 1.75f}, {GEMM_128x512, 128, 512, 2.10f}};
   GemmCfg best = GEMM_64x128;
   float best_cost = 3.4e38f;
+  long best_wgs = (long)((M + 63) / 64) * (N / 128);
   for (const Cand& c : cands) {
     if (N % c.bn) continue;
+    if (c.cfg == GEMM_128x512 && epi != EPI_SWIGLU) continue;
+    if (c.cfg == GEMM_256x256 && epi == EPI_RESID) continue;
     const long wgs = (long)((M + c.bm - 1) / c.bm) * (N / c.bn);
     const float cost = (float)((wgs + 255) / 256) * c.t;
     if (cost < best_cost) {
       best_cost = cost;
       best = c.cfg;
+      best_wgs = wgs;
     }
   }
+  if (workgroups) *workgroups = best_wgs;
   return best;
 }
 
 // Tile configuration and split-K factor for an M x N x K product (measured on MI355X at the
 // fusion step's shapes):
 //   * M <= 4 rows (a decode step): the skinny product, no split;
-//   * large M (>= 2048 rows, e.g. the first layer's full prompt) with a bf16 output and
-//     N % 256 == 0: 256 x 256 tiles of 8 wavefronts, no split (the fewest operand bytes per
-//     flop: 7-18% faster than the next best there);
-//   * SwiGLU (gate/up, widest output): no split, the tile swiglu_cfg's model ranks first
-//     (64 x 128 at 64 rows, 128 x 256 at 320, 256 x 256 at 640, 128 x 512 at 832 for Qwen);
+//   * SwiGLU (gate/up, widest output): no split (the epilogue needs whole sums), the tile
+//     tile_by_model ranks first (64 x 128 at 64 rows, 128 x 256 at 320, 256 x 256 at 640,
+//     128 x 512 at 832, 256 x 256 from 1600 for Qwen);
+//   * short reductions (K <= 2048: the Q/K/V and o-projections): the tile tile_by_model ranks
+//     first (64 x 128 at 832 rows, 128 x 128 at 1600, 128 x 128 for the 512 K/V columns of all
+//     5184 rows, 256 x 256 for all of Q/K/V there), no split, if it gives at least ~150
+//     workgroups; else 64 x 128 tiles of 4 wavefronts with a 4-stage ring and K split up to
+//     ~150 workgroups;
+//   * long reductions: large M (>= 2048 rows) with a bf16 output and N % 256 == 0: 256 x 256
+//     tiles of 8 wavefronts, no split (the fewest operand bytes per flop);
 //   * problems with >= 200 tiles of 128 x 256: those tiles (8 wavefronts), no split;
-//   * short reductions (K <= 2048: the Q/K/V and o-projections of the kept rows): 64 x 128
-//     tiles of 4 wavefronts with a 4-stage ring, split only while fewer than ~150 tiles;
-//   * long reductions (the FFN down-projection): up to 320 rows, 64 x 128 tiles with K split
-//     so that at most 256 workgroups run (64 rows: 15 against 20 us with 64 x 256); above,
+//   * other long reductions (the FFN down-projection): up to 320 rows, 64 x 128 tiles with K
+//     split so that at most 256 workgroups run (64 rows: 15 against 20 us with 64 x 256); above,
 //     128 x 256 tiles, K split so that about 210 workgroups run;
 //   each split keeps at least two 64-wide K-steps and its partials fit the buffer.
 GemmPlan gemm_plan(int M, int N, int K, int epi, long partial_cap_elems) {
@@ -929,17 +937,21 @@ GemmPlan gemm_plan(int M, int N, int K, int epi, long partial_cap_elems) {
     p.cfg = GEMM_GEMV;
     return p;
   }
-  if (M >= 2048 && epi != EPI_RESID && N % 256 == 0) {
-    p.cfg = GEMM_256x256;
+  if (epi == EPI_SWIGLU) {
+    p.cfg = tile_by_model(M, N, epi, nullptr);
     return p;
   }
-  if (epi == EPI_SWIGLU) {  // no split (the epilogue needs whole sums): the cheapest tile by model
-    p.cfg = swiglu_cfg(M, N);
+  if (K <= 2048) {
+    long wgs = 0;
+    p.cfg = tile_by_model(M, N, epi, &wgs);
+    if (wgs >= 150) return p;
+  } else if (M >= 2048 && epi != EPI_RESID && N % 256 == 0) {
+    p.cfg = GEMM_256x256;
     return p;
   }
   int bm = 128, bn = 128, target = 210;
   bool one_wave = false;  // split only as far as one wave of 256 workgroups
-  if (N % 256 == 0 && ((M + 127) / 128) * (N / 256) >= 200) {
+  if (K > 2048 && N % 256 == 0 && ((M + 127) / 128) * (N / 256) >= 200) {
     p.cfg = GEMM_128x256;
     return p;
   }

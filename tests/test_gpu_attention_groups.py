@@ -57,3 +57,39 @@ def test_attention_every_group_size(group):
         assert_close(rec.out_sel, att.reshape(len(kpos), hq * dh), "bf16",
                      f"group {group} layer {layer + 1} attention ({len(kpos)} kept rows)")
     eng.close()
+
+
+@pytest.mark.parametrize("chunk_lens", [(483,) * 6, (503,) * 18], ids=["12_ranges", "36_ranges"])
+def test_query_rows_over_a_long_context(chunk_lens):
+    """A layer that keeps only the 45 query rows (ratio 0) over a long context: kept sets of at
+    most 64 rows get 256-key ranges, so 2,943 rows give 12 ranges and 9,099 rows 36, which the
+    combine merges in one round of loads (up to 32 ranges) or in batches (more).  The attention
+    output of every query row equals the oracle's causal attention over the GPU's fused K/V,
+    with Q from the GPU's input rows of that layer."""
+    from rag_kv_cache_amd.pipeline import Engine, build_chunk_caches, make_buffers, run_layers
+    sh = replace(F.get_config("small_bf16").shape, name="small-bf16-long", n_layers=2)
+    wl = F.Workload(f"long_{len(chunk_lens)}", sh, chunk_lens, 45, (1.0, 0.0))
+    print(f"[attn] {wl.n_ctx} context + {wl.n_query} query rows", flush=True)
+    W = [F.layer_weights(sh, l) for l in range(1, sh.n_layers + 1)]
+    emb = F.embedding(sh)
+    eng = Engine(sh, max_tokens=wl.n_tokens + 8)
+    eng.load_all(lambda l: W[l - 1], emb)
+    chunks = F.chunk_tokens(wl)
+    cache, _ = build_chunk_caches(eng, chunks)
+    buf = make_buffers(eng, wl.n_tokens, len(chunks))
+    fused = [(eng.kv_empty(wl.n_tokens), eng.kv_empty(wl.n_tokens)) for _ in range(sh.n_layers)]
+    res = run_layers(eng, buf, F.all_tokens(wl), F.chunk_offsets(wl), wl.n_query, wl.schedule, fused,
+                     cache=cache, record=True)
+    eng.compute.synchronize()
+    prec = O.Precision("bf16")
+    hq, dh = sh.n_q_heads, sh.head_dim
+    rec = res.records[1]
+    assert rec.new_sel.tolist() == list(range(wl.n_ctx, wl.n_tokens))
+    loc = {int(p): i for i, p in enumerate(rec.sel)}
+    kpos = rec.new_sel
+    kloc = np.array([loc[int(p)] for p in kpos])
+    x = prec.store(O.rmsnorm(res.records[0].hidden_out[kloc], W[1]["g_attn"], sh.rms_eps))
+    q = prec.store(O.rope_rotate(O.project(x, W[1]["w_q"]).reshape(-1, hq, dh), kpos, sh.rope_base))
+    att = prec.store(O.causal_attention(q, _np(fused[1][0]), _np(fused[1][1]), kpos))
+    assert_close(rec.out_sel, att.reshape(len(kpos), hq * dh), "bf16", "query-row attention over the long context")
+    eng.close()
