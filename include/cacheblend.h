@@ -214,7 +214,8 @@ cb_status cb_synchronize(cb_ctx* ctx, int32_t layer);
  *   hidden_sel       device fp32 [n_sel][d_model]: residual-stream rows of S_l
  *   x_sel            device [n_sel][d_model] (dtype) or NULL: RMSNorm(hidden_sel) with this
  *                    layer's attention gain, already computed (cb_layer_rest's x_next of the
- *                    previous layer); NULL computes it here
+ *                    previous layer); NULL computes it here (for up to 4 rows in bf16
+ *                    the Q/K/V products form it from hidden_sel as they load it)
  *   kv_cached_k/_v   device [N_ctx][n_kv_heads][head_dim]: offset-0 chunk caches in
  *                    prompt order, or NULL (see 1.)
  *   kv_fused_k/_v    device [N_ctx + n_query][n_kv_heads][head_dim]: the layer's fused K/V
@@ -265,7 +266,9 @@ cb_status cb_decode_layer(cb_ctx* ctx, int32_t layer, const float* hidden_new, c
  * cb_blend_layer; hidden_next: device fp32 [n_new][d] (must not alias hidden_sel).
  * x_next: device [n_new][d] (dtype) or NULL: if given, also RMSNorm(hidden_next) with the
  * attention gain of layer + 1 (which must exist and have its weights set), the x_sel of the
- * next cb_blend_layer; it is fused with the down-projection's reduction. */
+ * next cb_blend_layer; it is fused with the down-projection's reduction.  For up to 4 rows
+ * in bf16, m is formed by the gate/up product from h1 as it loads it (no launch of its own);
+ * a decode step that passes no x_next lets the next layer do the same for its x. */
 cb_status cb_layer_rest(cb_ctx* ctx, int32_t layer, const float* hidden_sel, int32_t n_sel,
                         const int32_t* new_sel_local, int32_t n_new, const void* out_sel,
                         float* hidden_next, void* x_next, void* workspace, size_t workspace_bytes);

@@ -598,9 +598,19 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
                        n_chunks, c->rope, d.max_tokens, bf, c->cs);
     if (e != hipSuccess) return hip_fail(e, "rope_delta launch");
   }
-  // 2. x = RMSNorm(hidden_sel), unless the caller passes it
+  // 2. x = RMSNorm(hidden_sel), unless the caller passes it; a few rows (a decode step) go to the
+  //    skinny products, which form x from hidden_sel as they load it (no launch of its own)
   const void* x = x_sel;
-  if (!x) {
+  const bool norm_on_load =
+      !x && bf && cb::gemm_plan(n_sel, 2 * kvd, dm, cb::EPI_ROPE, 0).cfg == cb::GEMM_GEMV;
+  auto set_a = [&](cb::GemmArgs& g) {
+    if (norm_on_load) {
+      g.A = nullptr; g.a_f32 = hidden_sel; g.a_gain = W.g_attn; g.a_eps = d.rms_eps;
+    } else {
+      g.A = x;
+    }
+  };
+  if (!x && !norm_on_load) {
     void* xw = ws + wp.x;
     Timed t(c, CB_K_RMSNORM, (double)n_sel * dm * (4 + es));
     e = cb::rmsnorm(hidden_sel, dm, n_sel, dm, W.g_attn, d.rms_eps, xw, bf, c->cs);
@@ -616,7 +626,7 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
   void* fresh_kv = (char*)fresh + (fuse_q ? (size_t)qd * es : 0);
   {
     cb::GemmArgs g{};
-    g.A = x; g.lda = dm; g.a_rows = nullptr;
+    set_a(g); g.lda = dm; g.a_rows = nullptr;
     const size_t wes = S8.qkv ? 1 : es;  // bytes per weight
     g.B = fuse_q ? W.w_qkv : (const char*)W.w_qkv + (size_t)qd * dm * wes; g.ldb = dm;
     g.b_i8 = S8.qkv != nullptr; g.bscale = S8.qkv ? S8.qkv + (fuse_q ? 0 : qd) : nullptr;
@@ -652,7 +662,7 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
   const int q_ld = fuse_q ? fresh_ld : qd;
   if (!fuse_q) {
     cb::GemmArgs g{};
-    g.A = x; g.lda = dm; g.a_rows = new_sel_local; g.a_rows_total = n_sel;
+    set_a(g); g.lda = dm; g.a_rows = new_sel_local; g.a_rows_total = n_sel;
     g.B = W.w_qkv; g.ldb = dm;
     g.b_i8 = S8.qkv != nullptr; g.bscale = S8.qkv;
     g.M = nn; g.N = qd; g.K = dm;
@@ -727,6 +737,8 @@ cb_status cb_layer_rest(cb_ctx* c, int32_t layer, const float* hidden_sel, int32
   float* h1 = (float*)(ws + wp.h1);
   void* mn = ws + wp.mnorm;
   void* act = ws + wp.act;
+  // a few rows (a decode step): the skinny gate/up product forms RMSNorm(h1) as it loads h1
+  const bool norm_on_load = bf && cb::gemm_plan(n_new, 2 * ff, dm, cb::EPI_SWIGLU, 0).cfg == cb::GEMM_GEMV;
   hipError_t e;
   {  // h1 = hidden_sel[new_sel_local] + out_sel W_o^T, and mn = RMSNorm(h1) (fused for bf16)
     cb::GemmArgs g{};
@@ -736,7 +748,7 @@ cb_status cb_layer_rest(cb_ctx* c, int32_t layer, const float* hidden_sel, int32
     g.partial = (float*)(ws + wp.gpart);
     g.epi = cb::EPI_RESID; g.out = h1; g.ldo = dm; g.resid = hidden_sel; g.ldr = dm; g.resid_rows = new_sel_local;
     plan_gemm(g, bf, wp.gpart_elems);
-    if (bf) { g.norm_g = W.g_ffn; g.norm_eps = d.rms_eps; g.norm_out = mn; }
+    if (bf && !norm_on_load) { g.norm_g = W.g_ffn; g.norm_eps = d.rms_eps; g.norm_out = mn; }
     Timed t(c, CB_K_GEMM_O, 2.0 * g.M * g.N * g.K);
     e = bf ? cb::gemm_bf16(g, c->cs) : cb::gemm_f32(g, c->cs);
     if (e != hipSuccess) return hip_fail(e, "gemm(o) launch");
@@ -749,6 +761,7 @@ cb_status cb_layer_rest(cb_ctx* c, int32_t layer, const float* hidden_sel, int32
   {  // act = silu(m W_gate^T) * (m W_up^T)
     cb::GemmArgs g{};
     g.A = mn; g.lda = dm; g.B = W.w_gate_up; g.ldb = dm; g.swiglu_ffn = ff;
+    if (norm_on_load) { g.A = nullptr; g.a_f32 = h1; g.a_gain = W.g_ffn; g.a_eps = d.rms_eps; }
     g.b_i8 = S8.gate_up != nullptr; g.bscale = S8.gate_up;
     g.M = n_new; g.N = 2 * ff; g.K = dm;
     g.epi = cb::EPI_SWIGLU; g.out = act; g.ldo = ff;

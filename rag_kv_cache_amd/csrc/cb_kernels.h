@@ -23,6 +23,9 @@ struct GemmArgs {
   int cfg;               // bf16 tile configuration (GemmCfg), from gemm_plan
   int b_i8;              // B is int8 [N][ldb] with per-row (output channel) scales bscale[N]
   const float* bscale;
+  // skinny product (GEMM_GEMV) only: when a_f32 is set, A row m is RMSNorm(a_f32 row) * a_gain
+  // (row a_rows ? a_rows[m] : m, stride lda, K wide), formed as bf16 on load; A is not read
+  const float* a_f32; const float* a_gain; float a_eps;
 };
 hipError_t gemm_bf16(const GemmArgs& g, hipStream_t s);
 enum GemmCfg { GEMM_128x512 = 0, GEMM_128x256 = 1, GEMM_64x256 = 2, GEMM_128x128 = 3, GEMM_64x128 = 4, GEMM_256x256 = 5, GEMM_GEMV = 6 };

@@ -303,9 +303,12 @@ __global__ __launch_bounds__(64 * G * QT) void attn_bf16_kernel(AttnArgs a) {
 
 // Merge split-KV partials: out = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).  Only splits
 // whose first key is <= the row's position hold keys of that row.  One thread per
-// (row, head, 4 dims); the (m, l) and O partials of up to 8 splits are loaded at once, and
-// summed in split order.
-template <typename TO>
+// (row, head, 4 dims); the (m, l) and O partials are summed in split order.  NB = 1: up to 8
+// splits, every load issued at once; NB = 0: any number of splits, 8 at a time, in two passes
+// (maxima, then the weighted sum).  Separate instantiations, so that the few-split case keeps
+// its small register footprint (issuing 32 splits' loads at once measured no faster than the
+// two passes).
+template <typename TO, int NB>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   constexpr int NSB = 8;  // splits per batch of loads
   const int d4n = a.dh / 4;
@@ -341,24 +344,17 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
       acc[0] += v[j].x * w; acc[1] += v[j].y * w; acc[2] += v[j].z * w; acc[3] += v[j].w * w;
     }
   };
-  if (ns <= NSB) {  // one round of loads
-    float2 ml[NSB];
-    float4 v[NSB];
-    load(0, ml, v);
+  if constexpr (NB > 0) {  // NB batches, every load issued before any is used
+    float2 ml[NB][NSB];
+    float4 v[NB][NSB];
 #pragma unroll
-    for (int j = 0; j < NSB; ++j) M = fmaxf(M, ml[j].x);
-    add(ml, v);
-  } else if (ns <= 4 * NSB) {  // four batches, every load issued before any is used
-    float2 ml[4][NSB];
-    float4 v[4][NSB];
+    for (int b = 0; b < NB; ++b) load(b * NSB, ml[b], v[b]);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) load(b * NSB, ml[b], v[b]);
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int j = 0; j < NSB; ++j) M = fmaxf(M, ml[b][j].x);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) add(ml[b], v[b]);
+    for (int b = 0; b < NB; ++b) add(ml[b], v[b]);
   } else {
     for (int s0 = 0; s0 < ns; s0 += NSB) {  // the splits' maxima, a batch of loads at a time
       float mv[NSB];
@@ -722,7 +718,11 @@ hipError_t attn_bf16(const AttnArgs& a, hipStream_t s) {
   }
   if (e != hipSuccess || a.splits <= 1) return e;
   const long total = (long)a.n_q * a.hq * (a.dh / 4);
-  hipLaunchKernelGGL(attn_combine_kernel<bf16_t>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
+  const dim3 grid((unsigned)((total + 255) / 256));
+  if (a.splits <= 8)
+    hipLaunchKernelGGL((attn_combine_kernel<bf16_t, 1>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<bf16_t, 0>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -666,7 +666,11 @@ __device__ __forceinline__ float dot8_bf16_i8(const uint4 a, uint32_t wlo, uint3
   return s;
 }
 
-template <int EPI, int MR, int BT>
+// NORM: the activation rows are RMSNorm(g.a_f32 rows) * g.a_gain, formed on load: every
+// workgroup first reduces the squares of its MR rows (K floats each, from L2), then scales and
+// rounds each 8-element piece to bf16 as it streams K, so no separate normalisation launch is
+// needed (measured against staging the rows in LDS first, which delays the weight stream).
+template <int EPI, int MR, int BT, int NORM>
 __global__ __launch_bounds__(256) void gemv_bf16_kernel(GemmArgs g) {
   constexpr int NR = 2 * GV_P;  // weight rows of the workgroup
   __shared__ float part[4][MR][NR];
@@ -685,11 +689,46 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(GemmArgs g) {
     wrow[2 * q + 1] = B + (long)n_b * g.ldb * WB;
   }
   const bf16_t* arow[MR];
+  const float* hrow[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
     const int mm = m < g.M ? m : g.M - 1;
-    arow[m] = A + (g.a_rows ? (long)g.a_rows[mm] : (long)mm) * g.lda;
+    const long r = g.a_rows ? (long)g.a_rows[mm] : (long)mm;
+    arow[m] = A + r * g.lda;
+    hrow[m] = NORM ? g.a_f32 + r * g.lda : nullptr;
   }
+  float inv[MR];
+  if constexpr (NORM) {  // 1 / sqrt(mean of squares + eps) of each row
+    __shared__ float red[4][MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      float ss = 0.f;
+      for (int k = threadIdx.x * 4; k < g.K; k += 1024) {
+        const float4 v = *reinterpret_cast<const float4*>(hrow[m] + k);
+        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+      }
+      ss = wave_sum(ss);
+      if (lane == 0) red[wave][m] = ss;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+      inv[m] = 1.0f / sqrtf((red[0][m] + red[1][m] + red[2][m] + red[3][m]) / (float)g.K + g.a_eps);
+  }
+  // this lane's 8 activations at k: read as bf16, or (NORM) h * inv * gain rounded to bf16
+  auto load_a = [&](int m, int k) __attribute__((always_inline)) -> uint4 {
+    if constexpr (NORM) {
+      const float4 h0 = *reinterpret_cast<const float4*>(hrow[m] + k);
+      const float4 h1 = *reinterpret_cast<const float4*>(hrow[m] + k + 4);
+      const float4 g0 = *reinterpret_cast<const float4*>(g.a_gain + k);
+      const float4 g1 = *reinterpret_cast<const float4*>(g.a_gain + k + 4);
+      const float r = inv[m];
+      return make_uint4(pack_bf16x2(h0.x * r * g0.x, h0.y * r * g0.y), pack_bf16x2(h0.z * r * g0.z, h0.w * r * g0.w),
+                        pack_bf16x2(h1.x * r * g1.x, h1.y * r * g1.y), pack_bf16x2(h1.z * r * g1.z, h1.w * r * g1.w));
+    } else {
+      return *reinterpret_cast<const uint4*>(arow[m] + k);
+    }
+  };
   const int kq = g.K / 4;  // this wavefront's K range: [wave * kq, (wave + 1) * kq)
   float acc[MR][NR];
 #pragma unroll
@@ -699,7 +738,7 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(GemmArgs g) {
   for (int k = wave * kq + lane * 8; k < (wave + 1) * kq; k += 512) {
     uint4 a[MR];
 #pragma unroll
-    for (int m = 0; m < MR; ++m) a[m] = *reinterpret_cast<const uint4*>(arow[m] + k);
+    for (int m = 0; m < MR; ++m) a[m] = load_a(m, k);
     if constexpr (BT) {
       uint2 w[NR];
 #pragma unroll
@@ -748,18 +787,30 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(GemmArgs g) {
   }
 }
 
+template <int EPI, int BT, int NORM>
+hipError_t launch_gemv_n(const GemmArgs& g, hipStream_t s) {
+  const dim3 grid((unsigned)((g.N / 2 + GV_P - 1) / GV_P));
+  if (g.M == 1)
+    hipLaunchKernelGGL((gemv_bf16_kernel<EPI, 1, BT, NORM>), grid, dim3(256), 0, s, g);
+  else if (g.M == 2)
+    hipLaunchKernelGGL((gemv_bf16_kernel<EPI, 2, BT, NORM>), grid, dim3(256), 0, s, g);
+  else
+    hipLaunchKernelGGL((gemv_bf16_kernel<EPI, 4, BT, NORM>), grid, dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
 template <int EPI, int BT>
 hipError_t launch_gemv(const GemmArgs& g, hipStream_t s) {
   if (g.M > 4 || g.K % 32 != 0 || g.N % 2 != 0) return hipErrorInvalidValue;
   if (BT && !g.bscale) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((g.N / 2 + GV_P - 1) / GV_P));
-  if (g.M == 1)
-    hipLaunchKernelGGL((gemv_bf16_kernel<EPI, 1, BT>), grid, dim3(256), 0, s, g);
-  else if (g.M == 2)
-    hipLaunchKernelGGL((gemv_bf16_kernel<EPI, 2, BT>), grid, dim3(256), 0, s, g);
-  else
-    hipLaunchKernelGGL((gemv_bf16_kernel<EPI, 4, BT>), grid, dim3(256), 0, s, g);
-  return hipGetLastError();
+  if (g.a_f32) {  // rows normalised on load: the Q/K/V and gate/up products, whose inputs are RMSNorm rows
+    if constexpr (EPI == EPI_ROPE || EPI == EPI_SWIGLU) {
+      if (!g.a_gain) return hipErrorInvalidValue;
+      return launch_gemv_n<EPI, BT, 1>(g, s);
+    }
+    return hipErrorInvalidValue;
+  }
+  return launch_gemv_n<EPI, BT, 0>(g, s);
 }
 
 // ------------------------------------------------------------------ fp32 path
@@ -980,6 +1031,7 @@ GemmPlan gemm_plan(int M, int N, int K, int epi, long partial_cap_elems) {
 
 hipError_t gemm_bf16(const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0) return hipSuccess;
+  if (g.a_f32 && g.cfg != GEMM_GEMV) return hipErrorInvalidValue;  // normalise-on-load: skinny product only
   hipError_t e;
   switch (g.epi) {
     case EPI_ROPE: e = g.b_i8 ? launch_epi<EPI_ROPE, 1>(g, s) : launch_epi<EPI_ROPE, 0>(g, s); break;

@@ -81,12 +81,15 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, long ldh, 
   if (row >= n) return;
   const float* x = h + (long)row * ldh;
   TO* o = out + (long)row * d;
-  if (d <= 2048) {  // the row stays in registers: one read, every load in flight at once
-    float4 v[8];
+  if (d <= 2048) {  // the row and the gains stay in registers: every load in flight at once
+    float4 v[8], gg[8];
     const int e0 = lane * 4;
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (e0 + 256 * u < d) v[u] = *reinterpret_cast<const float4*>(x + e0 + 256 * u);
+      if (e0 + 256 * u < d) {
+        v[u] = *reinterpret_cast<const float4*>(x + e0 + 256 * u);
+        gg[u] = *reinterpret_cast<const float4*>(g + e0 + 256 * u);
+      }
     float ss = 0.f;
 #pragma unroll
     for (int u = 0; u < 8; ++u)
@@ -96,10 +99,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, long ldh, 
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int e = e0 + 256 * u;
-      if (e < d) {
-        const float4 gg = *reinterpret_cast<const float4*>(g + e);
-        store4<TO>(o + e, v[u].x * r * gg.x, v[u].y * r * gg.y, v[u].z * r * gg.z, v[u].w * r * gg.w);
-      }
+      if (e < d) store4<TO>(o + e, v[u].x * r * gg[u].x, v[u].y * r * gg[u].y, v[u].z * r * gg[u].z, v[u].w * r * gg[u].w);
     }
     return;
   }

@@ -466,8 +466,10 @@ def decode(eng: Engine, buf: RunBuffers, new_tokens: Sequence[int], n_past: int,
     cur = 0
     for l in range(s.n_layers):
         h_in, h_out = buf.hidden[cur], buf.hidden[1 - cur]
-        x_in = buf.xnorm[(l - 1) % 2] if l > 0 else None
-        x_out = buf.xnorm[l % 2] if l + 1 < s.n_layers else None
+        # up to 4 rows go to the skinny products, which normalise the residual rows as they load
+        # them; more rows take the normalised rows the previous layer's down-projection wrote
+        x_in = buf.xnorm[(l - 1) % 2] if l > 0 and n_new > 4 else None
+        x_out = buf.xnorm[l % 2] if l + 1 < s.n_layers and n_new > 4 else None
         L.cb_decode_layer(ctx, l, _ptr(h_in), _ptr(fused[l][0]), _ptr(fused[l][1]), n_past, n_new,
                           _ptr(buf.init_sel), _ptr(buf.out_sel), _ptr(ws), ws.numel(), x_new=_ptr(x_in))
         L.cb_layer_rest(ctx, l, _ptr(h_in), n_new, _ptr(buf.iota), n_new, _ptr(buf.out_sel), _ptr(h_out),

@@ -62,8 +62,8 @@ def test_attention_every_group_size(group):
 @pytest.mark.parametrize("chunk_lens", [(483,) * 6, (503,) * 18], ids=["12_ranges", "36_ranges"])
 def test_query_rows_over_a_long_context(chunk_lens):
     """A layer that keeps only the 45 query rows (ratio 0) over a long context: kept sets of at
-    most 64 rows get 256-key ranges, so 2,943 rows give 12 ranges and 9,099 rows 36, which the
-    combine merges in one round of loads (up to 32 ranges) or in batches (more).  The attention
+    most 64 rows get 256-key ranges, so 2,943 rows give 12 ranges and 9,099 rows 36, more than
+    the combine's one-round path takes (8): it merges them in batches.  The attention
     output of every query row equals the oracle's causal attention over the GPU's fused K/V,
     with Q from the GPU's input rows of that layer."""
     from rag_kv_cache_amd.pipeline import Engine, build_chunk_caches, make_buffers, run_layers
