@@ -231,7 +231,10 @@ cb_status cb_synchronize(cb_ctx* ctx, int32_t layer);
  *   n_new            host out: k + n_query, set before the call returns
  *   out_sel          device [k + n_query][n_q_heads * head_dim] out (dtype): attention
  *                    output of the kept rows (before the o-projection)
- *   deviation        device fp32 [n_sel] out or NULL: entries 0 .. n_sel-n_query-1 get d
+ *   deviation        device fp32 [n_sel] out or NULL: entries 0 .. n_sel-n_query-1 get d;
+ *                    with NULL, a layer that keeps every candidate (k = n_sel - n_query,
+ *                    whose selection d does not decide) skips step 3 and, in bf16, writes
+ *                    the fresh K/V rows of step 5 from the K/V product itself
  *   workspace        device scratch of at least cb_workspace_size(N, n_sel) bytes
  * CB_ESTATE if the layer was fetched and not yet synchronized. */
 cb_status cb_blend_layer(cb_ctx* ctx, int32_t layer, const float* hidden_sel, const void* x_sel,

@@ -621,6 +621,7 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
   //    every candidate (k == n_cand: layer 1 and any layer whose ratio no longer narrows), the kept
   //    rows are exactly the selected rows, so Q is produced by the same GEMM (Q | K | V).
   const bool fuse_q = k == (long)n_cand;
+  bool scattered = false;  // the fresh K/V already sit in the fused cache (see 3.)
   void* fresh = ws + wp.fresh;
   const int fresh_ld = fuse_q ? qd + 2 * kvd : 2 * kvd;
   void* fresh_kv = (char*)fresh + (fuse_q ? (size_t)qd * es : 0);
@@ -636,6 +637,13 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
     plan_gemm(g, bf, wp.gpart_elems);
     g.pos = sel_idx; g.rope = c->rope; g.rope_cols = fuse_q ? qd + kvd : kvd; g.head_dim = d.head_dim;
     g.max_pos = d.max_tokens - 1;
+    // every candidate kept and no deviation asked for: the deviation selects nothing, so the
+    // product's epilogue writes the fresh K/V rows into the fused cache itself (and the kept set)
+    if (fuse_q && bf && !deviation && g.splits == 1 && g.cfg != cb::GEMM_GEMV && kvd % 8 == 0 && qd % 8 == 0) {
+      g.kv_k = kv_fused_k; g.kv_v = kv_fused_v; g.kv_col0 = qd; g.kvd = kvd; g.kv_rows = (int)n_tok;
+      g.sel_out = new_sel_idx; g.local_out = new_sel_local;
+      scattered = true;
+    }
     Timed t(c, CB_K_GEMM_KV, 2.0 * g.M * g.N * g.K);
     e = bf ? cb::gemm_bf16(g, c->cs) : cb::gemm_f32(g, c->cs);
     if (e != hipSuccess) return hip_fail(e, "gemm(kv) launch");
@@ -644,7 +652,7 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
   //    candidate is kept (fuse_q), the kept set is sel itself and the same kernel writes it
   // 5. gradual filtering otherwise: top-k of the context rows + every query row
   float* dev = deviation ? deviation : (float*)(ws + wp.dev);
-  {
+  if (!scattered) {
     Timed t(c, CB_K_DEV_SCATTER, (double)n_sel * 2 * kvd * es * 2 + (double)n_cand * 2 * kvd * es);
     e = cb::dev_scatter(fresh_kv, fresh_ld, kv_fused_k, kv_fused_v, sel_idx, n_sel, n_cand, (int)n_tok, kvd,
                         n_ctx > 0 ? dev : nullptr, fuse_q ? new_sel_idx : nullptr, fuse_q ? new_sel_local : nullptr,

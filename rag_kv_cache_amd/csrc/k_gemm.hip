@@ -466,8 +466,23 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
       const int rl = it / CPR, c = (it - rl * CPR) * 8;
       const int m = m0 + rl;
       if (m >= g.M) continue;
-      *reinterpret_cast<uint4*>((bf16_t*)g.out + (long)m * g.ldo + colbase + c) =
-          *reinterpret_cast<const uint4*>(smem + rl * PB + c * 2);
+      const uint4 v = *reinterpret_cast<const uint4*>(smem + rl * PB + c * 2);
+      const int n = colbase + c;
+      if (EPI == EPI_ROPE && g.kv_k) {  // K/V columns scattered to the fused rows (8 never straddle K | V)
+        if (n == 0) {
+          g.sel_out[m] = g.pos[m];
+          g.local_out[m] = m;
+        }
+        if (n >= g.kv_col0) {
+          const int j = g.pos[m];
+          if (j < 0 || j >= g.kv_rows) continue;
+          const int kn = n - g.kv_col0;
+          bf16_t* dst = kn < g.kvd ? (bf16_t*)g.kv_k + (long)j * g.kvd + kn : (bf16_t*)g.kv_v + (long)j * g.kvd + (kn - g.kvd);
+          *reinterpret_cast<uint4*>(dst) = v;
+          continue;
+        }
+      }
+      *reinterpret_cast<uint4*>((bf16_t*)g.out + (long)m * g.ldo + n) = v;
     }
   }
 }
@@ -1032,6 +1047,9 @@ GemmPlan gemm_plan(int M, int N, int K, int epi, long partial_cap_elems) {
 hipError_t gemm_bf16(const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0) return hipSuccess;
   if (g.a_f32 && g.cfg != GEMM_GEMV) return hipErrorInvalidValue;  // normalise-on-load: skinny product only
+  if (g.kv_k && (g.epi != EPI_ROPE || g.splits != 1 || g.cfg == GEMM_GEMV || g.kvd % 8 != 0 || g.kv_col0 % 8 != 0 ||
+                 !g.kv_v || !g.sel_out || !g.local_out || !g.pos))
+    return hipErrorInvalidValue;  // scatter in the epilogue: unsplit MFMA tiles only
   hipError_t e;
   switch (g.epi) {
     case EPI_ROPE: e = g.b_i8 ? launch_epi<EPI_ROPE, 1>(g, s) : launch_epi<EPI_ROPE, 0>(g, s); break;

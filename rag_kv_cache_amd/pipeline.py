@@ -297,7 +297,8 @@ def run_layers(eng: Engine, buf: RunBuffers, tokens: np.ndarray, offsets: Sequen
         n_new = L.cb_blend_layer(ctx, l, _ptr(h_in), _ptr(ck), _ptr(cv), _ptr(fk), _ptr(fv),
                                  _ptr(buf.offsets) if n_chunks else 0, offs, n_chunks, _ptr(sel_in), n_sel,
                                  n_query, float(schedule[l]), _ptr(sel_out), _ptr(buf.new_local),
-                                 _ptr(buf.out_sel), _ptr(buf.dev), _ptr(ws), ws.numel(), x_sel=_ptr(x_in))
+                                 _ptr(buf.out_sel), _ptr(buf.dev) if record else 0, _ptr(ws), ws.numel(),
+                                 x_sel=_ptr(x_in))
         L.cb_layer_rest(ctx, l, _ptr(h_in), n_sel, _ptr(buf.new_local), n_new, _ptr(buf.out_sel), _ptr(h_out),
                         _ptr(ws), ws.numel(), x_next=_ptr(x_out))
         if record:

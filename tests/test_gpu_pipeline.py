@@ -214,3 +214,41 @@ def test_many_chunks_and_layers_batched_paths():
         for (a, b), (c, d) in zip(f0, f1):
             assert np.array_equal(a, c) and np.array_equal(b, d)
     eng.close()
+
+
+def test_kv_scatter_in_product_epilogue_gives_the_scatter_kernels_bits():
+    """With no deviation asked for (a run that records nothing), a layer that keeps every
+    candidate (layer 1 at ratio 1, layer 4 at an unchanged 15%) writes its fresh K/V into the
+    fused cache from the K/V product's epilogue, and the kept set with it, instead of running
+    the deviation + scatter kernel, whose deviation would select nothing.  On the Qwen shape's
+    first four layers (unsplit MFMA tiles: 5184 rows at layer 1, 832 at layer 4) the step gives
+    the same bits as the recorded run, which asks for deviations and takes the kernel."""
+    from dataclasses import replace
+    from rag_kv_cache_amd import _lib as L
+    from rag_kv_cache_amd.pipeline import Engine, build_chunk_caches, make_buffers, run_layers
+    base = F.get_config("qwen")
+    sh = replace(base.shape, name="qwen-4-layers", n_layers=4)
+    wl = replace(base, shape=sh, schedule=(1.0, 0.30, 0.15, 0.15))
+    W = [F.layer_weights(sh, l) for l in range(1, sh.n_layers + 1)]
+    eng = Engine(sh, max_tokens=wl.n_tokens + 8)
+    eng.load_all(lambda l: W[l - 1], F.embedding(sh))
+    cache, _ = build_chunk_caches(eng, F.chunk_tokens(wl))
+    outs = []
+    for record in (True, False):
+        buf = make_buffers(eng, wl.n_tokens, len(wl.chunk_lens))
+        fused = [(eng.kv_empty(wl.n_tokens), eng.kv_empty(wl.n_tokens)) for _ in range(sh.n_layers)]
+        L.cb_profile_enable(eng.ctx, True)
+        res = run_layers(eng, buf, F.all_tokens(wl), F.chunk_offsets(wl), wl.n_query, wl.schedule, fused,
+                         cache=cache, record=record)
+        eng.compute.synchronize()
+        L.cb_profile_enable(eng.ctx, False)
+        _, scatter_launches, _ = L.cb_profile_read(eng.ctx, L.CB_K_DEV_SCATTER)
+        outs.append((res.hidden[: res.n_final].cpu().numpy().copy(), res.sel[: res.n_final].cpu().numpy().copy(),
+                     [(bits(k), bits(v)) for k, v in fused], scatter_launches))
+    (h0, s0, f0, n0), (h1, s1, f1, n1) = outs
+    assert n0 == 4 and n1 == 2, (n0, n1)  # layers 2 and 3 narrow the set: their deviation selects
+    assert np.array_equal(s0, s1)
+    assert np.array_equal(h0, h1)
+    for (a, b), (c, d) in zip(f0, f1):
+        assert np.array_equal(a, c) and np.array_equal(b, d)
+    eng.close()
