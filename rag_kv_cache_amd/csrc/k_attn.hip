@@ -102,8 +102,6 @@ __global__ __launch_bounds__(64 * G * QT) void attn_bf16_kernel(AttnArgs a) {
   const int wrow0 = row0 + (wave / G) * 16 * RB;  // first query row of this wave
   const int l16 = lane & 15, lg = lane >> 4;
   const bf16_t* Q = reinterpret_cast<const bf16_t*>(a.q);
-  const char* Kg = reinterpret_cast<const char*>(a.k) + g * ROWB;
-  const char* Vg = reinterpret_cast<const char*>(a.v) + g * ROWB;
   const long kv_row_b = (long)a.hkv * ROWB;
   const float c = a.scale_log2;
 
@@ -111,29 +109,31 @@ __global__ __launch_bounds__(64 * G * QT) void attn_bf16_kernel(AttnArgs a) {
   // Lane l writes 16 bytes at slot l of the 1 KB block: row 4*(id%16) + l/16, slot l%16 holding
   // the row's 16-byte chunk (l%16) ^ swz(row) (swz_k for K, swz_v for V).
   const int my_ins = wave < N_HI ? INS_HI : INS_LO;
-  int ld_row[INS_HI], ld_lds[INS_HI];
-  const char* ld_src[INS_HI];
+  // Loads go through buffer descriptors over the n_tok rows of K and of V: a lane's byte offset
+  // within the tile is fixed, the tile's offset is scalar, so a load costs no vector ALU work.
+  // Keys past the split's range are loaded too (fused rows, or zeros past row n_tok from the
+  // descriptor's bound) and get probability 0 from the mask.
+  int ld_lds[INS_HI];
+  uint32_t ld_voff[INS_HI];
+  bool ld_k[INS_HI];
 #pragma unroll
   for (int i = 0; i < INS_HI; ++i) {
     const int id = wave + NW * i;
     const int blk = id & 15;
     const int row = 4 * blk + (lane >> 4);
     const int chunk = (lane & 15) ^ (id < 16 ? swz_k(row) : swz_v(row));
-    ld_row[i] = row;
-    ld_src[i] = (id < 16 ? Kg : Vg) + chunk * 16;
+    ld_voff[i] = (uint32_t)(row * kv_row_b + g * ROWB + chunk * 16);
+    ld_k[i] = id < 16;
     ld_lds[i] = (id < 16 ? 0 : TILE_B) + blk * 1024;
   }
+  const int kv_bytes = (int)((long)a.n_tok * kv_row_b);
   auto issue = [&](int t) __attribute__((always_inline)) {
     const int kt = kbeg + t * BKV;
     unsigned char* st = smem + (t % ATT_NS) * ATT_STAGE_B;
+    const int soff = (int)(kt * kv_row_b);
 #pragma unroll
-    for (int i = 0; i < INS_HI; ++i) {
-      if (i < my_ins) {
-        int key = kt + ld_row[i];
-        key = key < kend ? key : 0;
-        __builtin_amdgcn_global_load_lds((gvoid_t*)(ld_src[i] + key * kv_row_b), (lvoid_t*)(st + ld_lds[i]), 16, 0, 0);
-      }
-    }
+    for (int i = 0; i < INS_HI; ++i)
+      if (i < my_ins) buffer_load_lds16(ld_k[i] ? a.k : a.v, kv_bytes, st + ld_lds[i], ld_voff[i], soff);
   };
   // wait until tile t+1 has landed, with `more` = whether tile t+2 was issued after it (waves
   // that issued INS_HI loads per tile wait for one load of tile t+2 too: over-waiting is safe)
@@ -674,6 +674,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
 template <int G, int RB, int QT>
 hipError_t launch_gr(const AttnArgs& a, hipStream_t s) {
   constexpr int lds = ATT_NS * ATT_STAGE_B;
+  if ((long)a.n_tok * a.hkv * 128 * 2 >= (1L << 31)) return hipErrorInvalidValue;  // 32-bit buffer offsets
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<G, RB, QT>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
