@@ -108,7 +108,9 @@ __global__ __launch_bounds__(64 * G * QT) void attn_bf16_kernel(AttnArgs a) {
   // This wave's load instructions: ids wave, wave + NW, ...; id < 16 loads K rows 4*id.., else V.
   // Lane l writes 16 bytes at slot l of the 1 KB block: row 4*(id%16) + l/16, slot l%16 holding
   // the row's 16-byte chunk (l%16) ^ swz(row) (swz_k for K, swz_v for V).
-  const int my_ins = wave < N_HI ? INS_HI : INS_LO;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);  // the same value, in a scalar register: the
+                                                        // buffer descriptor chosen from it is uniform
+  const int my_ins = wv < N_HI ? INS_HI : INS_LO;
   // Loads go through buffer descriptors over the n_tok rows of K and of V: a lane's byte offset
   // within the tile is fixed, the tile's offset is scalar, so a load costs no vector ALU work.
   // Keys past the split's range are loaded too (fused rows, or zeros past row n_tok from the
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(64 * G * QT) void attn_bf16_kernel(AttnArgs a) {
   bool ld_k[INS_HI];
 #pragma unroll
   for (int i = 0; i < INS_HI; ++i) {
-    const int id = wave + NW * i;
+    const int id = wv + NW * i;
     const int blk = id & 15;
     const int row = 4 * blk + (lane >> 4);
     const int chunk = (lane & 15) ^ (id < 16 ? swz_k(row) : swz_v(row));
@@ -204,10 +206,12 @@ __global__ __launch_bounds__(64 * G * QT) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) s[rb][kb][r] = (kb * 16 + r <= thr) ? s[rb][kb][r] : NEG_INF;
       }
-      float mx = NEG_INF;
+      // this lane's 16 scores: a chain of 3-input maxima (v_max3_f32, 8 instructions)
+      float mx = fmaxf(fmaxf(s[rb][0][0], s[rb][0][1]), s[rb][0][2]);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        mx = fmaxf(mx, fmaxf(fmaxf(s[rb][kb][0], s[rb][kb][1]), fmaxf(s[rb][kb][2], s[rb][kb][3])));
+      for (int j = 3; j < 15; j += 2)
+        mx = fmaxf(fmaxf(mx, s[rb][j >> 2][j & 3]), s[rb][(j + 1) >> 2][(j + 1) & 3]);
+      mx = fmaxf(mx, s[rb][3][3]);
       mx = max4_rows(mx);
       const float m_new = fmaxf(m_i[rb], mx);
       const float alpha = (m_new == m_i[rb]) ? 1.f : __builtin_amdgcn_exp2f((m_i[rb] - m_new) * c);
