@@ -639,7 +639,7 @@ cb_status cb_blend_layer(cb_ctx* c, int32_t layer, const float* hidden_sel, cons
     g.max_pos = d.max_tokens - 1;
     // every candidate kept and no deviation asked for: the deviation selects nothing, so the
     // product's epilogue writes the fresh K/V rows into the fused cache itself (and the kept set)
-    if (fuse_q && bf && !deviation && g.splits == 1 && g.cfg != cb::GEMM_GEMV && kvd % 8 == 0 && qd % 8 == 0) {
+    if (fuse_q && bf && !deviation && kvd % 128 == 0 && qd % 128 == 0) {
       g.kv_k = kv_fused_k; g.kv_v = kv_fused_v; g.kv_col0 = qd; g.kvd = kvd; g.kv_rows = (int)n_tok;
       g.sel_out = new_sel_idx; g.local_out = new_sel_local;
       scattered = true;

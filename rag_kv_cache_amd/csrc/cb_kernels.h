@@ -26,9 +26,9 @@ struct GemmArgs {
   // skinny product (GEMM_GEMV) only: when a_f32 is set, A row m is RMSNorm(a_f32 row) * a_gain
   // (row a_rows ? a_rows[m] : m, stride lda, K wide), formed as bf16 on load; A is not read
   const float* a_f32; const float* a_gain; float a_eps;
-  // ROPE on the MFMA tiles without split only: when kv_k is set, logical columns kv_col0 ..
-  // kv_col0 + 2 kvd - 1 (K, then V) of row m go to row pos[m] of kv_k / kv_v ([kv_rows][kvd];
-  // rows outside are skipped) instead of out, and sel_out[m] = pos[m], local_out[m] = m
+  // ROPE only: when kv_k is set, logical columns kv_col0 .. kv_col0 + 2 kvd - 1 (K, then V) of
+  // row m go to row pos[m] of kv_k / kv_v ([kv_rows][kvd]; rows outside are skipped) instead of
+  // out, and sel_out[m] = pos[m], local_out[m] = m (every plan: tiles, split-K reduce, skinny)
   void* kv_k; void* kv_v; int kv_col0, kvd, kv_rows; int32_t* sel_out; int32_t* local_out;
 };
 hipError_t gemm_bf16(const GemmArgs& g, hipStream_t s);

@@ -49,6 +49,21 @@ __device__ __forceinline__ void epi_pair(const GemmArgs& g, int m, int n_a, int 
       va = ya;
       vb = yb;
     }
+    if (g.kv_k) {  // K/V columns go to the fused rows; the pair (n, n + 64) stays in one head
+      if (n_a == 0) {
+        g.sel_out[m] = g.pos[m];
+        g.local_out[m] = m;
+      }
+      if (n_a >= g.kv_col0) {
+        const int j = g.pos[m];
+        if (j < 0 || j >= g.kv_rows) return;
+        const int kn = n_a - g.kv_col0;
+        TO* d = kn < g.kvd ? (TO*)g.kv_k + (long)j * g.kvd + kn : (TO*)g.kv_v + (long)j * g.kvd + (kn - g.kvd);
+        Elem<TO>::st(d, va);
+        Elem<TO>::st(d + (n_b - n_a), vb);
+        return;
+      }
+    }
     TO* o = (TO*)g.out + (long)m * g.ldo;
     Elem<TO>::st(o + n_a, va);
     Elem<TO>::st(o + n_b, vb);
@@ -709,7 +724,7 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(GemmArgs g) {
   for (int m = 0; m < MR; ++m) {
     const int mm = m < g.M ? m : g.M - 1;
     const long r = g.a_rows ? (long)g.a_rows[mm] : (long)mm;
-    arow[m] = A + r * g.lda;
+    arow[m] = NORM ? nullptr : A + r * g.lda;
     hrow[m] = NORM ? g.a_f32 + r * g.lda : nullptr;
   }
   float inv[MR];
@@ -1047,9 +1062,9 @@ GemmPlan gemm_plan(int M, int N, int K, int epi, long partial_cap_elems) {
 hipError_t gemm_bf16(const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0) return hipSuccess;
   if (g.a_f32 && g.cfg != GEMM_GEMV) return hipErrorInvalidValue;  // normalise-on-load: skinny product only
-  if (g.kv_k && (g.epi != EPI_ROPE || g.splits != 1 || g.cfg == GEMM_GEMV || g.kvd % 8 != 0 || g.kv_col0 % 8 != 0 ||
-                 !g.kv_v || !g.sel_out || !g.local_out || !g.pos))
-    return hipErrorInvalidValue;  // scatter in the epilogue: unsplit MFMA tiles only
+  if (g.kv_k && (g.epi != EPI_ROPE || g.kvd % 128 != 0 || g.kv_col0 % 128 != 0 || !g.kv_v || !g.sel_out ||
+                 !g.local_out || !g.pos))
+    return hipErrorInvalidValue;  // K/V rows scattered by the epilogue: whole heads of 128 columns
   hipError_t e;
   switch (g.epi) {
     case EPI_ROPE: e = g.b_i8 ? launch_epi<EPI_ROPE, 1>(g, s) : launch_epi<EPI_ROPE, 0>(g, s); break;

@@ -216,21 +216,23 @@ def test_many_chunks_and_layers_batched_paths():
     eng.close()
 
 
-@pytest.mark.parametrize("weights", ["bf16", "int8"])
-def test_kv_scatter_in_product_epilogue_gives_the_scatter_kernels_bits(weights):
+@pytest.mark.parametrize("weights,schedule", [("bf16", (1.0, 0.30, 0.15, 0.15)), ("int8", (1.0, 0.30, 0.15, 0.15)),
+                                              ("bf16", (1.0, 0.30, 0.0, 0.0))])
+def test_kv_scatter_in_product_epilogue_gives_the_scatter_kernels_bits(weights, schedule):
     """With no deviation asked for (a run that records nothing), a layer that keeps every
-    candidate (layer 1 at ratio 1, layer 4 at an unchanged 15%) writes its fresh K/V into the
-    fused cache from the K/V product's epilogue, and the kept set with it, instead of running
-    the deviation + scatter kernel, whose deviation would select nothing.  On the Qwen shape's
-    first four layers (unsplit MFMA tiles: 5184 rows at layer 1, 832 at layer 4), with bf16 or
-    int8 weights, the step gives the same bits as the recorded run, which asks for deviations
-    and takes the kernel."""
+    candidate (layer 1 at ratio 1, layer 4 at an unchanged 15%, or layer 4 after layer 3 kept
+    only the query rows) writes its fresh K/V into the fused cache from the K/V product's
+    epilogue, and the kept set with it, instead of running the deviation + scatter kernel, whose
+    deviation would select nothing.  On the Qwen shape's first four layers (unsplit MFMA tiles:
+    5184 rows at layer 1, 832 at layer 4; split-K with the epilogue in the reduce: the 64 query
+    rows at layer 4), with bf16 or int8 weights, the step gives the same bits as the recorded run,
+    which asks for deviations and takes the kernel."""
     from dataclasses import replace
     from rag_kv_cache_amd import _lib as L
     from rag_kv_cache_amd.pipeline import Engine, build_chunk_caches, make_buffers, run_layers
     base = F.get_config("qwen")
     sh = replace(base.shape, name="qwen-4-layers", n_layers=4)
-    wl = replace(base, shape=sh, schedule=(1.0, 0.30, 0.15, 0.15))
+    wl = replace(base, shape=sh, schedule=schedule)
     eng = Engine(sh, max_tokens=wl.n_tokens + 8)
     if weights == "bf16":
         W = [F.layer_weights(sh, l) for l in range(1, sh.n_layers + 1)]
