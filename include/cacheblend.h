@@ -276,6 +276,14 @@ cb_status cb_layer_rest(cb_ctx* ctx, int32_t layer, const float* hidden_sel, int
                         const int32_t* new_sel_local, int32_t n_new, const void* out_sel,
                         float* hidden_next, void* x_next, void* workspace, size_t workspace_bytes);
 
+/* Where cb_layer_rest leaves two of its intermediates in the workspace, for checking a layer
+ * piece by piece: after cb_layer_rest(..., n_sel, ..., n_new, ...) returns and its stream has
+ * run, the workspace holds at byte offset *h1_offset the rows h1 (fp32 [n_new][d]) and at
+ * *act_offset the SwiGLU product silu(W_gate m) * (W_up m) (model dtype [n_new][ffn_dim]),
+ * until the next call that uses the workspace.  n_sel is the value given to cb_layer_rest.
+ * Host only; CB_EINVAL for a NULL pointer or a negative n_sel. */
+cb_status cb_layer_rest_intermediates(const cb_ctx* ctx, int32_t n_sel, size_t* h1_offset, size_t* act_offset);
+
 /* Selection variants (KVBoost page, section on seam repair).
  *
  * Deviation score of cb_blend_layer on this context (default CB_SCORE_L2):

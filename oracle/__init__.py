@@ -43,10 +43,10 @@ Parity status per function (what pins each one, see tests/test_oracle_*.py):
 """
 from .model import (  # noqa: F401
     Precision, F64, round_bf16, rope_cos_sin, rope_rotate, rope_delta, rmsnorm, project,
-    causal_attention, mlp, full_prefill, chunk_caches, cache_nbytes, dequantize,
+    causal_attention, swiglu, mlp, full_prefill, chunk_caches, cache_nbytes, dequantize,
 )
 from .blend import (  # noqa: F401
     k_for_ratio, topk_select, kv_deviation, cosine_deviation, seam_positions, blend_layer,
-    layer_rest, fuse_cache, blended_prefill, decode_step,
+    attn_residual, layer_rest, fuse_cache, blended_prefill, decode_step,
 )
 from . import controller, store  # noqa: F401

@@ -160,11 +160,17 @@ def blend_layer(shape, w: Dict[str, np.ndarray], prec: Precision, hidden_sel: np
             "k": k, "new_sel": new_sel, "new_local": new_local, "q": q, "out": out}
 
 
+def attn_residual(w: Dict[str, np.ndarray], hidden_sel: np.ndarray, new_local: Sequence[int],
+                  out: np.ndarray) -> np.ndarray:
+    """First half of step 8: h1 = h[kept] + out W_o^T (the residual after attention)."""
+    return np.asarray(hidden_sel, np.float64)[np.asarray(new_local)] + project(out, w["w_o"])
+
+
 def layer_rest(shape, w: Dict[str, np.ndarray], prec: Precision, hidden_sel: np.ndarray,
                new_local: Sequence[int], out: np.ndarray) -> np.ndarray:
     """Step 8: o-projection plus residual on the kept rows, then the SwiGLU FFN block.
     Returns the residual-stream rows of S_{l+1} for the next layer."""
-    h1 = np.asarray(hidden_sel, np.float64)[np.asarray(new_local)] + project(out, w["w_o"])
+    h1 = attn_residual(w, hidden_sel, new_local, out)
     return mlp(h1, w, shape.rms_eps, prec)
 
 

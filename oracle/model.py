@@ -131,11 +131,18 @@ def silu(x: np.ndarray) -> np.ndarray:
     return x / (1.0 + np.exp(-x))
 
 
-def mlp(h1: np.ndarray, w: Dict[str, np.ndarray], eps: float, prec: Precision) -> np.ndarray:
-    """Second half of the layer: h1 + W_down(silu(W_gate m) * W_up m), m = RMSNorm(h1)."""
+def swiglu(h1: np.ndarray, w: Dict[str, np.ndarray], eps: float, prec: Precision) -> np.ndarray:
+    """The FFN's inner activations: silu(W_gate m) * W_up m with m = RMSNorm(h1) (stored)."""
     m = prec.store(rmsnorm(h1, w["g_ffn"], eps))
-    act = prec.store(silu(project(m, w["w_gate"])) * project(m, w["w_up"]))
-    return h1 + project(act, w["w_down"])
+    return prec.store(silu(project(m, w["w_gate"])) * project(m, w["w_up"]))
+
+
+def mlp(h1: np.ndarray, w: Dict[str, np.ndarray], eps: float, prec: Precision, act=None) -> np.ndarray:
+    """Second half of the layer: h1 + W_down(silu(W_gate m) * W_up m), m = RMSNorm(h1).
+    act: the inner activations if already known (swiglu of the same h1), else computed."""
+    if act is None:
+        act = swiglu(h1, w, eps, prec)
+    return np.asarray(h1, np.float64) + project(act, w["w_down"])
 
 
 # ---------------------------------------------------------------- full prefill (ground truth)

@@ -76,6 +76,7 @@ _SIGS = {
                        C.POINTER(_I), _P, _P, _P, C.c_size_t],
     "cb_layer_rest": [_P, _I, _P, _I, _P, _I, _P, _P, _P, _P, C.c_size_t],
     "cb_decode_layer": [_P, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P, C.c_size_t],
+    "cb_layer_rest_intermediates": [_P, _I, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)],
     "cb_set_score_mode": [_P, _I],
     "cb_seam_select": [C.POINTER(_I), _I, _I, _I, C.POINTER(_I), _I, C.POINTER(_I)],
     "cb_plan_ratio": [_I, _I, C.c_double, C.c_double, C.c_double, C.c_double, C.c_float, C.c_float, _P],
@@ -211,6 +212,13 @@ def cb_layer_rest(ctx: int, layer: int, hidden_sel: int, n_sel: int, new_sel_loc
                   out_sel: int, hidden_next: int, workspace: int, workspace_bytes: int, x_next: int = 0) -> None:
     _check(_L.cb_layer_rest(ctx, layer, hidden_sel, n_sel, new_sel_local, n_new, out_sel, hidden_next,
                             x_next or None, workspace, workspace_bytes))
+
+
+def cb_layer_rest_intermediates(ctx: int, n_sel: int):
+    """(h1 byte offset, SwiGLU product byte offset) in the workspace after cb_layer_rest."""
+    h1, act = C.c_size_t(), C.c_size_t()
+    _check(_L.cb_layer_rest_intermediates(ctx, n_sel, C.byref(h1), C.byref(act)))
+    return h1.value, act.value
 
 
 CB_SCORE_L2, CB_SCORE_COSINE = 0, 1

@@ -720,6 +720,16 @@ cb_status cb_decode_layer(cb_ctx* c, int32_t layer, const float* hidden_new, con
                         nullptr, workspace, ws_bytes);
 }
 
+cb_status cb_layer_rest_intermediates(const cb_ctx* c, int32_t n_sel, size_t* h1_offset, size_t* act_offset) {
+  cb_status st = check_ctx(c);
+  if (st) return st;
+  if (n_sel < 0 || !h1_offset || !act_offset) return fail(CB_EINVAL, "negative n_sel or NULL output");
+  const WsPlan wp = plan_ws(c->d, n_sel, n_sel);
+  *h1_offset = wp.h1;
+  *act_offset = wp.act;
+  return CB_OK;
+}
+
 cb_status cb_layer_rest(cb_ctx* c, int32_t layer, const float* hidden_sel, int32_t n_sel,
                         const int32_t* new_sel_local, int32_t n_new, const void* out_sel, float* hidden_next,
                         void* x_next, void* workspace, size_t ws_bytes) {

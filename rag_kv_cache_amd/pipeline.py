@@ -180,6 +180,18 @@ class LayerRecord:
     deviation: np.ndarray
     out_sel: np.ndarray
     hidden_out: np.ndarray
+    h1: Optional[np.ndarray] = None    # residual after attention of the kept rows (fp32)
+    act: Optional[np.ndarray] = None   # SwiGLU product of the kept rows (as float32)
+
+
+def workspace_intermediates(eng: "Engine", ws: torch.Tensor, n_sel: int, n_new: int):
+    """h1 and the SwiGLU product that cb_layer_rest(n_sel -> n_new rows) left in ws, as host arrays."""
+    s = eng.shape
+    o_h1, o_act = L.cb_layer_rest_intermediates(eng.ctx, n_sel)
+    es = 2 if eng.dtype == torch.bfloat16 else 4
+    h1 = ws[o_h1: o_h1 + n_new * s.d_model * 4].view(torch.float32).reshape(n_new, s.d_model)
+    act = ws[o_act: o_act + n_new * s.ffn_dim * es].view(eng.dtype).reshape(n_new, s.ffn_dim)
+    return h1.cpu().numpy().copy(), act.float().cpu().numpy()
 
 
 @dataclass
@@ -303,11 +315,12 @@ def run_layers(eng: Engine, buf: RunBuffers, tokens: np.ndarray, offsets: Sequen
                         _ptr(ws), ws.numel(), x_next=_ptr(x_out))
         if record:
             cs.synchronize()
+            h1, act = workspace_intermediates(eng, ws, n_sel, n_new)
             records.append(LayerRecord(
                 sel=sel_in[:n_sel].cpu().numpy().copy(), new_sel=sel_out[:n_new].cpu().numpy().copy(),
                 deviation=buf.dev[: n_sel - n_query].cpu().numpy().copy(),
                 out_sel=buf.out_sel[:n_new].float().cpu().numpy().copy(),
-                hidden_out=h_out[:n_new].cpu().numpy().copy()))
+                hidden_out=h_out[:n_new].cpu().numpy().copy(), h1=h1, act=act))
         mark()
         n_sel, cur = n_new, 1 - cur
     final_sel = buf.sel[(s.n_layers - 1) % 2]

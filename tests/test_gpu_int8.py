@@ -4,7 +4,7 @@ fp32 sums) against the oracle running the dequantized model (q * s in float32):
     every layer teacher-forced on the GPU's own inputs, plus a decode step (the int8 skinny
     product);
   * the Yi-34B shape (d_model 7,168, FFN 20,480, GQA group 7) at its real per-layer sizes: the
-    first three layers teacher-forced on sampled rows and a decode step layer by layer."""
+    first three layers teacher-forced on every row and a decode step layer by layer."""
 from dataclasses import replace
 
 import numpy as np
@@ -14,7 +14,7 @@ import fixtures as F
 import oracle as O
 from parity_util import assert_close, check_selected, local_index
 from gpu_setup import to_np
-from sampled_checks import check_decode_teacher_forced, check_layer
+from layer_checks import check_decode_teacher_forced, check_layer
 
 pytestmark = pytest.mark.gpu
 
