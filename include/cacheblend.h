@@ -276,13 +276,22 @@ cb_status cb_layer_rest(cb_ctx* ctx, int32_t layer, const float* hidden_sel, int
                         const int32_t* new_sel_local, int32_t n_new, const void* out_sel,
                         float* hidden_next, void* x_next, void* workspace, size_t workspace_bytes);
 
-/* Where cb_layer_rest leaves two of its intermediates in the workspace, for checking a layer
- * piece by piece: after cb_layer_rest(..., n_sel, ..., n_new, ...) returns and its stream has
- * run, the workspace holds at byte offset *h1_offset the rows h1 (fp32 [n_new][d]) and at
- * *act_offset the SwiGLU product silu(W_gate m) * (W_up m) (model dtype [n_new][ffn_dim]),
- * until the next call that uses the workspace.  n_sel is the value given to cb_layer_rest.
- * Host only; CB_EINVAL for a NULL pointer or a negative n_sel. */
-cb_status cb_layer_rest_intermediates(const cb_ctx* ctx, int32_t n_sel, size_t* h1_offset, size_t* act_offset);
+/* Where the calls leave intermediates in the caller's workspace, for checking a layer piece by
+ * piece (host only; nothing is enqueued):
+ *   q_offset, q_ld  after cb_blend_layer(..., n_sel, ...) has run: Q of the kept rows after
+ *                   RoPE (model dtype; row j = the j-th kept row, rows q_ld elements apart),
+ *                   until cb_layer_rest reuses the workspace.  all_kept != 0 when that call kept
+ *                   every candidate (n_new == n_sel), which places Q in the joint Q|K|V product.
+ *   h1_offset       after cb_layer_rest(..., n_sel, ...) has run: h1 (fp32 [n_new][d]);
+ *   act_offset      then also the SwiGLU product silu(W_gate m) * (W_up m) (model dtype
+ *                   [n_new][ffn_dim]), both until the next call that uses the workspace.
+ * CB_EINVAL for a NULL pointer or a negative n_sel. */
+typedef struct {
+  size_t q_offset;
+  int32_t q_ld;
+  size_t h1_offset, act_offset;
+} cb_ws_views;
+cb_status cb_workspace_views(const cb_ctx* ctx, int32_t n_sel, int32_t all_kept, cb_ws_views* out);
 
 /* Selection variants (KVBoost page, section on seam repair).
  *
@@ -426,14 +435,16 @@ const char* cb_last_error(void);
 typedef enum {
   CB_K_EMBED = 0, CB_K_ROPE = 1, CB_K_RMSNORM = 2, CB_K_GEMM_KV = 3, CB_K_DEV_SCATTER = 4,
   CB_K_TOPK = 5, CB_K_GEMM_Q = 6, CB_K_ATTN = 7, CB_K_GEMM_O = 8, CB_K_GEMM_GATE_UP = 9,
-  CB_K_GEMM_DOWN = 10, CB_K_COUNT = 11
+  CB_K_GEMM_DOWN = 10, CB_K_FETCH = 11, CB_K_COUNT = 12
 } cb_kernel_id;
 /* Start (on != 0) or stop recording; starting clears earlier records.  At most 16384 timed
  * launches are kept; later ones are not timed. */
 cb_status cb_profile_enable(cb_ctx* ctx, int32_t on);
 /* Wait for the recorded events and report, for one id: total ms, number of launches, and
  * the algorithmic work of those launches (flops for GEMM and attention, bytes moved for
- * the others) as computed from their shapes. */
+ * the others, for CB_K_FETCH the cached K and V bytes read from host memory) as computed
+ * from their shapes.  Launches on the copy stream (fetches and their position updates) are
+ * timed on that stream. */
 cb_status cb_profile_read(cb_ctx* ctx, int32_t kernel_id, double* total_ms, int64_t* launches,
                           double* work);
 

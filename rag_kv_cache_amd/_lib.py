@@ -19,9 +19,9 @@ STATUS_NAMES = {0: "CB_OK", -1: "CB_EINVAL", -2: "CB_ESHAPE", -3: "CB_ESTATE", -
                 -5: "CB_ENOMEM", -6: "CB_EUNSUPPORTED"}
 CB_F32, CB_BF16 = 0, 1
 (CB_K_EMBED, CB_K_ROPE, CB_K_RMSNORM, CB_K_GEMM_KV, CB_K_DEV_SCATTER, CB_K_TOPK, CB_K_GEMM_Q, CB_K_ATTN,
- CB_K_GEMM_O, CB_K_GEMM_GATE_UP, CB_K_GEMM_DOWN, CB_K_COUNT) = range(12)
+ CB_K_GEMM_O, CB_K_GEMM_GATE_UP, CB_K_GEMM_DOWN, CB_K_FETCH, CB_K_COUNT) = range(13)
 KERNEL_NAMES = ["embed", "rope_delta", "rmsnorm", "gemm_kv", "dev_scatter", "topk", "gemm_q", "attention",
-                "gemm_o", "gemm_gate_up", "gemm_down"]
+                "gemm_o", "gemm_gate_up", "gemm_down", "fetch"]
 
 
 class CbError(RuntimeError):
@@ -76,7 +76,7 @@ _SIGS = {
                        C.POINTER(_I), _P, _P, _P, C.c_size_t],
     "cb_layer_rest": [_P, _I, _P, _I, _P, _I, _P, _P, _P, _P, C.c_size_t],
     "cb_decode_layer": [_P, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P, C.c_size_t],
-    "cb_layer_rest_intermediates": [_P, _I, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)],
+    "cb_workspace_views": [_P, _I, _I, _P],
     "cb_set_score_mode": [_P, _I],
     "cb_seam_select": [C.POINTER(_I), _I, _I, _I, C.POINTER(_I), _I, C.POINTER(_I)],
     "cb_plan_ratio": [_I, _I, C.c_double, C.c_double, C.c_double, C.c_double, C.c_float, C.c_float, _P],
@@ -214,11 +214,16 @@ def cb_layer_rest(ctx: int, layer: int, hidden_sel: int, n_sel: int, new_sel_loc
                             x_next or None, workspace, workspace_bytes))
 
 
-def cb_layer_rest_intermediates(ctx: int, n_sel: int):
-    """(h1 byte offset, SwiGLU product byte offset) in the workspace after cb_layer_rest."""
-    h1, act = C.c_size_t(), C.c_size_t()
-    _check(_L.cb_layer_rest_intermediates(ctx, n_sel, C.byref(h1), C.byref(act)))
-    return h1.value, act.value
+class cb_ws_views(C.Structure):
+    _fields_ = [("q_offset", C.c_size_t), ("q_ld", C.c_int32), ("h1_offset", C.c_size_t),
+                ("act_offset", C.c_size_t)]
+
+
+def cb_workspace_views(ctx: int, n_sel: int, all_kept: bool) -> "cb_ws_views":
+    """Byte offsets (and Q's row stride) of the intermediates the calls leave in the workspace."""
+    out = cb_ws_views()
+    _check(_L.cb_workspace_views(ctx, n_sel, int(bool(all_kept)), C.byref(out)))
+    return out
 
 
 CB_SCORE_L2, CB_SCORE_COSINE = 0, 1

@@ -451,7 +451,7 @@ cb_status cb_fetch_layer(cb_ctx* c, int32_t layer, const void* const* host_k, co
   if ((st = wait_release(c, layer))) return st;
   const int n_ctx = n_chunks > 0 ? offs[n_chunks] : 0;
   if (direct && n_ctx > 0) {  // one kernel per 64 chunks reads, rotates and writes the rows
-    Timed t(c, CB_K_ROPE, (double)n_ctx * c->d.n_kv_heads * c->d.head_dim * c->esize() * 4.0, c->xs);
+    Timed t(c, CB_K_FETCH, (double)n_ctx * c->d.n_kv_heads * c->d.head_dim * c->esize() * 2.0, c->xs);
     for (int c0 = 0; c0 < n_chunks; c0 += cb::kFetchMaxChunks) {
       cb::FetchChunks F{};
       F.n = std::min(cb::kFetchMaxChunks, n_chunks - c0);
@@ -720,13 +720,16 @@ cb_status cb_decode_layer(cb_ctx* c, int32_t layer, const float* hidden_new, con
                         nullptr, workspace, ws_bytes);
 }
 
-cb_status cb_layer_rest_intermediates(const cb_ctx* c, int32_t n_sel, size_t* h1_offset, size_t* act_offset) {
+cb_status cb_workspace_views(const cb_ctx* c, int32_t n_sel, int32_t all_kept, cb_ws_views* out) {
   cb_status st = check_ctx(c);
   if (st) return st;
-  if (n_sel < 0 || !h1_offset || !act_offset) return fail(CB_EINVAL, "negative n_sel or NULL output");
+  if (n_sel < 0 || !out) return fail(CB_EINVAL, "negative n_sel or NULL output");
   const WsPlan wp = plan_ws(c->d, n_sel, n_sel);
-  *h1_offset = wp.h1;
-  *act_offset = wp.act;
+  const int qd = c->d.n_q_heads * c->d.head_dim, kvd = c->d.n_kv_heads * c->d.head_dim;
+  out->q_offset = all_kept ? wp.fresh : wp.q;  // see steps 3 and 6a of cb_blend_layer
+  out->q_ld = all_kept ? qd + 2 * kvd : qd;
+  out->h1_offset = wp.h1;
+  out->act_offset = wp.act;
   return CB_OK;
 }
 

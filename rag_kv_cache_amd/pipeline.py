@@ -114,6 +114,49 @@ class Engine:
                                   _ptr(t["w_down"]), _ptr(t["s_qkv"]), _ptr(t["s_o"]), _ptr(t["s_gate_up"]),
                                   _ptr(t["s_down"]), _ptr(t["g_attn"]), _ptr(t["g_ffn"]))
 
+    def load_layer_device(self, layer: int, seed: int, int8: bool = False) -> None:
+        """Random weights of `layer` drawn on the device: N(0, 0.02) float32 from torch's
+        generator seeded with `seed`, then bf16 (or, with int8, quantized per output row: s =
+        max|w| / 127, q = round half to even of w / s clamped to +-127); gains 1.  For benchmarks
+        at sizes where drawing on the host would take minutes; the values differ from the
+        fixtures' draws."""
+        s = self.shape
+        d, qd, kvd, f = s.d_model, s.n_q_heads * s.head_dim, s.n_kv_heads * s.head_dim, s.ffn_dim
+        g = torch.Generator(device=self.device)
+        g.manual_seed(int(seed))
+
+        def draw(rows, cols):
+            w = torch.randn(rows, cols, generator=g, device=self.device, dtype=torch.float32)
+            w.mul_(0.02)
+            if not int8:
+                return w.to(self.dtype), None
+            sc = w.abs().amax(dim=1) / 127.0
+            q = torch.round(w / torch.where(sc > 0, sc, torch.ones_like(sc))[:, None]).clamp_(-127, 127)
+            return q.to(torch.int8), sc.contiguous()
+
+        parts = {n: draw(r, c) for n, (r, c) in
+                 {"qkv": (qd + 2 * kvd, d), "o": (d, qd), "gate_up": (2 * f, d), "down": (d, f)}.items()}
+        t = {"w_" + n: parts[n][0] for n in parts}
+        t["g_attn"] = torch.ones(d, dtype=torch.float32, device=self.device)
+        t["g_ffn"] = torch.ones(d, dtype=torch.float32, device=self.device)
+        self.weights[layer] = t
+        if int8:
+            for n in parts:
+                t["s_" + n] = parts[n][1]
+            L.cb_set_layer_weights_i8(self.ctx, layer, _ptr(t["w_qkv"]), _ptr(t["w_o"]), _ptr(t["w_gate_up"]),
+                                      _ptr(t["w_down"]), _ptr(t["s_qkv"]), _ptr(t["s_o"]), _ptr(t["s_gate_up"]),
+                                      _ptr(t["s_down"]), _ptr(t["g_attn"]), _ptr(t["g_ffn"]))
+        else:
+            L.cb_set_layer_weights(self.ctx, layer, _ptr(t["w_qkv"]), _ptr(t["w_o"]), _ptr(t["w_gate_up"]),
+                                   _ptr(t["w_down"]), _ptr(t["g_attn"]), _ptr(t["g_ffn"]))
+
+    def load_embedding_device(self, seed: int) -> None:
+        """Embedding table [vocab, d] of N(0, 0.02) values drawn on the device (see load_layer_device)."""
+        s = self.shape
+        g = torch.Generator(device=self.device)
+        g.manual_seed(int(seed))
+        self.emb = (torch.randn(s.vocab, s.d_model, generator=g, device=self.device) * 0.02).to(self.dtype)
+
     def load_embedding(self, emb: np.ndarray) -> None:
         self.emb = self._dev(emb)
 
@@ -177,20 +220,34 @@ def make_buffers(eng: Engine, n_tokens: int, n_chunks: int) -> RunBuffers:
 class LayerRecord:
     sel: np.ndarray
     new_sel: np.ndarray
-    deviation: np.ndarray
-    out_sel: np.ndarray
-    hidden_out: np.ndarray
+    deviation: Optional[np.ndarray]
+    out_sel: Optional[np.ndarray]
+    hidden_out: Optional[np.ndarray]
     h1: Optional[np.ndarray] = None    # residual after attention of the kept rows (fp32)
     act: Optional[np.ndarray] = None   # SwiGLU product of the kept rows (as float32)
+    q: Optional[np.ndarray] = None     # Q of the kept rows after RoPE (as float32)
+
+
+def workspace_q(eng: "Engine", ws: torch.Tensor, n_sel: int, n_new: int) -> np.ndarray:
+    """Q of the kept rows (after RoPE) that cb_blend_layer(n_sel -> n_new rows) left in ws,
+    as a host float32 array [n_new, H_q * d_h]; read it before cb_layer_rest reuses ws."""
+    s = eng.shape
+    v = L.cb_workspace_views(eng.ctx, n_sel, n_new == n_sel)
+    es = 2 if eng.dtype == torch.bfloat16 else 4
+    qd = s.n_q_heads * s.head_dim
+    if n_new == 0:
+        return np.zeros((0, qd), np.float32)
+    rows = ws[v.q_offset: v.q_offset + ((n_new - 1) * v.q_ld + qd) * es].view(eng.dtype)
+    return torch.as_strided(rows, (n_new, qd), (v.q_ld, 1)).float().cpu().numpy()
 
 
 def workspace_intermediates(eng: "Engine", ws: torch.Tensor, n_sel: int, n_new: int):
     """h1 and the SwiGLU product that cb_layer_rest(n_sel -> n_new rows) left in ws, as host arrays."""
     s = eng.shape
-    o_h1, o_act = L.cb_layer_rest_intermediates(eng.ctx, n_sel)
+    v = L.cb_workspace_views(eng.ctx, n_sel, n_new == n_sel)
     es = 2 if eng.dtype == torch.bfloat16 else 4
-    h1 = ws[o_h1: o_h1 + n_new * s.d_model * 4].view(torch.float32).reshape(n_new, s.d_model)
-    act = ws[o_act: o_act + n_new * s.ffn_dim * es].view(eng.dtype).reshape(n_new, s.ffn_dim)
+    h1 = ws[v.h1_offset: v.h1_offset + n_new * s.d_model * 4].view(torch.float32).reshape(n_new, s.d_model)
+    act = ws[v.act_offset: v.act_offset + n_new * s.ffn_dim * es].view(eng.dtype).reshape(n_new, s.ffn_dim)
     return h1.cpu().numpy().copy(), act.float().cpu().numpy()
 
 
@@ -229,6 +286,10 @@ def run_layers(eng: Engine, buf: RunBuffers, tokens: np.ndarray, offsets: Sequen
     upload_inputs=False reuses the token ids and offsets already on the device (a repeated
     step then enqueues no host-to-device copy); with initial_sel, sel_uploaded=True likewise
     reuses the rows and their token ids uploaded by an earlier call with the same initial_sel.
+    record: True keeps every layer's sets, deviations, attention output, residual rows and
+    intermediates on the host (the deviation is then written, which runs the deviation + scatter
+    kernel at every layer); "sets" keeps only each layer's selected and kept positions, without
+    changing which kernels run.
     paced (prefetch modes): layer l+2's fetch waits until the compute stream has reached layer l,
     so that the fetches spread over the step instead of running back to back at its start.  layer_events, if given, receives a CUDA event
     recorded on the compute stream before the first layer and after every layer.
@@ -309,18 +370,27 @@ def run_layers(eng: Engine, buf: RunBuffers, tokens: np.ndarray, offsets: Sequen
         n_new = L.cb_blend_layer(ctx, l, _ptr(h_in), _ptr(ck), _ptr(cv), _ptr(fk), _ptr(fv),
                                  _ptr(buf.offsets) if n_chunks else 0, offs, n_chunks, _ptr(sel_in), n_sel,
                                  n_query, float(schedule[l]), _ptr(sel_out), _ptr(buf.new_local),
-                                 _ptr(buf.out_sel), _ptr(buf.dev) if record else 0, _ptr(ws), ws.numel(),
+                                 _ptr(buf.out_sel), _ptr(buf.dev) if record is True else 0, _ptr(ws), ws.numel(),
                                  x_sel=_ptr(x_in))
+        q_rec = None
+        if record is True:
+            cs.synchronize()
+            q_rec = workspace_q(eng, ws, n_sel, n_new)
         L.cb_layer_rest(ctx, l, _ptr(h_in), n_sel, _ptr(buf.new_local), n_new, _ptr(buf.out_sel), _ptr(h_out),
                         _ptr(ws), ws.numel(), x_next=_ptr(x_out))
-        if record:
+        if record == "sets":
+            cs.synchronize()
+            records.append(LayerRecord(sel=sel_in[:n_sel].cpu().numpy().copy(),
+                                       new_sel=sel_out[:n_new].cpu().numpy().copy(),
+                                       deviation=None, out_sel=None, hidden_out=None))
+        elif record:
             cs.synchronize()
             h1, act = workspace_intermediates(eng, ws, n_sel, n_new)
             records.append(LayerRecord(
                 sel=sel_in[:n_sel].cpu().numpy().copy(), new_sel=sel_out[:n_new].cpu().numpy().copy(),
                 deviation=buf.dev[: n_sel - n_query].cpu().numpy().copy(),
                 out_sel=buf.out_sel[:n_new].float().cpu().numpy().copy(),
-                hidden_out=h_out[:n_new].cpu().numpy().copy(), h1=h1, act=act))
+                hidden_out=h_out[:n_new].cpu().numpy().copy(), h1=h1, act=act, q=q_rec))
         mark()
         n_sel, cur = n_new, 1 - cur
     final_sel = buf.sel[(s.n_layers - 1) % 2]

@@ -73,11 +73,12 @@ def attention_rows(q, fk, fv, pos, block=256):
 def check_rest(sh, w, what, h, kloc, out_gpu, h1_gpu, act_gpu, h_out_gpu):
     """The rest of a layer in three pieces, each fed the GPU's own input to it."""
     h1_ref = O.attn_residual(w, h, kloc, out_gpu)
-    assert_close(h1_gpu, h1_ref, "bf16", f"{what}: residual after attention")
+    use = {"h1": assert_close(h1_gpu, h1_ref, "bf16", f"{what}: residual after attention")}
     act_ref = O.swiglu(h1_gpu, w, sh.rms_eps, PREC)
-    assert_close(act_gpu, act_ref, "bf16", f"{what}: SwiGLU product")
+    use["swiglu"] = assert_close(act_gpu, act_ref, "bf16", f"{what}: SwiGLU product")
     h_ref = O.mlp(h1_gpu, w, sh.rms_eps, PREC, act=act_gpu)
-    assert_close(h_out_gpu, h_ref, "bf16", f"{what}: layer output")
+    use["out"] = assert_close(h_out_gpu, h_ref, "bf16", f"{what}: layer output")
+    return use
 
 
 def check_layer(wl, layer, w, rec, h, cache_kv, fused_kv):
@@ -138,17 +139,22 @@ def check_layer(wl, layer, w, rec, h, cache_kv, fused_kv):
         assert_close(fk[untouched], k_rot[untouched], "bf16", f"{tag}: re-rotated K of rows not recomputed")
         assert np.array_equal(fv[untouched], cv[untouched]), f"{tag}: V of rows not recomputed"
 
-    # 4. attention output of every kept row (the oracle's Q of the GPU's input rows)
+    # 4. Q of every kept row against the oracle's Q of the GPU's input rows; the attention output
+    #    of every kept row against the oracle's attention of the GPU's Q over the GPU's fused rows
     loc = {int(p): i for i, p in enumerate(sel)}
     kloc = np.array([loc[int(p)] for p in new], dtype=np.int64)
     q = PREC.store(O.rope_rotate(O.project(x[kloc], w["w_q"]).reshape(-1, hq, dh), new, sh.rope_base))
-    att = PREC.store(attention_rows(q, fk, fv, new)).reshape(len(new), hq * dh)
-    assert_close(rec.out_sel, att, "bf16", f"{tag}: attention output")
+    use = {"q": assert_close(rec.q, q.reshape(len(new), hq * dh), "bf16", f"{tag}: Q of the kept rows")}
+    att = PREC.store(attention_rows(rec.q.astype(np.float64).reshape(-1, hq, dh), fk, fv, new))
+    att = att.reshape(len(new), hq * dh)
+    use["attention"] = assert_close(rec.out_sel, att, "bf16", f"{tag}: attention output")
+    use["attention_max_abs"] = float(np.abs(rec.out_sel - att).max(initial=0.0))
 
     # 5. rest of the layer, piece by piece
-    check_rest(sh, w, tag, h, kloc, rec.out_sel, rec.h1, rec.act, rec.hidden_out)
+    use.update(check_rest(sh, w, tag, h, kloc, rec.out_sel, rec.h1, rec.act, rec.hidden_out))
     _log(f"{tag}: {len(sel)} -> {len(new)} rows, {flips} tie-band flips, all rows checked "
-         f"in {time.perf_counter() - t0:.1f} s")
+         f"in {time.perf_counter() - t0:.1f} s; share of the bar used: "
+         + ", ".join(f"{k} {v:.3g}" for k, v in use.items()))
     return flips
 
 
@@ -173,7 +179,7 @@ def check_decode_teacher_forced(eng, buf, fused, wl, W, emb, tok):
     GPU's input row of that layer and the GPU's fused rows."""
     import torch
     from rag_kv_cache_amd import _lib as L
-    from rag_kv_cache_amd.pipeline import _ptr, workspace_intermediates
+    from rag_kv_cache_amd.pipeline import _ptr, workspace_intermediates, workspace_q
     sh = wl.shape
     n = wl.n_tokens
     cs = eng.compute
@@ -190,6 +196,8 @@ def check_decode_teacher_forced(eng, buf, fused, wl, W, emb, tok):
         fk, fv = to_np(fused[l][0][:n]), to_np(fused[l][1][:n])
         L.cb_decode_layer(eng.ctx, l, _ptr(h_in), _ptr(fused[l][0]), _ptr(fused[l][1]), n, 1, _ptr(buf.init_sel),
                           _ptr(buf.out_sel), _ptr(ws), ws.numel())
+        cs.synchronize()
+        q_gpu = workspace_q(eng, ws, 1, 1).astype(np.float64)
         L.cb_layer_rest(eng.ctx, l, _ptr(h_in), 1, _ptr(buf.iota), 1, _ptr(buf.out_sel), _ptr(h_out), _ptr(ws),
                         ws.numel())
         cs.synchronize()
@@ -201,7 +209,11 @@ def check_decode_teacher_forced(eng, buf, fused, wl, W, emb, tok):
         r = O.blend_layer(sh, W[l], PREC, hin, np.concatenate([fk, zero]), np.concatenate([fv, zero]), n,
                           np.array([n]), 1, 0.0)
         out = to_np(buf.out_sel[:1])
-        assert_close(out, r["out"].reshape(1, -1), "bf16", f"decode attention output layer {l + 1}")
+        assert_close(q_gpu, r["q"].reshape(1, -1), "bf16", f"decode Q layer {l + 1}")
+        fk1 = np.concatenate([fk, to_np(fused[l][0][n:n + 1])])
+        fv1 = np.concatenate([fv, to_np(fused[l][1][n:n + 1])])
+        att = PREC.store(O.causal_attention(q_gpu.reshape(1, sh.n_q_heads, sh.head_dim), fk1, fv1, [n]))
+        assert_close(out, att.reshape(1, -1), "bf16", f"decode attention output layer {l + 1}")
         assert_close(to_np(fused[l][0][n:n + 1]), r["fused_k"][n:n + 1], "bf16", f"decode K layer {l + 1}")
         assert_close(to_np(fused[l][1][n:n + 1]), r["fused_v"][n:n + 1], "bf16", f"decode V layer {l + 1}")
         check_rest(sh, W[l], f"decode layer {l + 1}", hin, [0], out, h1.astype(np.float64),

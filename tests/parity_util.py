@@ -11,18 +11,21 @@ TOL = {"f32": dict(atol=1e-5, rtol=1e-5), "bf16": dict(atol=2e-2, rtol=1e-2)}
 TIE_BAND = 1e-3
 
 
-def assert_close(got, ref, dtype: str, what: str = ""):
-    """|got - ref| <= atol + rtol |ref| element by element."""
+def assert_close(got, ref, dtype: str, what: str = "") -> float:
+    """|got - ref| <= atol + rtol |ref| element by element.  Returns the largest share of that
+    bound any element uses (0 = equal, 1 = at the bar)."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, f"{what}: shape {got.shape} != {ref.shape}"
     t = TOL[dtype]
     err = np.abs(got - ref)
-    bad = err > t["atol"] + t["rtol"] * np.abs(ref)
+    bound = t["atol"] + t["rtol"] * np.abs(ref)
+    bad = err > bound
     if bad.any():
         i = np.unravel_index(np.argmax(err - t["rtol"] * np.abs(ref)), err.shape)
         raise AssertionError(f"{what}: {bad.sum()} of {bad.size} elements out of tolerance {t}; "
                              f"worst at {i}: got {got[i]!r} ref {ref[i]!r}; max abs err {err.max():.3e}")
+    return float((err / bound).max(initial=0.0))
 
 
 def check_selected(gpu_new, ref_new, ref_dev, cand_pos, k, n_query):
