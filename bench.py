@@ -1,22 +1,29 @@
 #!/usr/bin/env python3
 """Benchmark of the blended (CacheBlend-fused) prefill on one MI355X.
 
-One step = one whole blended prefill of the Qwen2.5-1.5B-shaped workload: 28 decoder layers,
-d_model 1536, 12 query / 2 KV heads of 128, FFN 8960, bf16, random-init weights N(0, 0.02);
-10 independently cached chunks of 512 uniform-random tokens + a 64-token query; layer 1
-recomputes every row, layer 2 keeps 30% of the context rows, layers 3.. keep 15%.
-Per layer: RoPE position update of the cached K, RMSNorm + fresh K/V GEMM of the selected
-rows, deviation + scatter, top-k, Q GEMM + sparse-query attention of the kept rows, then
-o-projection and SwiGLU FFN on the kept rows.
+One step = one whole blended prefill of the Llama-70B-shaped workload at 16K context: 80
+decoder layers, d_model 8192, 64 query / 8 KV heads of 128, FFN 28672, bf16, random-init
+weights N(0, 0.02) (about 137 GB, drawn on the device); 32 independently cached chunks of 512
+uniform-random tokens + a 256-token query; layer 1 recomputes every row, layers 2.. keep 15% of
+the context rows.  The chunks' cached K/V sit in pinned host memory (the library's chunk store,
+filled by the chunk producer) and are fetched per layer over PCIe on a copy stream, two layers
+ahead of the compute stream (CacheBlend explainer, "Pipelined design"; the review's Llama-70B
+example, where recompute rather than loading bounds a layer).
 
-value = context tokens / s = N_ctx * steps / wall time of the timed steps, with every input
-(weights, chunk caches, token ids) resident in HBM when timing starts.  A step is replayed
-from a HIP graph recorded once (the shapes of every layer are known on the host, so the
-whole prefill is one graph); the eager-launch time of the same step is reported too.  The pinned-host
-variant (cached KV fetched one layer ahead over PCIe on a second stream) is reported in
-extra fields, not as value.
+T_blend of a step is timed with HIP events from the first fetch enqueue (copy stream) to the
+end of the last layer (compute stream); steps run one at a time (each prefill alone, synchronized
+before the next starts).  value = context tokens / s = N_ctx * steps / wall time of the timed
+steps.  Model weights, token ids and the chunk store are resident (HBM / pinned host) before
+timing starts; the cached KV crosses PCIe inside every step.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+Extra fields of the same JSON line: the 4K-context Llama-70B prompt on the same engine; the
+16K prompt with the cached KV already in HBM and its full recompute (graph replay); per-layer
+load / recompute / overlap; the Qwen2.5-1.5B-shaped workload (pinned-host single prefill,
+HBM-resident graph replay and the rows built beyond the hot path: store, decode, controller,
+selection variants, int8 weights); the Mistral-7B-shaped ratio sweep; Yi-34B-shaped bf16 and
+int8-weight prefills.
+
+    python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--only-headline] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -34,7 +41,9 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_PCIE_GBS = 64.0       # PCIe 5.0 x16, one direction
 DECODE_ROWS = 32           # fused-KV rows kept free after the prompt for the decode steps
+DEVICE_SEED = 1234         # seed of the weights drawn on the device (layer l: DEVICE_SEED + l)
 
 
 def log(msg: str) -> None:
@@ -44,7 +53,6 @@ def log(msg: str) -> None:
 def schedule_text(sched):
     """'1.0, 0.30, 0.15 x 26' for a schedule whose last ratio repeats."""
     s = [float(x) for x in sched]
-    head = s
     n_tail = 1
     while n_tail < len(s) and s[-n_tail - 1] == s[-1]:
         n_tail += 1
@@ -54,74 +62,249 @@ def schedule_text(sched):
     return ", ".join(parts + [tail + (f" x {n_tail}" if n_tail > 1 else "")])
 
 
-def describe(wl):
+def describe(wl, where: str, weights: str):
     sh = wl.shape
     lens = sorted(set(wl.chunk_lens))
     chunks = (f"{len(wl.chunk_lens)}x{lens[0]}-token" if len(lens) == 1
               else f"{len(wl.chunk_lens)} ragged ({min(lens)}-{max(lens)} token)")
     return (f"{wl.name}: {sh.name}-shaped blended prefill, {sh.n_layers} layers, d_model {sh.d_model}, "
             f"{sh.n_q_heads}/{sh.n_kv_heads} heads of {sh.head_dim}, FFN {sh.ffn_dim}, {sh.dtype}; {chunks} cached "
-            f"chunks + {wl.n_query}-token query, recompute {schedule_text(wl.schedule)}, cached KV resident in HBM")
+            f"chunks + {wl.n_query}-token query, recompute {schedule_text(wl.schedule)}; {where}; {weights}")
 
 
-def attention_flops(shape, records, n_query):
-    """4 * H_q * d_h * sum over kept rows of (position + 1), summed over layers."""
+def attention_flops(shape, records):
+    """4 * H_q * d_h * sum over kept rows of (position + 1), per layer."""
     return [4.0 * shape.n_q_heads * shape.head_dim * float((r.new_sel.astype(np.int64) + 1).sum()) for r in records]
 
 
-# The gate/up product's tile choice: (rows, cols, wavefronts, modelled microseconds per K-step
-# of a workgroup) for each candidate; a launch costs ceil(workgroups / 256) K-step times, the
-# cheapest candidate wins, and from 2,048 rows up the 256 x 256 tile is taken outright.
-_SWIGLU_TILES = ((64, 128, 4, 0.72), (128, 128, 4, 0.83), (64, 256, 4, 1.04), (128, 256, 8, 1.13),
-                 (256, 256, 8, 1.75), (128, 512, 8, 2.10))
+def sync():
+    import torch
+    torch.cuda.synchronize()
 
 
-def swiglu_tile(rows, n):
-    """(bm, bn, wavefronts, workgroups) of the gate/up launch over `rows` rows and n = 2 ffn
-    output columns, as the library plans it."""
-    if rows >= 2048 and n % 256 == 0:
-        bm, bn, nw = 256, 256, 8
-    else:
-        best = None
-        for bm_, bn_, nw_, t in _SWIGLU_TILES:
-            if n % bn_:
-                continue
-            cost = -(-(-(-rows // bm_) * (n // bn_)) // 256) * t
-            if best is None or cost < best[0]:
-                best = (cost, bm_, bn_, nw_)
-        _, bm, bn, nw = best
-    tiles = -(-rows // bm) * (n // bn)
-    return bm, bn, nw, 8 * (-(-tiles // 8))  # workgroups: tiles rounded up to a multiple of 8
+_STREAMS = []
 
 
-def gate_up_traffic(shape, kept_rows):
-    """Mean HBM bytes per launch of the FFN gate/up GEMM over one step, from the committed
-    rocprofv3 counter summary (FETCH_SIZE / WRITE_SIZE, scaled by a plain copy's reading),
-    or None if that summary is missing, lacks one of the step's launches, or was taken on
-    another version of the kernel source.  A launch is identified by its tile (in the kernel's
-    name) and its grid size in threads (workgroups x 64 x wavefronts)."""
+def streams():
+    """The one (compute, copy) stream pair every engine of this process uses.  HIP spreads
+    streams over a few hardware queues (4 here) in creation order, so streams made per engine
+    can land on one queue, which then runs the copy stream's fetches and the compute stream's
+    kernels one after the other; one pair made first keeps them on separate queues."""
+    import torch
+    if not _STREAMS:
+        _STREAMS.extend([torch.cuda.Stream(), torch.cuda.Stream()])
+    return tuple(_STREAMS)
+
+
+def device_engine(sh, max_tokens, int8=False):
+    """An engine whose weights are drawn on the device (N(0, 0.02), layer l seeded DEVICE_SEED + l)."""
+    from rag_kv_cache_amd.pipeline import Engine
+    eng = Engine(sh, max_tokens=max_tokens, streams=streams())
+    for l in range(sh.n_layers):
+        eng.load_layer_device(l, DEVICE_SEED + l + 1, int8=int8)
+    eng.load_embedding_device(DEVICE_SEED)
+    sync()
+    return eng
+
+
+def graph_ms(eng, fn, steps, warmup):
+    """Capture fn (a whole step enqueued on the compute stream) as a HIP graph and time its
+    replays: ms per replay over `steps` replays after `warmup`."""
+    import torch
+    from rag_kv_cache_amd.pipeline import capture_step
+    fn()
+    g = capture_step(eng, fn)
+    cs = eng.compute
+    with torch.cuda.stream(cs):
+        for _ in range(warmup):
+            g.replay()
+    cs.synchronize()
+    sync()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(cs):
+        for _ in range(steps):
+            g.replay()
+    cs.synchronize()
+    sync()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    del g
+    return ms
+
+
+def kernel_table(eng, prof_steps, attn_work, pcie_peak):
+    """Per-kernel HIP-event durations (cb_profile) over `prof_steps` profiled steps, with each
+    kernel's algorithmic rate against its roofline."""
+    from rag_kv_cache_amd import _lib as L
+    mfma = (L.CB_K_GEMM_KV, L.CB_K_GEMM_Q, L.CB_K_ATTN, L.CB_K_GEMM_O, L.CB_K_GEMM_GATE_UP, L.CB_K_GEMM_DOWN)
+    kernels = {}
+    for kid, name in enumerate(L.KERNEL_NAMES):
+        ms, n, work = L.cb_profile_read(eng.ctx, kid)
+        if n == 0:
+            continue
+        if kid == L.CB_K_ATTN:
+            work = attn_work * prof_steps
+        bound = "mfma" if kid in mfma else ("pcie" if kid == L.CB_K_FETCH else "hbm")
+        scale = 1e12 if bound == "mfma" else 1e9
+        rate = work / (ms * 1e-3) / scale if ms > 0 else 0.0
+        peak = {"mfma": PEAK_BF16_TFLOPS, "hbm": PEAK_HBM_GBS, "pcie": pcie_peak}[bound]
+        kernels[name] = {"ms_total_per_step": round(ms / prof_steps, 4), "launches_per_step": n // prof_steps,
+                         "us_per_launch": round(ms * 1e3 / n, 2), "bound": bound, "achieved": round(rate, 2),
+                         "unit": "TFLOP/s" if bound == "mfma" else "GB/s", "peak": peak,
+                         "frac": round(rate / peak, 4), "work_per_launch": work / n}
+    return kernels
+
+
+def traffic_from_profiles(kernel, workload, launches_per_step):
+    """HBM bytes per launch of `kernel` averaged over one step of `workload`, from the committed
+    rocprofv3 counter summary profiles/<kernel>_<workload>_traffic.txt (FETCH_SIZE and WRITE_SIZE
+    per dispatch, each scaled by what it reads for a plain device copy; the step's launches are
+    the last ones of the profiled run), or None if that summary is missing, covers another
+    number of launches per step, or was taken on another version of the kernel's source."""
     import hashlib
     import re
-    path = os.path.join(ROOT, "profiles", "gemm_gate_up_qwen_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    m = re.search(r"source_sha256 (\S+): ([0-9a-f]{64})", text)
-    if not m:
-        return None
-    src = os.path.join(ROOT, m.group(1))
-    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != m.group(2):
-        return None
-    per_launch = {(int(bm), int(bn), int(g)): float(mb) for g, mb, bm, bn in re.findall(
-        r"^\s*(\d+)\s+\d+\s+[\d.]+\s+[\d.]+\s+([\d.]+)\s+gemm_bf16_kernel<(\d+), (\d+),", text, re.M)}
-    total = 0.0
-    for rows in kept_rows:
-        bm, bn, nw, wgs = swiglu_tile(rows, 2 * shape.ffn_dim)
-        key = (bm, bn, wgs * 64 * nw)
-        if key not in per_launch:
+    for src, digest in re.findall(r"source_sha256 (\S+): ([0-9a-f]{64})", text):
+        p = os.path.join(ROOT, src)
+        if not os.path.exists(p) or hashlib.sha256(open(p, "rb").read()).hexdigest() != digest:
             return None
-        total += per_launch[key] * 1e6
-    return total / len(kept_rows)
+    m = re.search(r"step average over the last (\d+) launches: ([\d.]+) MB per launch", text)
+    if not m or int(m.group(1)) != launches_per_step:
+        return None
+    return round(float(m.group(2)) * 1e6)
+
+
+def run_prompt_pinned(eng, store, wl, steps, warmup, profile=False, overlap=False, hbm=False, full=False,
+                      full_steps=2):
+    """One prompt on an engine whose chunk store holds the prompt's chunks: the blended prefill
+    with the cached KV fetched from the store's pinned arena, timed one prefill at a time (the
+    contract's steps), plus optionally a kernel profile, per-layer load / recompute / overlap,
+    the same prefill with the cached KV already in HBM (graph replay) and the full recompute
+    (ratio 1 at every layer, graph replay)."""
+    import torch
+    import fixtures as F
+    from rag_kv_cache_amd import _lib as L
+    from rag_kv_cache_amd.pipeline import build_chunk_caches, make_buffers, run_layers
+    sh = wl.shape
+    chunks = F.chunk_tokens(wl)
+    tokens = F.all_tokens(wl)
+    offs = [int(o) for o in F.chunk_offsets(wl)]
+    slots = store.lookup_prompt(chunks, hold=True)
+    assert slots is not None, "the chunk store lacks a chunk of the prompt"
+    hc = store.host_cache(slots)
+    n_tok = wl.n_tokens
+    buf = make_buffers(eng, n_tok, len(chunks))
+    fused = [(eng.kv_empty(n_tok), eng.kv_empty(n_tok)) for _ in range(sh.n_layers)]
+    rec = run_layers(eng, buf, tokens, offs, wl.n_query, wl.schedule, fused, host_cache=hc, record="sets")
+    sync()
+    attn_fl = attention_flops(sh, rec.records)
+    kept = [len(r.new_sel) for r in rec.records]
+
+    def prefill(layer_events=None):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(eng.copy)   # T_blend starts at the first fetch enqueue
+        run_layers(eng, buf, tokens, offs, wl.n_query, wl.schedule, fused, host_cache=hc, upload_inputs=False,
+                   layer_events=layer_events)
+        e1.record(eng.compute)
+        return e0, e1
+
+    for _ in range(warmup):
+        prefill()
+        sync()
+    sync()
+    evs = []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        evs.append(prefill())
+        sync()  # each prefill alone: the next one's fetch does not overlap this one's compute
+    wall = time.perf_counter() - t0
+    t_blend = [a.elapsed_time(b) for a, b in evs]
+    layer_ev = []
+    prefill(layer_ev)
+    sync()
+    per_layer = [layer_ev[i].elapsed_time(layer_ev[i + 1]) for i in range(len(layer_ev) - 1)]
+    out = {"n_ctx": wl.n_ctx, "n_query": wl.n_query, "steps": steps, "warmup": warmup,
+           "wall_ms_per_step": round(wall / steps * 1e3, 4),
+           "context_tokens_per_s": round(wl.n_ctx * steps / wall, 1),
+           "t_blend_ms": {"median": round(float(np.median(t_blend)), 4), "min": round(min(t_blend), 4),
+                          "max": round(max(t_blend), 4)},
+           "per_layer_ms": {"layer1": round(per_layer[0], 4), "layer2": round(per_layer[1], 4),
+                            "steady_median": round(float(np.median(per_layer[2:])), 4),
+                            "steady_min": round(float(np.min(per_layer[2:])), 4),
+                            "steady_max": round(float(np.max(per_layer[2:])), 4)},
+           "kept_rows_per_layer": kept[:3] + ["..."],
+           "host_kv_bytes_per_step": int(2 * sh.n_layers * wl.n_ctx * sh.n_kv_heads * sh.head_dim * 2)}
+    log(f"{wl.name}: pinned-host blended prefill {out['wall_ms_per_step']:.3f} ms/step (T_blend median "
+        f"{out['t_blend_ms']['median']:.3f} ms), {out['context_tokens_per_s']:,.0f} context tokens/s; layer 1 "
+        f"{per_layer[0]:.3f} ms, steady {out['per_layer_ms']['steady_median']:.3f} ms")
+    if profile:
+        L.cb_profile_enable(eng.ctx, True)
+        prefill()
+        sync()
+        L.cb_profile_enable(eng.ctx, False)
+        out["kernels"] = kernel_table(eng, 1, sum(attn_fl), PEAK_PCIE_GBS)
+        out["attention_flops_per_step"] = sum(attn_fl)
+    if overlap:
+        out["per_layer_overlap"] = run_overlap(eng, buf, tokens, offs, wl, fused, hc, reps=2)
+    if hbm:
+        cache, _ = build_chunk_caches(eng, chunks)
+        ms = graph_ms(eng, lambda: run_layers(eng, buf, tokens, offs, wl.n_query, wl.schedule, fused, cache=cache,
+                                              upload_inputs=False), steps, warmup)
+        out["hbm_resident"] = {"ms_per_step": round(ms, 4), "context_tokens_per_s": round(wl.n_ctx / ms * 1e3, 1),
+                               "note": "cached KV already in HBM (position update of every layer in one launch), "
+                                       "graph replay"}
+        log(f"{wl.name}: cached KV in HBM, graph replay {ms:.3f} ms/step")
+        del cache
+    if full:
+        full_sched = [1.0] * sh.n_layers
+        ms = graph_ms(eng, lambda: run_layers(eng, buf, tokens, offs, wl.n_query, full_sched, fused,
+                                              upload_inputs=False), full_steps, 1)
+        out["full_recompute"] = {"ms_per_step": round(ms, 4), "speedup_of_blend": round(ms / out["wall_ms_per_step"], 3),
+                                 "note": "ratio 1 at every layer (every row recomputed, no cache), graph replay"}
+        log(f"{wl.name}: full recompute {ms:.3f} ms/step ({ms / out['wall_ms_per_step']:.2f}x the blended prefill)")
+    for sl in slots:
+        store.release(sl)
+    del buf, fused
+    torch.cuda.empty_cache()
+    return out
+
+
+def run_headline(args):
+    """The Llama-70B-shaped workload: 16K prompt (value) and 4K prompt on one engine."""
+    import fixtures as F
+    from rag_kv_cache_amd.pipeline import ChunkStore, produce_chunks
+    import torch
+    wl = F.get_config(args.config)
+    sh = wl.shape
+    # the 4K prompt of the same shape: its chunks are the first chunks of the 16K prompt
+    small = {"l70_16k": "l70_4k"}.get(args.config)
+    t0 = time.perf_counter()
+    eng = device_engine(sh, wl.n_tokens + DECODE_ROWS)
+    log(f"{wl.name}: {sh.n_layers} layers of weights drawn on the device in {time.perf_counter() - t0:.1f} s")
+    chunks = F.chunk_tokens(wl)
+    store = ChunkStore(eng, max(wl.chunk_lens), len(chunks) + 2, pinned=True)
+    t0 = time.perf_counter()
+    produce_chunks(eng, store, chunks)
+    t_prod = time.perf_counter() - t0
+    log(f"{wl.name}: chunk producer filled the pinned store in {t_prod:.1f} s")
+    res = run_prompt_pinned(eng, store, wl, args.steps, args.warmup, profile=True,
+                            overlap=not args.only_headline, hbm=not args.only_headline,
+                            full=not args.only_headline, full_steps=max(2, args.steps // 8))
+    res["producer_context_tokens_per_s"] = round(wl.n_ctx / t_prod, 1)
+    other = None
+    if small and not args.only_headline:
+        wl4 = F.get_config(small)
+        other = run_prompt_pinned(eng, store, wl4, args.steps, args.warmup, profile=True, full=True,
+                                  full_steps=max(2, args.steps // 4))
+        other["workload"] = describe(wl4, "cached KV in pinned host memory (chunk store), fetched two layers ahead",
+                                     "weights drawn on the device")
+    store.close()
+    eng.close()
+    del eng
+    torch.cuda.empty_cache()
+    return wl, res, other
 
 
 def run_controller(eng, buf, tokens, offs, wl, fused, host, full_ms, overlap, steps):
@@ -207,10 +390,11 @@ def run_controller(eng, buf, tokens, offs, wl, fused, host, full_ms, overlap, st
 
 def _fetch_layer(eng, buf, host, offs, l, fused):
     from rag_kv_cache_amd import _lib as L
+    from rag_kv_cache_amd.pipeline import _ptr
     n_chunks = len(offs) - 1
-    L.cb_fetch_layer(eng.ctx, l, [int(host[l][c][0].data_ptr()) for c in range(n_chunks)],
-                     [int(host[l][c][1].data_ptr()) for c in range(n_chunks)], offs, n_chunks,
-                     int(buf.offsets.data_ptr()), int(fused[l][0].data_ptr()), int(fused[l][1].data_ptr()))
+    L.cb_fetch_layer(eng.ctx, l, [_ptr(host[l][c][0]) for c in range(n_chunks)],
+                     [_ptr(host[l][c][1]) for c in range(n_chunks)], offs, n_chunks,
+                     _ptr(buf.offsets), _ptr(fused[l][0]), _ptr(fused[l][1]))
 
 
 def run_overlap(eng, buf, tokens, offs, wl, fused, host, reps: int = 5, eps_ms: float = 0.02):
@@ -260,7 +444,7 @@ def run_overlap(eng, buf, tokens, offs, wl, fused, host, reps: int = 5, eps_ms: 
     med = lambda rows: [float(np.median(c)) for c in zip(*rows)]
     t_load, t_rec, t_ov = med(loads), med(recs), med(ovs)
     excess = [t_ov[l] - max(t_load[l], t_rec[l]) for l in range(nl)]
-    steady = list(range(3, nl))
+    steady = list(range(3, nl)) if nl > 4 else list(range(nl))
     ok = [l for l in range(nl) if excess[l] <= eps_ms]
     log(f"overlap (steady medians): load {np.median([t_load[l] for l in steady]):.4f}, recompute "
         f"{np.median([t_rec[l] for l in steady]):.4f}, overlapped {np.median([t_ov[l] for l in steady]):.4f} ms; "
@@ -373,7 +557,7 @@ def run_int8(wl, steps, warmup):
     from rag_kv_cache_amd import _lib as L
     from rag_kv_cache_amd.pipeline import Engine, build_chunk_caches, capture_step, make_buffers, run_layers
     sh = wl.shape
-    eng = Engine(sh, max_tokens=wl.n_tokens + 8)
+    eng = Engine(sh, max_tokens=wl.n_tokens + 8, streams=streams())
     for l in range(sh.n_layers):
         eng.load_layer_int8(l, F.layer_weights_int8(sh, l + 1))
     eng.load_embedding(F.embedding(sh))
@@ -528,6 +712,143 @@ def run_store(eng, buf, tokens, offs, wl, fused, steps):
     return out
 
 
+
+
+def run_qwen(args):
+    """The Qwen2.5-1.5B-shaped workload (fixture weights): pinned-host single prefill, HBM-resident
+    graph replay with its per-kernel table, full recompute and lower bounds by graph replay,
+    per-layer overlap, and the rows beyond the hot path (controller, selection variants, decode,
+    chunk store, int8 weights)."""
+    import torch
+    import fixtures as F
+    from rag_kv_cache_amd import _lib as L
+    from rag_kv_cache_amd.pipeline import Engine, build_chunk_caches, make_buffers, run_layers
+    wl = F.get_config("qwen")
+    sh = wl.shape
+    chunks = F.chunk_tokens(wl)
+    tokens = F.all_tokens(wl)
+    offs = [int(o) for o in F.chunk_offsets(wl)]
+    n_ctx, n_tok = wl.n_ctx, wl.n_tokens
+    eng = Engine(sh, max_tokens=n_tok + 64, streams=streams())
+    for l in range(sh.n_layers):
+        eng.load_layer(l, F.layer_weights(sh, l + 1))
+    eng.load_embedding(F.embedding(sh))
+    cache, host = build_chunk_caches(eng, chunks, pinned_host=True)
+    buf = make_buffers(eng, n_tok + DECODE_ROWS, len(chunks))
+    fused = [(eng.kv_empty(n_tok + DECODE_ROWS), eng.kv_empty(n_tok + DECODE_ROWS)) for _ in range(sh.n_layers)]
+    cs = eng.compute
+    rec = run_layers(eng, buf, tokens, offs, wl.n_query, wl.schedule, fused, cache=cache, record="sets")
+    attn_fl = attention_flops(sh, rec.records)
+    out = {"workload": describe(wl, "see the fields for where the cached KV lives", "fixture weights")}
+
+    def step(**kw):
+        return run_layers(eng, buf, tokens, offs, wl.n_query, wl.schedule, fused, upload_inputs=False, **kw)
+
+    # pinned host: one prefill at a time, events from the first fetch enqueue to the last layer
+    for _ in range(2):
+        step(host_cache=host)
+    sync()
+    evs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(eng.copy)
+        step(host_cache=host)
+        e1.record(cs)
+        sync()
+        evs.append((e0, e1))
+    wall = time.perf_counter() - t0
+    tb = [a.elapsed_time(b) for a, b in evs]
+    out["pinned_host"] = {"wall_ms_per_step": round(wall / args.steps * 1e3, 4),
+                          "context_tokens_per_s": round(n_ctx * args.steps / wall, 1),
+                          "t_blend_ms_median": round(float(np.median(tb)), 4),
+                          "note": "cached KV in pinned host memory, fetched two layers ahead; one prefill at a time"}
+    # back to back: each prefill's fetches overlap the previous prefill's compute
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(host_cache=host)
+    sync()
+    bb = (time.perf_counter() - t0) / args.steps * 1e3
+    out["pinned_host_back_to_back_ms"] = round(bb, 4)
+    log(f"qwen: pinned host {out['pinned_host']['wall_ms_per_step']:.3f} ms/prefill alone "
+        f"(T_blend {out['pinned_host']['t_blend_ms_median']:.3f}), {bb:.3f} ms back to back")
+    # cached KV in HBM: graph replay, and its per-kernel table
+    hbm_ms = graph_ms(eng, lambda: step(cache=cache), args.steps, args.warmup)
+    L.cb_profile_enable(eng.ctx, True)
+    for _ in range(3):
+        step(cache=cache)
+    cs.synchronize()
+    L.cb_profile_enable(eng.ctx, False)
+    kernels = kernel_table(eng, 3, sum(attn_fl), PEAK_PCIE_GBS)
+    evl = []
+    step(cache=cache, layer_events=evl)
+    cs.synchronize()
+    per_layer = [evl[i].elapsed_time(evl[i + 1]) for i in range(len(evl) - 1)]
+    out["hbm_resident"] = {"ms_per_step": round(hbm_ms, 4), "context_tokens_per_s": round(n_ctx / hbm_ms * 1e3, 1),
+                           "per_layer_ms": {"layer1": round(per_layer[0], 4), "layer2": round(per_layer[1], 4),
+                                            "layer3": round(per_layer[2], 4),
+                                            "steady_median": round(float(np.median(per_layer[3:])), 4)},
+                           "kernels": kernels, "note": "cached KV resident in HBM, graph replay"}
+    log(f"qwen: HBM-resident graph replay {hbm_ms:.3f} ms/step")
+    full_ms = graph_ms(eng, lambda: run_layers(eng, buf, tokens, offs, wl.n_query, [1.0] * sh.n_layers, fused,
+                                               cache=cache, upload_inputs=False), max(3, args.steps // 2), 1)
+    out["full_recompute_ms"] = round(full_ms, 4)
+    out["speedup_vs_full_recompute"] = {"hbm_resident": round(full_ms / hbm_ms, 3),
+                                        "pinned_host": round(full_ms / out["pinned_host"]["wall_ms_per_step"], 3),
+                                        "note": "full recompute by graph replay on the same kernels"}
+    log(f"qwen: full recompute {full_ms:.3f} ms/step")
+    out["prefetch_per_layer"] = run_overlap(eng, buf, tokens, offs, wl, fused, host)
+    out["full_reuse"] = run_reuse(eng, buf, tokens, offs, wl, fused, cache, args.steps)
+    out["loading_controller"] = run_controller(eng, buf, tokens, offs, wl, fused, host, full_ms,
+                                               out["prefetch_per_layer"], args.steps)
+    out["selection_variants"] = run_variants(eng, buf, tokens, offs, wl, fused, cache, args.steps)
+    out["decode"] = run_decode(eng, buf, tokens, offs, wl, fused, cache)
+    out["chunk_store"] = run_store(eng, buf, tokens, offs, wl, fused, args.steps)
+    out["peaks_measured"] = run_peaks(eng)
+    eng.close()
+    del eng, cache, host, buf, fused
+    torch.cuda.empty_cache()
+    out["int8_weights"] = run_int8(wl, args.steps, args.warmup)
+    return out
+
+
+def run_hbm_shape(name, ratios, args, int8=False):
+    """A shape whose cached KV stays in HBM (Mistral-7B, Yi-34B): weights drawn on the device,
+    chunk caches built by the chunk producer, the blended prefill by graph replay at each ratio
+    (schedule 1.0, r, r, ...) and the full recompute."""
+    import torch
+    import fixtures as F
+    from rag_kv_cache_amd.pipeline import build_chunk_caches, make_buffers, run_layers
+    wl = F.get_config(name)
+    sh = wl.shape
+    chunks = F.chunk_tokens(wl)
+    tokens = F.all_tokens(wl)
+    offs = [int(o) for o in F.chunk_offsets(wl)]
+    eng = device_engine(sh, wl.n_tokens + 8, int8=int8)
+    cache, _ = build_chunk_caches(eng, chunks)
+    buf = make_buffers(eng, wl.n_tokens, len(chunks))
+    fused = [(eng.kv_empty(wl.n_tokens), eng.kv_empty(wl.n_tokens)) for _ in range(sh.n_layers)]
+    run_layers(eng, buf, tokens, offs, wl.n_query, wl.schedule, fused, cache=cache)
+    out = {"workload": describe(wl, "cached KV resident in HBM, graph replay",
+                                "int8 weights (per-output-channel scales) drawn and quantized on the device"
+                                if int8 else "weights drawn on the device")}
+    for r in ratios:
+        sched = [1.0] + [r] * (sh.n_layers - 1)
+        ms = graph_ms(eng, lambda: run_layers(eng, buf, tokens, offs, wl.n_query, sched, fused, cache=cache,
+                                              upload_inputs=False), args.steps, args.warmup)
+        out[f"r{r:.2f}"] = {"ms_per_step": round(ms, 4), "context_tokens_per_s": round(wl.n_ctx / ms * 1e3, 1)}
+        log(f"{name}{' int8' if int8 else ''}: ratio {r:.2f}: {ms:.3f} ms/step, {wl.n_ctx / ms * 1e3:,.0f} context tokens/s")
+    if not int8:
+        full = graph_ms(eng, lambda: run_layers(eng, buf, tokens, offs, wl.n_query, [1.0] * sh.n_layers, fused,
+                                                upload_inputs=False), max(2, args.steps // 4), 1)
+        out["full_recompute_ms"] = round(full, 4)
+        log(f"{name}: full recompute {full:.3f} ms/step")
+    eng.close()
+    del eng, cache, buf, fused
+    torch.cuda.empty_cache()
+    return out
+
+
 def _host_info():
     """CPU model, logical CPUs and the BLAS numpy was built with."""
     model = "unknown"
@@ -549,81 +870,90 @@ def _host_info():
     return {"cpu_model": model, "logical_cpus": os.cpu_count(), "blas": blas}
 
 
-def cpu_baseline(wl, budget_s: float = 25.0):
-    """The oracle (fp64 NumPy with bf16 rounding points) on a bounded sample of the same
-    workload: layer 1 (every row), layer 2 (all rows scored, 30% kept), layer 3 (15% kept)
-    and steady layers until the time budget; tokens/s extrapolated to all layers.  The first
-    steady layer is timed a second time with BLAS limited to one thread.  The chunk caches are
-    random bf16-valued arrays of the real shape (their values do not change the oracle's cost);
-    weights and tokens are the fixtures'."""
+def _oracle_layer_flops(sh, n_sel, n_keep, n_keys):
+    """Flops of one oracle layer as the oracle computes them: the K/V products of the selected
+    rows, Q, o-projection and FFN of the kept rows, and attention scores and sums over keys
+    0 .. n_keys - 1 for every kept row (the oracle masks inside a full score matrix)."""
+    d, qd, kvd, f = sh.d_model, sh.n_q_heads * sh.head_dim, sh.n_kv_heads * sh.head_dim, sh.ffn_dim
+    return (2.0 * n_sel * d * 2 * kvd + 2.0 * n_keep * d * qd + 4.0 * n_keep * n_keys * qd
+            + 2.0 * n_keep * qd * d + 6.0 * n_keep * d * f)
+
+
+def cpu_baseline(wl, budget_s: float = 20.0):
+    """The oracle (fp64 NumPy, bf16 rounding points emulated) on a bounded sample of the same
+    workload: one steady layer (the kept rows at the workload's ratio, attending over the whole
+    prompt) run on a fraction of its kept rows, the fraction grown until the time budget is
+    used; the steady layer's time is the sample's scaled by the row fraction (every part of the
+    layer is linear in the kept rows at a fixed prompt), layers 1 and 2 by the oracle's own flop
+    counts relative to the steady layer.  Weights are the fixtures' layer-3 draws; the residual
+    rows and the chunk caches are random values of the real shape (the oracle's cost does not
+    depend on them)."""
     import fixtures as F
     import oracle as O
     try:
-        from threadpoolctl import threadpool_info, threadpool_limits
+        from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
-        threadpool_limits = None
         threads = os.cpu_count() or 1
     sh = wl.shape
     prec = O.Precision("bf16")
     rng = np.random.default_rng(0)
-    E = F.embedding(sh)
-    tokens = F.all_tokens(wl)
-    n_ctx, n_tok, n_q = wl.n_ctx, wl.n_tokens, wl.n_query
-    hidden = np.asarray(E[tokens], np.float64)
-    del E
-    sel = np.arange(n_tok)
-    times = []
-    single = None
-    t_start = time.perf_counter()
-    for l in range(sh.n_layers):
-        w = F.layer_weights(sh, l + 1)
-        kc = prec.store(rng.standard_normal((n_ctx, sh.n_kv_heads, sh.head_dim)) * 0.3)
-        vc = prec.store(rng.standard_normal((n_ctx, sh.n_kv_heads, sh.head_dim)) * 0.3)
+    n_ctx, n_q, n_tok = wl.n_ctx, wl.n_query, wl.n_tokens
+    offs = F.chunk_offsets(wl)
+    r = float(wl.schedule[-1])
+    k = O.k_for_ratio(r, n_ctx, n_ctx)
+    w = F.layer_weights(sh, 3)
+    caches = [(prec.store(rng.standard_normal((offs[c + 1] - offs[c], sh.n_kv_heads, sh.head_dim)) * 0.3),
+               prec.store(rng.standard_normal((offs[c + 1] - offs[c], sh.n_kv_heads, sh.head_dim)) * 0.3))
+              for c in range(len(offs) - 1)]
+    kept_ctx = np.sort(rng.choice(n_ctx, size=k, replace=False))
 
-        def one_layer():
-            fk, fv = O.fuse_cache(sh, prec, [(kc, vc)], [0, n_ctx], n_q)
-            r = O.blend_layer(sh, w, prec, hidden, fk, fv, n_ctx, sel, n_q, wl.schedule[l])
-            return O.layer_rest(sh, w, prec, hidden, r["new_local"], r["out"]), r["new_sel"]
-
+    def sample(frac):
+        m = max(1, int(round(k * frac)))
+        sel = np.concatenate([np.sort(rng.choice(kept_ctx, size=m, replace=False)), np.arange(n_ctx, n_tok)])
+        hidden = rng.standard_normal((len(sel), sh.d_model))
         t0 = time.perf_counter()
-        h_next, s_next = one_layer()
-        times.append(time.perf_counter() - t0)
-        if l == 3 and threadpool_limits is not None:
-            with threadpool_limits(limits=1):
-                t0 = time.perf_counter()
-                one_layer()
-                single = time.perf_counter() - t0
-        hidden, sel = h_next, s_next
-        if l >= 4 and time.perf_counter() - t_start > budget_s:
+        fk, fv = O.fuse_cache(sh, prec, caches, offs, n_q)
+        res = O.blend_layer(sh, w, prec, hidden, fk, fv, n_ctx, sel, n_q, m / n_ctx)
+        O.layer_rest(sh, w, prec, hidden, res["new_local"], res["out"])
+        return time.perf_counter() - t0, len(sel)
+
+    frac = 1.0 / 32
+    runs = []
+    spent = 0.0
+    while True:
+        t, rows = sample(frac)
+        runs.append((frac, rows, t))
+        spent += t
+        if frac >= 1.0 or spent + 2.5 * t > budget_s:
             break
-    steady = float(np.median(times[3:])) if len(times) > 3 else times[-1]
-    total = sum(times[:3]) + steady * (sh.n_layers - 3)
-    out = {"value": n_ctx / total, "unit": "context tokens/s", "cores": int(threads), "kind": "oracle",
-           "sample": (f"oracle (fp64 NumPy, bf16 rounding emulated) on layers 1-{len(times)} of the same workload "
-                      f"with random-valued chunk caches of the real shape; layer times "
-                      f"{[round(t, 3) for t in times]} s; blended prefill extrapolated as "
-                      f"T1+T2+T3+{sh.n_layers - 3}*median(steady) = {total:.2f} s")}
+        frac = min(1.0, frac * 2)
+    frac, rows, t = runs[-1]
+    t_steady = t * (k + n_q) / rows
+    f_steady = _oracle_layer_flops(sh, k + n_q, k + n_q, n_tok)
+    t1 = t_steady * _oracle_layer_flops(sh, n_tok, n_tok, n_tok) / f_steady
+    t2 = t_steady * _oracle_layer_flops(sh, n_tok, k + n_q, n_tok) / f_steady
+    total = t1 + t2 + (sh.n_layers - 2) * t_steady
+    out = {"value": round(n_ctx / total, 3), "unit": "context tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": (f"oracle (fp64 NumPy, bf16 rounding emulated): one steady layer of {wl.name} "
+                      f"({k + n_q} kept rows over {n_tok} keys) run on {rows} of its kept rows in {t:.2f} s "
+                      f"(runs: {[(round(a, 4), b, round(c, 2)) for a, b, c in runs]}); steady layer {t_steady:.1f} s "
+                      f"by the row fraction, layers 1 and 2 {t1:.1f} s and {t2:.1f} s by the oracle's flop counts; "
+                      f"blended prefill estimated at {total:.0f} s for {sh.n_layers} layers")}
     out.update(_host_info())
-    if single is not None:
-        out["single_thread_steady_layer_s"] = round(single, 3)
-        out["all_threads_steady_layer_s"] = round(times[3], 3)
     return out
 
 
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="qwen")
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="l70_16k", help="workload of the headline line (fixtures.CONFIGS)")
+    ap.add_argument("--only-headline", action="store_true",
+                    help="only the headline prompt's timed steps and kernel profile (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=25.0)
-    ap.add_argument("--only-blend", action="store_true",
-                    help="skip the pinned-host and full-recompute passes (profiling runs)")
-    ap.add_argument("--ratios", default="",
-                    help="comma-separated steady ratios: also time the graph-replayed prefill with the schedule "
-                         "1.0, r, r, ... for each (e.g. 0.10,0.15,0.20 for the Mistral-7B-shaped sweep)")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain device-to-device copy of 256 MiB, 3 times (counter calibration)")
     args = ap.parse_args()
@@ -631,210 +961,67 @@ def main() -> int:
         print("bench.py measures one GPU only: the fusion step is built and timed on a single MI355X "
               "(sharding across GPUs is a design note, not implemented)", file=sys.stderr)
         return 2
-
     import torch
-    import fixtures as F
-    from rag_kv_cache_amd import _lib as L
-    from rag_kv_cache_amd.pipeline import Engine, build_chunk_caches, capture_step, make_buffers, run_layers
 
-    wl = F.get_config(args.config)
+    wl, head, other = run_headline(args)
     sh = wl.shape
-    chunks = F.chunk_tokens(wl)
-    tokens = F.all_tokens(wl)
-    offs = [int(o) for o in F.chunk_offsets(wl)]
-    n_ctx, n_tok = wl.n_ctx, wl.n_tokens
-    log(f"workload {wl.name}: {sh.n_layers} layers, d {sh.d_model}, heads {sh.n_q_heads}/{sh.n_kv_heads}, "
-        f"N_ctx {n_ctx} + query {wl.n_query}")
-
-    t0 = time.perf_counter()
-    eng = Engine(sh, max_tokens=n_tok + 64)  # room for decode steps after the prefill
-    for l in range(sh.n_layers):
-        eng.load_layer(l, F.layer_weights(sh, l + 1))
-    eng.load_embedding(F.embedding(sh))
-    torch.cuda.synchronize()
-    log(f"weights uploaded in {time.perf_counter() - t0:.1f} s")
-    t0 = time.perf_counter()
-    cache, host = build_chunk_caches(eng, chunks, pinned_host=True)
-    log(f"chunk caches built in {time.perf_counter() - t0:.1f} s")
-
-    extra = DECODE_ROWS  # rows after the prompt for the decode steps
-    buf = make_buffers(eng, n_tok + extra, len(chunks))
-    fused = [(eng.kv_empty(n_tok + extra), eng.kv_empty(n_tok + extra)) for _ in range(sh.n_layers)]
-    cs = eng.compute
-    rec = run_layers(eng, buf, tokens, offs, wl.n_query, wl.schedule, fused, cache=cache, record=True)
-    attn_fl = attention_flops(sh, rec.records, wl.n_query)
-    kept = [len(r.new_sel) for r in rec.records]
-
-    def step(**kw):
-        return run_layers(eng, buf, tokens, offs, wl.n_query, wl.schedule, fused, upload_inputs=False, **kw)
-
-    for _ in range(args.warmup):
-        step(cache=cache)
-    cs.synchronize()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(cache=cache)
-    cs.synchronize()
-    torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - t0) / args.steps * 1e3
-    log(f"blended prefill, eager launches: {eager_ms:.3f} ms/step")
-
-    # the same step recorded once as a HIP graph and replayed: one launch per step
-    graph = capture_step(eng, lambda: step(cache=cache))
-    with torch.cuda.stream(cs):
-        for _ in range(args.warmup):
-            graph.replay()
-    cs.synchronize()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    with torch.cuda.stream(cs):
-        for _ in range(args.steps):
-            graph.replay()
-    cs.synchronize()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall = t1 - t0
-    ms_step = wall / args.steps * 1e3
-    value = n_ctx * args.steps / wall
-    log(f"blended prefill, graph replay: {ms_step:.3f} ms/step, {value:,.0f} context tokens/s")
-
-    sweep = None
-    if args.ratios:
-        sweep = {}
-        for r in [float(x) for x in args.ratios.split(",") if x]:
-            sched = [1.0] + [r] * (sh.n_layers - 1)
-            g = capture_step(eng, lambda: run_layers(eng, buf, tokens, offs, wl.n_query, sched, fused, cache=cache,
-                                                     upload_inputs=False))
-            with torch.cuda.stream(cs):
-                for _ in range(args.warmup):
-                    g.replay()
-            cs.synchronize()
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            with torch.cuda.stream(cs):
-                for _ in range(args.steps):
-                    g.replay()
-            cs.synchronize()
-            torch.cuda.synchronize()
-            ms = (time.perf_counter() - t0) / args.steps * 1e3
-            sweep[f"{r:.2f}"] = {"ms_per_step": round(ms, 4), "context_tokens_per_s": round(n_ctx / ms * 1e3, 1)}
-            log(f"ratio {r:.2f}: {ms:.3f} ms/step, {n_ctx / ms * 1e3:,.0f} context tokens/s")
-            del g
-
-    # the same steps again with a HIP event pair around every launch (per-kernel durations)
-    L.cb_profile_enable(eng.ctx, True)
-    for _ in range(args.steps):
-        step(cache=cache)
-    cs.synchronize()
-    L.cb_profile_enable(eng.ctx, False)
-
-    kernels = {}
-    for kid, name in enumerate(L.KERNEL_NAMES):
-        ms, n, work = L.cb_profile_read(eng.ctx, kid)
-        if n == 0:
-            continue
-        if kid == L.CB_K_ATTN:
-            work = sum(attn_fl) * args.steps
-        bound = "mfma" if kid in (L.CB_K_GEMM_KV, L.CB_K_GEMM_Q, L.CB_K_ATTN, L.CB_K_GEMM_O,
-                                  L.CB_K_GEMM_GATE_UP, L.CB_K_GEMM_DOWN) else "hbm"
-        rate = work / (ms * 1e-3) / (1e12 if bound == "mfma" else 1e9) if ms > 0 else 0.0
-        peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_HBM_GBS
-        kernels[name] = {"ms_total_per_step": round(ms / args.steps, 4), "launches_per_step": n // args.steps,
-                         "us_per_launch": round(ms * 1e3 / n, 2), "bound": bound,
-                         "achieved": round(rate, 2), "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
-                         "frac": round(rate / peak, 4)}
-    dom = max(kernels, key=lambda k: kernels[k]["ms_total_per_step"])
-    dk = kernels[dom]
-    traffic = gate_up_traffic(sh, kept) if dom == "gemm_gate_up" and args.config == "qwen" else None
-    roofline = {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"],
-                "peak": PEAK_BF16_TFLOPS if dk["bound"] == "mfma" else PEAK_HBM_GBS, "unit": dk["unit"],
-                "frac": dk["frac"], "traffic": None if traffic is None else round(traffic)}
-
-    # per-layer latency (one extra profiled step with events at layer boundaries)
-    evs = []
-    step(cache=cache, layer_events=evs)
-    cs.synchronize()
-    per_layer = [evs[i].elapsed_time(evs[i + 1]) for i in range(len(evs) - 1)]
-
-    pcie_ms = full_ms = controller = variants = decode_ms = store_res = overlap = reuse = peaks = int8 = None
-    if not args.only_blend:
-        # PCIe-inclusive variant: cached KV in pinned host memory, fetched one layer ahead
-        for _ in range(2):
-            step(host_cache=host)
-        cs.synchronize()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            step(host_cache=host)
-        cs.synchronize()
-        torch.cuda.synchronize()
-        pcie_ms = (time.perf_counter() - t0) / args.steps * 1e3
-
-        # full recompute on the same GPU and kernels (ratio 1 at every layer)
-        full_sched = [1.0] * sh.n_layers
-        run_layers(eng, buf, tokens, offs, wl.n_query, full_sched, fused, cache=cache, upload_inputs=False)
-        cs.synchronize()
-        t0 = time.perf_counter()
-        n_full = max(3, args.steps // 4)
-        for _ in range(n_full):
-            run_layers(eng, buf, tokens, offs, wl.n_query, full_sched, fused, cache=cache, upload_inputs=False)
-        cs.synchronize()
-        full_ms = (time.perf_counter() - t0) / n_full * 1e3
-        log(f"pinned-host prefetch: {pcie_ms:.3f} ms/step; full recompute: {full_ms:.3f} ms/step")
-        overlap = run_overlap(eng, buf, tokens, offs, wl, fused, host)
-        reuse = run_reuse(eng, buf, tokens, offs, wl, fused, cache, args.steps)
-        controller = run_controller(eng, buf, tokens, offs, wl, fused, host, full_ms, overlap, args.steps)
-        variants = run_variants(eng, buf, tokens, offs, wl, fused, cache, args.steps)
-        decode_ms = run_decode(eng, buf, tokens, offs, wl, fused, cache)
-        store_res = run_store(eng, buf, tokens, offs, wl, fused, args.steps)
-        peaks = run_peaks(eng)
-        int8 = run_int8(wl, args.steps, args.warmup) if wl.shape.dtype == "bf16" else None
+    kernels = head.get("kernels", {})
+    dom = max(kernels, key=lambda k: kernels[k]["ms_total_per_step"]) if kernels else None
+    roofline = None
+    if dom:
+        dk = kernels[dom]
+        roofline = {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"],
+                    "unit": dk["unit"], "frac": dk["frac"],
+                    "traffic": traffic_from_profiles(dom, wl.name, dk["launches_per_step"]),
+                    "work_per_launch": dk["work_per_launch"], "us_per_launch": dk["us_per_launch"]}
+    extra = {}
+    if not args.only_headline:
+        def guarded(fn, *a, **kw):
+            try:
+                return fn(*a, **kw)
+            except Exception as e:  # an extra must not cost the headline line; the error is reported
+                log(f"{fn.__name__} failed: {e!r}")
+                return {"error": repr(e)}
+        extra["qwen"] = guarded(run_qwen, args)
+        extra["mistral_sweep"] = guarded(run_hbm_shape, "mistral_r15", (0.10, 0.15, 0.20), args)
+        extra["yi"] = {"bf16": guarded(run_hbm_shape, "yi_r15", (0.15,), args),
+                       "int8": guarded(run_hbm_shape, "yi_r15", (0.15,), args, int8=True)}
     if args.calib_copy:
-        src = torch.empty(128 << 20, dtype=torch.bfloat16, device=eng.device)
+        src = torch.empty(128 << 20, dtype=torch.bfloat16, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
-        torch.cuda.synchronize()
-
+        sync()
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         cpu = cpu_baseline(wl, args.cpu_budget)
-        log(f"cpu oracle: {cpu['value']:.1f} context tokens/s on {cpu['cores']} threads")
+        log(f"cpu oracle: {cpu['value']:.2f} context tokens/s on {cpu['cores']} threads")
 
+    value = head["context_tokens_per_s"]
     out = {
         "metric": "blended-prefill context tokens/s @ r=15% + per-layer ms; % HBM/MFMA peak",
-        "value": round(value, 1), "unit": "context tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "value": value, "unit": "context tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": head["wall_ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": sh.dtype, "data": "synthetic",
-        "config": {"workload": describe(wl), "n_ctx": n_ctx, "n_query": wl.n_query,
-                   "schedule": schedule_text(wl.schedule)},
+        "config": {"workload": describe(wl, "cached KV in pinned host memory (the chunk store's arena, filled by "
+                                            "the chunk producer), fetched per layer two layers ahead on a copy "
+                                            "stream inside every step; one prefill per step, T_blend from the "
+                                            "first fetch enqueue to the last layer's end",
+                                        "random weights N(0, 0.02) drawn on the device (torch generator, seeded)"),
+                   "n_ctx": wl.n_ctx, "n_query": wl.n_query, "schedule": schedule_text(wl.schedule)},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "per_layer_ms": {"layer1": round(per_layer[0], 4), "layer2": round(per_layer[1], 4),
-                         "layer3": round(per_layer[2], 4),
-                         "steady_median": round(float(np.median(per_layer[3:])), 4)},
-        "kept_rows_per_layer": kept[:4] + ["..."],
-        "kernels": kernels,
-        "pcie_prefetch": None if pcie_ms is None else {
-            "ms_per_step": round(pcie_ms, 4), "context_tokens_per_s": round(n_ctx / pcie_ms * 1e3, 1),
-            "host_kv_bytes_per_step": int(2 * sh.n_layers * n_ctx * sh.n_kv_heads * sh.head_dim * 2)},
-        "prefetch_per_layer": overlap,
-        "eager_ms_per_step": round(eager_ms, 4),
-        "full_recompute_ms": None if full_ms is None else round(full_ms, 4),
-        "full_reuse": reuse,
-        "peaks_measured": peaks,
-        "loading_controller": controller,
-        "selection_variants": variants,
-        "decode": decode_ms,
-        "chunk_store": store_res,
-        "ratio_sweep": sweep,
-        "int8_weights": int8,
-        "speedup_vs_full_recompute": None if full_ms is None else round(full_ms / ms_step, 3),
+        "t_blend_ms": head["t_blend_ms"],
+        "per_layer_ms": head["per_layer_ms"],
+        "kept_rows_per_layer": head["kept_rows_per_layer"],
+        "kernels": {k: {kk: vv for kk, vv in v.items() if kk != "work_per_launch"} for k, v in kernels.items()},
+        "headline_detail": {k: v for k, v in head.items()
+                            if k not in ("kernels", "t_blend_ms", "per_layer_ms", "kept_rows_per_layer")},
+        "l70_4k": other,
     }
+    out.update(extra)
     print(json.dumps(out), flush=True)
-    eng.close()
     return 0
 
 
