@@ -245,6 +245,22 @@ cb_status cb_blend_layer(cb_ctx* ctx, int32_t layer, const float* hidden_sel, co
                          float ratio, int32_t* new_sel_idx, int32_t* new_sel_local, int32_t* n_new,
                          void* out_sel, float* deviation, void* workspace, size_t workspace_bytes);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): cb_blend_layer with the library's own static
+ * workspace instead of a workspace argument; every other argument as in cb_blend_layer.  The
+ * workspace is one file-scope device array of 128 MiB per device (held from the library's
+ * load until the process ends).  A call whose cb_workspace_size(N, n_sel) exceeds 128 MiB
+ * returns CB_ENOMEM before anything is enqueued.  Nothing is allocated.  The array keeps the
+ * last call's contents and is shared by every call on that device: calls that overlap on one
+ * device (other streams, other threads, other contexts) race on it, so callers serialize them. */
+cb_status cb_blend_layer_static(cb_ctx* ctx, int32_t layer, const float* hidden_sel, const void* x_sel,
+                                const void* kv_cached_k, const void* kv_cached_v,
+                                void* kv_fused_k, void* kv_fused_v,
+                                const int32_t* chunk_offsets_dev, const int32_t* chunk_offsets_host,
+                                int32_t n_chunks, const int32_t* sel_idx, int32_t n_sel, int32_t n_query,
+                                float ratio, int32_t* new_sel_idx, int32_t* new_sel_local, int32_t* n_new,
+                                void* out_sel, float* deviation);
+
 /* Generation with the fused KV (CacheBlend review: the answer is generated with the fused KV
  * cache).  One layer of a decode step for n_new new tokens at positions n_past .. n_past +
  * n_new - 1: fresh Q/K/V of the new rows (RoPE at their positions) from hidden_new (device fp32

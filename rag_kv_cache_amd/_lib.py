@@ -75,6 +75,8 @@ _SIGS = {
     "cb_blend_layer": [_P, _I, _P, _P, _P, _P, _P, _P, _P, C.POINTER(_I), _I, _P, _I, _I, C.c_float, _P, _P,
                        C.POINTER(_I), _P, _P, _P, C.c_size_t],
     "cb_layer_rest": [_P, _I, _P, _I, _P, _I, _P, _P, _P, _P, C.c_size_t],
+    "cb_blend_layer_static": [_P, _I, _P, _P, _P, _P, _P, _P, _P, C.POINTER(_I), _I, _P, _I, _I, C.c_float, _P,
+                              _P, C.POINTER(_I), _P, _P],
     "cb_decode_layer": [_P, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P, C.c_size_t],
     "cb_workspace_views": [_P, _I, _I, _P],
     "cb_set_score_mode": [_P, _I],
@@ -198,6 +200,20 @@ def cb_blend_layer(ctx: int, layer: int, hidden_sel: int, kv_cached_k: int, kv_c
                              kv_fused_v, chunk_offsets_dev or None, _i32(chunk_offsets_host), n_chunks,
                              sel_idx, n_sel, n_query, ratio, new_sel_idx, new_sel_local, C.byref(n_new),
                              out_sel, deviation or None, workspace, workspace_bytes))
+    return n_new.value
+
+
+def cb_blend_layer_static(ctx: int, layer: int, hidden_sel: int, kv_cached_k: int, kv_cached_v: int,
+                          kv_fused_k: int, kv_fused_v: int, chunk_offsets_dev: int,
+                          chunk_offsets_host: Sequence[int], n_chunks: int, sel_idx: int, n_sel: int,
+                          n_query: int, ratio: float, new_sel_idx: int, new_sel_local: int, out_sel: int,
+                          deviation: int, x_sel: int = 0) -> int:
+    """cb_blend_layer on the library's static workspace (no workspace argument).  Returns n_new."""
+    n_new = _I()
+    _check(_L.cb_blend_layer_static(ctx, layer, hidden_sel, x_sel or None, kv_cached_k or None, kv_cached_v or None,
+                                    kv_fused_k, kv_fused_v, chunk_offsets_dev or None, _i32(chunk_offsets_host),
+                                    n_chunks, sel_idx, n_sel, n_query, ratio, new_sel_idx, new_sel_local,
+                                    C.byref(n_new), out_sel, deviation or None))
     return n_new.value
 
 

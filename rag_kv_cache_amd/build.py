@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "librag_kv_cache_amd.so")
-SOURCES = ["k_stream.hip", "k_topk.hip", "k_gemm.hip", "k_attn.hip", "cacheblend.cpp", "store.cpp"]
+SOURCES = ["k_stream.hip", "k_topk.hip", "k_gemm.hip", "k_attn.hip", "cacheblend.cpp", "store.cpp", "noalloc.hip"]
 HEADERS = ["cb_common.h", "cb_kernels.h", "cb_host.h", os.path.join("..", "..", "include", "cacheblend.h")]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
