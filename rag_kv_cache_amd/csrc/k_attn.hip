@@ -693,13 +693,19 @@ hipError_t launch_gr(const AttnArgs& a, hipStream_t s) {
 
 template <int G>
 hipError_t launch_g(const AttnArgs& a, hipStream_t s) {
-  constexpr int QT = G <= 6 ? 2 : 1;  // 12 wavefronts at most: more would cap registers below need
-  return launch_gr<G, 1, QT>(a, s);
+  if constexpr (G >= 7) {
+    // one wavefront per head with two 16-row blocks: each K or V fragment read from LDS feeds
+    // two MFMAs (the tile's LDS reads per MFMA halve); G wavefronts of ~200 registers
+    return launch_gr<G, 2, 1>(a, s);
+  } else {
+    constexpr int QT = G <= 6 ? 2 : 1;  // 12 wavefronts at most: more would cap registers below need
+    return launch_gr<G, 1, QT>(a, s);
+  }
 }
 
 }  // namespace
 
-int attn_rows_per_wg(int group) { return group <= 6 ? 32 : 16; }
+int attn_rows_per_wg(int group) { return group <= 6 ? 32 : 32; }
 
 // Whether the vector-ALU decode kernel takes n_q query rows of a GQA group of `group` heads.
 bool attn_decode_fits(int n_q, int group) {
