@@ -283,6 +283,9 @@ def run_headline(args):
     t0 = time.perf_counter()
     eng = device_engine(sh, wl.n_tokens + DECODE_ROWS)
     log(f"{wl.name}: {sh.n_layers} layers of weights drawn on the device in {time.perf_counter() - t0:.1f} s")
+    from rag_kv_cache_amd import _lib as L
+    L.cb_set_fetch_mode(eng.ctx, {"auto": L.CB_FETCH_AUTO, "kernel": L.CB_FETCH_KERNEL,
+                                  "copy": L.CB_FETCH_COPY}[args.fetch])
     chunks = F.chunk_tokens(wl)
     store = ChunkStore(eng, max(wl.chunk_lens), len(chunks) + 2, pinned=True)
     t0 = time.perf_counter()
@@ -668,6 +671,9 @@ def run_store(eng, buf, tokens, offs, wl, fused, steps):
     from rag_kv_cache_amd.pipeline import ChunkStore, produce_chunks, run_layers
     import fixtures as F
     sh = wl.shape
+    from rag_kv_cache_amd import _lib as L
+    L.cb_set_fetch_mode(eng.ctx, {"auto": L.CB_FETCH_AUTO, "kernel": L.CB_FETCH_KERNEL,
+                                  "copy": L.CB_FETCH_COPY}[args.fetch])
     chunks = F.chunk_tokens(wl)
     store = ChunkStore(eng, max(wl.chunk_lens), len(chunks) + 2, pinned=True)
     torch.cuda.synchronize()
@@ -954,6 +960,10 @@ def main() -> int:
                     help="only the headline prompt's timed steps and kernel profile (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--fetch", choices=("auto", "kernel", "copy"), default="auto",
+                    help="how the headline engine fetches the cached KV (cb_set_fetch_mode): the library's choice "
+                         "by chunk size, the fetch kernel reading pinned host memory over PCIe, or the copy engine "
+                         "(one copy per chunk and K/V) + the position update")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain device-to-device copy of 256 MiB, 3 times (counter calibration)")
     args = ap.parse_args()

@@ -142,13 +142,20 @@ cb_status cb_embed(cb_ctx* ctx, const int32_t* tokens, int32_t n, const void* ta
  * kv_cached_k = kv_cached_v = NULL to cb_blend_layer.  chunk_offsets_dev: the same offsets
  * on the device.  CB_ESTATE if the layer already has a fetch that no cb_synchronize has
  * consumed. */
-/* How cb_fetch_layer moves the rows.  CB_FETCH_KERNEL (default): when every chunk pointer is
- * page-locked host memory that kernels can read at the same address (hipHostMalloc, torch's
- * pinned tensors), one kernel on the copy stream reads the rows over PCIe, rotates K and writes
- * K and V into the fused buffers (one pass, no per-chunk copy commands); other pointers fall
- * back to the copy engine.  CB_FETCH_COPY: always the copy engine (hipMemcpyAsync per chunk),
- * then the rotation in place.  Results are identical.  CB_EINVAL for another mode. */
-typedef enum { CB_FETCH_COPY = 0, CB_FETCH_KERNEL = 1 } cb_fetch_mode;
+/* How cb_fetch_layer moves the rows.  CB_FETCH_KERNEL: when every chunk pointer is page-locked
+ * host memory that kernels can read at the same address (hipHostMalloc, torch's pinned
+ * tensors), one kernel on the copy stream reads the rows over PCIe, rotates K and writes K and
+ * V into the fused buffers (one pass, no per-chunk copy commands); other pointers fall back to
+ * the copy engine.  CB_FETCH_COPY: always the copy engine (hipMemcpyAsync per chunk), then the
+ * rotation in place.  CB_FETCH_AUTO (default): the copy engine when a chunk's K (or V) averages
+ * at least 1 MiB, else as CB_FETCH_KERNEL.  The fetch kernel loads faster when the per-copy
+ * cost of the copy engine dominates (small chunks: a load-bound layer), but it holds CUs that
+ * the compute stream's kernels then lack; large copies amortize that cost, and the copy engine
+ * leaves every CU to compute (measured on MI355X: 256 KiB chunks load at about 16 GB/s through
+ * the copy engine against 31 GB/s with the kernel; with 1 MiB chunks of a compute-bound layer
+ * the prefill ran 2% faster through the copy engine).  Results are identical.  CB_EINVAL for
+ * another mode. */
+typedef enum { CB_FETCH_COPY = 0, CB_FETCH_KERNEL = 1, CB_FETCH_AUTO = 2 } cb_fetch_mode;
 cb_status cb_set_fetch_mode(cb_ctx* ctx, int32_t mode);
 
 /* Launch shape of the CB_FETCH_KERNEL path: `blocks` workgroups of `threads` threads (a

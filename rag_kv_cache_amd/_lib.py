@@ -164,7 +164,7 @@ def cb_fetch_layer_device(ctx: int, layer: int, cache_k: int, cache_v: int, chun
                                     n_chunks, chunk_offsets_dev or None, fused_k, fused_v))
 
 
-CB_FETCH_COPY, CB_FETCH_KERNEL = 0, 1
+CB_FETCH_COPY, CB_FETCH_KERNEL, CB_FETCH_AUTO = 0, 1, 2
 
 
 def cb_set_fetch_mode(ctx: int, mode: int) -> None:

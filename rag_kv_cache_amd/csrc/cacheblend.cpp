@@ -65,6 +65,8 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // loads fastest alone (43 against 31 GB/s): the fetch slows the compute kernels while it runs,
 // and spread over more CUs it slows them more.
 constexpr cb::FetchLaunch kFetchLaunchDefault{8, 512, 2};
+// CB_FETCH_AUTO takes the copy engine from this many bytes per chunk and tensor (K or V) on.
+constexpr size_t kFetchCopyMinBytes = size_t(1) << 20;
 
 struct cb_ctx {
   cb_model_desc d{};
@@ -82,7 +84,7 @@ struct cb_ctx {
   std::vector<hipEvent_t> release_ev;  // per layer: the compute stream is done with its fused K/V
   std::vector<int> state;
   int score_mode = CB_SCORE_L2;
-  int fetch_mode = CB_FETCH_KERNEL;
+  int fetch_mode = CB_FETCH_AUTO;
   cb::FetchLaunch fetch_launch = kFetchLaunchDefault;
   bool prof = false;
   std::vector<ProfRec> recs;
@@ -150,7 +152,7 @@ void plan_gemm(cb::GemmArgs& g, bool bf, long cap_elems) {
 void attn_splits(int n_q, int n_tok, int group, long cap_rows, int& splits, int& split_len) {
   const bool small = n_q <= kAttnSmallRows;
   const bool few = cb::attn_decode_fits(n_q, group);  // the decode kernel: 64-key ranges, any multiple of 16
-  int len = few ? 64 : (small ? 256 : (n_q < 1200 ? 1024 : 2048));
+  int len = few ? 64 : (small ? 256 : (n_q < 1200 ? 1024 : (n_q < 2048 ? 2048 : 4096)));
   int s = (n_tok + len - 1) / len;
   s = std::min(s, small ? kAttnSmallSplits : kAttnMaxSplits);
   while (s > 1 && (long)s * n_q > cap_rows) --s;
@@ -415,7 +417,8 @@ bool kernel_readable_host(const void* p) {
 cb_status cb_set_fetch_mode(cb_ctx* c, int32_t mode) {
   cb_status st = check_ctx(c);
   if (st) return st;
-  if (mode != CB_FETCH_COPY && mode != CB_FETCH_KERNEL) return fail(CB_EINVAL, "unknown fetch mode %d", mode);
+  if (mode != CB_FETCH_COPY && mode != CB_FETCH_KERNEL && mode != CB_FETCH_AUTO)
+    return fail(CB_EINVAL, "unknown fetch mode %d", mode);
   c->fetch_mode = mode;
   return CB_OK;
 }
@@ -445,6 +448,8 @@ cb_status cb_fetch_layer(cb_ctx* c, int32_t layer, const void* const* host_k, co
   for (int ch = 0; ch < n_chunks; ++ch)
     if (offs[ch + 1] > offs[ch] && (!host_k[ch] || !host_v[ch])) return fail(CB_EINVAL, "chunk %d host pointer NULL", ch);
   bool direct = c->fetch_mode == CB_FETCH_KERNEL;
+  if (c->fetch_mode == CB_FETCH_AUTO && n_chunks > 0)  // see cb_set_fetch_mode
+    direct = (size_t)offs[n_chunks] * row / (size_t)n_chunks < kFetchCopyMinBytes;
   for (int ch = 0; direct && ch < n_chunks; ++ch)
     if (offs[ch + 1] > offs[ch] && !(kernel_readable_host(host_k[ch]) && kernel_readable_host(host_v[ch])))
       direct = false;

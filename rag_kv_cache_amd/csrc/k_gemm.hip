@@ -153,6 +153,13 @@ __device__ __forceinline__ uint4 i8x8_to_bf16(uint32_t lo, uint32_t hi) {
   return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
 }
 
+// Row halves in which an fp32 output tile is staged: two when the whole tile (BM rows of BN
+// fp32 + 16 bytes) exceeds the 160 KiB of LDS.
+template <int BM, int BN>
+constexpr int gemm_f32_halves() {
+  return BM * (BN * 4 + 16) > 160 * 1024 ? 2 : 1;
+}
+
 // BT = 0: bf16 weights, global -> LDS by DMA like the activations.  BT = 1: int8 weights with a
 // per-output-channel scale (g.bscale): a K-step's weight tile goes global -> registers one
 // K-step ahead, is converted to bf16 (exact) and written to the same LDS layout, so the MFMA
@@ -387,37 +394,47 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
   barrier();
   const int rl_base = wm * WTM + (lane >> 4) * 4;  // tile row of acc[i][.][0] is rl_base + 16 i
   if (g.splits > 1 || EPI == EPI_RESID) {
+    // fp32 tiles too large for LDS (256 x 256: 260 KiB) are staged and written in row halves,
+    // each half by the waves whose accumulator rows lie in it
     constexpr int PF = BN * 4 + 16;  // fp32 staging row pitch (bytes)
+    constexpr int HALVES = gemm_f32_halves<BM, BN>();
+    constexpr int HR = BM / HALVES;  // tile rows per half
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int hf = 0; hf < HALVES; ++hf) {
+      if (hf > 0) barrier();  // the previous half's reads of the staging rows are done
 #pragma unroll
-      for (int q = 0; q < FN / 2; ++q) {
-        const int tc = wn * WTN + q * 32 + (lane & 15);
-        const int la = stage_col<EPI, BN>(tc), lb = stage_col<EPI, BN>(tc + 16);
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          unsigned char* row = smem + (rl_base + i * 16 + r) * PF;
-          *reinterpret_cast<float*>(row + la * 4) = acc[i][2 * q][r];
-          *reinterpret_cast<float*>(row + lb * 4) = acc[i][2 * q + 1][r];
+        for (int q = 0; q < FN / 2; ++q) {
+          const int tc = wn * WTN + q * 32 + (lane & 15);
+          const int la = stage_col<EPI, BN>(tc), lb = stage_col<EPI, BN>(tc + 16);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int rl = rl_base + i * 16 + r - hf * HR;
+            if (HALVES > 1 && (rl < 0 || rl >= HR)) continue;
+            unsigned char* row = smem + rl * PF;
+            *reinterpret_cast<float*>(row + la * 4) = acc[i][2 * q][r];
+            *reinterpret_cast<float*>(row + lb * 4) = acc[i][2 * q + 1][r];
+          }
         }
-      }
-    barrier();
-    constexpr int CPR = BN / 4;  // 16-byte chunks per row
-    for (int it = tid; it < BM * CPR; it += 64 * NW) {
-      const int rl = it / CPR, c = (it - rl * CPR) * 4;
-      const int m = m0 + rl;
-      if (m >= g.M) continue;
-      const float4 v = *reinterpret_cast<const float4*>(smem + rl * PF + c * 4);
-      if (g.splits > 1) {
-        int n;
-        if (EPI == EPI_SWIGLU) n = c < BN / 2 ? tn * (BN / 2) + c : g.swiglu_ffn + tn * (BN / 2) + (c - BN / 2);
-        else n = tn * BN + c;
-        *reinterpret_cast<float4*>(g.partial + ((long)blockIdx.y * g.M + m) * g.N + n) = v;
-      } else {
-        const long rr = g.resid_rows ? (long)g.resid_rows[m] : (long)m;
-        const float4 r4 = *reinterpret_cast<const float4*>(g.resid + rr * g.ldr + tn * BN + c);
-        *reinterpret_cast<float4*>((float*)g.out + (long)m * g.ldo + tn * BN + c) =
-            make_float4(r4.x + v.x, r4.y + v.y, r4.z + v.z, r4.w + v.w);
+      barrier();
+      constexpr int CPR = BN / 4;  // 16-byte chunks per row
+      for (int it = tid; it < HR * CPR; it += 64 * NW) {
+        const int rl = it / CPR, c = (it - rl * CPR) * 4;
+        const int m = m0 + hf * HR + rl;
+        if (m >= g.M) continue;
+        const float4 v = *reinterpret_cast<const float4*>(smem + rl * PF + c * 4);
+        if (g.splits > 1) {
+          int n;
+          if (EPI == EPI_SWIGLU) n = c < BN / 2 ? tn * (BN / 2) + c : g.swiglu_ffn + tn * (BN / 2) + (c - BN / 2);
+          else n = tn * BN + c;
+          *reinterpret_cast<float4*>(g.partial + ((long)blockIdx.y * g.M + m) * g.N + n) = v;
+        } else {
+          const long rr = g.resid_rows ? (long)g.resid_rows[m] : (long)m;
+          const float4 r4 = *reinterpret_cast<const float4*>(g.resid + rr * g.ldr + tn * BN + c);
+          *reinterpret_cast<float4*>((float*)g.out + (long)m * g.ldo + tn * BN + c) =
+              make_float4(r4.x + v.x, r4.y + v.y, r4.z + v.z, r4.w + v.w);
+        }
       }
     }
   } else {
@@ -502,11 +519,13 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
   }
 }
 
-// LDS bytes one launch needs: the operand ring, or the staged output tile if larger.
+// LDS bytes one launch needs: the operand ring, or the staged output tile if larger (an fp32
+// tile in row halves when whole it would exceed the LDS).
 template <int BM, int BN, int NS, int EPI>
 constexpr int gemm_lds_bytes(bool f32_out) {
   constexpr int ring = NS * (BM + BN) * BK * 2;
-  const int stage = f32_out ? BM * (BN * 4 + 16) : BM * ((EPI == EPI_SWIGLU ? BN / 2 : BN) * 2 + 16);
+  const int stage = f32_out ? (BM / gemm_f32_halves<BM, BN>()) * (BN * 4 + 16)
+                            : BM * ((EPI == EPI_SWIGLU ? BN / 2 : BN) * 2 + 16);
   return ring > stage ? ring : stage;
 }
 
@@ -935,11 +954,9 @@ hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
     case GEMM_128x512:  // planned for the SwiGLU epilogue only
       if constexpr (EPI == EPI_SWIGLU) { e = launch_dma<128, 512, 2, 4, 2, EPI, BT>(g, s); break; }
       return hipErrorInvalidValue;
-    case GEMM_256x256:  // bf16 output, no split (the fp32 staged tile would not fit in LDS)
-      if constexpr (EPI != EPI_RESID) {
-        if (g.splits == 1) { e = launch_dma<256, 256, 2, 4, 2, EPI, BT>(g, s); break; }
-      }
-      return hipErrorInvalidValue;
+    case GEMM_256x256:  // fp32 outputs (residual, split-K partials) staged in row halves
+      e = launch_dma<256, 256, 2, 4, 2, EPI, BT>(g, s);
+      break;
     case GEMM_128x256: e = launch_dma<128, 256, 2, 4, 3, EPI, BT>(g, s); break;
     case GEMM_64x256: e = launch_dma<64, 256, 1, 4, 3, EPI, BT>(g, s); break;
     case GEMM_128x128: e = launch_dma<128, 128, 2, 2, 3, EPI, BT>(g, s); break;
@@ -965,7 +982,8 @@ hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
 // workgroups): 64x128 0.72 us, 128x128 0.83, 64x256 1.04, 128x256 1.13, 256x256 1.75, 128x512
 // 2.10.  The model ranks the measured tiles of the gate/up products of the Qwen2.5-1.5B shape at
 // 64..5184 rows and of the Mistral-7B shape at 640..1024 rows within 10% of the best.  128 x 512
-// is built for the SwiGLU epilogue only and 256 x 256 for every epilogue but the residual add.
+// is built for the SwiGLU epilogue only.  Short reductions keep to bf16-output tiles for the
+// residual add (256 x 256 is left out there: its fp32 tile is staged in two halves).
 GemmCfg tile_by_model(int M, int N, int epi, long* workgroups) {
   struct Cand {
     GemmCfg cfg;
@@ -1005,13 +1023,48 @@ GemmCfg tile_by_model(int M, int N, int epi, long* workgroups) {
 //     5184 rows, 256 x 256 for all of Q/K/V there), no split, if it gives at least ~150
 //     workgroups; else 64 x 128 tiles of 4 wavefronts with a 4-stage ring and K split up to
 //     ~150 workgroups;
-//   * long reductions: large M (>= 2048 rows) with a bf16 output and N % 256 == 0: 256 x 256
-//     tiles of 8 wavefronts, no split (the fewest operand bytes per flop);
+//   * long reductions over large M (>= 2048 rows) with N % 256 == 0: long_reduction_plan;
 //   * problems with >= 200 tiles of 128 x 256: those tiles (8 wavefronts), no split;
 //   * other long reductions (the FFN down-projection): up to 320 rows, 64 x 128 tiles with K
 //     split so that at most 256 workgroups run (64 rows: 15 against 20 us with 64 x 256); above,
 //     128 x 256 tiles, K split so that about 210 workgroups run;
 //   each split keeps at least two 64-wide K-steps and its partials fit the buffer.
+// Long reductions (K > 2048) over many rows (M >= 2048, N % 256 == 0): 128 x 256 or 256 x 256
+// tiles with K split 1..4 ways, the cheapest by the tile model (waves x t(cfg) per K-step x
+// K-steps per split) plus what the split costs: the reduce reads the s fp32 partial planes (and,
+// for the residual epilogue, the residual) and writes the output, about (s + 2) M N 4 + 2 M N
+// bytes at ~4 TB/s; an unsplit residual output is followed by its own RMSNorm pass, M N 6 bytes
+// at ~2.8 TB/s (the rates measured for those kernels on MI355X).  Llama-70B shape, 2714 rows:
+// the down-projection (K 28672) and the o-projection (K 8192) take 256 x 256 split 2, the
+// Q/K/V product 256 x 256 unsplit; at 16640 rows every product takes 256 x 256 unsplit.
+static GemmPlan long_reduction_plan(int M, int N, int K, int epi, long partial_cap_elems) {
+  struct Cand {
+    GemmCfg cfg;
+    int bm, bn;
+    float t;
+  };
+  constexpr Cand cands[] = {{GEMM_128x256, 128, 256, 1.13f}, {GEMM_256x256, 256, 256, 1.75f}};
+  const int nk = K / 64;
+  const double mn = (double)M * N;
+  GemmPlan best{GEMM_128x256, 1};
+  double best_cost = 1e300;
+  for (const Cand& c : cands) {
+    const long tiles = (long)((M + c.bm - 1) / c.bm) * (N / c.bn);
+    for (int sp = 1; sp <= 4; ++sp) {
+      if (sp > 1 && (nk / sp < 2 || (long)sp * M * N > partial_cap_elems)) break;
+      const double waves = (double)((tiles * sp + 255) / 256);
+      double cost = waves * c.t * ((nk + sp - 1) / sp);
+      if (sp > 1) cost += ((sp + 2) * mn * 4 + mn * 2) / 4.0e6;  // us at 4 TB/s
+      else if (epi == EPI_RESID) cost += mn * 6 / 2.8e6;
+      if (cost < best_cost) {
+        best_cost = cost;
+        best = GemmPlan{c.cfg, sp};
+      }
+    }
+  }
+  return best;
+}
+
 GemmPlan gemm_plan(int M, int N, int K, int epi, long partial_cap_elems) {
   GemmPlan p{GEMM_128x128, 1};
   if (M <= 4 && K % 32 == 0) {  // a few rows (decode): weight streaming on the vector ALUs
@@ -1026,9 +1079,8 @@ GemmPlan gemm_plan(int M, int N, int K, int epi, long partial_cap_elems) {
     long wgs = 0;
     p.cfg = tile_by_model(M, N, epi, &wgs);
     if (wgs >= 150) return p;
-  } else if (M >= 2048 && epi != EPI_RESID && N % 256 == 0) {
-    p.cfg = GEMM_256x256;
-    return p;
+  } else if (M >= 2048 && N % 256 == 0) {
+    return long_reduction_plan(M, N, K, epi, partial_cap_elems);
   }
   int bm = 128, bn = 128, target = 210;
   bool one_wave = false;  // split only as far as one wave of 256 workgroups

@@ -9,7 +9,16 @@
         FETCH_SIZE / WRITE_SIZE per dispatch of the kernels matching REGEX, grouped by grid
         size, each scaled by what the counter reads for a plain device copy of B bytes (the
         dispatch with grid N); the sha256 of FILE is recorded so that a reader can tell
-        whether the kernel source changed since the counters were taken
+        whether the kernel source changed since the counters were taken; with --last N, also
+        the average over the last N matching dispatches (one step's launches when the profiled
+        run ends with a step)
+    python -m rag_kv_cache_amd.profsummary counters <results.db> [<results.db> ...] --kernel REGEX
+        [--cus 256] [--last N]
+        every counter of the matching dispatches, mean per (kernel, grid), from one or more
+        counter runs (one pass per run); derived where the inputs are there: MFMA busy share
+        SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x CUs x 4 SIMDs), VALU instructions per
+        MFMA instruction, LDS-wait share of wave cycles; --last N also averages the last N
+        matching dispatches
 """
 from __future__ import annotations
 
@@ -69,8 +78,8 @@ def traffic(fetch_db: str, write_db: str, kernel_re: str, calib_grid: int, calib
                 agg[(name, gs)].append(val)
         return agg
     f, w = read(fetch_db, "FETCH_SIZE"), read(write_db, "WRITE_SIZE")
-    cf = [statistics.mean(v) for (n, g), v in f.items() if g == calib_grid]
-    cw = [statistics.mean(v) for (n, g), v in w.items() if g == calib_grid]
+    cf = [statistics.mean(v) for (n, g), v in f.items() if g == calib_grid and "copyBuffer" in n]
+    cw = [statistics.mean(v) for (n, g), v in w.items() if g == calib_grid and "copyBuffer" in n]
     kib = calib_bytes / 1024.0
     sf = kib / cf[0] if cf else float("nan")
     sw = kib / cw[0] if cw else float("nan")
@@ -89,6 +98,80 @@ def traffic(fetch_db: str, write_db: str, kernel_re: str, calib_grid: int, calib
     return "\n".join(lines)
 
 
+def _dispatch_counters(path: str, kernel_re: str):
+    """{dispatch_id: (kernel name, grid, {counter: value})} of the matching dispatches."""
+    db = sqlite3.connect(path)
+    rx = re.compile(kernel_re)
+    out = {}
+    for did, name, cn, val, gs in db.execute(
+            "select dispatch_id, kernel_name, counter_name, value, grid_size from counters_collection"):
+        if not rx.search(name):
+            continue
+        rec = out.setdefault(did, (name, gs, {}))
+        rec[2][cn] = rec[2].get(cn, 0.0) + val
+    return out
+
+
+def counters(paths, kernel_re: str, cus: int, last: int, xcds: int = 8) -> str:
+    runs = [_dispatch_counters(p, kernel_re) for p in paths]
+    groups = defaultdict(lambda: defaultdict(list))
+    for run in runs:
+        for did in sorted(run):
+            name, gs, vals = run[did]
+            for cn, v in vals.items():
+                groups[(_short(name).split("(")[0], gs)][cn].append(v)
+    names = sorted({cn for g in groups.values() for cn in g})
+    lines = [f"{'grid':>9} {'n':>5} " + " ".join(f"{n[:22]:>22}" for n in names) + "  derived  kernel"]
+
+    def derived(m):
+        parts = []
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in m and m.get("GRBM_GUI_ACTIVE"):
+            # GRBM_GUI_ACTIVE is summed over the XCDs: one XCD's count is the dispatch's cycles
+            cyc = m["GRBM_GUI_ACTIVE"] / xcds
+            parts.append(f"mfma_busy {m['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * cus * 4):.3f}")
+        if "SQ_INSTS_VALU" in m and m.get("SQ_INSTS_MFMA"):
+            parts.append(f"valu/mfma {m['SQ_INSTS_VALU'] / m['SQ_INSTS_MFMA']:.2f}")
+        if "SQ_WAIT_INST_LDS" in m and m.get("SQ_WAVE_CYCLES"):
+            parts.append(f"lds_wait/wave {m['SQ_WAIT_INST_LDS'] / m['SQ_WAVE_CYCLES']:.3f}")
+        if "SQ_ACTIVE_INST_VALU" in m and m.get("SQ_WAVE_CYCLES"):
+            parts.append(f"valu_active/wave {m['SQ_ACTIVE_INST_VALU'] / m['SQ_WAVE_CYCLES']:.3f}")
+        return ", ".join(parts)
+
+    for (name, gs), cmap in sorted(groups.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+        m = {cn: statistics.mean(v) for cn, v in cmap.items()}
+        n = max(len(v) for v in cmap.values())
+        lines.append(f"{gs:9d} {n:5d} " + " ".join(f"{m.get(c, float('nan')):22.0f}" for c in names)
+                     + f"  {derived(m)}  {name[:70]}")
+    if last:
+        m = {}
+        for run in runs:
+            dids = sorted(run)[-last:]
+            for cn in {c for d in dids for c in run[d][2]}:
+                m[cn] = statistics.mean(run[d][2].get(cn, 0.0) for d in dids)
+        lines.append(f"last {last} dispatches: " + ", ".join(f"{c} {m[c]:.0f}" for c in sorted(m))
+                     + (f"; {derived(m)}" if derived(m) else ""))
+    return "\n".join(lines)
+
+
+def traffic_last(fetch_db: str, write_db: str, kernel_re: str, calib_grid: int, calib_bytes: float, last: int) -> str:
+    """Mean scaled HBM bytes of the last `last` matching dispatches (in dispatch order)."""
+    f = _dispatch_counters(fetch_db, kernel_re + "|copyBuffer")
+    w = _dispatch_counters(write_db, kernel_re + "|copyBuffer")
+    kib = calib_bytes / 1024.0
+    cf = [v[2]["FETCH_SIZE"] for v in f.values() if v[1] == calib_grid and "copyBuffer" in v[0]]
+    cw = [v[2]["WRITE_SIZE"] for v in w.values() if v[1] == calib_grid and "copyBuffer" in v[0]]
+    sf = kib / statistics.mean(cf) if cf else float("nan")
+    sw = kib / statistics.mean(cw) if cw else float("nan")
+    rx = re.compile(kernel_re)
+    fd = [d for d in sorted(f) if rx.search(f[d][0])][-last:]
+    wd = [d for d in sorted(w) if rx.search(w[d][0])][-last:]
+    if len(fd) < last or len(wd) < last:
+        return f"(fewer than {last} matching dispatches)"
+    mb = statistics.mean(f[d][2]["FETCH_SIZE"] * sf for d in fd) * 1024 / 1e6 + \
+        statistics.mean(w[d][2]["WRITE_SIZE"] * sw for d in wd) * 1024 / 1e6
+    return f"step average over the last {last} launches: {mb:.2f} MB per launch"
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -101,8 +184,15 @@ def main() -> int:
     x.add_argument("--kernel", required=True)
     x.add_argument("--calib-grid", type=int, default=131072)
     x.add_argument("--calib-bytes", type=float, default=float(256 << 20))
-    x.add_argument("--source", default="")
-    for p in (t, x):
+    x.add_argument("--source", action="append", default=[])
+    x.add_argument("--last", type=int, default=0)
+    c = sub.add_parser("counters")
+    c.add_argument("dbs", nargs="+")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--cus", type=int, default=256)
+    c.add_argument("--xcds", type=int, default=8)
+    c.add_argument("--last", type=int, default=0)
+    for p in (t, x, c):
         p.add_argument("--command", action="append", default=[])
         p.add_argument("--note", default="")
         p.add_argument("--out", default="")
@@ -115,10 +205,14 @@ def main() -> int:
         if a.steps:
             nl, first, cnt = (int(v) for v in a.steps.split(","))
             text += "\n" + step_kernels(a.db, nl, first, cnt) + "\n"
+    elif a.cmd == "counters":
+        text += counters(a.dbs, a.kernel, a.cus, a.last, a.xcds) + "\n"
     else:
-        if a.source:
-            text += f"source_sha256 {a.source}: {hashlib.sha256(open(a.source, 'rb').read()).hexdigest()}\n"
+        for src in a.source:
+            text += f"source_sha256 {src}: {hashlib.sha256(open(src, 'rb').read()).hexdigest()}\n"
         text += traffic(a.fetch_db, a.write_db, a.kernel, a.calib_grid, a.calib_bytes) + "\n"
+        if a.last:
+            text += traffic_last(a.fetch_db, a.write_db, a.kernel, a.calib_grid, a.calib_bytes, a.last) + "\n"
     if a.out:
         open(a.out, "w").write(text)
     else:
