@@ -12,7 +12,8 @@
 //   in registers as the B operand), so every lane owns one query row's scores: lane l has
 //   row (l & 15) and keys 4*(l >> 4) + r of each 16-key block;
 //   online softmax in fp32 (exp2 with log2(e)/sqrt(d) folded into the scale), row max and
-//   sum over the four lanes of a row by two lane swaps (permlane16/32);
+//   sum over the four lanes of a row by two lane swaps (permlane16/32), the reference maximum
+//   moved (and O rescaled) only when a score exceeds it by more than 2^8 in probability;
 //   O^T += V^T P^T: P (rounded to bf16) is already in B-operand layout, V^T fragments come
 //   from LDS transpose reads of the row-major V tile;
 //   split-KV: grid.y splits the key range so short query sets still fill the chip; a split
@@ -74,6 +75,7 @@ __device__ __forceinline__ int swz_k(int row) { return row & 15; }
 __device__ __forceinline__ int swz_v(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
 
 constexpr int ATT_NS = 4;                     // LDS stages (K + V tile each)
+constexpr float ATT_LAZY = 8.f;               // probabilities against a stale maximum stay <= 2^8
 constexpr int ATT_STAGE_B = 2 * 64 * 256;     // 64 keys x 256 B (one head) for K, then V
 
 template <int G, int RB, int QT>
@@ -214,8 +216,18 @@ __global__ __launch_bounds__(64 * G * QT) void attn_bf16_kernel(AttnArgs a) {
       mx = fmaxf(mx, s[rb][3][3]);
       mx = max4_rows(mx);
       const float m_new = fmaxf(m_i[rb], mx);
-      const float alpha = (m_new == m_i[rb]) ? 1.f : __builtin_amdgcn_exp2f((m_i[rb] - m_new) * c);
-      const float mc = (m_new == NEG_INF) ? 0.f : m_new * c;
+      // Lazy rescaling: the reference maximum m_i moves only when a row of the wavefront sees a
+      // scaled score more than ATT_LAZY (log2 units) above it; until then the probabilities are
+      // taken against the older reference (at most 2^ATT_LAZY), which leaves O / l unchanged and
+      // skips the rescale of O.  A row's first valid keys always move it (from -inf).
+      if (__ballot((m_new - m_i[rb]) * c > ATT_LAZY)) {
+        const float alpha = (m_new == m_i[rb]) ? 1.f : __builtin_amdgcn_exp2f((m_i[rb] - m_new) * c);
+        l_i[rb] *= alpha;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) o[rb][d] *= alpha;
+        m_i[rb] = m_new;
+      }
+      const float mc = (m_i[rb] == NEG_INF) ? 0.f : m_i[rb] * c;
       float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
@@ -225,12 +237,7 @@ __global__ __launch_bounds__(64 * G * QT) void attn_bf16_kernel(AttnArgs a) {
           s[rb][kb][r] = p;
           rs += p;
         }
-      l_i[rb] = l_i[rb] * alpha + rs;  // this lane's share of the row sum (reduced at the end)
-      m_i[rb] = m_new;
-      if (__ballot(alpha != 1.f)) {
-#pragma unroll
-        for (int d = 0; d < 8; ++d) o[rb][d] *= alpha;
-      }
+      l_i[rb] += rs;  // this lane's share of the row sum (reduced at the end)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const u32x4_t w = {pack_bf16x2(s[rb][2 * ks][0], s[rb][2 * ks][1]), pack_bf16x2(s[rb][2 * ks][2], s[rb][2 * ks][3]),
