@@ -245,6 +245,10 @@ def run_prompt_pinned(eng, store, wl, steps, warmup, profile=False, overlap=Fals
         sync()
         L.cb_profile_enable(eng.ctx, False)
         out["kernels"] = kernel_table(eng, 1, sum(attn_fl), PEAK_PCIE_GBS)
+        for name in ("fetch", "rope_delta"):  # the fetch and its position update run on the copy stream
+            if name in out["kernels"]:
+                out["kernels"][name]["stream"] = ("copy: beside the compute stream's kernels, so its event time "
+                                                  "includes waiting for CUs they hold")
         out["attention_flops_per_step"] = sum(attn_fl)
     if overlap:
         out["per_layer_overlap"] = run_overlap(eng, buf, tokens, offs, wl, fused, hc, reps=2)
@@ -400,7 +404,7 @@ def _fetch_layer(eng, buf, host, offs, l, fused):
                      _ptr(buf.offsets), _ptr(fused[l][0]), _ptr(fused[l][1]))
 
 
-def run_overlap(eng, buf, tokens, offs, wl, fused, host, reps: int = 5, eps_ms: float = 0.02):
+def run_overlap(eng, buf, tokens, offs, wl, fused, host, reps: int = 5, eps_ms: float = 0.02, eps_rel: float = 0.01):
     """Per-layer T_load, T_recompute and T_overlapped of the pinned-host prefetched prefill, medians
     over `reps` runs:
       * T_load[l]: layer l's fetch alone (cached K/V of every chunk over PCIe + position update),
@@ -410,7 +414,8 @@ def run_overlap(eng, buf, tokens, offs, wl, fused, host, reps: int = 5, eps_ms: 
         fused buffers already holding the re-rotated cache (no fetch);
       * T_overlapped[l]: layer l on the compute stream in the pipelined run (fetches two layers
         ahead on the copy stream), including any wait for its fetch.
-    The pipeline claim is checked per layer as T_overlapped <= max(T_load, T_recompute) + eps."""
+    The pipeline claim is checked per layer as T_overlapped <= max(T_load, T_recompute) + eps, with
+    eps = eps_ms, and again with eps = max(eps_ms, eps_rel * max(...)) for layers of several ms."""
     import torch
     from rag_kv_cache_amd import _lib as L
     from rag_kv_cache_amd.pipeline import run_layers
@@ -449,9 +454,12 @@ def run_overlap(eng, buf, tokens, offs, wl, fused, host, reps: int = 5, eps_ms: 
     excess = [t_ov[l] - max(t_load[l], t_rec[l]) for l in range(nl)]
     steady = list(range(3, nl)) if nl > 4 else list(range(nl))
     ok = [l for l in range(nl) if excess[l] <= eps_ms]
+    ok_rel = [l for l in range(nl) if excess[l] <= max(eps_ms, eps_rel * max(t_load[l], t_rec[l]))]
     log(f"overlap (steady medians): load {np.median([t_load[l] for l in steady]):.4f}, recompute "
         f"{np.median([t_rec[l] for l in steady]):.4f}, overlapped {np.median([t_ov[l] for l in steady]):.4f} ms; "
-        f"{len(ok)}/{nl} layers within max(load, recompute) + {eps_ms} ms")
+        f"{len(ok)}/{nl} layers within max(load, recompute) + {eps_ms} ms, {len(ok_rel)}/{nl} within "
+        f"+ max({eps_ms} ms, {eps_rel:.0%}); sum overlapped {sum(t_ov):.3f} vs sum max "
+        f"{sum(max(a, b) for a, b in zip(t_load, t_rec)):.3f} ms")
     r4 = lambda v: [round(x, 4) for x in v]
     return {"t_load_ms": r4(t_load), "t_recompute_ms": r4(t_rec), "t_overlapped_ms": r4(t_ov),
             "steady_median_ms": {"load": round(float(np.median([t_load[l] for l in steady])), 4),
@@ -461,6 +469,8 @@ def run_overlap(eng, buf, tokens, offs, wl, fused, host, reps: int = 5, eps_ms: 
                        "overlapped": round(sum(t_ov), 4),
                        "max_per_layer": round(sum(max(a, b) for a, b in zip(t_load, t_rec)), 4)},
             "check": {"eps_ms": eps_ms, "layers_within": len(ok), "layers": nl,
+                      "eps_rel": eps_rel, "layers_within_rel": len(ok_rel),
+                      "sum_overlapped_over_sum_max": round(sum(t_ov) / sum(max(a, b) for a, b in zip(t_load, t_rec)), 4),
                       "max_excess_ms": round(max(excess), 4),
                       "steady_median_excess_ms": round(float(np.median([excess[l] for l in steady])), 4)},
             "note": "per-layer medians over %d runs; T_load: each layer's fetch alone on the copy stream; "
@@ -671,9 +681,6 @@ def run_store(eng, buf, tokens, offs, wl, fused, steps):
     from rag_kv_cache_amd.pipeline import ChunkStore, produce_chunks, run_layers
     import fixtures as F
     sh = wl.shape
-    from rag_kv_cache_amd import _lib as L
-    L.cb_set_fetch_mode(eng.ctx, {"auto": L.CB_FETCH_AUTO, "kernel": L.CB_FETCH_KERNEL,
-                                  "copy": L.CB_FETCH_COPY}[args.fetch])
     chunks = F.chunk_tokens(wl)
     store = ChunkStore(eng, max(wl.chunk_lens), len(chunks) + 2, pinned=True)
     torch.cuda.synchronize()

@@ -311,64 +311,79 @@ __global__ __launch_bounds__(1024) void fetch_rope_kernel(FetchChunks F, T* kf, 
 // One wavefront per recomputed row i (position j = sel[i]): for context rows (i < n_cand)
 // dev[i] = sum over the row's K and V elements of (fresh - fused)^2, read before the
 // fused row is overwritten; then fused[j] <- fresh[i].  fresh row layout: K heads then
-// V heads (row_elems each).  Per-lane sequential sums then a fixed butterfly: the result
-// does not depend on scheduling.
+// V heads (row_elems each).  LPR lanes per row (the row's 16-byte pieces, at most 64: a
+// wavefront holds 64 / LPR rows, so narrow rows still use every lane), each piece's loads issued
+// before any use.  Per-lane sequential sums then a fixed butterfly over the row's lanes: the
+// result does not depend on scheduling.
 // When the layer keeps every recomputed row (copy_sel set), the kept set is sel itself:
 // copy_sel[i] = sel[i], copy_local[i] = i.  cosine != 0 scores 1 - <fresh, fused> /
 // (|fresh| |fused|) over the row's K and V instead of the squared distance (0 when both rows
 // are zero, 1 when only one is).
-template <typename T>
+template <typename T, int LPR>
 __global__ __launch_bounds__(256) void dev_scatter_kernel(const T* fresh, long ld_fresh, T* fk, T* fv,
                                                           const int32_t* sel, int n_sel, int n_cand, int n_tok,
                                                           int row_elems, float* dev, int32_t* copy_sel,
                                                           int32_t* copy_local, int cosine) {
   constexpr int VE = Vec16<T>::N;
-  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (i >= n_sel) return;
-  const int j = sel[i];
-  if (copy_sel && lane == 0) {
+  constexpr int RPW = 64 / LPR;  // rows per wavefront, LPR lanes each
+  const int lane = threadIdx.x & 63, l = lane % LPR;
+  const int i = (blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / LPR;
+  const bool valid = i < n_sel;
+  const int j = valid ? sel[i] : -1;
+  if (valid && copy_sel && l == 0) {
     copy_sel[i] = j;
     copy_local[i] = i;
   }
-  const bool score = dev != nullptr && i < n_cand;
-  if (j < 0 || j >= n_tok) {
-    if (score && lane == 0) dev[i] = __builtin_nanf("");
-    return;
-  }
-  const T* fr = fresh + (long)i * ld_fresh;
-  T* dk = fk + (long)j * row_elems;
-  T* dv = fv + (long)j * row_elems;
+  const bool score = dev != nullptr && valid && i < n_cand;
+  const bool ok = valid && j >= 0 && j < n_tok;
   float acc = 0.f, na = 0.f, nb = 0.f;
-  for (int e = lane * VE; e < row_elems; e += 64 * VE) {
-    const uint4 nk = *reinterpret_cast<const uint4*>(fr + e);
-    const uint4 nv = *reinterpret_cast<const uint4*>(fr + row_elems + e);
-    if (score) {
-      float a[VE], b[VE];
+  if (ok) {
+    const T* fr = fresh + (long)i * ld_fresh;
+    T* dk = fk + (long)j * row_elems;
+    T* dv = fv + (long)j * row_elems;
+    for (int e = l * VE; e < row_elems; e += LPR * VE) {
+      // every load of the piece first (fresh K and V, and the fused rows they replace)
+      const uint4 nk = *reinterpret_cast<const uint4*>(fr + e);
+      const uint4 nv = *reinterpret_cast<const uint4*>(fr + row_elems + e);
+      uint4 ok4 = make_uint4(0, 0, 0, 0), ov4 = make_uint4(0, 0, 0, 0);
+      if (score) {
+        ok4 = *reinterpret_cast<const uint4*>(dk + e);
+        ov4 = *reinterpret_cast<const uint4*>(dv + e);
+      }
+      if (score) {
+        float a[VE], b[VE];
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        Vec16<T>::load(fr + half * row_elems + e, a);
-        Vec16<T>::load((half ? dv : dk) + e, b);
-        if (cosine) {
+        for (int half = 0; half < 2; ++half) {
+          const uint4 x = half ? nv : nk, y = half ? ov4 : ok4;
+          Vec16<T>::load(reinterpret_cast<const T*>(&x), a);
+          Vec16<T>::load(reinterpret_cast<const T*>(&y), b);
+          if (cosine) {
 #pragma unroll
-          for (int q = 0; q < VE; ++q) { acc += a[q] * b[q]; na += a[q] * a[q]; nb += b[q] * b[q]; }
-        } else {
+            for (int q = 0; q < VE; ++q) { acc += a[q] * b[q]; na += a[q] * a[q]; nb += b[q] * b[q]; }
+          } else {
 #pragma unroll
-          for (int q = 0; q < VE; ++q) { const float t = a[q] - b[q]; acc += t * t; }
+            for (int q = 0; q < VE; ++q) { const float t = a[q] - b[q]; acc += t * t; }
+          }
         }
       }
+      *reinterpret_cast<uint4*>(dk + e) = nk;
+      *reinterpret_cast<uint4*>(dv + e) = nv;
     }
-    *reinterpret_cast<uint4*>(dk + e) = nk;
-    *reinterpret_cast<uint4*>(dv + e) = nv;
   }
-  if (score) {
-    acc = wave_sum(acc);
-    if (cosine) {
-      na = wave_sum(na);
-      nb = wave_sum(nb);
-      acc = (na == 0.f || nb == 0.f) ? (na == nb ? 0.f : 1.f) : 1.0f - acc / (sqrtf(na) * sqrtf(nb));
+  if (dev != nullptr) {  // uniform: every lane takes part in the row sums
+#pragma unroll
+    for (int o = LPR / 2; o >= 1; o >>= 1) {
+      acc += __shfl_xor(acc, o, 64);
+      if (cosine) {
+        na += __shfl_xor(na, o, 64);
+        nb += __shfl_xor(nb, o, 64);
+      }
     }
-    if (lane == 0) dev[i] = acc;
+    if (score && l == 0) {
+      if (!ok) acc = __builtin_nanf("");
+      else if (cosine) acc = (na == 0.f || nb == 0.f) ? (na == nb ? 0.f : 1.f) : 1.0f - acc / (sqrtf(na) * sqrtf(nb));
+      dev[i] = acc;
+    }
   }
 }
 
@@ -457,13 +472,25 @@ hipError_t dev_scatter(const void* fresh, long ld_fresh, void* fk, void* fv, con
                        int n_cand, int n_tok, int row_elems, float* dev, int32_t* copy_sel, int32_t* copy_local,
                        int cosine, int bf16, hipStream_t s) {
   if (n_sel <= 0) return hipSuccess;
-  dim3 grid((n_sel + 3) / 4);
-  if (bf16)
-    hipLaunchKernelGGL(dev_scatter_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)fresh, ld_fresh,
-                       (bf16_t*)fk, (bf16_t*)fv, sel, n_sel, n_cand, n_tok, row_elems, dev, copy_sel, copy_local, cosine);
-  else
-    hipLaunchKernelGGL(dev_scatter_kernel<float>, grid, dim3(256), 0, s, (const float*)fresh, ld_fresh,
-                       (float*)fk, (float*)fv, sel, n_sel, n_cand, n_tok, row_elems, dev, copy_sel, copy_local, cosine);
+  // lanes per row: the row's 16-byte pieces, at most 64 (wider rows loop), at least 16
+  const int pieces = row_elems / (bf16 ? 8 : 4);
+  const int lpr = pieces >= 64 ? 64 : (pieces >= 32 ? 32 : 16);
+  if (row_elems % (bf16 ? 8 : 4) != 0) return hipErrorInvalidValue;
+  const int rows_per_wg = 4 * (64 / lpr);
+  dim3 grid((n_sel + rows_per_wg - 1) / rows_per_wg);
+#define CB_DEV_SCATTER(T, LPR)                                                                                 \
+  hipLaunchKernelGGL((dev_scatter_kernel<T, LPR>), grid, dim3(256), 0, s, (const T*)fresh, ld_fresh, (T*)fk, \
+                     (T*)fv, sel, n_sel, n_cand, n_tok, row_elems, dev, copy_sel, copy_local, cosine)
+  if (bf16) {
+    if (lpr == 64) CB_DEV_SCATTER(bf16_t, 64);
+    else if (lpr == 32) CB_DEV_SCATTER(bf16_t, 32);
+    else CB_DEV_SCATTER(bf16_t, 16);
+  } else {
+    if (lpr == 64) CB_DEV_SCATTER(float, 64);
+    else if (lpr == 32) CB_DEV_SCATTER(float, 32);
+    else CB_DEV_SCATTER(float, 16);
+  }
+#undef CB_DEV_SCATTER
   return hipGetLastError();
 }
 
