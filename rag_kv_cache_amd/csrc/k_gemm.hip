@@ -1029,43 +1029,54 @@ GemmCfg tile_by_model(int M, int N, int epi, long* workgroups) {
 //     split so that at most 256 workgroups run (64 rows: 15 against 20 us with 64 x 256); above,
 //     128 x 256 tiles, K split so that about 210 workgroups run;
 //   each split keeps at least two 64-wide K-steps and its partials fit the buffer.
-// Long reductions (K > 2048) over many rows (M >= 2048, N % 256 == 0): 128 x 256 or 256 x 256
-// tiles with K split 1..4 ways, the cheapest by the tile model (waves x t(cfg) per K-step x
-// K-steps per split) plus what the split costs: the reduce reads the s fp32 partial planes (and,
-// for the residual epilogue, the residual) and writes the output, about (s + 2) M N 4 + 2 M N
-// bytes at ~4 TB/s; an unsplit residual output is followed by its own RMSNorm pass, M N 6 bytes
-// at ~2.8 TB/s (the rates measured for those kernels on MI355X).  Llama-70B shape, 2714 rows:
-// the down-projection (K 28672) and the o-projection (K 8192) take 256 x 256 split 2, the
-// Q/K/V product 256 x 256 unsplit; at 16640 rows every product takes 256 x 256 unsplit.
-static GemmPlan long_reduction_plan(int M, int N, int K, int epi, long partial_cap_elems) {
-  struct Cand {
-    GemmCfg cfg;
-    int bm, bn;
-    float t;
-  };
-  constexpr Cand cands[] = {{GEMM_128x256, 128, 256, 1.13f}, {GEMM_256x256, 256, 256, 1.75f}};
+// Long reductions (K > 2048, N % 256 == 0): 128 x 128, 128 x 256 or 256 x 256 tiles with K
+// split 1..max_split ways, the cheapest by the tile model (waves x t(cfg) per K-step x K-steps
+// per split) plus what the split costs: the reduce reads the s fp32 partial planes (and, for the
+// residual epilogue, the residual) and writes the output, about (s + 2) M N 4 + 2 M N bytes at
+// ~4 TB/s; an unsplit residual output is followed by its own RMSNorm pass, M N 6 bytes at
+// ~2.8 TB/s (the rates measured for those kernels on MI355X).  Llama-70B shape, 2714 rows: the
+// down-projection (K 28672) and the o-projection (K 8192) take 256 x 256 split 2, the Q/K/V
+// product 256 x 256 unsplit; at 16640 rows every product takes 256 x 256 unsplit.
+struct LongCand {
+  GemmCfg cfg;
+  int bm, bn;
+  float t;
+};
+constexpr LongCand kLongCands[] = {{GEMM_128x128, 128, 128, 0.83f}, {GEMM_128x256, 128, 256, 1.13f},
+                                   {GEMM_256x256, 256, 256, 1.75f}};
+
+// Modelled microseconds of a long reduction with tile c split sp ways (see long_reduction_plan).
+static double long_reduction_cost(const LongCand& c, int sp, int M, int N, int K, int epi) {
   const int nk = K / 64;
   const double mn = (double)M * N;
+  const long tiles = (long)((M + c.bm - 1) / c.bm) * (N / c.bn);
+  double cost = (double)((tiles * sp + 255) / 256) * c.t * ((nk + sp - 1) / sp);
+  if (sp > 1) cost += ((sp + 2) * mn * 4 + mn * 2) / 4.0e6;  // the reduce at 4 TB/s
+  else if (epi == EPI_RESID) cost += mn * 6 / 2.8e6;        // the RMSNorm pass at 2.8 TB/s
+  return cost;
+}
+
+static GemmPlan long_reduction_plan(int M, int N, int K, int epi, long partial_cap_elems, int max_split,
+                                    double* cost_out) {
+  const int nk = K / 64;
   GemmPlan best{GEMM_128x256, 1};
   double best_cost = 1e300;
-  for (const Cand& c : cands) {
-    const long tiles = (long)((M + c.bm - 1) / c.bm) * (N / c.bn);
-    for (int sp = 1; sp <= 4; ++sp) {
+  for (const LongCand& c : kLongCands) {
+    if (N % c.bn) continue;
+    for (int sp = 1; sp <= max_split; ++sp) {
       if (sp > 1 && (nk / sp < 2 || (long)sp * M * N > partial_cap_elems)) break;
-      const double waves = (double)((tiles * sp + 255) / 256);
-      double cost = waves * c.t * ((nk + sp - 1) / sp);
-      if (sp > 1) cost += ((sp + 2) * mn * 4 + mn * 2) / 4.0e6;  // us at 4 TB/s
-      else if (epi == EPI_RESID) cost += mn * 6 / 2.8e6;
+      const double cost = long_reduction_cost(c, sp, M, N, K, epi);
       if (cost < best_cost) {
         best_cost = cost;
         best = GemmPlan{c.cfg, sp};
       }
     }
   }
+  if (cost_out) *cost_out = best_cost;
   return best;
 }
 
-GemmPlan gemm_plan(int M, int N, int K, int epi, long partial_cap_elems) {
+static GemmPlan gemm_plan_rule(int M, int N, int K, int epi, long partial_cap_elems) {
   GemmPlan p{GEMM_128x128, 1};
   if (M <= 4 && K % 32 == 0) {  // a few rows (decode): weight streaming on the vector ALUs
     p.cfg = GEMM_GEMV;
@@ -1080,7 +1091,7 @@ GemmPlan gemm_plan(int M, int N, int K, int epi, long partial_cap_elems) {
     p.cfg = tile_by_model(M, N, epi, &wgs);
     if (wgs >= 150) return p;
   } else if (M >= 2048 && N % 256 == 0) {
-    return long_reduction_plan(M, N, K, epi, partial_cap_elems);
+    return long_reduction_plan(M, N, K, epi, partial_cap_elems, 4, nullptr);
   }
   int bm = 128, bn = 128, target = 210;
   bool one_wave = false;  // split only as far as one wave of 256 workgroups
@@ -1102,12 +1113,28 @@ GemmPlan gemm_plan(int M, int N, int K, int epi, long partial_cap_elems) {
     bn = 256;
   }
   const int tiles = ((M + bm - 1) / bm) * (N / bn);
-  if (tiles >= target) return p;
-  const int nk = K / 64;
-  int sp = one_wave ? target / tiles : (target + tiles - 1) / tiles;
-  sp = sp > 8 ? 8 : (sp < 1 ? 1 : sp);
-  while (sp > 1 && (nk / sp < 2 || (long)sp * M * N > partial_cap_elems)) --sp;
-  p.splits = sp;
+  if (tiles < target) {
+    const int nk = K / 64;
+    int sp = one_wave ? target / tiles : (target + tiles - 1) / tiles;
+    sp = sp > 8 ? 8 : (sp < 1 ? 1 : sp);
+    while (sp > 1 && (nk / sp < 2 || (long)sp * M * N > partial_cap_elems)) --sp;
+    p.splits = sp;
+  }
+  return p;
+}
+
+// A long reduction over more than 320 and fewer than 2048 rows keeps the rule above unless the
+// cost model of long_reduction_plan (splits up to 8) predicts at least 10% less time (Llama-70B
+// shape at 870 rows: Q/K/V 256 x 256 split 3, down 256 x 256 split 2; Mistral-7B at 832 and 1024
+// rows: Q/K/V 128 x 256 unsplit, down 256 x 256 split 4; Yi-34B at 832: o and down 256 x 256
+// split 2); the Qwen shape's products keep the rule.
+GemmPlan gemm_plan(int M, int N, int K, int epi, long partial_cap_elems) {
+  const GemmPlan p = gemm_plan_rule(M, N, K, epi, partial_cap_elems);
+  if (epi == EPI_SWIGLU || p.cfg == GEMM_GEMV || K <= 2048 || M <= 320 || M >= 2048 || N % 256) return p;
+  double model = 0.0;
+  const GemmPlan q = long_reduction_plan(M, N, K, epi, partial_cap_elems, 8, &model);
+  for (const LongCand& c : kLongCands)
+    if (c.cfg == p.cfg && model < 0.9 * long_reduction_cost(c, p.splits, M, N, K, epi)) return q;
   return p;
 }
 
