@@ -154,6 +154,24 @@ def kernel_table(eng, prof_steps, attn_work, pcie_peak):
     return kernels
 
 
+def mfma_busy_from_profiles(workload):
+    """{kernel name: MFMA-busy share of SIMD cycles} over one step's launches of each product and
+    of the attention, from the committed rocprofv3 counter summary
+    profiles/mfma_busy_by_kernel_<workload>.txt, or {} if it is missing or was taken on other
+    kernel sources."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"mfma_busy_by_kernel_{workload}.txt")
+    if not os.path.exists(path):
+        return {}
+    text = open(path).read()
+    for src, digest in re.findall(r"source_sha256 (\S+): ([0-9a-f]{64})", text):
+        p = os.path.join(ROOT, src)
+        if not os.path.exists(p) or hashlib.sha256(open(p, "rb").read()).hexdigest() != digest:
+            return {}
+    return {k: float(v) for k, v in re.findall(r"^(\w+): last \d+ dispatches: .*?mfma_busy ([\d.]+)", text, re.M)}
+
+
 def traffic_from_profiles(kernel, workload, launches_per_step):
     """HBM bytes per launch of `kernel` averaged over one step of `workload`, from the committed
     rocprofv3 counter summary profiles/<kernel>_<workload>_traffic.txt (FETCH_SIZE and WRITE_SIZE
@@ -965,6 +983,9 @@ def main() -> int:
     ap.add_argument("--config", default="l70_16k", help="workload of the headline line (fixtures.CONFIGS)")
     ap.add_argument("--only-headline", action="store_true",
                     help="only the headline prompt's timed steps and kernel profile (profiling runs)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="the headline workload only (with its overlap, HBM-resident and full-recompute passes), "
+                         "no other configurations")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--fetch", choices=("auto", "kernel", "copy"), default="auto",
@@ -990,9 +1011,10 @@ def main() -> int:
         roofline = {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"],
                     "unit": dk["unit"], "frac": dk["frac"],
                     "traffic": traffic_from_profiles(dom, wl.name, dk["launches_per_step"]),
+                    "mfma_busy_counter": mfma_busy_from_profiles(wl.name).get(dom),
                     "work_per_launch": dk["work_per_launch"], "us_per_launch": dk["us_per_launch"]}
     extra = {}
-    if not args.only_headline:
+    if not args.only_headline and not args.no_extras:
         def guarded(fn, *a, **kw):
             try:
                 return fn(*a, **kw)
@@ -1016,6 +1038,7 @@ def main() -> int:
         log(f"cpu oracle: {cpu['value']:.2f} context tokens/s on {cpu['cores']} threads")
 
     value = head["context_tokens_per_s"]
+    busy = mfma_busy_from_profiles(wl.name)
     out = {
         "metric": "blended-prefill context tokens/s @ r=15% + per-layer ms; % HBM/MFMA peak",
         "value": value, "unit": "context tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -1032,7 +1055,15 @@ def main() -> int:
         "t_blend_ms": head["t_blend_ms"],
         "per_layer_ms": head["per_layer_ms"],
         "kept_rows_per_layer": head["kept_rows_per_layer"],
-        "kernels": {k: {kk: vv for kk, vv in v.items() if kk != "work_per_launch"} for k, v in kernels.items()},
+        "kernels": {k: dict({kk: vv for kk, vv in v.items() if kk != "work_per_launch"},
+                            **({"mfma_busy_counter": busy[k]} if k in busy else {})) for k, v in kernels.items()},
+        "mfma_busy_counter": busy or None,
+        "mfma_busy_note": ("mfma_busy_counter: share of SIMD cycles the MFMA pipe is busy over one step's launches "
+                           "of each GEMM epilogue and of the attention (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES / "
+                           "(GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs), profiles/mfma_busy_by_kernel_<workload>.txt; "
+                           "gemm_kv_q holds the K/V and Q products, gemm_o_down the o- and down-projections); frac "
+                           "is the event-timed rate against the 2.5 PFLOP/s peak at 2.4 GHz, so busy / frac ~ "
+                           "2.4 GHz / the clock the chip holds"),
         "headline_detail": {k: v for k, v in head.items()
                             if k not in ("kernels", "t_blend_ms", "per_layer_ms", "kept_rows_per_layer")},
         "l70_4k": other,

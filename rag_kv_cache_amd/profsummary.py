@@ -112,7 +112,7 @@ def _dispatch_counters(path: str, kernel_re: str):
     return out
 
 
-def counters(paths, kernel_re: str, cus: int, last: int, xcds: int = 8) -> str:
+def counters(paths, kernel_re: str, cus: int, last: int, xcds: int = 8, label: str = "") -> str:
     runs = [_dispatch_counters(p, kernel_re) for p in paths]
     groups = defaultdict(lambda: defaultdict(list))
     for run in runs:
@@ -148,8 +148,8 @@ def counters(paths, kernel_re: str, cus: int, last: int, xcds: int = 8) -> str:
             dids = sorted(run)[-last:]
             for cn in {c for d in dids for c in run[d][2]}:
                 m[cn] = statistics.mean(run[d][2].get(cn, 0.0) for d in dids)
-        lines.append(f"last {last} dispatches: " + ", ".join(f"{c} {m[c]:.0f}" for c in sorted(m))
-                     + (f"; {derived(m)}" if derived(m) else ""))
+        lines.append((f"{label}: " if label else "") + f"last {last} dispatches: "
+                     + ", ".join(f"{c} {m[c]:.0f}" for c in sorted(m)) + (f"; {derived(m)}" if derived(m) else ""))
     return "\n".join(lines)
 
 
@@ -192,6 +192,8 @@ def main() -> int:
     c.add_argument("--cus", type=int, default=256)
     c.add_argument("--xcds", type=int, default=8)
     c.add_argument("--last", type=int, default=0)
+    c.add_argument("--label", default="", help="name printed before the --last line")
+    c.add_argument("--only-last", action="store_true", help="print only the --last line")
     for p in (t, x, c):
         p.add_argument("--command", action="append", default=[])
         p.add_argument("--note", default="")
@@ -206,7 +208,8 @@ def main() -> int:
             nl, first, cnt = (int(v) for v in a.steps.split(","))
             text += "\n" + step_kernels(a.db, nl, first, cnt) + "\n"
     elif a.cmd == "counters":
-        text += counters(a.dbs, a.kernel, a.cus, a.last, a.xcds) + "\n"
+        out = counters(a.dbs, a.kernel, a.cus, a.last, a.xcds, a.label)
+        text += (out.splitlines()[-1] if a.only_last else out) + "\n"
     else:
         for src in a.source:
             text += f"source_sha256 {src}: {hashlib.sha256(open(src, 'rb').read()).hexdigest()}\n"
