@@ -955,7 +955,11 @@ hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
       if constexpr (EPI == EPI_SWIGLU) { e = launch_dma<128, 512, 2, 4, 2, EPI, BT>(g, s); break; }
       return hipErrorInvalidValue;
     case GEMM_256x256:  // fp32 outputs (residual, split-K partials) staged in row halves
-      e = launch_dma<256, 256, 2, 4, 2, EPI, BT>(g, s);
+      // sixteen wavefronts (four per SIMD, 64 x 64 each) hide more of the operand-load latency
+      // than eight (128 x 64 each: 2-8% slower on the FFN products); the RoPE epilogue and the
+      // int8 weight path need the eight-wavefront register budget
+      if constexpr (EPI != EPI_ROPE && BT == 0) e = launch_dma<256, 256, 4, 4, 2, EPI, BT>(g, s);
+      else e = launch_dma<256, 256, 2, 4, 2, EPI, BT>(g, s);
       break;
     case GEMM_128x256: e = launch_dma<128, 256, 2, 4, 3, EPI, BT>(g, s); break;
     case GEMM_64x256: e = launch_dma<64, 256, 1, 4, 3, EPI, BT>(g, s); break;
