@@ -146,9 +146,10 @@ cb_status cb_embed(cb_ctx* ctx, const int32_t* tokens, int32_t n, const void* ta
  * host memory that kernels can read at the same address (hipHostMalloc, torch's pinned
  * tensors), one kernel on the copy stream reads the rows over PCIe, rotates K and writes K and
  * V into the fused buffers (one pass, no per-chunk copy commands); other pointers fall back to
- * the copy engine.  CB_FETCH_COPY: always the copy engine (hipMemcpyAsync per chunk), then the
- * rotation in place.  CB_FETCH_AUTO (default): the copy engine when a chunk's K (or V) averages
- * at least 1 MiB, else as CB_FETCH_KERNEL.  The fetch kernel loads faster when the per-copy
+ * the copy engine.  CB_FETCH_COPY: always the copy engine, then the rotation in place; chunks
+ * whose host rows follow one another (host_k[c + 1] starts where chunk c's K rows end, and the
+ * same for V) go as one hipMemcpyAsync per run of such chunks.  CB_FETCH_AUTO (default): the
+ * copy engine when those copies average at least 1 MiB, else as CB_FETCH_KERNEL.  The fetch kernel loads faster when the per-copy
  * cost of the copy engine dominates (small chunks: a load-bound layer), but it holds CUs that
  * the compute stream's kernels then lack; large copies amortize that cost, and the copy engine
  * leaves every CU to compute (measured on MI355X: 256 KiB chunks load at about 16 GB/s through
@@ -396,10 +397,13 @@ cb_status cb_chunk_key(const int32_t* tokens, int32_t n, const uint64_t* prior, 
 typedef struct cb_store cb_store;
 
 /* A store of n_slots chunks of at most max_chunk_tokens tokens for the model desc (its
- * n_layers, n_kv_heads, head_dim, dtype).  One slot holds, per layer, K then V, each
- * [max_chunk_tokens][n_kv_heads][head_dim] of dtype; the arena of n_slots slots is allocated
- * once, pinned (hipHostMalloc, pinned != 0; the form cb_fetch_layer copies from without a
- * staging copy) or pageable (malloc).  The index is open addressing with linear probing over
+ * n_layers, n_kv_heads, head_dim, dtype).  One slot holds, per layer, K and V, each
+ * [max_chunk_tokens][n_kv_heads][head_dim] of dtype.  The arena is layer-major: for each layer,
+ * the K rows of slots 0 .. n_slots - 1 back to back, then their V rows, so that full-length
+ * entries in consecutive slots (a producer's chunks, filled in order) are one contiguous range
+ * per layer, which cb_fetch_layer moves in one copy.  It is allocated once, pinned
+ * (hipHostMalloc, pinned != 0; the form cb_fetch_layer copies from without a staging copy) or
+ * pageable (malloc).  The index is open addressing with linear probing over
  * n_slots * 5/4 + 1 buckets of 16 bytes (key, slot), kept at most 80% full; deletion moves
  * later buckets back (no tombstones).  CB_EINVAL for non-positive sizes, CB_ENOMEM when the
  * arena cannot be allocated. */

@@ -447,9 +447,18 @@ cb_status cb_fetch_layer(cb_ctx* c, int32_t layer, const void* const* host_k, co
   const size_t row = (size_t)c->d.n_kv_heads * c->d.head_dim * c->esize();
   for (int ch = 0; ch < n_chunks; ++ch)
     if (offs[ch + 1] > offs[ch] && (!host_k[ch] || !host_v[ch])) return fail(CB_EINVAL, "chunk %d host pointer NULL", ch);
+  // runs of chunks whose K rows, and whose V rows, follow one another in host memory: the
+  // fused rows of consecutive chunks are adjacent too, so a run is one copy each for K and V
+  std::vector<int> run_end;  // chunk index one past each run
+  for (int ch = 0; ch < n_chunks; ++ch) {
+    const size_t bytes = (size_t)(offs[ch + 1] - offs[ch]) * row;
+    const bool joins = ch + 1 < n_chunks && (const char*)host_k[ch] + bytes == (const char*)host_k[ch + 1] &&
+                       (const char*)host_v[ch] + bytes == (const char*)host_v[ch + 1];
+    if (!joins) run_end.push_back(ch + 1);
+  }
   bool direct = c->fetch_mode == CB_FETCH_KERNEL;
   if (c->fetch_mode == CB_FETCH_AUTO && n_chunks > 0)  // see cb_set_fetch_mode
-    direct = (size_t)offs[n_chunks] * row / (size_t)n_chunks < kFetchCopyMinBytes;
+    direct = (size_t)offs[n_chunks] * row / run_end.size() < kFetchCopyMinBytes;
   for (int ch = 0; direct && ch < n_chunks; ++ch)
     if (offs[ch + 1] > offs[ch] && !(kernel_readable_host(host_k[ch]) && kernel_readable_host(host_v[ch])))
       direct = false;
@@ -475,8 +484,8 @@ cb_status cb_fetch_layer(cb_ctx* c, int32_t layer, const void* const* host_k, co
     c->state[layer] = LS_FETCHED;
     return CB_OK;
   }
-  for (int ch = 0; ch < n_chunks; ++ch) {
-    const size_t bytes = (size_t)(offs[ch + 1] - offs[ch]) * row;
+  for (size_t r = 0, ch = 0; r < run_end.size(); ch = run_end[r++]) {
+    const size_t bytes = (size_t)(offs[run_end[r]] - offs[ch]) * row;
     if (!bytes) continue;
     hipError_t e = hipMemcpyAsync((char*)fused_k + (size_t)offs[ch] * row, host_k[ch], bytes, hipMemcpyHostToDevice, c->xs);
     if (e == hipSuccess)

@@ -440,12 +440,21 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
   } else {
     constexpr int OW = EPI == EPI_SWIGLU ? BN / 2 : BN;  // output columns of the tile
     constexpr int PB = OW * 2 + 16;                      // bf16 staging row pitch (bytes)
-    // RoPE: positions of this lane's rows, then the cos/sin of each of its column pairs (heads
-    // are 128 wide on the bf16 path; a pair's first column is dim < 64 of its head), loaded
-    // before any use so that the loads overlap.
-    constexpr int NR = EPI == EPI_ROPE ? FM * 4 : 1, NP = EPI == EPI_ROPE ? FM * (FN / 2) * 4 : 1;
+    // RoPE: positions of this lane's rows up front; the cos/sin of its column pairs (heads are
+    // 128 wide on the bf16 path; a pair's first column is dim < 64 of its head) one 16-row block
+    // ahead of their use, in two register sets, so that the loads overlap the rotation of the
+    // previous block without holding the whole tile's factors at once.
+    constexpr int NR = EPI == EPI_ROPE ? FM * 4 : 1, NP = EPI == EPI_ROPE ? (FN / 2) * 4 : 1;
     int prow[NR];
-    float2 cs[NP];
+    float2 cs[2][NP];
+    auto load_cs = [&](int i, float2 (&c)[NP]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int q = 0; q < FN / 2; ++q) {
+        const int n_a = logical_col<EPI, BN>(g, tn, wn * WTN + q * 32 + (lane & 15));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) c[q * 4 + r] = g.rope[prow[i * 4 + r] + (n_a & 127)];
+      }
+    };
     if (EPI == EPI_ROPE) {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -456,17 +465,11 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
           const int p = g.pos[m];
           prow[i * 4 + r] = (p < 0 ? 0 : (p > g.max_pos ? g.max_pos : p)) * 64;
         }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int q = 0; q < FN / 2; ++q) {
-          const int n_a = logical_col<EPI, BN>(g, tn, wn * WTN + q * 32 + (lane & 15));
-#pragma unroll
-          for (int r = 0; r < 4; ++r) cs[(i * (FN / 2) + q) * 4 + r] = g.rope[prow[i * 4 + r] + (n_a & 127)];
-        }
+      load_cs(0, cs[0]);
     }
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
+      if (EPI == EPI_ROPE && i + 1 < FM) load_cs(i + 1, cs[(i + 1) & 1]);
 #pragma unroll
       for (int q = 0; q < FN / 2; ++q) {
         const int tc = wn * WTN + q * 32 + (lane & 15);
@@ -481,7 +484,7 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
             *reinterpret_cast<bf16_t*>(row + la * 2) = f32_to_bf16(silu(va) * vb);
           } else {
             if (rot) {
-              const float2 t = cs[(i * (FN / 2) + q) * 4 + r];
+              const float2 t = cs[i & 1][q * 4 + r];
               const float ya = va * t.x - vb * t.y;
               vb = vb * t.x + va * t.y;
               va = ya;
@@ -491,6 +494,8 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
           }
         }
       }
+      if (EPI == EPI_ROPE) __builtin_amdgcn_sched_barrier(0);  // keep the next block's loads here
+    }
     barrier();
     constexpr int CPR = OW / 8;
     const int colbase = EPI == EPI_SWIGLU ? tn * (BN / 2) : tn * BN;
@@ -956,9 +961,9 @@ hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
       return hipErrorInvalidValue;
     case GEMM_256x256:  // fp32 outputs (residual, split-K partials) staged in row halves
       // sixteen wavefronts (four per SIMD, 64 x 64 each) hide more of the operand-load latency
-      // than eight (128 x 64 each: 2-8% slower on the FFN products); the RoPE epilogue and the
-      // int8 weight path need the eight-wavefront register budget
-      if constexpr (EPI != EPI_ROPE && BT == 0) e = launch_dma<256, 256, 4, 4, 2, EPI, BT>(g, s);
+      // than eight (128 x 64 each: 2-8% slower on the FFN products); the int8 weight path needs
+      // the eight-wavefront register budget
+      if constexpr (BT == 0) e = launch_dma<256, 256, 4, 4, 2, EPI, BT>(g, s);
       else e = launch_dma<256, 256, 2, 4, 2, EPI, BT>(g, s);
       break;
     case GEMM_128x256: e = launch_dma<128, 256, 2, 4, 3, EPI, BT>(g, s); break;

@@ -1,7 +1,8 @@
 // Host-side chunk KV store: 64-bit SHA-256 keys of chunk token ids, an open-addressing index
 // of 16-byte buckets in host memory, fixed-size entries in a (pinned) host arena holding every
-// layer's K and V of one chunk prefilled alone at positions 0.., and least-recently-used
-// eviction of entries that no caller holds.
+// layer's K and V of one chunk prefilled alone at positions 0.. (layer-major, so that the
+// entries of consecutive slots are adjacent within a layer), and least-recently-used eviction
+// of entries that no caller holds.
 //
 // Pages: CacheBlend explainer, integration with vLLM (a CPU-memory hash table, about 16 MB per
 // million chunks, locates each chunk's KV); KVBoost article, dual hash keys (content key from
@@ -388,9 +389,11 @@ cb_status cb_store_layer(cb_store* s, int32_t slot, int32_t layer, void** host_k
   std::lock_guard<std::mutex> g(s->mu);
   if (slot < 0 || slot >= s->n_slots || !s->e[slot].used) return cbi_fail(CB_EINVAL, "slot %d not in use", slot);
   if (layer < 0 || layer >= s->n_layers) return cbi_fail(CB_EINVAL, "layer %d outside [0, %d)", layer, s->n_layers);
-  unsigned char* base = s->arena + (size_t)slot * s->slot_bytes + (size_t)layer * 2 * s->layer_bytes;
+  // layer-major: [layer][K, V][slot][max_chunk_tokens rows]
+  const size_t plane = (size_t)s->n_slots * s->layer_bytes;
+  unsigned char* base = s->arena + (size_t)layer * 2 * plane + (size_t)slot * s->layer_bytes;
   if (host_k) *host_k = base;
-  if (host_v) *host_v = base + s->layer_bytes;
+  if (host_v) *host_v = base + plane;
   if (n_tokens) *n_tokens = s->e[slot].len;
   return CB_OK;
 }

@@ -111,7 +111,9 @@ def test_prefetch_path_equals_hbm_path():
     copied by the copy engine and rotated in place, or from pageable
     memory, which falls back to the copy engine), the HBM-resident cache re-rotated by copy on
     the copy stream, and re-rotated inside each cb_blend_layer, all give bit-identical results
-    to the HBM-resident cache re-rotated for every layer in one launch (cb_rotate_layers)."""
+    to the HBM-resident cache re-rotated for every layer in one launch (cb_rotate_layers).  The
+    copy-engine case also runs with chunks adjacent in host memory (one copy per run)."""
+    import torch
     from rag_kv_cache_amd.pipeline import build_chunk_caches, make_buffers, run_layers
     cfg = "small_bf16"
     wl = F.get_config(cfg)
@@ -121,18 +123,33 @@ def test_prefetch_path_equals_hbm_path():
     cache, host = build_chunk_caches(eng, chunks, pinned_host=True)
     pageable = [[(k.clone(), v.clone()) for k, v in layer] for layer in host]  # not page-locked
     assert not pageable[0][0][0].is_pinned()
+    # chunks adjacent in host memory (as consecutive chunk-store entries are): the copy path moves
+    # each run of adjacent chunks in one copy; here chunks 0-1 form one run and the rest another
+    runs = []
+    for layer in host:
+        n0 = layer[0][0].shape[0] + layer[1][0].shape[0]
+        kk = [torch.cat([k for k, _ in layer[:2]]).pin_memory(), torch.cat([k for k, _ in layer[2:]]).pin_memory()]
+        vv = [torch.cat([v for _, v in layer[:2]]).pin_memory(), torch.cat([v for _, v in layer[2:]]).pin_memory()]
+        row, out = 0, []
+        for c, (k, _) in enumerate(layer):
+            part = 0 if c < 2 else 1
+            r0 = row if c < 2 else row - n0
+            out.append((kk[part][r0: r0 + k.shape[0]], vv[part][r0: r0 + k.shape[0]]))
+            row += k.shape[0]
+        runs.append(out)
+    assert runs[0][1][0].data_ptr() == runs[0][0][0].data_ptr() + runs[0][0][0].numel() * runs[0][0][0].element_size()
     outs = []
     shapes = {"prefetch_3x192x2": (3, 192, 2), "prefetch_1x64x1": (1, 64, 1), "prefetch_40x1024x4": (40, 1024, 4)}
-    for mode in ("hbm", "prefetch", "prefetch_copy", "prefetch_pageable", "hbm_copy_stream", "hbm_per_layer",
-                 *shapes):
+    for mode in ("hbm", "prefetch", "prefetch_copy", "prefetch_copy_runs", "prefetch_pageable", "hbm_copy_stream",
+                 "hbm_per_layer", *shapes):
         buf = make_buffers(eng, wl.n_tokens, len(chunks))
         fused = fused_buffers(eng, wl.n_tokens)
         pre = mode.startswith("prefetch")
-        L.cb_set_fetch_mode(eng.ctx, L.CB_FETCH_COPY if mode == "prefetch_copy" else L.CB_FETCH_KERNEL)
+        L.cb_set_fetch_mode(eng.ctx, L.CB_FETCH_COPY if mode.startswith("prefetch_copy") else L.CB_FETCH_KERNEL)
         L.cb_set_fetch_launch(eng.ctx, *shapes.get(mode, (0, 0, 0)))
+        hc = {"prefetch_pageable": pageable, "prefetch_copy_runs": runs}.get(mode, host)
         res = run_layers(eng, buf, F.all_tokens(wl), F.chunk_offsets(wl), wl.n_query, wl.schedule, fused,
-                         cache=None if pre else cache,
-                         host_cache=(pageable if mode == "prefetch_pageable" else host) if pre else None,
+                         cache=None if pre else cache, host_cache=hc if pre else None,
                          rotate_on_copy_stream=mode == "hbm_copy_stream", batch_rotation=mode != "hbm_per_layer")
         eng.compute.synchronize()
         L.cb_set_fetch_mode(eng.ctx, L.CB_FETCH_KERNEL)

@@ -185,14 +185,19 @@ def test_arena_layout(make_store):
     row = n_kv * hd * 4
     slots = [L.cb_store_insert(s, [10 + i] * (i + 1))[0] for i in range(3)]
     addr = {}
+    n_slots = 3
     for sl in slots:
         for l in range(n_layers):
             k, v, n = L.cb_store_layer(s, sl, l)
-            assert n == sl + 1 and v - k == max_tok * row
+            assert n == sl + 1 and v - k == n_slots * max_tok * row
             addr[(sl, l)] = (k, v)
+    # layer-major: per layer the K rows of every slot back to back, then their V rows, so that
+    # consecutive slots' entries of one layer are adjacent (one copy for a run of them)
     base = addr[(0, 0)][0]
     for (sl, l), (k, v) in addr.items():
-        assert k - base == (sl * n_layers + l) * 2 * max_tok * row
+        assert k - base == (l * 2 * n_slots + sl) * max_tok * row
+        if sl + 1 < n_slots:
+            assert addr[(sl + 1, l)][0] - k == max_tok * row and addr[(sl + 1, l)][1] - v == max_tok * row
     # bytes written through one entry's pointers stay where they were put
     for (sl, l), (k, v) in addr.items():
         ctypes.memmove(k, bytes([sl * 16 + l * 2]) * (max_tok * row), max_tok * row)
