@@ -337,11 +337,21 @@ def run_controller(eng, buf, tokens, offs, wl, fused, host, full_ms, overlap, st
     at the ratio it plans (layer 1 stays at 1):
       * cb_plan_ratio (the explainer's model): the load bandwidth of a whole step's cached KV
         fetched alone, and the full prefill split evenly over the layers and tokens;
-      * cb_plan_ratio_measured: a layer's load time from the per-layer fetch measurement, and a
+      * cb_plan_ratio_measured: a layer's load time from the per-layer fetch measurement, a
         layer's recompute time measured at ratio 1 (every row) and at ratio 0 (no context row:
-        the fixed part), layer 1 counted at its own measured time.
+        the fixed part), the first layer at its time in the pipelined run, the first filtering
+        layer's extra cost (scoring every context row) measured at ratio 0, and the contention
+        of a fetch running beside the compute: the excess of each layer (after the first two)
+        over max(T_load, T_recompute), summed, over the summed min(T_load, T_recompute).  The
+        contention depends on the operating point (a compute-bound pipeline lets the copy
+        stream run ahead and finish early, a balanced one keeps the fetch beside every layer),
+        so it is taken first from the workload's pipelined run, then once more from one
+        pipelined run at the planned ratio (a calibration run, not one of the timed runs), and
+        the plan is made again with it and with the recompute line redrawn through the time
+        measured there.
     Both with a ratio floor of 5% (below the workload's 15%, so that the plan is not just the
-    floor) and no ceiling."""
+    floor) and no ceiling; each plan's prefill is timed alone, like the headline (events from the
+    first fetch enqueue to the last layer's end, median of the runs)."""
     import torch
     from rag_kv_cache_amd import _lib as L
     from rag_kv_cache_amd.pipeline import run_layers
@@ -366,15 +376,16 @@ def run_controller(eng, buf, tokens, offs, wl, fused, host, full_ms, overlap, st
         sched = [1.0] + [float(plan.ratio) if plan.load else 1.0] * (nl - 1)
         kw = dict(host_cache=host) if plan.load else dict(cache=None)
         n = max(3, steps // 2)
+        ms = []
         for r in range(n + 2):
-            if r == 2:
-                eng.compute.synchronize()
-                torch.cuda.synchronize()
-                t0 = time.perf_counter()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(eng.copy)
             run_layers(eng, buf, tokens, offs, wl.n_query, sched, fused, upload_inputs=False, **kw)
-        eng.compute.synchronize()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / n * 1e3
+            e1.record(eng.compute)
+            torch.cuda.synchronize()
+            if r >= 2:
+                ms.append(e0.elapsed_time(e1))
+        return float(np.median(ms))
 
     def summary(plan, ms):
         return {"load": bool(plan.load), "ratio": round(float(plan.ratio), 4),
@@ -393,24 +404,67 @@ def run_controller(eng, buf, tokens, offs, wl, fused, host, full_ms, overlap, st
     # the measured model (the fused buffers hold every layer's re-rotated cache after a fetch pass)
     t_full = layer_times([1.0] * nl)
     t_zero = layer_times([1.0] + [0.0] * (nl - 1))
-    t_first = float(t_full[0])
     t_full_l = float(np.median(t_full[1:]))
     t_fixed_l = min(float(np.median(t_zero[2:])), t_full_l)
+    t_select = max(0.0, float(t_zero[1]) - t_fixed_l)
     t_load_l = float(np.median(overlap["t_load_ms"])) * 1e-3
-    meas = L.cb_plan_ratio_measured(nl, kv_layer, kv_layer / t_load_l, 0.0, t_first, t_full_l, t_fixed_l, r_min, r_max)
+    def contention_of(t_ov, t_rec):
+        tl_ = np.array(overlap["t_load_ms"][2:]) * 1e-3
+        tr_, to_ = np.asarray(t_rec[2:]), np.asarray(t_ov[2:])
+        return float(np.maximum(to_ - np.maximum(tl_, tr_), 0.0).sum() / np.minimum(tl_, tr_).sum())
+
+    contention0 = contention_of(np.array(overlap["t_overlapped_ms"]) * 1e-3, np.array(overlap["t_recompute_ms"]) * 1e-3)
+    t_first = float(overlap["t_overlapped_ms"][0]) * 1e-3  # the pipelined first layer (waits for fetches)
+
+    def plan(k, t_fix):
+        return L.cb_plan_ratio_measured(nl, kv_layer, kv_layer / t_load_l, 0.0, t_first, t_full_l, t_fix, r_min,
+                                        r_max, t_select_layer=t_select, contention=k)
+
+    meas = plan(contention0, t_fixed_l)
+    contention, t_fixed_c, calib = contention0, t_fixed_l, None
+    if meas.load:
+        # calibration at the planned ratio r0: per-layer times pipelined and alone give the
+        # contention there, and the recompute line is redrawn through (r0, T_recompute alone)
+        # and (1, t_full) (small ratios cost more than the line from ratio 0: tile rounding of
+        # the few kept rows); then the plan is made again
+        r0 = float(meas.ratio)
+        sched = [1.0] + [r0] * (nl - 1)
+        t_alone = layer_times(sched)
+        rows = []
+        for r in range(3):
+            evs = []
+            run_layers(eng, buf, tokens, offs, wl.n_query, sched, fused, upload_inputs=False, host_cache=host,
+                       layer_events=evs)
+            eng.compute.synchronize()
+            rows.append([evs[i].elapsed_time(evs[i + 1]) for i in range(nl)])
+        t_pipe = np.median(np.array(rows), axis=0) * 1e-3
+        contention = contention_of(t_pipe, t_alone)
+        t_r0 = float(np.median(t_alone[2:]))
+        if r0 < 1.0 and t_r0 < t_full_l:
+            t_fixed_c = max(0.0, t_r0 - r0 * (t_full_l - t_r0) / (1.0 - r0))
+        meas = plan(contention, t_fixed_c)
+        calib = {"ratio": round(r0, 4), "t_recompute_alone_median_ms": round(t_r0 * 1e3, 4),
+                 "t_layer_pipelined_median_ms": round(float(np.median(t_pipe[2:])) * 1e3, 4),
+                 "sum_pipelined_ms": round(float(t_pipe.sum()) * 1e3, 4),
+                 "t_fixed_layer_redrawn_ms": round(t_fixed_c * 1e3, 4)}
     meas_ms = run_plan(meas)
     log(f"controller (even split): load {bw / 1e9:.1f} GB/s, ratio {even.ratio:.3f}, predicted "
         f"{even.t_total * 1e3:.3f} ms, measured {even_ms:.3f} ms/step")
-    log(f"controller (measured layer times: first {t_first * 1e3:.3f}, full {t_full_l * 1e3:.3f}, fixed "
-        f"{t_fixed_l * 1e3:.3f}, load {t_load_l * 1e3:.3f} ms): ratio {meas.ratio:.3f} (load={meas.load}), "
-        f"predicted {meas.t_total * 1e3:.3f} ms, measured {meas_ms:.3f} ms/step")
+    log(f"controller (measured layer times: first {t_first * 1e3:.3f}, first filter +{t_select * 1e3:.3f}, full "
+        f"{t_full_l * 1e3:.3f}, fixed {t_fixed_l * 1e3:.3f}, load {t_load_l * 1e3:.3f} ms, contention "
+        f"{contention0:.3f} at the workload's ratio, {contention:.3f} at the plan's): ratio {meas.ratio:.3f} "
+        f"(load={meas.load}), predicted {meas.t_total * 1e3:.3f} ms, measured {meas_ms:.3f} ms/step")
     return {"r_min": r_min, "r_max": r_max,
             "even_split": dict(summary(even, even_ms), load_bandwidth_GBps=round(bw / 1e9, 2),
                                prefill_us_per_token=round(pre * 1e6, 4)),
             "measured_layers": dict(summary(meas, meas_ms), t_first_ms=round(t_first * 1e3, 4),
-                                    t_full_layer_ms=round(t_full_l * 1e3, 4),
-                                    t_fixed_layer_ms=round(t_fixed_l * 1e3, 4)),
-            "schedule": "1.0, then the planned ratio (pinned-host cache fetched two layers ahead; eager launches)"}
+                                    t_select_ms=round(t_select * 1e3, 4), t_full_layer_ms=round(t_full_l * 1e3, 4),
+                                    t_fixed_layer_ms=round(t_fixed_l * 1e3, 4),
+                                    contention_workload_ratio=round(contention0, 4), contention=round(contention, 4),
+                                    calibration_at_plan=calib,
+                                    prediction_error=round(meas.t_total * 1e3 / meas_ms - 1, 4)),
+            "schedule": "1.0, then the planned ratio (pinned-host cache fetched two layers ahead; eager launches; "
+                        "each prefill timed alone)"}
 
 
 def _fetch_layer(eng, buf, host, offs, l, fused):
@@ -753,7 +807,7 @@ def run_qwen(args):
     import torch
     import fixtures as F
     from rag_kv_cache_amd import _lib as L
-    from rag_kv_cache_amd.pipeline import Engine, build_chunk_caches, make_buffers, run_layers
+    from rag_kv_cache_amd.pipeline import ChunkStore, Engine, build_chunk_caches, make_buffers, produce_chunks, run_layers
     wl = F.get_config("qwen")
     sh = wl.shape
     chunks = F.chunk_tokens(wl)
@@ -764,7 +818,13 @@ def run_qwen(args):
     for l in range(sh.n_layers):
         eng.load_layer(l, F.layer_weights(sh, l + 1))
     eng.load_embedding(F.embedding(sh))
-    cache, host = build_chunk_caches(eng, chunks, pinned_host=True)
+    cache, _ = build_chunk_caches(eng, chunks)
+    # the pinned-host cache is the chunk store's arena, filled by the chunk producer (consecutive
+    # slots, so each layer's chunks are adjacent and fetched in one copy per tensor)
+    hstore = ChunkStore(eng, max(wl.chunk_lens), len(chunks) + 2, pinned=True)
+    produce_chunks(eng, hstore, chunks)
+    hslots = hstore.lookup_prompt(chunks, hold=True)
+    host = hstore.host_cache(hslots)
     buf = make_buffers(eng, n_tok + DECODE_ROWS, len(chunks))
     fused = [(eng.kv_empty(n_tok + DECODE_ROWS), eng.kv_empty(n_tok + DECODE_ROWS)) for _ in range(sh.n_layers)]
     cs = eng.compute
@@ -836,6 +896,9 @@ def run_qwen(args):
     out["decode"] = run_decode(eng, buf, tokens, offs, wl, fused, cache)
     out["chunk_store"] = run_store(eng, buf, tokens, offs, wl, fused, args.steps)
     out["peaks_measured"] = run_peaks(eng)
+    for sl in hslots:
+        hstore.release(sl)
+    hstore.close()
     eng.close()
     del eng, cache, host, buf, fused
     torch.cuda.empty_cache()

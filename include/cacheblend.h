@@ -364,17 +364,24 @@ cb_status cb_plan_ratio(int32_t n_ctx, int32_t n_layers, double kv_bytes_per_tok
  * t_fixed_layer), where t_full_layer is a layer recomputing every row and t_fixed_layer a layer
  * recomputing none (query rows, attention over the cache, fixed kernel costs); t_fixed_layer = 0
  * is the explainer's linear model.  Per layer T_load = kv_bytes_layer / bandwidth +
- * latency_layer_s.  Loading pays when max(T_load, T_recompute(r_min)) < t_full_layer; then
- * ratio = (T_load - t_fixed_layer) / (t_full_layer - t_fixed_layer) clamped to [r_min, r_max]
- * and T_layer = max(T_load, T_recompute(ratio)); otherwise load = 0, ratio = 1, T_layer =
- * t_full_layer, t_load_layer = 0.  The first layer recomputes every row in either case:
- * t_total = t_first_layer + (n_layers - 1) * T_layer.  break_even_bandwidth =
- * kv_bytes_layer / t_full_layer.  CB_EINVAL for non-positive sizes, bandwidth or t_full_layer,
- * negative latency or t_first_layer, t_fixed_layer outside [0, t_full_layer], or ratios outside
- * 0 <= r_min <= r_max <= 1. */
+ * latency_layer_s.  The fetch and the compute running side by side slow each other: the
+ * longer of the two is stretched by `contention` seconds per second of overlap with the other
+ * (measured; 0 is the review's max(T_load, T_recompute)): T_layer(r) = max(T_load,
+ * T_recompute(r)) + contention * min(T_load, T_recompute(r)).  Loading pays when
+ * T_layer(r_min) < t_full_layer; then ratio = (T_load - t_fixed_layer) / (t_full_layer -
+ * t_fixed_layer) clamped to [r_min, r_max] (the recompute the load hides) and T_layer =
+ * T_layer(ratio); otherwise load = 0,
+ * ratio = 1, T_layer = t_full_layer, t_load_layer = 0.  The first layer recomputes every row in
+ * either case; when loading, the next layer, the first to filter (it scores every context row),
+ * adds t_select_layer over a later layer: t_total = t_first_layer + t_select_layer + (n_layers -
+ * 1) * T_layer (t_first_layer + (n_layers - 1) * t_full_layer when not loading).
+ * break_even_bandwidth = kv_bytes_layer / t_full_layer.  CB_EINVAL for non-positive sizes,
+ * bandwidth or t_full_layer, negative latency, t_first_layer, t_select_layer or contention,
+ * t_fixed_layer outside [0, t_full_layer], or ratios outside 0 <= r_min <= r_max <= 1. */
 cb_status cb_plan_ratio_measured(int32_t n_layers, double kv_bytes_layer, double bandwidth, double latency_layer_s,
-                                 double t_first_layer, double t_full_layer, double t_fixed_layer, float r_min,
-                                 float r_max, cb_ratio_plan* out);
+                                 double t_first_layer, double t_select_layer, double t_full_layer,
+                                 double t_fixed_layer, double contention, float r_min, float r_max,
+                                 cb_ratio_plan* out);
 
 /* ---------------------------------------------------------------- chunk KV store
  * The offline side of the path: every chunk is prefilled alone at positions 0.. (CacheBlend

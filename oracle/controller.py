@@ -19,6 +19,16 @@ ratio-independent part and the full first layer); the planned ratio is the large
 recompute still hides under the layer's load, kept inside [r_min, r_max] (the quality floor
 and the point past which recompute cannot hide); when the bandwidth is at or below break-even
 the plan is to recompute everything and load nothing.
+
+Beyond the pages (plan_ratio_measured only; both terms default to zero, which is the model
+above): the review's max(T_load, T_recompute) assumes the load and the recompute do not slow
+each other; measured on one GPU the fetch of a later layer stretches the compute it runs
+beside, by a measured `contention` (seconds of compute added per second of fetch running
+beside it, and the same for the fetch when the compute runs beside it), so a layer takes
+max(T_load, T_rec) + contention * min(T_load, T_rec); and the first filtering layer, which
+scores every context row, costs a measured t_select over a later layer at the same ratio (the
+review's "filling the pipeline").  The planned ratio stays the pages' rule (recompute as much
+as the load hides).
 """
 from __future__ import annotations
 
@@ -70,17 +80,23 @@ def plan_ratio(n_ctx: int, n_layers: int, kv_bytes_per_token_layer: float, bandw
 
 def plan_ratio_measured(n_layers: int, kv_bytes_layer: float, bandwidth: float, t_first_layer: float,
                         t_full_layer: float, t_fixed_layer: float, r_min: float, r_max: float,
-                        latency_layer: float = 0.0) -> Plan:
+                        latency_layer: float = 0.0, t_select_layer: float = 0.0,
+                        contention: float = 0.0) -> Plan:
     """The same policy with a layer's recompute time measured on the GPU instead of an even
     split of the full prefill.  Reading: the explainer's T_recompute = r * T_prefill, taken per
     layer with a ratio-independent part added, T_recompute(r) = t_fixed + r (t_full - t_fixed)
     (t_full: a layer recomputing every row; t_fixed: a layer recomputing none, i.e. the query
     rows, norms, attention over the cache and the fixed kernel costs); t_fixed = 0 is the
-    explainer's model.  Loading pays when a layer's load, and the least recompute allowed,
-    both take less than recomputing the layer: max(T_load, T_recompute(r_min)) < t_full.  The
-    first layer recomputes every row whatever the plan (layer 1 scores all tokens), so the step
-    is t_first + (L - 1) T_layer.  break_even: the bandwidth at which a layer's load (latency
-    aside) takes t_full."""
+    explainer's model.  With a load beside it a layer takes
+    T_layer(r) = max(T_load, T_recompute(r)) + contention * min(T_load, T_recompute(r)): the
+    longer of the two is stretched by the overlap with the other.  Loading pays when
+    T_layer(r_min) < t_full (a layer that loads nothing recomputes every row with no fetch
+    beside it).  The ratio is the largest in [r_min, r_max] whose recompute fits under the load,
+    T_recompute(r) = T_load, as in plan_ratio.  The first
+    layer recomputes every row whatever the plan (layer 1 scores all tokens), and when loading
+    the next one, the first to filter, adds t_select: the step is
+    t_first + t_select + (L - 1) T_layer.  break_even: the bandwidth at which a layer's load
+    (latency aside) takes t_full."""
     be = kv_bytes_layer / t_full_layer
     tl = t_load(1, kv_bytes_layer, bandwidth, latency_layer)
     slope = t_full_layer - t_fixed_layer
@@ -88,10 +104,13 @@ def plan_ratio_measured(n_layers: int, kv_bytes_layer: float, bandwidth: float, 
     def rec(r):
         return t_fixed_layer + r * slope
 
-    if max(tl, rec(r_min)) >= t_full_layer:
+    def layer(r):
+        tr = rec(r)
+        return max(tl, tr) + contention * min(tl, tr)
+
+    if layer(r_min) >= t_full_layer:
         return Plan(False, 1.0, 0.0, t_full_layer, t_full_layer,
                     t_first_layer + (n_layers - 1) * t_full_layer, be)
     r = (tl - t_fixed_layer) / slope
     r = min(max(r, r_min), r_max)
-    tr = rec(r)
-    return Plan(True, r, tl, tr, t_layer(tl, tr), t_first_layer + (n_layers - 1) * t_layer(tl, tr), be)
+    return Plan(True, r, tl, rec(r), layer(r), t_first_layer + t_select_layer + (n_layers - 1) * layer(r), be)

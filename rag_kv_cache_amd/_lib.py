@@ -83,7 +83,7 @@ _SIGS = {
     "cb_seam_select": [C.POINTER(_I), _I, _I, _I, C.POINTER(_I), _I, C.POINTER(_I)],
     "cb_plan_ratio": [_I, _I, C.c_double, C.c_double, C.c_double, C.c_double, C.c_float, C.c_float, _P],
     "cb_plan_ratio_measured": [_I, C.c_double, C.c_double, C.c_double, C.c_double, C.c_double, C.c_double,
-                               C.c_float, C.c_float, _P],
+                               C.c_double, C.c_double, C.c_float, C.c_float, _P],
     "cb_sha256": [_P, C.c_size_t, _P],
     "cb_chunk_key": [_P, _I, _P, _I, C.POINTER(C.c_uint64)],
     "cb_store_create": [C.POINTER(cb_model_desc), _I, _I, _I, C.POINTER(_P)],
@@ -273,10 +273,11 @@ def cb_plan_ratio(n_ctx: int, n_layers: int, kv_bytes_per_token_layer: float, ba
 
 def cb_plan_ratio_measured(n_layers: int, kv_bytes_layer: float, bandwidth: float, latency_layer_s: float,
                            t_first_layer: float, t_full_layer: float, t_fixed_layer: float, r_min: float,
-                           r_max: float) -> cb_ratio_plan:
+                           r_max: float, t_select_layer: float = 0.0, contention: float = 0.0) -> cb_ratio_plan:
     out = cb_ratio_plan()
     _check(_L.cb_plan_ratio_measured(n_layers, kv_bytes_layer, bandwidth, latency_layer_s, t_first_layer,
-                                     t_full_layer, t_fixed_layer, r_min, r_max, C.byref(out)))
+                                     t_select_layer, t_full_layer, t_fixed_layer, contention, r_min, r_max,
+                                     C.byref(out)))
     return out
 
 

@@ -882,29 +882,33 @@ cb_status cb_plan_ratio(int32_t n_ctx, int32_t n_layers, double kvb, double bw, 
 }
 
 cb_status cb_plan_ratio_measured(int32_t n_layers, double kv_bytes_layer, double bw, double lat, double t_first,
-                                 double t_full, double t_fixed, float r_min, float r_max, cb_ratio_plan* out) {
+                                 double t_select, double t_full, double t_fixed, double contention, float r_min,
+                                 float r_max, cb_ratio_plan* out) {
   if (!out) return fail(CB_EINVAL, "out is NULL");
-  if (n_layers <= 0 || !(kv_bytes_layer > 0) || !(bw > 0) || !(lat >= 0) || !(t_first >= 0) || !(t_full > 0) ||
-      !(t_fixed >= 0) || !(t_fixed <= t_full))
-    return fail(CB_EINVAL, "need n_layers, bytes, bandwidth, t_full > 0, latency, t_first >= 0, 0 <= t_fixed <= t_full");
+  if (n_layers <= 0 || !(kv_bytes_layer > 0) || !(bw > 0) || !(lat >= 0) || !(t_first >= 0) || !(t_select >= 0) ||
+      !(t_full > 0) || !(t_fixed >= 0) || !(t_fixed <= t_full) || !(contention >= 0))
+    return fail(CB_EINVAL, "need n_layers, bytes, bandwidth, t_full > 0, latency, t_first, t_select, contention >= 0, "
+                           "0 <= t_fixed <= t_full");
   if (!(r_min >= 0.f) || !(r_max >= r_min) || !(r_max <= 1.f)) return fail(CB_EINVAL, "need 0 <= r_min <= r_max <= 1");
   const double slope = t_full - t_fixed;
   const double tl = kv_bytes_layer / bw + lat;
+  auto layer = [&](double tr) { return std::max(tl, tr) + contention * std::min(tl, tr); };
   cb_ratio_plan p{};
   p.break_even_bandwidth = kv_bytes_layer / t_full;
-  if (std::max(tl, t_fixed + (double)r_min * slope) >= t_full) {  // loading cannot beat recomputing the layer
+  if (layer(t_fixed + (double)r_min * slope) >= t_full) {  // loading cannot beat recomputing the layer
     p.load = 0;
     p.ratio = 1.f;
     p.t_recompute_layer = p.t_layer = t_full;
+    p.t_total = t_first + (double)(n_layers - 1) * p.t_layer;
   } else {
     p.load = 1;
     p.t_load_layer = tl;
     const double r = std::min<double>(std::max<double>((tl - t_fixed) / slope, r_min), r_max);
     p.ratio = (float)r;
     p.t_recompute_layer = t_fixed + r * slope;
-    p.t_layer = std::max(tl, p.t_recompute_layer);
+    p.t_layer = layer(p.t_recompute_layer);
+    p.t_total = t_first + t_select + (double)(n_layers - 1) * p.t_layer;
   }
-  p.t_total = t_first + (double)(n_layers - 1) * p.t_layer;
   *out = p;
   return CB_OK;
 }

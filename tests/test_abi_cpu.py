@@ -121,8 +121,12 @@ def test_plan_ratio_measured_matches_oracle():
         lat = float(rng.choice([0.0, 1e-5]))
         r_min = float(np.float32(rng.uniform(0, 0.3)))
         r_max = float(np.float32(rng.uniform(r_min, 1.0)))
-        got = L.cb_plan_ratio_measured(nl, kvb, bw, lat, t_first, t_full, t_fix, r_min, r_max)
-        ref = C.plan_ratio_measured(nl, kvb, bw, t_first, t_full, t_fix, r_min, r_max, latency_layer=lat)
+        t_sel = float(rng.choice([0.0, rng.uniform(0, 0.5) * t_full]))
+        k = float(rng.choice([0.0, rng.uniform(0, 0.6)]))
+        got = L.cb_plan_ratio_measured(nl, kvb, bw, lat, t_first, t_full, t_fix, r_min, r_max,
+                                       t_select_layer=t_sel, contention=k)
+        ref = C.plan_ratio_measured(nl, kvb, bw, t_first, t_full, t_fix, r_min, r_max, latency_layer=lat,
+                                    t_select_layer=t_sel, contention=k)
         assert bool(got.load) == ref.load
         assert abs(got.ratio - ref.ratio) <= 1e-6 * max(1.0, ref.ratio)
         for f in ("t_load_layer", "t_recompute_layer", "t_layer", "t_total"):
@@ -133,3 +137,6 @@ def test_plan_ratio_measured_matches_oracle():
                 (4, 1e6, 1e9, 0.0, 1e-3, 1e-3, 0.0, 0.6, 0.5)]:
         with pytest.raises(L.CbError):
             L.cb_plan_ratio_measured(*bad)
+    for kw in ({"t_select_layer": -1e-3}, {"contention": -0.1}):
+        with pytest.raises(L.CbError):
+            L.cb_plan_ratio_measured(4, 1e6, 1e9, 0.0, 1e-3, 1e-3, 0.0, 0.1, 0.5, **kw)

@@ -135,3 +135,51 @@ def test_measured_plan_special_cases():
     # raises the ratio to its ceiling and the layer takes the load time
     p = C.plan_ratio_measured(32, 16e-3 * 1e9, 1e9, 20e-3, 20e-3, 0.0, 0.15, 0.5)
     assert p.load and p.ratio == 0.5 and abs(p.t_layer - 16e-3) < 1e-15
+
+
+def test_contended_plan_against_a_grid_search():
+    # with contention k a loading layer takes max(T_load, T_rec) + k min(T_load, T_rec); the ratio
+    # is still the largest on a fine grid whose recompute fits under the load (else r_min), and
+    # the plan loads only when that layer time at r_min beats recomputing the layer
+    rng = np.random.default_rng(11)
+    grid = np.linspace(0.0, 1.0, 100001)
+    for _ in range(200):
+        t_full = float(rng.uniform(0.2e-3, 2e-3))
+        t_fix = float(rng.uniform(0, 0.6)) * t_full
+        tl = float(rng.uniform(0.3, 1.2)) * t_full
+        k = float(rng.uniform(0.0, 0.5))
+        t_sel = float(rng.uniform(0.0, 0.3)) * t_full
+        r_min, r_max = 0.05, 0.8
+        p = C.plan_ratio_measured(28, tl * 40e9, 40e9, 1e-3, t_full, t_fix, r_min, r_max,
+                                  t_select_layer=t_sel, contention=k)
+        rec = t_fix + grid * (t_full - t_fix)
+        tr_min = t_fix + r_min * (t_full - t_fix)
+        if max(tl, tr_min) + k * min(tl, tr_min) >= t_full:
+            assert not p.load and p.ratio == 1.0 and p.t_layer == t_full
+            assert abs(p.t_total - (1e-3 + 27 * t_full)) <= 1e-12 * p.t_total
+            continue
+        ok = grid[(rec <= tl) & (grid >= r_min) & (grid <= r_max)]
+        want = ok.max() if len(ok) else r_min
+        assert p.load and abs(p.ratio - want) <= 1.01e-5
+        tr = t_fix + p.ratio * (t_full - t_fix)
+        assert abs(p.t_layer - (max(tl, tr) + k * min(tl, tr))) <= 1e-15 + 1e-12 * p.t_layer
+        assert abs(p.t_total - (1e-3 + t_sel + 27 * p.t_layer)) <= 1e-15 + 1e-12 * p.t_total
+
+
+def test_contended_plan_worked_cases():
+    # hand-worked: load 1 ms, t_fixed 0.2 ms, t_full 2.2 ms (slope 2 ms), contention 0.25:
+    # r = (1 - 0.2) / 2 = 0.4, T_rec = 1 ms, T_layer = max(1, 1) + 0.25 * 1 = 1.25 ms;
+    # 10 layers, first 3 ms, first filter +0.5 ms: 3 + 0.5 + 9 * 1.25 = 14.75 ms
+    p = C.plan_ratio_measured(10, 1e6, 1e9, 3e-3, 2.2e-3, 0.2e-3, 0.05, 0.9, t_select_layer=0.5e-3, contention=0.25)
+    assert p.load and abs(p.ratio - 0.4) < 1e-12 and abs(p.t_layer - 1.25e-3) < 1e-15
+    assert abs(p.t_total - 14.75e-3) < 1e-15
+    # a light load under the ratio floor 0.5: T_rec = 1.2 ms, T_layer = 1.2 + 0.25 * 0.1 = 1.225 ms
+    p = C.plan_ratio_measured(10, 1e5, 1e9, 3e-3, 2.2e-3, 0.2e-3, 0.5, 0.9, contention=0.25)
+    assert p.load and p.ratio == 0.5 and abs(p.t_layer - 1.225e-3) < 1e-15
+    # contention that makes the floor's layer slower than recomputing: floor 0.9 -> T_rec 2.0 ms,
+    # T_layer = 2.0 + 0.5 * 1.0 = 2.5 ms >= 2.2 ms: recompute everything, no first-filter cost
+    p = C.plan_ratio_measured(10, 1e6, 1e9, 3e-3, 2.2e-3, 0.2e-3, 0.9, 1.0, t_select_layer=0.5e-3, contention=0.5)
+    assert not p.load and p.ratio == 1.0 and abs(p.t_total - (3e-3 + 9 * 2.2e-3)) < 1e-15
+    # the same without contention loads (T_layer = max(1, 2.0) = 2.0 < 2.2)
+    p = C.plan_ratio_measured(10, 1e6, 1e9, 3e-3, 2.2e-3, 0.2e-3, 0.9, 1.0)
+    assert p.load and p.ratio == 0.9 and abs(p.t_layer - 2.0e-3) < 1e-15
