@@ -93,6 +93,9 @@ typedef struct cb_ctx cb_ctx;
  * cos/sin table for positions 0 .. max_tokens-1 in double precision (stored fp32). */
 cb_status cb_create(const cb_model_desc* desc, int32_t device, void* compute_stream,
                     void* copy_stream, cb_ctx** out);
+/* Synchronize the context's streams, then free its events and tables and the context itself,
+ * whatever fails along the way; CB_EHIP reports the first HIP error met (a stream that could
+ * not be synchronized, e.g. after a device fault).  NULL is a no-op. */
 cb_status cb_destroy(cb_ctx* ctx);
 
 /* Register the weights of `layer`.  Must precede cb_blend_layer / cb_layer_rest on it. */
@@ -416,7 +419,8 @@ typedef struct cb_store cb_store;
  * arena cannot be allocated. */
 cb_status cb_store_create(const cb_model_desc* desc, int32_t max_chunk_tokens, int32_t n_slots, int32_t pinned,
                           cb_store** out);
-/* Frees the arena.  Copies into or out of it must have completed. */
+/* Frees the arena and the store.  Copies into or out of it must have completed.  CB_EHIP if
+ * freeing the pinned arena fails (the store is released all the same). */
 cb_status cb_store_destroy(cb_store* store);
 
 /* Slot of the committed entry whose tokens and prior keys equal these (key match verified

@@ -175,10 +175,12 @@ struct Timed {
     c->recs.push_back(ProfRec{kernel, work, c->ev_pool[c->ev_used], c->ev_pool[c->ev_used + 1]});
     c->ev_used += 2;
     rec = &c->recs.back();
-    hipEventRecord(rec->start, st);
+    // profiling is best effort: a failed record leaves this launch untimed (cb_profile_read
+    // then reports the events' own error), it does not fail the launch it brackets
+    (void)hipEventRecord(rec->start, st);
   }
   ~Timed() {
-    if (rec) hipEventRecord(rec->stop, st);
+    if (rec) (void)hipEventRecord(rec->stop, st);
   }
 };
 
@@ -289,17 +291,24 @@ cb_status cb_create(const cb_model_desc* desc, int32_t device, void* compute_str
 
 cb_status cb_destroy(cb_ctx* c) {
   if (!c) return CB_OK;
-  hipSetDevice(c->device);
-  if (c->cs) hipStreamSynchronize(c->cs);
-  if (c->xs && c->xs != c->cs) hipStreamSynchronize(c->xs);
-  if (!c->cs) hipDeviceSynchronize();
+  // everything is released whatever fails; the first failure is reported (a stream that
+  // cannot be synchronized, e.g. after a device fault, shows up here)
+  hipError_t first = hipSuccess;
+  auto note = [&](hipError_t e) {
+    if (e != hipSuccess && first == hipSuccess) first = e;
+  };
+  note(hipSetDevice(c->device));
+  if (c->cs) note(hipStreamSynchronize(c->cs));
+  if (c->xs && c->xs != c->cs) note(hipStreamSynchronize(c->xs));
+  if (!c->cs) note(hipDeviceSynchronize());
   for (hipEvent_t ev : c->fetch_ev)
-    if (ev) hipEventDestroy(ev);
-  for (hipEvent_t ev : c->ev_pool) hipEventDestroy(ev);
+    if (ev) note(hipEventDestroy(ev));
+  for (hipEvent_t ev : c->ev_pool) note(hipEventDestroy(ev));
   for (hipEvent_t ev : c->release_ev)
-    if (ev) hipEventDestroy(ev);
-  if (c->rope) hipFree(c->rope);
+    if (ev) note(hipEventDestroy(ev));
+  if (c->rope) note(hipFree(c->rope));
   delete c;
+  if (first != hipSuccess) return hip_fail(first, "cb_destroy (resources released)");
   return CB_OK;
 }
 

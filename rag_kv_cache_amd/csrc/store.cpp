@@ -294,11 +294,13 @@ cb_status cb_store_create(const cb_model_desc* d, int32_t max_chunk_tokens, int3
 
 cb_status cb_store_destroy(cb_store* s) {
   if (!s) return CB_OK;
+  hipError_t e = hipSuccess;
   if (s->arena) {
-    if (s->pinned) hipHostFree(s->arena);
+    if (s->pinned) e = hipHostFree(s->arena);
     else std::free(s->arena);
   }
   delete s;
+  if (e != hipSuccess) return cbi_fail(CB_EHIP, "hipHostFree (store arena): %s", hipGetErrorString(e));
   return CB_OK;
 }
 
