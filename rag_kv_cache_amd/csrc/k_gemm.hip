@@ -165,7 +165,7 @@ constexpr int gemm_f32_halves() {
 // K-step ahead, is converted to bf16 (exact) and written to the same LDS layout, so the MFMA
 // loop is unchanged; the scale multiplies the fp32 sums before the epilogue (split-K: in the
 // reduce).
-template <int BM, int BN, int WM, int WN, int NS, int EPI, int BT>
+template <int BM, int BN, int WM, int WN, int NS, int EPI, int BT, int XB = 0>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2))) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -177,6 +177,7 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
   constexpr int LPW = A_PW + B_PW;                   // load instructions per wave per K-step
   static_assert(FN % 2 == 0 && A_INS % NW == 0 && B_INS % NW == 0, "tile shape");
   static_assert(NS >= 2 && NS <= 8, "stages");
+  static_assert(XB == 0 || (XB == 1 && BT == 0), "a deeper weight ring: bf16 weights only");
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int tiles_m = (g.M + BM - 1) / BM;
@@ -306,6 +307,75 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
   // stage was read for the last time before iteration t's barrier and is next read in
   // iteration t+NS > t+1.
   constexpr int LPWD = BT ? A_PW : LPW;  // DMA instructions per wave per K-step
+  if constexpr (XB == 1) {
+    // A deeper weight ring: NS stages of the activation tile, NS + 1 of the weight tile, in
+    // two separate rings (activations first, then weights).  Weight K-step t + NS + 1 is issued
+    // in iteration t, after the activation K-step t + NS, so each weight load gets one more
+    // iteration to land; the wait before the barrier of iteration t leaves only the weight
+    // loads of K-step t + 2 in flight (issued after the activations of K-step t + 1).
+    constexpr int NSB = NS + 1;
+    constexpr int SA_B = BM * ROWB, SB_B = BN * ROWB;
+    unsigned char* const ra = smem;
+    unsigned char* const rbw = smem + NS * SA_B;
+    auto issue_a = [&](int kt, int sa) __attribute__((always_inline)) {
+      unsigned char* base = ra + sa * SA_B;
+#pragma unroll
+      for (int i = 0; i < A_PW; ++i) buffer_load_lds16(g.A, a_bytes, base + (wv * A_PW + i) * 1024, a_vo[i], kt * BK * 2);
+    };
+    auto issue_b = [&](int kt, int sb) __attribute__((always_inline)) {
+      unsigned char* base = rbw + sb * SB_B;
+#pragma unroll
+      for (int i = 0; i < B_PW; ++i) buffer_load_lds16(g.B, b_bytes, base + (wv * B_PW + i) * 1024, b_vo[i], kt * BK * 2);
+    };
+    const int b_roff = (wn * WTN + fr) * ROWB;  // fragment row of the weight tile within a stage
+    auto readx = [&](int sa, int sb, int ks, bf16x8_t (&af)[FM], bf16x8_t (&bfr)[FN]) __attribute__((always_inline)) {
+      const unsigned char* pa = ra + sa * SA_B + (ks ? sw1 : sw0);
+      const unsigned char* pb = rbw + sb * SB_B + (ks ? sw1 : sw0);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(pa + a_off + i * 16 * ROWB);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(pb + b_roff + j * 16 * ROWB);
+    };
+#pragma unroll
+    for (int s = 0; s < NSB; ++s) {
+      if (s < NS && s < nk) issue_a(s, s);
+      if (s < nk) issue_b(s, s);
+    }
+    wait_vm<0>();
+    barrier();
+    bf16x8_t a0[FM], b0[FN], a1[FM], b1[FN];
+    readx(0, 0, 0, a0, b0);
+    int sa = 0, sb = 0, t = 0;
+    for (; t + NSB < nk; ++t) {
+      readx(sa, sb, 1, a1, b1);
+      mma(a0, b0);
+      wait_lgkm0();
+      wait_vm<Sat63<B_PW>::v>();  // K-step t+1 landed (weights of t+2 may be in flight)
+      barrier();
+      issue_a(t + NS, sa);
+      issue_b(t + NSB, sb);
+      sa = sa + 1 == NS ? 0 : sa + 1;
+      sb = sb + 1 == NSB ? 0 : sb + 1;
+      readx(sa, sb, 0, a0, b0);
+      mma(a1, b1);
+    }
+    for (; t + 1 < nk; ++t) {  // the last NS K-steps: refill what remains, wait for everything
+      readx(sa, sb, 1, a1, b1);
+      mma(a0, b0);
+      wait_lgkm0();
+      wait_vm<0>();
+      barrier();
+      if (t + NS < nk) issue_a(t + NS, sa);
+      if (t + NSB < nk) issue_b(t + NSB, sb);
+      sa = sa + 1 == NS ? 0 : sa + 1;
+      sb = sb + 1 == NSB ? 0 : sb + 1;
+      readx(sa, sb, 0, a0, b0);
+      mma(a1, b1);
+    }
+    readx(sa, sb, 1, a1, b1);
+    mma(a0, b0);
+    mma(a1, b1);
+  } else {
 #pragma unroll
   for (int s = 0; s < NS; ++s)
     if (s < nk) issue(s, s);
@@ -368,6 +438,7 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
   read(st, 1, a1, b1);
   mma(a0, b0);
   mma(a1, b1);
+  }
   if constexpr (BT) {  // per-output-channel weight scales (split-K partials stay unscaled)
     if (g.splits == 1) {
 #pragma unroll
@@ -526,19 +597,19 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
 
 // LDS bytes one launch needs: the operand ring, or the staged output tile if larger (an fp32
 // tile in row halves when whole it would exceed the LDS).
-template <int BM, int BN, int NS, int EPI>
+template <int BM, int BN, int NS, int EPI, int XB = 0>
 constexpr int gemm_lds_bytes(bool f32_out) {
-  constexpr int ring = NS * (BM + BN) * BK * 2;
+  constexpr int ring = NS * (BM + BN) * BK * 2 + XB * BN * BK * 2;
   const int stage = f32_out ? (BM / gemm_f32_halves<BM, BN>()) * (BN * 4 + 16)
                             : BM * ((EPI == EPI_SWIGLU ? BN / 2 : BN) * 2 + 16);
   return ring > stage ? ring : stage;
 }
 
-template <int BM, int BN, int WM, int WN, int NS, int EPI, int BT>
+template <int BM, int BN, int WM, int WN, int NS, int EPI, int BT, int XB = 0>
 hipError_t launch_dma(const GemmArgs& g, hipStream_t s) {
   constexpr int kMaxLds = 160 * 1024;
-  static_assert(NS * (BM + BN) * BK * 2 <= kMaxLds, "LDS");
-  const int lds = gemm_lds_bytes<BM, BN, NS, EPI>(g.splits > 1 || EPI == EPI_RESID);
+  static_assert(NS * (BM + BN) * BK * 2 + XB * BN * BK * 2 <= kMaxLds, "LDS");
+  const int lds = gemm_lds_bytes<BM, BN, NS, EPI, XB>(g.splits > 1 || EPI == EPI_RESID);
   if (lds > kMaxLds || g.N % BN != 0 || g.splits < 1 || g.splits > g.K / BK) return hipErrorInvalidValue;
   // operand byte offsets are 32-bit buffer offsets
   const long a_rows = g.a_rows_total ? g.a_rows_total : g.M;
@@ -546,14 +617,14 @@ hipError_t launch_dma(const GemmArgs& g, hipStream_t s) {
   if (BT && (!g.bscale || g.ldb % 16 != 0)) return hipErrorInvalidValue;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<BM, BN, WM, WN, NS, EPI, BT>,
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<BM, BN, WM, WN, NS, EPI, BT, XB>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int tiles = ((g.M + BM - 1) / BM) * (g.N / BN);
   const int grid_x = 8 * ((tiles + 7) / 8);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, NS, EPI, BT>), dim3(grid_x, g.splits), dim3(64 * WM * WN), lds, s, g);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, NS, EPI, BT, XB>), dim3(grid_x, g.splits), dim3(64 * WM * WN), lds, s, g);
   return hipGetLastError();
 }
 
@@ -963,8 +1034,15 @@ hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
       // sixteen wavefronts (four per SIMD, 64 x 64 each) hide more of the operand-load latency
       // than eight (128 x 64 each: 2-8% slower on the FFN products); the int8 weight path needs
       // the eight-wavefront register budget
-      if constexpr (BT == 0) e = launch_dma<256, 256, 4, 4, 2, EPI, BT>(g, s);
-      else e = launch_dma<256, 256, 2, 4, 2, EPI, BT>(g, s);
+      if constexpr (BT == 0) {
+        // up to 4096 rows the weight tile gets a third stage (the 160 KiB of LDS hold 2
+        // activation and 3 weight stages): steady 70B gate/up 2021 -> 1982 us, down 1338 ->
+        // 1261 us; at 16640 rows the two-stage ring is 2% faster
+        if (g.M <= 4096) e = launch_dma<256, 256, 4, 4, 2, EPI, BT, 1>(g, s);
+        else e = launch_dma<256, 256, 4, 4, 2, EPI, BT, 0>(g, s);
+      } else {
+        e = launch_dma<256, 256, 2, 4, 2, EPI, BT>(g, s);
+      }
       break;
     case GEMM_128x256: e = launch_dma<128, 256, 2, 4, 3, EPI, BT>(g, s); break;
     case GEMM_64x256: e = launch_dma<64, 256, 1, 4, 3, EPI, BT>(g, s); break;
