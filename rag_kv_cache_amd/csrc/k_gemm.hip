@@ -177,7 +177,7 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
   constexpr int LPW = A_PW + B_PW;                   // load instructions per wave per K-step
   static_assert(FN % 2 == 0 && A_INS % NW == 0 && B_INS % NW == 0, "tile shape");
   static_assert(NS >= 2 && NS <= 8, "stages");
-  static_assert(XB == 0 || (XB == 1 && BT == 0), "a deeper weight ring: bf16 weights only");
+  static_assert(XB == 0 || (XB >= 1 && XB <= 4 && BT == 0), "a deeper weight ring: bf16 weights only");
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int tiles_m = (g.M + BM - 1) / BM;
@@ -308,12 +308,14 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
   // iteration t+NS > t+1.
   constexpr int LPWD = BT ? A_PW : LPW;  // DMA instructions per wave per K-step
   if constexpr (XB == 1) {
-    // A deeper weight ring: NS stages of the activation tile, NS + 1 of the weight tile, in
-    // two separate rings (activations first, then weights).  Weight K-step t + NS + 1 is issued
-    // in iteration t, after the activation K-step t + NS, so each weight load gets one more
-    // iteration to land; the wait before the barrier of iteration t leaves only the weight
-    // loads of K-step t + 2 in flight (issued after the activations of K-step t + 1).
-    constexpr int NSB = NS + 1;
+    // A deeper weight ring: NS stages of the activation tile, NS + XB of the weight tile, in
+    // two separate rings (activations first, then weights).  Weight K-step t + NS + XB is
+    // issued in iteration t, after the activation K-step t + NS, so each weight load gets XB
+    // more iterations to land; the wait before the barrier of iteration t must see the
+    // activations of K-step t + 1 (issued in iteration t + 1 - NS): what was issued after them
+    // may still be in flight, i.e. that iteration's weights and the NS - 2 later iterations'
+    // loads (the weights of K-step t + 1 were issued XB iterations before its activations).
+    constexpr int NSB = NS + XB;
     constexpr int SA_B = BM * ROWB, SB_B = BN * ROWB;
     unsigned char* const ra = smem;
     unsigned char* const rbw = smem + NS * SA_B;
@@ -350,7 +352,7 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)
       readx(sa, sb, 1, a1, b1);
       mma(a0, b0);
       wait_lgkm0();
-      wait_vm<Sat63<B_PW>::v>();  // K-step t+1 landed (weights of t+2 may be in flight)
+      wait_vm<Sat63<B_PW + (NS - 2) * LPW>::v>();  // K-step t+1 landed
       barrier();
       issue_a(t + NS, sa);
       issue_b(t + NSB, sb);
