@@ -20,7 +20,7 @@ and a decode step on the fused KV is checked layer by layer the same way.
 
 Row blocks of the attention run on a thread pool with single-threaded BLAS: each query row's
 output depends only on its own query and the keys, so the blocks are the oracle's function on
-a subset of rows.  The bf16 bar is the benchmark spec's (max-abs 2e-2 / rel 1e-2) throughout.
+a subset of rows.  The bf16 bar is the fixed max-abs 2e-2 / rel 1e-2 throughout.
 """
 from __future__ import annotations
 
