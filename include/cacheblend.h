@@ -152,13 +152,13 @@ cb_status cb_embed(cb_ctx* ctx, const int32_t* tokens, int32_t n, const void* ta
  * the copy engine.  CB_FETCH_COPY: always the copy engine, then the rotation in place; chunks
  * whose host rows follow one another (host_k[c + 1] starts where chunk c's K rows end, and the
  * same for V) go as one hipMemcpyAsync per run of such chunks.  CB_FETCH_AUTO (default): the
- * copy engine when those copies average at least 1 MiB, else as CB_FETCH_KERNEL.  The fetch kernel loads faster when the per-copy
- * cost of the copy engine dominates (small chunks: a load-bound layer), but it holds CUs that
- * the compute stream's kernels then lack; large copies amortize that cost, and the copy engine
- * leaves every CU to compute (measured on MI355X: 256 KiB chunks load at about 16 GB/s through
- * the copy engine against 31 GB/s with the kernel; with 1 MiB chunks of a compute-bound layer
- * the prefill ran 2% faster through the copy engine).  Results are identical.  CB_EINVAL for
- * another mode. */
+ * copy engine when those copies average at least 1 MiB, else as CB_FETCH_KERNEL.  The fetch
+ * kernel loads faster when the per-copy cost of the copy engine dominates (small chunks: a
+ * load-bound layer), but it holds CUs that the compute stream's kernels then lack; large copies
+ * amortize that cost, and the copy engine leaves every CU to compute (measured on MI355X: 256
+ * KiB chunks load at about 16 GB/s through the copy engine against 31 GB/s with the kernel;
+ * with 1 MiB chunks of a compute-bound layer the prefill ran 2% faster through the copy
+ * engine).  Results are identical.  CB_EINVAL for another mode. */
 typedef enum { CB_FETCH_COPY = 0, CB_FETCH_KERNEL = 1, CB_FETCH_AUTO = 2 } cb_fetch_mode;
 cb_status cb_set_fetch_mode(cb_ctx* ctx, int32_t mode);
 

@@ -65,7 +65,8 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // loads fastest alone (43 against 31 GB/s): the fetch slows the compute kernels while it runs,
 // and spread over more CUs it slows them more.
 constexpr cb::FetchLaunch kFetchLaunchDefault{8, 512, 2};
-// CB_FETCH_AUTO takes the copy engine from this many bytes per chunk and tensor (K or V) on.
+// CB_FETCH_AUTO takes the copy engine when the copies average this many bytes or more (one copy
+// per run of chunks adjacent in host memory, per tensor K or V).
 constexpr size_t kFetchCopyMinBytes = size_t(1) << 20;
 
 struct cb_ctx {
