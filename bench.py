@@ -345,10 +345,11 @@ def run_controller(eng, buf, tokens, offs, wl, fused, host, full_ms, overlap, st
         over max(T_load, T_recompute), summed, over the summed min(T_load, T_recompute).  The
         contention depends on the operating point (a compute-bound pipeline lets the copy
         stream run ahead and finish early, a balanced one keeps the fetch beside every layer),
-        so it is taken first from the workload's pipelined run, then once more from one
-        pipelined run at the planned ratio (a calibration run, not one of the timed runs), and
-        the plan is made again with it and with the recompute line redrawn through the time
-        measured there.
+        so it is taken first from the workload's pipelined run, then from pipelined runs at the
+        planned ratio (calibration runs, not timed ones): the plan is made again with the
+        contention and the recompute time measured there, and calibrated again at its new ratio
+        until it lands on a ratio already calibrated; the plan's predicted time is the model's
+        at that ratio with that ratio's own calibration.
     Both with a ratio floor of 5% (below the workload's 15%, so that the plan is not just the
     floor) and no ceiling; each plan's prefill is timed alone, like the headline (events from the
     first fetch enqueue to the last layer's end, median of the runs)."""
@@ -420,14 +421,10 @@ def run_controller(eng, buf, tokens, offs, wl, fused, host, full_ms, overlap, st
         return L.cb_plan_ratio_measured(nl, kv_layer, kv_layer / t_load_l, 0.0, t_first, t_full_l, t_fix, r_min,
                                         r_max, t_select_layer=t_select, contention=k)
 
-    meas = plan(contention0, t_fixed_l)
-    contention, t_fixed_c, calib = contention0, t_fixed_l, None
-    if meas.load:
-        # calibration at the planned ratio r0: per-layer times pipelined and alone give the
-        # contention there, and the recompute line is redrawn through (r0, T_recompute alone)
-        # and (1, t_full) (small ratios cost more than the line from ratio 0: tile rounding of
-        # the few kept rows); then the plan is made again
-        r0 = float(meas.ratio)
+    def calibrate(r0):
+        """Per-layer times at ratio r0, pipelined and alone: the contention there, and the
+        recompute line redrawn through (r0, T_recompute alone) and (1, t_full) (small ratios cost
+        more than the line from ratio 0: tile rounding of the few kept rows)."""
         sched = [1.0] + [r0] * (nl - 1)
         t_alone = layer_times(sched)
         rows = []
@@ -438,15 +435,39 @@ def run_controller(eng, buf, tokens, offs, wl, fused, host, full_ms, overlap, st
             eng.compute.synchronize()
             rows.append([evs[i].elapsed_time(evs[i + 1]) for i in range(nl)])
         t_pipe = np.median(np.array(rows), axis=0) * 1e-3
-        contention = contention_of(t_pipe, t_alone)
+        k = contention_of(t_pipe, t_alone)
         t_r0 = float(np.median(t_alone[2:]))
+        t_fix = t_fixed_l
         if r0 < 1.0 and t_r0 < t_full_l:
-            t_fixed_c = max(0.0, t_r0 - r0 * (t_full_l - t_r0) / (1.0 - r0))
+            t_fix = max(0.0, t_r0 - r0 * (t_full_l - t_r0) / (1.0 - r0))
+        return k, t_fix, {"ratio": round(r0, 4), "t_recompute_alone_median_ms": round(t_r0 * 1e3, 4),
+                          "t_layer_pipelined_median_ms": round(float(np.median(t_pipe[2:])) * 1e3, 4),
+                          "sum_pipelined_ms": round(float(t_pipe.sum()) * 1e3, 4),
+                          "t_fixed_layer_redrawn_ms": round(t_fix * 1e3, 4)}
+
+    # calibration at the planned ratio, then the plan is made again with what was measured there,
+    # until the plan lands on a ratio already calibrated (at most four calibrations; the small
+    # ratios' cost steps can make two ratios point at each other).  The plan's time is then the
+    # model's at that ratio with that ratio's own calibration.
+    meas = plan(contention0, t_fixed_l)
+    contention, calibs, cal_at = contention0, [], {}
+    key = lambda r: int(round(r * wl.n_ctx))  # kept context rows
+    while meas.load and len(calibs) < 4:
+        r0 = float(meas.ratio)
+        if key(r0) in cal_at:
+            break
+        contention, t_fixed_c, cal = calibrate(r0)
+        calibs.append(cal)
+        cal_at[key(r0)] = (contention, t_fixed_c, cal)
         meas = plan(contention, t_fixed_c)
-        calib = {"ratio": round(r0, 4), "t_recompute_alone_median_ms": round(t_r0 * 1e3, 4),
-                 "t_layer_pipelined_median_ms": round(float(np.median(t_pipe[2:])) * 1e3, 4),
-                 "sum_pipelined_ms": round(float(t_pipe.sum()) * 1e3, 4),
-                 "t_fixed_layer_redrawn_ms": round(t_fixed_c * 1e3, 4)}
+    calib = None
+    if meas.load and key(float(meas.ratio)) in cal_at:
+        r_star = float(meas.ratio)
+        contention, t_fixed_c, calib = cal_at[key(r_star)]
+        meas = L.cb_plan_ratio_measured(nl, kv_layer, kv_layer / t_load_l, 0.0, t_first, t_full_l, t_fixed_c, r_star,
+                                        r_star, t_select_layer=t_select, contention=contention)
+    elif calibs:
+        calib = calibs[-1]
     meas_ms = run_plan(meas)
     log(f"controller (even split): load {bw / 1e9:.1f} GB/s, ratio {even.ratio:.3f}, predicted "
         f"{even.t_total * 1e3:.3f} ms, measured {even_ms:.3f} ms/step")
@@ -461,7 +482,7 @@ def run_controller(eng, buf, tokens, offs, wl, fused, host, full_ms, overlap, st
                                     t_select_ms=round(t_select * 1e3, 4), t_full_layer_ms=round(t_full_l * 1e3, 4),
                                     t_fixed_layer_ms=round(t_fixed_l * 1e3, 4),
                                     contention_workload_ratio=round(contention0, 4), contention=round(contention, 4),
-                                    calibration_at_plan=calib,
+                                    calibration_at_plan=calib, calibrations=calibs,
                                     prediction_error=round(meas.t_total * 1e3 / meas_ms - 1, 4)),
             "schedule": "1.0, then the planned ratio (pinned-host cache fetched two layers ahead; eager launches; "
                         "each prefill timed alone)"}
