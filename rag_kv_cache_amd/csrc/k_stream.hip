@@ -73,7 +73,38 @@ __device__ __forceinline__ void row_scale_store(const float* x, int d, const flo
   }
 }
 
-template <typename TO>
+// Rows of at most 256 U elements: the whole row in registers, every load in flight at once (the
+// gains with it when GG), one read of the row.
+template <typename TO, int U, bool GG>
+__device__ __forceinline__ void rmsnorm_row_regs(const float* x, int d, const float* g, float eps, TO* o, int lane) {
+  float4 v[U], gg[GG ? U : 1];
+  const int e0 = lane * 4;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (e0 + 256 * u < d) {
+      v[u] = *reinterpret_cast<const float4*>(x + e0 + 256 * u);
+      if constexpr (GG) gg[u] = *reinterpret_cast<const float4*>(g + e0 + 256 * u);
+    }
+  float ss = 0.f;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (e0 + 256 * u < d) ss += sq4(v[u]);
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int e = e0 + 256 * u;
+    if (e < d) {
+      const float4 q = GG ? gg[GG ? u : 0] : *reinterpret_cast<const float4*>(g + e);
+      store4<TO>(o + e, v[u].x * r * q.x, v[u].y * r * q.y, v[u].z * r * q.z, v[u].w * r * q.w);
+    }
+  }
+}
+
+// W = 0: rows up to 2048 wide; W = 1: up to 8192 (128 registers of row, the gains, L2-resident,
+// loaded after the sum; a separate instantiation so that the narrow rows keep their occupancy);
+// W = 2: any width, the row read twice.  The sum of squares has the same order in all three.
+template <typename TO, int W>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, long ldh, int n, int d, const float* g,
                                                       float eps, TO* out) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -81,31 +112,15 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, long ldh, 
   if (row >= n) return;
   const float* x = h + (long)row * ldh;
   TO* o = out + (long)row * d;
-  if (d <= 2048) {  // the row and the gains stay in registers: every load in flight at once
-    float4 v[8], gg[8];
-    const int e0 = lane * 4;
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (e0 + 256 * u < d) {
-        v[u] = *reinterpret_cast<const float4*>(x + e0 + 256 * u);
-        gg[u] = *reinterpret_cast<const float4*>(g + e0 + 256 * u);
-      }
-    float ss = 0.f;
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (e0 + 256 * u < d) ss += sq4(v[u]);
-    ss = wave_sum(ss);
+  if constexpr (W == 0) {
+    rmsnorm_row_regs<TO, 8, true>(x, d, g, eps, o, lane);
+  } else if constexpr (W == 1) {
+    rmsnorm_row_regs<TO, 32, false>(x, d, g, eps, o, lane);
+  } else {
+    const float ss = row_sumsq(x, d, lane);
     const float r = 1.0f / sqrtf(ss / (float)d + eps);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = e0 + 256 * u;
-      if (e < d) store4<TO>(o + e, v[u].x * r * gg[u].x, v[u].y * r * gg[u].y, v[u].z * r * gg[u].z, v[u].w * r * gg[u].w);
-    }
-    return;
+    row_scale_store<TO>(x, d, g, r, o, lane);
   }
-  const float ss = row_sumsq(x, d, lane);
-  const float r = 1.0f / sqrtf(ss / (float)d + eps);
-  row_scale_store<TO>(x, d, g, r, o, lane);
 }
 
 // ---------------------------------------------------------------- RoPE position update
@@ -403,10 +418,13 @@ hipError_t rmsnorm(const float* h, long ldh, int n, int d, const float* g, float
                    hipStream_t s) {
   if (n <= 0) return hipSuccess;
   dim3 grid((n + 3) / 4);
-  if (bf16)
-    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, grid, dim3(256), 0, s, h, ldh, n, d, g, eps, (bf16_t*)out);
-  else
-    hipLaunchKernelGGL(rmsnorm_kernel<float>, grid, dim3(256), 0, s, h, ldh, n, d, g, eps, (float*)out);
+  auto go = [&](auto kb, auto kf) {
+    if (bf16) hipLaunchKernelGGL(kb, grid, dim3(256), 0, s, h, ldh, n, d, g, eps, (bf16_t*)out);
+    else hipLaunchKernelGGL(kf, grid, dim3(256), 0, s, h, ldh, n, d, g, eps, (float*)out);
+  };
+  if (d <= 2048) go(rmsnorm_kernel<bf16_t, 0>, rmsnorm_kernel<float, 0>);
+  else if (d <= 8192) go(rmsnorm_kernel<bf16_t, 1>, rmsnorm_kernel<float, 1>);
+  else go(rmsnorm_kernel<bf16_t, 2>, rmsnorm_kernel<float, 2>);
   return hipGetLastError();
 }
 
