@@ -1,9 +1,11 @@
 """Summaries of rocprofv3 results databases, for the text files kept under profiles/.
 
-    python -m rag_kv_cache_amd.profsummary trace <results.db> [--command ...] [--out file]
-        per kernel symbol: launches, total / average / min / max duration; then, for the
-        kernels of one blended-prefill step (identified by their grid sizes), the average
-        duration per launch over the steps replayed from the HIP graph
+    python -m rag_kv_cache_amd.profsummary trace <results.db> [--steps L,FIRST,COUNT]
+        [--role LABEL=REGEX ...] [--command ...] [--out file]
+        per kernel symbol: launches, total / average / min / max duration; then, with --steps,
+        per kernel the launches and average duration over steps FIRST .. FIRST+COUNT-1 (a step
+        starts at its embedding launch), and per --role the average over those steps' launches
+        whose kernel name matches REGEX
     python -m rag_kv_cache_amd.profsummary traffic <fetch.db> <write.db> --kernel REGEX
         [--calib-grid N --calib-bytes B] [--source FILE] [--command ...] [--out file]
         FETCH_SIZE / WRITE_SIZE per dispatch of the kernels matching REGEX, grouped by grid
@@ -49,9 +51,11 @@ def trace_table(db_path: str) -> str:
     return "\n".join(lines)
 
 
-def step_kernels(db_path: str, n_layers: int, first_step: int, n_steps: int) -> str:
+def step_kernels(db_path: str, n_layers: int, first_step: int, n_steps: int, roles=()) -> str:
     """Per-kernel averages over steps first_step .. first_step+n_steps-1 of a run whose steps each
-    hold exactly n_layers embed-delimited layers; a step starts at an embedding launch."""
+    hold exactly n_layers embed-delimited layers; a step starts at an embedding launch.  roles:
+    (label, regex) pairs; each gets the average over every launch in those steps whose kernel
+    name matches (e.g. one product's launches at every layer, whatever the instantiation)."""
     db = sqlite3.connect(db_path)
     rows = db.execute("select name, duration, grid_x, grid_y, start from kernels order by start").fetchall()
     starts = [i for i, r in enumerate(rows) if "embed_kernel" in r[0]]
@@ -66,6 +70,11 @@ def step_kernels(db_path: str, n_layers: int, first_step: int, n_steps: int) -> 
              f"{'per_step':>8} {'us_per_step':>11} {'avg_us':>9}  kernel"]
     for name, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"{len(v) / n_steps:8.1f} {sum(v) / 1e3 / n_steps:11.2f} {statistics.mean(v) / 1e3:9.2f}  {name[:100]}")
+    for label, rx in roles:
+        v = [dur for name, dur, _, _, _ in rows[lo:hi] if re.search(rx, _short(name))]
+        if v:
+            lines.append(f"role {label}: {len(v) / n_steps:.1f} launches per step, {statistics.mean(v) / 1e3:.2f} us "
+                         f"per launch on average, {sum(v) / 1e3 / n_steps:.2f} us per step (kernels matching {rx!r})")
     return "\n".join(lines)
 
 
@@ -178,6 +187,7 @@ def main() -> int:
     t = sub.add_parser("trace")
     t.add_argument("db")
     t.add_argument("--steps", default="", help="N_LAYERS,FIRST,COUNT: per-step kernel averages")
+    t.add_argument("--role", action="append", default=[], help="LABEL=REGEX: average over a step's matching launches")
     x = sub.add_parser("traffic")
     x.add_argument("fetch_db")
     x.add_argument("write_db")
@@ -206,7 +216,8 @@ def main() -> int:
         text += trace_table(a.db) + "\n"
         if a.steps:
             nl, first, cnt = (int(v) for v in a.steps.split(","))
-            text += "\n" + step_kernels(a.db, nl, first, cnt) + "\n"
+            roles = [tuple(r.split("=", 1)) for r in a.role]
+            text += "\n" + step_kernels(a.db, nl, first, cnt, roles) + "\n"
     elif a.cmd == "counters":
         out = counters(a.dbs, a.kernel, a.cus, a.last, a.xcds, a.label)
         text += (out.splitlines()[-1] if a.only_last else out) + "\n"
