@@ -147,9 +147,11 @@ void plan_gemm(cb::GemmArgs& g, bool bf, long cap_elems) {
   g.splits = p.splits;
 }
 
-// Split-KV: key ranges of 256 keys for the few rows of a decode step, 1024 keys for small kept
-// sets, 2048 for large ones (measured best for
-// the causal row-length mix of the fused prompt), bounded by the partial buffer.
+// Split-KV: key ranges of 64 keys for the few rows of the decode kernel, 256 for up to 64 rows,
+// then 1024, 2048 and 4096 keys from 1200 and 2048 kept rows on (measured best for the causal
+// row-length mix of the fused prompt), fewer ranges when the partial buffer (2048 rows x 16
+// ranges) cannot hold them all: a dense prompt of 16,640 rows (layer 1) runs unsplit, its
+// 520 row blocks x KV heads filling the chip by themselves.
 void attn_splits(int n_q, int n_tok, int group, long cap_rows, int& splits, int& split_len) {
   const bool small = n_q <= kAttnSmallRows;
   const bool few = cb::attn_decode_fits(n_q, group);  // the decode kernel: 64-key ranges, any multiple of 16
