@@ -147,10 +147,10 @@ void plan_gemm(cb::GemmArgs& g, bool bf, long cap_elems) {
   g.splits = p.splits;
 }
 
-// Split-KV: key ranges of 64 keys for the few rows of the decode kernel, 256 for up to 64 rows,
-// then 1024, 2048 and 4096 keys from 1200 and 2048 kept rows on (measured best for the causal
-// row-length mix of the fused prompt), fewer ranges when the partial buffer (2048 rows x 16
-// ranges) cannot hold them all: a dense prompt of 16,640 rows (layer 1) runs unsplit, its
+// Split-KV key ranges: 64 keys for the few rows of the decode kernel, 256 for up to 64 rows,
+// 1024 below 1200 rows, 2048 below 2048 rows and 4096 from there on (measured best for the
+// causal row-length mix of the fused prompt); fewer ranges when the partial buffer (2048 rows x
+// 16 ranges) cannot hold them all, so a dense prompt of 16,640 rows (layer 1) runs unsplit, its
 // 520 row blocks x KV heads filling the chip by themselves.
 void attn_splits(int n_q, int n_tok, int group, long cap_rows, int& splits, int& split_len) {
   const bool small = n_q <= kAttnSmallRows;
