@@ -689,12 +689,10 @@ template <int G, int RB, int QT>
 hipError_t launch_gr(const AttnArgs& a, hipStream_t s) {
   constexpr int lds = ATT_NS * ATT_STAGE_B;
   if ((long)a.n_tok * a.hkv * 128 * 2 >= (1L << 31)) return hipErrorInvalidValue;  // 32-bit buffer offsets
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<G, RB, QT>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // once per process (a function-local static is initialised once, also under concurrent calls)
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)attn_bf16_kernel<G, RB, QT>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
   constexpr int BQ = 16 * RB * QT;
   dim3 grid(((a.n_q + BQ - 1) / BQ) * a.hkv, a.splits);
   hipLaunchKernelGGL((attn_bf16_kernel<G, RB, QT>), grid, dim3(64 * G * QT), lds, s, a);

@@ -13,7 +13,9 @@
 //   * workgroup tile BM x BN x 64 with WM x WN wavefronts, each owning a (BM/WM) x (BN/WN)
 //     block of 16x16 MFMA tiles;
 //   * operands go global -> LDS directly (buffer_load_dwordx4 ... lds, no staging registers) into
-//     a 3-stage ring, two K-steps ahead of the MFMAs; one barrier per K-step;
+//     an NS-stage ring (2 to 4 stages by tile; the 256 x 256 tile up to 4096 rows keeps a third
+//     stage of the weight tile in a ring of its own), so the loads run NS - 1 K-steps (the
+//     weights' one more) ahead of the MFMAs; one barrier per K-step;
 //   * inside each tile the weight rows are permuted in 16-row blocks so that the two
 //     columns of every epilogue pair land in adjacent MFMA tiles: the same lane then holds
 //     both values and the epilogue runs from registers;
@@ -617,13 +619,10 @@ hipError_t launch_dma(const GemmArgs& g, hipStream_t s) {
   const long a_rows = g.a_rows_total ? g.a_rows_total : g.M;
   if (a_rows * g.lda * 2 >= (1L << 31) || (long)g.N * g.ldb * (BT ? 1 : 2) >= (1L << 31)) return hipErrorInvalidValue;
   if (BT && (!g.bscale || g.ldb % 16 != 0)) return hipErrorInvalidValue;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<BM, BN, WM, WN, NS, EPI, BT, XB>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // once per process (a function-local static is initialised once, also under concurrent calls)
+  static const hipError_t attr = hipFuncSetAttribute((const void*)gemm_bf16_kernel<BM, BN, WM, WN, NS, EPI, BT, XB>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+  if (attr != hipSuccess) return attr;
   const int tiles = ((g.M + BM - 1) / BM) * (g.N / BN);
   const int grid_x = 8 * ((tiles + 7) / 8);
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, NS, EPI, BT, XB>), dim3(grid_x, g.splits), dim3(64 * WM * WN), lds, s, g);
