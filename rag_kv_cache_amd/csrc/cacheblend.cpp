@@ -148,14 +148,15 @@ void plan_gemm(cb::GemmArgs& g, bool bf, long cap_elems) {
 }
 
 // Split-KV key ranges: 64 keys for the few rows of the decode kernel, 256 for up to 64 rows,
-// 1024 below 1200 rows, 2048 below 2048 rows and 4096 from there on (measured best for the
-// causal row-length mix of the fused prompt); fewer ranges when the partial buffer (2048 rows x
-// 16 ranges) cannot hold them all, so a dense prompt of 16,640 rows (layer 1) runs unsplit, its
+// 1024 below 1200 rows, 2048 below 2048 rows and 4800 from there on (measured best for the
+// causal row-length mix of the fused prompt: at 2714 rows over 16,640 keys, 4 ranges of 4160
+// keys against 5 of 3328 or 3 of 5568); fewer ranges when the partial buffer (2048 rows x 16
+// ranges) cannot hold them all, so a dense prompt of 16,640 rows (layer 1) runs unsplit, its
 // 520 row blocks x KV heads filling the chip by themselves.
 void attn_splits(int n_q, int n_tok, int group, long cap_rows, int& splits, int& split_len) {
   const bool small = n_q <= kAttnSmallRows;
   const bool few = cb::attn_decode_fits(n_q, group);  // the decode kernel: 64-key ranges, any multiple of 16
-  int len = few ? 64 : (small ? 256 : (n_q < 1200 ? 1024 : (n_q < 2048 ? 2048 : 4096)));
+  int len = few ? 64 : (small ? 256 : (n_q < 1200 ? 1024 : (n_q < 2048 ? 2048 : 4800)));
   int s = (n_tok + len - 1) / len;
   s = std::min(s, small ? kAttnSmallSplits : kAttnMaxSplits);
   while (s > 1 && (long)s * n_q > cap_rows) --s;
